@@ -1,0 +1,220 @@
+"""CPU oracle of the pair-interaction path (float64, plain C, OpenMP over jets).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by
+the CPU-baseline leg of ``bench.py``; never by the product package.  The C
+source (``oracle.c``) is independent of the HIP library: no shared code,
+headers or constants.  Every function here takes numpy arrays, upcasts them
+exactly to float64 and returns float64 results.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+EPS = 1e-8  # feature clamp used by every workload
+
+
+class _Mlp(C.Structure):
+    _fields_ = [
+        ("w1", C.c_void_p), ("b1", C.c_void_p), ("w2", C.c_void_p), ("b2", C.c_void_p),
+        ("w3", C.c_void_p), ("b3", C.c_void_p), ("w4", C.c_void_p), ("b4", C.c_void_p),
+        ("bn_gamma", C.c_void_p * 3), ("bn_beta", C.c_void_p * 3),
+        ("bn_mean", C.c_void_p * 3), ("bn_var", C.c_void_p * 3),
+        ("in_gamma", C.c_void_p), ("in_beta", C.c_void_p),
+        ("in_mean", C.c_void_p), ("in_var", C.c_void_p),
+        ("bn_eps", C.c_double),
+    ]
+
+
+def build(force: bool = True) -> str:
+    from . import build as _b
+    return _b.build(force=force)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        L = C.CDLL(_LIB_PATH)
+        i64, dp, u8p = C.c_int64, C.c_void_p, C.c_void_p
+        L.oracle_num_threads.restype = C.c_int
+        L.oracle_set_num_threads.argtypes = [C.c_int]
+        L.oracle_particle.argtypes = [dp, dp]
+        L.oracle_pair_feature.argtypes = [dp, dp, C.c_double, dp]
+        L.oracle_gelu.argtypes = [C.c_double]
+        L.oracle_gelu.restype = C.c_double
+        L.oracle_mlp_pair.argtypes = [C.POINTER(_Mlp), dp, dp]
+        L.oracle_pair_features.argtypes = [dp, u8p, i64, i64, C.c_double, dp]
+        L.oracle_pair_mlp.argtypes = [dp, u8p, i64, i64, C.POINTER(_Mlp), dp]
+        L.oracle_pair_embed.argtypes = [dp, u8p, i64, i64, C.c_double, C.POINTER(_Mlp), dp]
+        L.oracle_attention.argtypes = [dp, dp, dp, dp, u8p, i64, i64, i64, i64, dp]
+        L.oracle_pair_embed_attention.argtypes = [dp, u8p, i64, i64, C.c_double,
+                                                  C.POINTER(_Mlp), dp, dp, dp, i64, dp]
+        L.oracle_block_stack.argtypes = [dp, dp, dp, dp, dp, dp, u8p, i64, i64, i64, i64,
+                                         i64, dp]
+        for f in ("oracle_pair_features", "oracle_pair_mlp", "oracle_pair_embed",
+                  "oracle_attention", "oracle_pair_embed_attention", "oracle_block_stack"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _u8(m):
+    return np.ascontiguousarray(np.asarray(m) != 0, dtype=np.uint8)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(C.c_void_p) if a is not None else None
+
+
+class _MlpArgs:
+    """Keeps the float64 copies alive while the C struct points at them."""
+
+    def __init__(self, p: dict):
+        self.arrs = {}
+        for k, v in p.items():
+            if isinstance(v, np.ndarray):
+                self.arrs[k] = _f64(v)
+        a = self.arrs
+        s = _Mlp()
+        for i in range(1, 5):
+            setattr(s, f"w{i}", _ptr(a[f"w{i}"]))
+            b = a.get(f"b{i}")
+            setattr(s, f"b{i}", _ptr(b) if b is not None else None)
+        for i in range(3):
+            s.bn_gamma[i] = _ptr(a[f"bn{i + 1}_gamma"])
+            s.bn_beta[i] = _ptr(a[f"bn{i + 1}_beta"])
+            s.bn_mean[i] = _ptr(a[f"bn{i + 1}_mean"])
+            s.bn_var[i] = _ptr(a[f"bn{i + 1}_var"])
+        if "in_gamma" in a:
+            s.in_gamma, s.in_beta = _ptr(a["in_gamma"]), _ptr(a["in_beta"])
+            s.in_mean, s.in_var = _ptr(a["in_mean"]), _ptr(a["in_var"])
+        s.bn_eps = float(p.get("bn_eps", 1e-5))
+        self.struct = s
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
+
+
+def particle(p4) -> np.ndarray:
+    """(pT, y, phi) of one energy-first 4-vector."""
+    p = _f64(p4).reshape(4)
+    out = np.zeros(3)
+    lib().oracle_particle(_ptr(p), _ptr(out))
+    return out
+
+
+def pair_feature(pa, pb, eps: float = EPS) -> np.ndarray:
+    """[ln kT, ln z, ln dR, ln m2] of one pair of 4-vectors."""
+    a, b = _f64(pa).reshape(4), _f64(pb).reshape(4)
+    out = np.zeros(4)
+    lib().oracle_pair_feature(_ptr(a), _ptr(b), float(eps), _ptr(out))
+    return out
+
+
+def gelu(x: float) -> float:
+    return lib().oracle_gelu(float(x))
+
+
+def mlp_pair(params: dict, f4) -> np.ndarray:
+    m = _MlpArgs(params)
+    f = _f64(f4).reshape(4)
+    out = np.zeros(8)
+    lib().oracle_mlp_pair(C.byref(m.struct), _ptr(f), _ptr(out))
+    return out
+
+
+def pair_features(p4, mask, eps: float = EPS) -> np.ndarray:
+    """F (B, 4, P, P) from p4 (B, P, 4) and mask (B, P)."""
+    p = _f64(p4)
+    B, P = p.shape[:2]
+    m = _u8(mask)
+    F = np.zeros((B, 4, P, P))
+    rc = lib().oracle_pair_features(_ptr(p), _ptr(m), B, P, float(eps), _ptr(F))
+    assert rc == 0
+    return F
+
+
+def pair_mlp(F, mask, params: dict) -> np.ndarray:
+    """U (B, 8, P, P) from features F (B, 4, P, P)."""
+    f = _f64(F)
+    B, _, P, _ = f.shape
+    m = _u8(mask)
+    a = _MlpArgs(params)
+    U = np.zeros((B, 8, P, P))
+    rc = lib().oracle_pair_mlp(_ptr(f), _ptr(m), B, P, C.byref(a.struct), _ptr(U))
+    assert rc == 0
+    return U
+
+
+def pair_embed(p4, mask, params: dict, eps: float = EPS) -> np.ndarray:
+    """U (B, 8, P, P) from p4 (B, P, 4): features then MLP, pair by pair."""
+    p = _f64(p4)
+    B, P = p.shape[:2]
+    m = _u8(mask)
+    a = _MlpArgs(params)
+    U = np.zeros((B, 8, P, P))
+    rc = lib().oracle_pair_embed(_ptr(p), _ptr(m), B, P, float(eps), C.byref(a.struct),
+                                 _ptr(U))
+    assert rc == 0
+    return U
+
+
+def attention(Q, K, V, U, mask) -> np.ndarray:
+    """O (B, H, P, D): masked softmax(Q K^T / sqrt(D) + U) V per head."""
+    q, k, v, u = _f64(Q), _f64(K), _f64(V), _f64(U)
+    B, H, P, D = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and u.shape == (B, H, P, P)
+    m = _u8(mask)
+    O = np.zeros((B, H, P, D))
+    rc = lib().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(m), B, H, P, D,
+                                _ptr(O))
+    assert rc == 0
+    return O
+
+
+def pair_embed_attention(p4, mask, params: dict, Q, K, V, eps: float = EPS) -> np.ndarray:
+    p = _f64(p4)
+    q, k, v = _f64(Q), _f64(K), _f64(V)
+    B, H, P, D = q.shape
+    assert H == 8 and p.shape == (B, P, 4)
+    m = _u8(mask)
+    a = _MlpArgs(params)
+    O = np.zeros((B, H, P, D))
+    rc = lib().oracle_pair_embed_attention(_ptr(p), _ptr(m), B, P, float(eps),
+                                           C.byref(a.struct), _ptr(q), _ptr(k), _ptr(v), D,
+                                           _ptr(O))
+    assert rc == 0
+    return O
+
+
+def block_stack(X0, Wq, Wk, Wv, Wo, U, mask) -> np.ndarray:
+    """X after L layers of X <- X + Attn(X Wq, X Wk, X Wv; U) Wo."""
+    x0 = _f64(X0)
+    B, P, Cw = x0.shape
+    wq, wk, wv, wo = _f64(Wq), _f64(Wk), _f64(Wv), _f64(Wo)
+    L = wq.shape[0]
+    u = _f64(U)
+    H = u.shape[1]
+    m = _u8(mask)
+    X = np.zeros_like(x0)
+    rc = lib().oracle_block_stack(_ptr(x0), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(u),
+                                  _ptr(m), B, P, Cw, H, L, _ptr(X))
+    assert rc == 0
+    return X

@@ -1,0 +1,190 @@
+"""Pins of the oracle's masked biased attention and block stack.
+
+Attention is softmax(Q K^T / sqrt(d) + bias) V per head (ml4sci_cms_e2e26
+README, "How the Kernel Fusion Works", Fusion 3), with the padding mask
+excluding keys.  Pinned by brute force in pure Python on tiny inputs, by
+PyTorch's CPU float64 scaled_dot_product_attention with a float mask, and by
+closed-form special cases.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fn
+
+import oracle
+from pair_interaction_particle_amd import synth
+
+
+def _rand(rng, B, H, P, D):
+    return [rng.normal(0, 1, size=(B, H, P, D)) for _ in range(3)] + [
+        rng.normal(0, 2, size=(B, H, P, P))]
+
+
+def _brute(Q, K, V, U, mask):
+    B, H, P, D = Q.shape
+    O = np.zeros_like(Q)
+    for b in range(B):
+        for h in range(H):
+            for a in range(P):
+                if not mask[b, a]:
+                    continue
+                keys = [c for c in range(P) if mask[b, c]]
+                s = [sum(Q[b, h, a, d] * K[b, h, c, d] for d in range(D)) / math.sqrt(D)
+                     + U[b, h, a, c] for c in keys]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                Z = sum(e)
+                for d in range(D):
+                    O[b, h, a, d] = sum(e[i] * V[b, h, c, d] for i, c in enumerate(keys)) / Z
+    return O
+
+
+def test_brute_force_tiny():
+    rng = np.random.default_rng(1)
+    Q, K, V, U = _rand(rng, 2, 2, 7, 4)
+    mask = np.array([[1, 1, 1, 0, 1, 1, 0], [1, 1, 1, 1, 1, 1, 1]], np.uint8)
+    np.testing.assert_allclose(oracle.attention(Q, K, V, U, mask), _brute(Q, K, V, U, mask),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_matches_torch_sdpa_with_float_mask():
+    rng = np.random.default_rng(2)
+    B, H, P, D = 3, 8, 24, 16
+    Q, K, V, U = _rand(rng, B, H, P, D)
+    mask = (np.arange(P)[None] < np.array([24, 13, 1])[:, None]).astype(np.uint8)
+    mask[0, 5] = 0
+    O = oracle.attention(Q, K, V, U, mask)
+    bias = torch.from_numpy(U).clone()
+    bias.masked_fill_(torch.from_numpy(mask[:, None, None, :] == 0).expand_as(bias), -math.inf)
+    ref = Fn.scaled_dot_product_attention(torch.from_numpy(Q), torch.from_numpy(K),
+                                          torch.from_numpy(V), attn_mask=bias).numpy()
+    real = mask.astype(bool)
+    for b in range(B):
+        np.testing.assert_allclose(O[b][:, real[b]], ref[b][:, real[b]], rtol=1e-12, atol=1e-13)
+        assert np.all(O[b][:, ~real[b]] == 0)
+
+
+def test_rows_of_p_sum_to_one():
+    # With V rows the unit vectors e_c (D >= P), O row a is the probability row.
+    rng = np.random.default_rng(3)
+    B, H, P = 1, 2, 10
+    D = 16
+    Q, K, _, U = _rand(rng, B, H, P, D)
+    V = np.zeros((B, H, P, D))
+    V[..., np.arange(P), np.arange(P)] = 1.0
+    mask = np.array([[1, 1, 0, 1, 1, 1, 1, 0, 1, 1]], np.uint8)
+    O = oracle.attention(Q, K, V, U, mask)
+    real = mask[0].astype(bool)
+    np.testing.assert_allclose(O[0][:, real].sum(-1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(O[0][:, real][..., ~np.pad(real, (0, D - P))] == 0)  # padded keys: weight 0
+    assert np.all(O[0][:, real] >= 0)
+
+
+def test_zero_queries_give_softmax_of_bias():
+    rng = np.random.default_rng(4)
+    _, K, V, U = _rand(rng, 1, 1, 9, 16)
+    Q = np.zeros_like(K)
+    mask = np.ones((1, 9), np.uint8)
+    O = oracle.attention(Q, K, V, U, mask)
+    e = np.exp(U[0, 0] - U[0, 0].max(-1, keepdims=True))
+    p = e / e.sum(-1, keepdims=True)
+    np.testing.assert_allclose(O[0, 0], p @ V[0, 0], rtol=1e-13, atol=1e-14)
+
+
+def test_row_constant_bias_is_plain_attention_and_one_key_copies_v():
+    rng = np.random.default_rng(5)
+    Q, K, V, U = _rand(rng, 1, 2, 8, 16)
+    mask = np.ones((1, 8), np.uint8)
+    Urow = np.broadcast_to(U[..., :1], U.shape).copy()  # constant along keys
+    O1 = oracle.attention(Q, K, V, Urow, mask)
+    O0 = oracle.attention(Q, K, V, np.zeros_like(U), mask)
+    np.testing.assert_allclose(O1, O0, rtol=1e-13, atol=1e-14)
+    one = np.zeros((1, 8), np.uint8)
+    one[0, 4] = 1
+    O = oracle.attention(Q, K, V, U, one)
+    np.testing.assert_allclose(O[0, :, 4], V[0, :, 4], rtol=0, atol=1e-15)
+    assert np.all(O[0, :, np.arange(8) != 4] == 0)
+
+
+def test_bias_is_added_after_scaling_and_not_transposed():
+    rng = np.random.default_rng(6)
+    Q, K, V, U = _rand(rng, 1, 1, 6, 16)
+    mask = np.ones((1, 6), np.uint8)
+    O = oracle.attention(Q, K, V, U, mask)
+    s = Q[0, 0] @ K[0, 0].T / 4.0 + U[0, 0]
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    np.testing.assert_allclose(O[0, 0], p @ V[0, 0], rtol=1e-13, atol=1e-14)
+    s_t = Q[0, 0] @ K[0, 0].T / 4.0 + U[0, 0].T
+    p_t = np.exp(s_t - s_t.max(-1, keepdims=True))
+    p_t /= p_t.sum(-1, keepdims=True)
+    assert np.abs(O[0, 0] - p_t @ V[0, 0]).max() > 1e-3
+
+
+def test_permutation_equivariance_and_padding_ignored():
+    rng = np.random.default_rng(7)
+    Q, K, V, U = _rand(rng, 1, 3, 12, 16)
+    mask = np.array([[1] * 9 + [0] * 3], np.uint8)
+    O = oracle.attention(Q, K, V, U, mask)
+    perm = rng.permutation(12)
+    Op = oracle.attention(Q[:, :, perm], K[:, :, perm], V[:, :, perm],
+                          U[:, :, perm][:, :, :, perm], mask[:, perm])
+    np.testing.assert_allclose(Op, O[:, :, perm], rtol=1e-13, atol=1e-14)
+    Q2, K2, V2, U2 = (x.copy() for x in (Q, K, V, U))
+    for x in (Q2, K2, V2):
+        x[:, :, 9:] = np.nan
+    U2[:, :, 9:, :] = np.nan
+    U2[:, :, :, 9:] = 1e30
+    np.testing.assert_array_equal(oracle.attention(Q2, K2, V2, U2, mask), O)
+
+
+def test_all_masked_jet_gives_zeros():
+    rng = np.random.default_rng(8)
+    Q, K, V, U = _rand(rng, 2, 2, 5, 16)
+    mask = np.zeros((2, 5), np.uint8)
+    mask[1, :2] = 1
+    O = oracle.attention(Q, K, V, U, mask)
+    assert np.all(O[0] == 0) and np.isfinite(O).all()
+
+
+def test_pair_embed_attention_is_embed_then_attention():
+    d = synth.make_workload("tiny")
+    U = oracle.pair_embed(d["p4"], d["mask"], d["mlp"])
+    O1 = oracle.attention(d["q"], d["k"], d["v"], U, d["mask"])
+    O2 = oracle.pair_embed_attention(d["p4"], d["mask"], d["mlp"], d["q"], d["k"], d["v"])
+    np.testing.assert_array_equal(O1, O2)
+
+
+def _torch_stack(X0, Wq, Wk, Wv, Wo, U, mask):
+    B, P, C = X0.shape
+    H = U.shape[1]
+    D = C // H
+    X = torch.from_numpy(X0.astype(np.float64))
+    bias = torch.from_numpy(U).clone()
+    km = torch.from_numpy(mask == 0)
+    bias.masked_fill_(km[:, None, None, :].expand_as(bias), -math.inf)
+    qm = torch.from_numpy(mask != 0)[:, None, :, None]
+    for l in range(Wq.shape[0]):
+        w = [torch.from_numpy(x[l].astype(np.float64)) for x in (Wq, Wk, Wv, Wo)]
+        q, k, v = ((X @ wi).reshape(B, P, H, D).transpose(1, 2) for wi in w[:3])
+        o = Fn.scaled_dot_product_attention(q, k, v, attn_mask=bias)
+        o = torch.where(qm, o, torch.zeros_like(o))  # padded queries give 0
+        X = X + o.transpose(1, 2).reshape(B, P, C) @ w[3]
+    return X.numpy()
+
+
+def test_block_stack_matches_torch_composition():
+    rng = np.random.default_rng(9)
+    B, P, C, H, L = 2, 12, 32, 2, 3
+    mask = (np.arange(P)[None] < np.array([12, 7])[:, None]).astype(np.uint8)
+    x0, wq, wk, wv, wo = synth.make_block_stack(B, P, C, L, mask, rng=rng)
+    U = rng.normal(0, 1, size=(B, H, P, P))
+    X = oracle.block_stack(x0, wq, wk, wv, wo, U, mask)
+    ref = _torch_stack(x0, wq, wk, wv, wo, U, mask)
+    np.testing.assert_allclose(X, ref, rtol=1e-11, atol=1e-11)
+    assert np.all(X[1, 7:] == 0)  # padded rows stay 0
+    # L = 0 is the identity
+    X0 = oracle.block_stack(x0, wq[:0], wk[:0], wv[:0], wo[:0], U, mask)
+    np.testing.assert_array_equal(X0, x0.astype(np.float64))

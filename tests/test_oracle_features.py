@@ -1,0 +1,205 @@
+"""Pins of the oracle's pair features against what the pages and mathematics fix.
+
+The four features are named in the ml4sci_cms_e2e26 README ("How the Kernel
+Fusion Works", Fusion 2) and defined in the Particle Transformer paper the
+README lists under References.  The pages print no worked example, so the
+expected values below are derived by hand, in closed form, from integer
+4-vectors; the symmetry tests follow the gist.science summary of "Virtues and
+Vices of Equivariant Transformers" (Methodologie: ParT pair features are
+invariant under SO(2) x SO+(1,1)).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from pair_interaction_particle_amd import synth
+
+EPS = 1e-8
+LN_EPS = math.log(EPS)
+
+
+def f(pa, pb):
+    return oracle.pair_feature(np.array(pa, float), np.array(pb, float), EPS)
+
+
+def check(got, lnkt, lnz, lndr, lnm2, tol=1e-13):
+    np.testing.assert_allclose(got, [lnkt, lnz, lndr, lnm2], rtol=0, atol=tol)
+
+
+def test_two_particles_transverse_right_angle():
+    # (E,px,py,pz) = (1,1,0,0) and (1,0,1,0): y = 0 for both, dphi = pi/2,
+    # pT = 1 for both, m2 = 2^2 - 1 - 1 = 2.
+    dr = math.pi / 2
+    check(f([1, 1, 0, 0], [1, 0, 1, 0]), math.log(dr), math.log(0.5), math.log(dr),
+          math.log(2.0))
+
+
+def test_two_particles_pythagorean_quadruples():
+    # a = (3,1,2,2), b = (7,2,3,-6): both massless (1+4+4 = 9, 4+9+36 = 49).
+    # y_a = 1/2 ln 5, y_b = 1/2 ln(1/13)  ->  dy = 1/2 ln 65.
+    # phi_a - phi_b = atan 2 - atan 1.5 = atan(0.5 / 4) = atan(1/8).
+    # pT_a = sqrt 5 < pT_b = sqrt 13.  m2 = 10^2 - 3^2 - 5^2 - 4^2 = 50.
+    dr = math.sqrt((0.5 * math.log(65)) ** 2 + math.atan(1 / 8) ** 2)
+    pta, ptb = math.sqrt(5), math.sqrt(13)
+    check(f([3, 1, 2, 2], [7, 2, 3, -6]), math.log(pta * dr), math.log(pta / (pta + ptb)),
+          math.log(dr), math.log(50.0))
+
+
+def test_two_particles_second_quadruple():
+    # a = (9,4,4,7), b = (9,1,4,8), both massless (81 = 16+16+49 = 1+16+64).
+    # y_a = 1/2 ln(16/2), y_b = 1/2 ln(17/1)  ->  |dy| = 1/2 ln(17/8).
+    # phi_a = pi/4, phi_b = atan 4  ->  |dphi| = atan((4-1)/(1+4)) = atan(3/5).
+    # pT_a = sqrt 32 > pT_b = sqrt 17.  m2 = 18^2 - 5^2 - 8^2 - 15^2 = 10.
+    dr = math.sqrt((0.5 * math.log(17 / 8)) ** 2 + math.atan(0.6) ** 2)
+    pta, ptb = math.sqrt(32), math.sqrt(17)
+    check(f([9, 4, 4, 7], [9, 1, 4, 8]), math.log(ptb * dr), math.log(ptb / (pta + ptb)),
+          math.log(dr), math.log(10.0))
+
+
+def test_diagonal_pair_hits_the_clamps():
+    # a paired with itself: dR = 0 so kT = 0 -> ln eps; z = 1/2; the massless
+    # particle has m2 = (2E)^2 - |2p|^2 = 36 - 36 = 0 -> ln eps.
+    check(f([3, 1, 2, 2], [3, 1, 2, 2]), LN_EPS, math.log(0.5), LN_EPS, LN_EPS)
+
+
+def test_diagonal_pair_of_a_massive_particle():
+    # (5,1,2,2): m^2 = 25 - 9 = 16; the self-pair has m2 = 4 m^2 = 64.
+    check(f([5, 1, 2, 2], [5, 1, 2, 2]), LN_EPS, math.log(0.5), LN_EPS, math.log(64.0))
+
+
+def test_phi_wraps_into_minus_pi_pi():
+    # a = (3,-2,-1,2), b = (3,1,2,2): same rapidity 1/2 ln 5, same pT sqrt 5.
+    # phi_a = -pi + atan(1/2), phi_b = atan 2 = pi/2 - atan(1/2): the raw
+    # difference -3pi/2 + 2 atan(1/2) ~ -3.785 wraps to pi/2 + 2 atan(1/2).
+    # m2 = 6^2 - 1 - 1 - 16 = 18.
+    dr = math.pi / 2 + 2 * math.atan(0.5)
+    pt = math.sqrt(5)
+    check(f([3, -2, -1, 2], [3, 1, 2, 2]), math.log(pt * dr), math.log(0.5), math.log(dr),
+          math.log(18.0))
+
+
+def test_rapidity_not_pseudorapidity_for_massive_particle():
+    # a = (5,1,2,2) massive (m^2 = 16): y_a = 1/2 ln(7/3), while its
+    # pseudorapidity would be 1/2 ln 5.  b = (7,2,3,-6): y_b = 1/2 ln(1/13).
+    # dy = 1/2 ln(91/3); dphi = atan(1/8); m2 = 12^2 - 3^2 - 5^2 - 4^2 = 94.
+    dr = math.sqrt((0.5 * math.log(91 / 3)) ** 2 + math.atan(1 / 8) ** 2)
+    pta, ptb = math.sqrt(5), math.sqrt(13)
+    check(f([5, 1, 2, 2], [7, 2, 3, -6]), math.log(pta * dr), math.log(pta / (pta + ptb)),
+          math.log(dr), math.log(94.0))
+
+
+def test_particle_kinematics():
+    pt, y, phi = oracle.particle([5, 1, 2, 2])
+    assert pt == pytest.approx(math.sqrt(5), abs=1e-15)
+    assert y == pytest.approx(0.5 * math.log(7 / 3), abs=1e-15)
+    assert phi == pytest.approx(math.atan(2.0), abs=1e-15)
+
+
+def _massless(rng, n, y_spread=1.0):
+    pt = np.exp(rng.uniform(np.log(0.5), np.log(500), n))
+    y = rng.normal(0, y_spread, n)
+    phi = rng.uniform(-np.pi, np.pi, n)
+    p4 = np.stack([pt * np.cosh(y), pt * np.cos(phi), pt * np.sin(phi), pt * np.sinh(y)], -1)
+    return p4, pt, y, phi
+
+
+def test_massless_m2_closed_form():
+    # For massless a, b: m2 = 2 pT_a pT_b (cosh dy - cos dphi).
+    rng = np.random.default_rng(11)
+    p4, pt, y, phi = _massless(rng, 64)
+    checked = 0
+    for i in range(0, 64, 2):
+        a, b = i, i + 1
+        dy, dphi = y[a] - y[b], phi[a] - phi[b]
+        if dy * dy + dphi * dphi < 0.05 ** 2:
+            continue  # keep the direct fp64 formula well conditioned
+        m2 = 2 * pt[a] * pt[b] * (np.cosh(dy) - np.cos(dphi))
+        got = f(p4[a], p4[b])
+        assert got[3] == pytest.approx(np.log(m2), abs=1e-10)
+        # dR from the generating (y, phi) with the wrap done by mod
+        dphi_w = (dphi + np.pi) % (2 * np.pi) - np.pi
+        dr = np.hypot(dy, dphi_w)
+        assert got[2] == pytest.approx(np.log(dr), abs=1e-12)
+        assert got[0] == pytest.approx(np.log(min(pt[a], pt[b]) * dr), abs=1e-12)
+        assert got[1] == pytest.approx(np.log(min(pt[a], pt[b]) / (pt[a] + pt[b])), abs=1e-12)
+        checked += 1
+    assert checked > 20
+
+
+def _rotate_boost(p4, alpha, eta):
+    E, px, py, pz = p4[..., 0], p4[..., 1], p4[..., 2], p4[..., 3]
+    c, s = np.cos(alpha), np.sin(alpha)
+    ch, sh = np.cosh(eta), np.sinh(eta)
+    return np.stack([E * ch + pz * sh, px * c - py * s, px * s + py * c, pz * ch + E * sh], -1)
+
+
+def test_invariance_under_azimuthal_rotation_and_longitudinal_boost():
+    rng = np.random.default_rng(5)
+    p4, *_ = _massless(rng, 24, y_spread=0.8)
+    # give a few particles a mass so that rapidity != pseudorapidity matters
+    m = np.where(rng.random(24) < 0.3, rng.uniform(0.5, 3.0, 24), 0.0)
+    p4[:, 0] = np.sqrt(p4[:, 1] ** 2 + p4[:, 2] ** 2 + p4[:, 3] ** 2 + m ** 2)
+    mask = np.ones((1, 24), np.uint8)
+    F0 = oracle.pair_features(p4[None], mask, EPS)
+    for alpha, eta in [(0.7, 0.0), (0.0, -1.3), (2.9, 0.9), (-2.2, 2.1)]:
+        F1 = oracle.pair_features(_rotate_boost(p4, alpha, eta)[None], mask, EPS)
+        np.testing.assert_allclose(F1, F0, rtol=0, atol=2e-9)
+
+
+def test_m2_invariant_under_general_lorentz_boost():
+    rng = np.random.default_rng(9)
+    p4, *_ = _massless(rng, 16, y_spread=0.5)
+    mask = np.ones((1, 16), np.uint8)
+    F0 = oracle.pair_features(p4[None], mask, EPS)
+    for _ in range(3):
+        n = rng.normal(size=3)
+        n /= np.linalg.norm(n)
+        beta = rng.uniform(0.2, 0.8)
+        g = 1 / np.sqrt(1 - beta ** 2)
+        Lam = np.eye(4)
+        Lam[0, 0] = g
+        Lam[0, 1:] = Lam[1:, 0] = -g * beta * n
+        Lam[1:, 1:] += (g - 1) * np.outer(n, n)
+        F1 = oracle.pair_features((p4 @ Lam.T)[None], mask, EPS)
+        off = ~np.eye(16, dtype=bool)
+        # only ln m2 is invariant under a general boost; compare well-separated pairs
+        big = F0[0, 3][off] > np.log(1e-2)
+        np.testing.assert_allclose(F1[0, 3][off][big], F0[0, 3][off][big], rtol=0, atol=1e-9)
+        # and the transverse features do change (the test would notice a wrong feature)
+        assert np.abs(F1[0, 0] - F0[0, 0]).max() > 1e-3
+
+
+def test_pair_symmetry_is_exact():
+    p4, mask, _ = synth.make_jets(3, 32, 20, 32, seed=3)
+    F = oracle.pair_features(p4, mask, EPS)
+    np.testing.assert_array_equal(F, np.swapaxes(F, 2, 3))
+
+
+def test_grid_matches_single_pair_and_masks():
+    p4, mask, n = synth.make_jets(2, 16, 9, 16, seed=1)
+    mask = mask.copy()
+    mask[1, 3] = 0  # a non-prefix hole
+    F = oracle.pair_features(p4, mask, EPS)
+    for b in range(2):
+        for a in range(16):
+            for c in range(16):
+                want = f(p4[b, a], p4[b, c]) if (mask[b, a] and mask[b, c]) else np.zeros(4)
+                np.testing.assert_array_equal(F[b, :, a, c], want)
+    # diagonal of real particles: kT and dR clamp, z = 1/2
+    for b in range(2):
+        for a in np.nonzero(mask[b])[0]:
+            assert F[b, 0, a, a] == LN_EPS and F[b, 2, a, a] == LN_EPS
+            assert F[b, 1, a, a] == pytest.approx(math.log(0.5), abs=1e-15)
+
+
+def test_padding_values_are_ignored():
+    p4, mask, n = synth.make_jets(2, 16, 8, 12, seed=2)
+    F0 = oracle.pair_features(p4, mask, EPS)
+    bad = p4.astype(np.float64).copy()
+    pad = mask == 0
+    bad[pad] = np.nan
+    bad[0, -1] = [1e30, -1e30, 1e30, 0]
+    F1 = oracle.pair_features(bad, mask, EPS)
+    np.testing.assert_array_equal(F1, F0)
