@@ -1,0 +1,287 @@
+// abi.hip -- the extern "C" entry points of libpip: argument validation, the
+// host-side BatchNorm fold and MFMA operand packing, and kernel dispatch.
+// Every check happens before the first HIP call, so an invalid call costs no
+// GPU work and can be exercised without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "pip_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+pip_status hip_status(hipError_t e) { return e == hipSuccess ? PIP_OK : PIP_ERR_HIP; }
+
+// Sizes the kernels take for the pair grid: 16 <= P <= 256, P % 16 == 0.
+pip_status check_pair_grid(int64_t B, int64_t P) {
+    if (B < 0 || P < 0) return PIP_ERR_SHAPE;
+    if (B == 0 || P == 0) return PIP_OK;
+    if (P % 16 != 0 || P > PIP_MAX_P) return PIP_ERR_UNSUPPORTED;
+    if (B > (int64_t)1 << 24) return PIP_ERR_UNSUPPORTED;  // keeps the grid in range
+    return PIP_OK;
+}
+
+// The handle's weights live on the device it was created on.
+pip_status check_device(const pip_pair_mlp *m) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return PIP_ERR_HIP;
+    return dev == m->device ? PIP_OK : PIP_ERR_UNSUPPORTED;
+}
+
+uint16_t host_bf16(float x) {  // round to nearest even; NaN stays NaN
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pip_status_string(int s) {
+    switch (s) {
+        case PIP_OK: return "ok";
+        case PIP_ERR_NULL: return "null pointer";
+        case PIP_ERR_SHAPE: return "bad shape";
+        case PIP_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case PIP_ERR_DTYPE: return "unknown dtype";
+        case PIP_ERR_UNSUPPORTED: return "unsupported size or configuration";
+        case PIP_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int pip_version(void) { return PIP_VERSION; }
+
+pip_status pip_pair_mlp_fold(const pip_pair_mlp_params *raw, float *w_out, float *b_out) {
+    if (!raw || !w_out || !b_out) return PIP_ERR_NULL;
+    if (!raw->w1 || !raw->w2 || !raw->w3 || !raw->w4) return PIP_ERR_NULL;
+    for (int k = 0; k < 3; ++k)
+        if (!raw->bn_gamma[k] || !raw->bn_beta[k] || !raw->bn_mean[k] || !raw->bn_var[k])
+            return PIP_ERR_NULL;
+    const int nin = (raw->in_gamma != 0) + (raw->in_beta != 0) + (raw->in_mean != 0) +
+                    (raw->in_var != 0);
+    if (nin != 0 && nin != 4) return PIP_ERR_NULL;
+    const double eps = raw->bn_eps;
+
+    // input BatchNorm as x' = si * x + ti (identity when absent)
+    double si[4], ti[4];
+    for (int k = 0; k < 4; ++k) {
+        if (nin) {
+            const double v = (double)raw->in_var[k] + eps;
+            if (!(v > 0.0)) return PIP_ERR_SHAPE;
+            si[k] = (double)raw->in_gamma[k] / sqrt(v);
+            ti[k] = (double)raw->in_beta[k] - si[k] * (double)raw->in_mean[k];
+        } else {
+            si[k] = 1.0;
+            ti[k] = 0.0;
+        }
+    }
+    const float *W[3] = {raw->w1, raw->w2, raw->w3};
+    const float *bias[3] = {raw->b1, raw->b2, raw->b3};
+    const int nins[3] = {4, 64, 64};
+    float *wo = w_out;
+    for (int l = 0; l < 3; ++l) {
+        const int ni = nins[l];
+        for (int o = 0; o < 64; ++o) {
+            const double v = (double)raw->bn_var[l][o] + eps;
+            if (!(v > 0.0)) return PIP_ERR_SHAPE;
+            const double s = (double)raw->bn_gamma[l][o] / sqrt(v);
+            double z = bias[l] ? (double)bias[l][o] : 0.0;
+            for (int i = 0; i < ni; ++i) {
+                const double w = (double)W[l][o * ni + i];
+                if (l == 0) {
+                    wo[o * ni + i] = (float)(s * w * si[i]);
+                    z += w * ti[i];
+                } else {
+                    wo[o * ni + i] = (float)(s * w);
+                }
+            }
+            b_out[64 * l + o] =
+                (float)(s * (z - (double)raw->bn_mean[l][o]) + (double)raw->bn_beta[l][o]);
+        }
+        wo += 64 * ni;
+    }
+    for (int i = 0; i < 8 * 64; ++i) wo[i] = raw->w4[i];
+    for (int o = 0; o < 8; ++o) b_out[192 + o] = raw->b4 ? raw->b4[o] : 0.0f;
+    return PIP_OK;
+}
+
+pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **out) {
+    if (!out) return PIP_ERR_NULL;
+    *out = nullptr;
+    std::vector<float> w(64 * 4 + 2 * 64 * 64 + 8 * 64), b(200);
+    pip_status st = pip_pair_mlp_fold(raw, w.data(), b.data());
+    if (st != PIP_OK) return st;
+    const float *W1 = w.data(), *W2 = W1 + 256, *W3 = W2 + 4096, *W4 = W3 + 4096;
+
+    // float32 operands (layouts in pip_internal.h)
+    std::vector<float> p32(pip::kW32Ops * 64);
+    for (int c = 0; c < 4; ++c)
+        for (int l = 0; l < 64; ++l) p32[pip::kW32L1 + c * 64 + l] = W1[(16 * c + l % 16) * 4 + l / 16];
+    const float *Wh[2] = {W2, W3};
+    const int offs[2] = {pip::kW32L2, pip::kW32L3};
+    for (int t = 0; t < 2; ++t)
+        for (int co = 0; co < 4; ++co)
+            for (int ci = 0; ci < 4; ++ci)
+                for (int r = 0; r < 4; ++r)
+                    for (int l = 0; l < 64; ++l)
+                        p32[offs[t] + ((co * 4 + ci) * 4 + r) * 64 + l] =
+                            Wh[t][(16 * co + l % 16) * 64 + 16 * ci + 4 * (l / 16) + r];
+    for (int ci = 0; ci < 4; ++ci)
+        for (int r = 0; r < 4; ++r)
+            for (int l = 0; l < 64; ++l)
+                p32[pip::kW32L4 + (ci * 4 + r) * 64 + l] =
+                    (l % 16 < 8) ? W4[(l % 16) * 64 + 16 * ci + 4 * (l / 16) + r] : 0.0f;
+
+    // bfloat16 operands: 8 values per lane; slot j < 4 -> channel 32s + 4g + j,
+    // slot j >= 4 -> channel 32s + 16 + 4g + (j - 4)
+    std::vector<uint16_t> p16(pip::kW16Ops * 64 * 8);
+    auto chan = [](int s, int g, int j) { return 32 * s + (j < 4 ? 0 : 16) + 4 * g + (j & 3); };
+    const int offs16[2] = {pip::kW16L2, pip::kW16L3};
+    for (int t = 0; t < 2; ++t)
+        for (int co = 0; co < 4; ++co)
+            for (int s = 0; s < 2; ++s)
+                for (int l = 0; l < 64; ++l)
+                    for (int j = 0; j < 8; ++j)
+                        p16[offs16[t] + ((co * 2 + s) * 64 + l) * 8 + j] =
+                            host_bf16(Wh[t][(16 * co + l % 16) * 64 + chan(s, l / 16, j)]);
+    for (int s = 0; s < 2; ++s)
+        for (int l = 0; l < 64; ++l)
+            for (int j = 0; j < 8; ++j)
+                p16[pip::kW16L4 + (s * 64 + l) * 8 + j] =
+                    (l % 16 < 8) ? host_bf16(W4[(l % 16) * 64 + chan(s, l / 16, j)]) : 0;
+
+    pip_pair_mlp *m = new pip_pair_mlp();
+    m->w32 = nullptr;
+    m->w16 = nullptr;
+    m->bias = nullptr;
+    hipError_t e = hipGetDevice(&m->device);
+    if (e == hipSuccess) e = hipMalloc((void **)&m->w32, p32.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void **)&m->w16, p16.size() * sizeof(uint16_t));
+    if (e == hipSuccess) e = hipMalloc((void **)&m->bias, b.size() * sizeof(float));
+    if (e == hipSuccess)
+        e = hipMemcpy(m->w32, p32.data(), p32.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(m->w16, p16.data(), p16.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(m->bias, b.data(), b.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        pip_pair_mlp_destroy(m);
+        return PIP_ERR_HIP;
+    }
+    *out = m;
+    return PIP_OK;
+}
+
+pip_status pip_pair_mlp_destroy(pip_pair_mlp *m) {
+    if (!m) return PIP_ERR_NULL;
+    hipError_t e = hipSuccess, e2;
+    if (m->w32 && (e2 = hipFree(m->w32)) != hipSuccess) e = e2;
+    if (m->w16 && (e2 = hipFree(m->w16)) != hipSuccess) e = e2;
+    if (m->bias && (e2 = hipFree(m->bias)) != hipSuccess) e = e2;
+    delete m;
+    return hip_status(e);
+}
+
+pip_status pip_pair_features(const float *p4, const uint8_t *mask, int64_t B, int64_t P,
+                             float *F, void *stream) {
+    pip_status st = check_pair_grid(B, P);
+    if (st != PIP_OK || B == 0 || P == 0) return st;
+    if (!p4 || !mask || !F) return PIP_ERR_NULL;
+    if (!aligned16(p4) || !aligned16(F)) return PIP_ERR_ALIGN;
+    return hip_status(pip::launch_pair_features(p4, mask, (int)B, (int)P, F, (hipStream_t)stream));
+}
+
+pip_status pip_pair_embed(const float *p4, const uint8_t *mask, int64_t B, int64_t P,
+                          const pip_pair_mlp *mlp, void *U, int u_dtype, void *stream) {
+    if (u_dtype != PIP_F32 && u_dtype != PIP_BF16) return PIP_ERR_DTYPE;
+    pip_status st = check_pair_grid(B, P);
+    if (st != PIP_OK || B == 0 || P == 0) return st;
+    if (!p4 || !mask || !mlp || !U) return PIP_ERR_NULL;
+    if (!aligned16(p4) || !aligned16(U)) return PIP_ERR_ALIGN;
+    if ((st = check_device(mlp)) != PIP_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (u_dtype == PIP_F32)
+        return hip_status(pip::launch_pair_embed_f32(p4, mask, (int)B, (int)P, mlp, (float *)U, s));
+    return hip_status(pip::launch_pair_embed_bf16(p4, mask, (int)B, (int)P, mlp, (uint16_t *)U, s));
+}
+
+pip_status pip_pair_bias_attention(const void *Q, const void *K, const void *V, const void *U,
+                                   const uint8_t *mask, int64_t B, int64_t H, int64_t P,
+                                   int64_t D, void *O, int dtype, void *stream) {
+    if (dtype != PIP_F32 && dtype != PIP_BF16) return PIP_ERR_DTYPE;
+    if (H < 0 || D < 0) return PIP_ERR_SHAPE;
+    pip_status st = check_pair_grid(B, P);
+    if (st != PIP_OK) return st;
+    if (B == 0 || P == 0 || H == 0) return PIP_OK;
+    if (!Q || !K || !V || !U || !mask || !O) return PIP_ERR_NULL;
+    if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
+    if (B * H > ((int64_t)1 << 31) - 1) return PIP_ERR_UNSUPPORTED;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(O))
+        return PIP_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == PIP_F32)
+        return hip_status(pip::launch_attention_f32((const float *)Q, (const float *)K,
+                                                    (const float *)V, (const float *)U, mask,
+                                                    (int)B, (int)H, (int)P, (float *)O, s));
+    return hip_status(pip::launch_attention_bf16((const uint16_t *)Q, (const uint16_t *)K,
+                                                 (const uint16_t *)V, (const uint16_t *)U, mask,
+                                                 (int)B, (int)H, (int)P, (uint16_t *)O, s));
+}
+
+pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
+                                    const pip_pair_mlp *mlp, const void *Q, const void *K,
+                                    const void *V, int64_t B, int64_t P, int64_t D, void *O,
+                                    int dtype, void *stream) {
+    if (dtype != PIP_F32 && dtype != PIP_BF16) return PIP_ERR_DTYPE;
+    if (D < 0) return PIP_ERR_SHAPE;
+    pip_status st = check_pair_grid(B, P);
+    if (st != PIP_OK || B == 0 || P == 0) return st;
+    if (!p4 || !mask || !mlp || !Q || !K || !V || !O) return PIP_ERR_NULL;
+    if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
+    if (!aligned16(p4) || !aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+        return PIP_ERR_ALIGN;
+    if ((st = check_device(mlp)) != PIP_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == PIP_F32)
+        return hip_status(pip::launch_embed_attention_f32(p4, mask, (int)B, (int)P, mlp,
+                                                          (const float *)Q, (const float *)K,
+                                                          (const float *)V, (float *)O, s));
+    return hip_status(pip::launch_embed_attention_bf16(
+        p4, mask, (int)B, (int)P, mlp, (const uint16_t *)Q, (const uint16_t *)K,
+        (const uint16_t *)V, (uint16_t *)O, s));
+}
+
+size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C) {
+    if (B <= 0 || P <= 0 || C <= 0) return 0;
+    return (size_t)B * (size_t)P * (size_t)C * sizeof(float);
+}
+
+pip_status pip_block_stack(float *X, const float *Wq, const float *Wk, const float *Wv,
+                           const float *Wo, const float *U, const uint8_t *mask, int64_t B,
+                           int64_t P, int64_t C, int64_t H, int64_t L, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    if (C < 0 || H < 0 || L < 0) return PIP_ERR_SHAPE;
+    pip_status st = check_pair_grid(B, P);
+    if (st != PIP_OK) return st;
+    if (B == 0 || P == 0 || L == 0) return PIP_OK;
+    if (!X || !Wq || !Wk || !Wv || !Wo || !U || !mask) return PIP_ERR_NULL;
+    if (H == 0 || C != (int64_t)PIP_HEAD_DIM * H) return PIP_ERR_SHAPE;
+    if (C > 256 || C % 64 != 0) return PIP_ERR_UNSUPPORTED;
+    if (!workspace) return PIP_ERR_NULL;
+    if (workspace_bytes < pip_block_stack_workspace_bytes(B, P, C)) return PIP_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
+        !aligned16(Wo) || !aligned16(U) || !aligned16(workspace))
+        return PIP_ERR_ALIGN;
+    return hip_status(pip::launch_block_stack(X, Wq, Wk, Wv, Wo, U, mask, (int)B, (int)P,
+                                              (int)C, (int)H, (int)L, (float *)workspace,
+                                              (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+"""Host-side checks of libpip that need no GPU: the library loads and exports
+every function include/pip.h declares, argument validation returns its
+documented status before any HIP call, and the host BatchNorm fold agrees with
+the oracle's unfolded MLP."""
+import ctypes as C
+import math
+import subprocess
+
+import numpy as np
+import pytest
+import scipy.special as sp
+
+import oracle
+from pair_interaction_particle_amd import binding, synth
+
+OK, NULL, SHAPE, ALIGN, DTYPE, UNSUP = 0, 1, 2, 3, 4, 5
+# Fake device addresses: never dereferenced, because every call below fails
+# validation before it reaches the GPU.
+A16, A17 = 0x10000, 0x10001
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = binding.header_functions()
+    assert len(names) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(L, n)
+    assert L.pip_version() == 1
+    assert L.pip_status_string(3) == b"pointer not 16-byte aligned"
+
+
+def test_pair_features_validation(L):
+    f = L.pip_pair_features
+    assert f(None, A16, 1, 16, A16, None) == NULL
+    assert f(A16, A16, -1, 16, A16, None) == SHAPE
+    assert f(A16, A16, 1, -16, A16, None) == SHAPE
+    assert f(A16, A16, 1, 24, A16, None) == UNSUP
+    assert f(A16, A16, 1, 272, A16, None) == UNSUP
+    assert f(A17, A16, 1, 16, A16, None) == ALIGN
+    assert f(A16, A16, 1, 16, A17, None) == ALIGN
+    assert f(A16, A16, 0, 16, A16, None) == OK  # empty batch: nothing to do
+    assert f(A16, A16, 3, 0, A16, None) == OK
+    assert f(None, None, 0, 16, None, None) == OK  # empty: pointers unchecked
+    assert f(None, None, 2, 17, None, None) == UNSUP  # sizes are checked first
+
+
+def test_pair_embed_validation(L):
+    f = L.pip_pair_embed
+    assert f(A16, A16, 1, 16, None, A16, 0, None) == NULL
+    assert f(A16, A16, 1, 16, A16, A16, 7, None) == DTYPE
+    assert f(A16, A16, 1, 40, A16, A16, 0, None) == UNSUP
+    assert f(A16, A16, 1, 16, A16, A17, 1, None) == ALIGN
+    assert f(A16, A16, -2, 16, A16, A16, 0, None) == SHAPE
+    assert f(A16, A16, 0, 16, A16, A16, 0, None) == OK
+
+
+def test_attention_validation(L):
+    f = L.pip_pair_bias_attention
+    args = [A16] * 4 + [A16]
+    assert f(None, A16, A16, A16, A16, 1, 8, 16, 16, A16, 0, None) == NULL
+    assert f(*args, 1, 8, 16, 32, A16, 0, None) == UNSUP  # D != 16
+    assert f(*args, 1, 8, 20, 16, A16, 0, None) == UNSUP  # P % 16
+    assert f(*args, 1, -1, 16, 16, A16, 0, None) == SHAPE
+    assert f(*args, 1, 8, 16, 16, A16, 2, None) == DTYPE
+    assert f(A16, A16, A17, A16, A16, 1, 8, 16, 16, A16, 0, None) == ALIGN
+    assert f(*args, 1, 0, 16, 16, A16, 0, None) == OK  # no heads
+    g = L.pip_pair_embed_attention
+    assert g(A16, A16, None, A16, A16, A16, 1, 16, 16, A16, 0, None) == NULL
+    assert g(A16, A16, A16, A16, A16, A16, 1, 16, 8, A16, 0, None) == UNSUP
+    assert g(A16, A16, A16, A16, A16, A16, 1, 16, 16, A17, 0, None) == ALIGN
+
+
+def test_block_stack_validation(L):
+    f = L.pip_block_stack
+    ws = L.pip_block_stack_workspace_bytes(2, 16, 128)
+    assert ws == 2 * 16 * 128 * 4
+    w = [A16] * 7
+    assert f(*w, 2, 16, 128, 8, 1, None, ws, None) == NULL
+    assert f(*w, 2, 16, 128, 8, 1, A16, ws - 4, None) == SHAPE
+    assert f(*w, 2, 16, 100, 8, 1, A16, ws, None) == SHAPE  # C != 16 H
+    assert f(*w, 2, 16, 128, 8, 1, A17, ws, None) == ALIGN
+    assert f(*w, 2, 16, 128, 8, 0, None, 0, None) == OK  # zero layers
+
+
+def _params(seed, **kw):
+    return synth.make_mlp_params(rng=np.random.default_rng(seed), **kw)
+
+
+@pytest.mark.parametrize("kw", [{}, {"biases": True}, {"biases": True, "input_bn": True}])
+def test_host_fold_reproduces_the_unfolded_mlp(kw):
+    p = _params(21, **kw)
+    (w1, w2, w3, w4), (b1, b2, b3, b4) = binding.fold(p)
+    rng = np.random.default_rng(22)
+    for _ in range(20):
+        f = rng.normal(0, 5, size=4)
+        h = f
+        for w, b in ((w1, b1), (w2, b2), (w3, b3)):
+            z = w.astype(np.float64) @ h + b
+            h = z * sp.ndtr(z)
+        u = w4.astype(np.float64) @ h + b4
+        ref = oracle.mlp_pair(p, f)
+        np.testing.assert_allclose(u, ref, rtol=0, atol=2e-5 * (1 + np.abs(ref).max()))
+
+
+def test_fold_validation(L):
+    p = _params(1)
+    p["bn2_var"] = np.full(64, -1.0, np.float32)  # var + eps <= 0
+    with pytest.raises(binding.PipError) as e:
+        binding.fold(p)
+    assert e.value.status == SHAPE
+    q = _params(1, input_bn=True)
+    del q["in_var"]  # partial input BN
+    with pytest.raises(binding.PipError) as e:
+        binding.fold(q)
+    assert e.value.status == NULL

@@ -1,0 +1,202 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs, element by element.
+
+Bars: float32 |err| <= 1e-4 (1 + |ref|); bfloat16 |err| <= 2e-2 (1 + |ref|);
+every output that involves a padded slot is +0.0 bit for bit.  The oracle's
+inputs are always the synthetic inputs themselves (bf16 workloads: the
+bf16-rounded values), never anything the GPU produced.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pair_interaction_particle_amd import binding as pip
+from pair_interaction_particle_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL32, TOLBF = 1e-4, 2e-2
+
+
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda", 0)
+
+
+def g(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(dev())
+    return t if dtype is None else t.to(dtype)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def assert_close(got, ref, tol, what):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    bound = tol * (1.0 + np.abs(ref))
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.unravel_index(np.argmax(np.where(bad, err / bound, 0)), ref.shape)
+        raise AssertionError("%s: %d of %d beyond tolerance; worst at %s got %r ref %r"
+                             % (what, bad.sum(), bad.size, idx, got[idx], ref[idx]))
+
+
+def assert_zero_bits(t_np, sel, what):
+    a = np.ascontiguousarray(t_np)
+    bits = a.view(np.uint32) if a.dtype == np.float32 else a.view(np.uint16)
+    nz = bits[sel] != 0
+    assert not nz.any(), "%s: %d padded entries are not +0.0" % (what, nz.sum())
+
+
+def pair_mask(mask):
+    m = mask.astype(bool)
+    return m[:, :, None] & m[:, None, :]
+
+
+def ragged_jets(B, P, ns, seed, hole=True, sigma=0.4):
+    p4, mask, _ = synth.make_jets(B, P, 1, P, fixed_n=tuple(ns), seed=seed, sigma=sigma)
+    if hole and B > 0 and ns[0] > 3:
+        mask = mask.copy()
+        mask[0, 2] = 0  # a non-prefix hole
+    return p4, mask
+
+
+def mlp_for(seed, **kw):
+    return synth.make_mlp_params(rng=np.random.default_rng(seed), **kw)
+
+
+# ---------------------------------------------------------------- features
+@pytest.mark.parametrize("B,P,ns", [(2, 16, (11, 16)), (5, 48, (48, 33, 1, 0, 17)),
+                                    (2, 256, (256, 131))])
+def test_pair_features(B, P, ns):
+    p4, mask = ragged_jets(B, P, ns, seed=B * 100 + P)
+    F = host(pip.pair_features(g(p4), g(mask)))
+    ref = oracle.pair_features(p4, mask)
+    real = pair_mask(mask)
+    assert_close(F, ref, TOL32, "features")
+    assert_zero_bits(F.transpose(0, 2, 3, 1), ~real, "features padding")
+
+
+# ---------------------------------------------------------------- pair embed
+@pytest.mark.parametrize("B,P,ns,kw", [
+    (2, 16, (11, 16), {}),
+    (6, 64, (64, 50, 17, 16, 1, 0), {"biases": True, "input_bn": True}),
+    (3, 256, (256, 200, 33), {"biases": True}),
+])
+def test_pair_embed_f32_ragged(B, P, ns, kw):
+    p4, mask = ragged_jets(B, P, ns, seed=7 + P)
+    params = mlp_for(P, **kw)
+    mlp = pip.PairMLP(params)
+    U = host(pip.pair_embed(g(p4), g(mask), mlp))
+    ref = oracle.pair_embed(p4, mask, params)
+    assert_close(U, ref, TOL32, "U f32")
+    real = pair_mask(mask)
+    assert_zero_bits(U.transpose(0, 2, 3, 1), ~real, "U padding")
+    np.testing.assert_array_equal(U, U.transpose(0, 1, 3, 2))  # exactly symmetric
+
+
+def test_pair_embed_f32_kernel_workload():
+    d = synth.make_workload("kernel")
+    mlp = pip.PairMLP(d["mlp"])
+    U = host(pip.pair_embed(g(d["p4"]), g(d["mask"]), mlp))
+    ref = oracle.pair_embed(d["p4"], d["mask"], d["mlp"])
+    assert_close(U, ref, TOL32, "U f32 (B=128, P=128)")
+    assert_zero_bits(U.transpose(0, 2, 3, 1), ~pair_mask(d["mask"]), "U padding")
+
+
+def test_pair_embed_bf16_large_workload():
+    d = synth.make_workload("large_bf16")
+    mlp = pip.PairMLP(d["mlp"])
+    U = host(pip.pair_embed(g(d["p4"]), g(d["mask"]), mlp, dtype="bf16"))
+    ref = oracle.pair_embed(d["p4"], d["mask"], d["mlp"])
+    assert_close(U, ref, TOLBF, "U bf16 (B=64, P=256)")
+    assert_zero_bits(U.transpose(0, 2, 3, 1), ~pair_mask(d["mask"]), "U bf16 padding")
+
+
+def test_pair_embed_ignores_padding_values():
+    p4, mask = ragged_jets(3, 32, (20, 32, 9), seed=3)
+    params = mlp_for(3, biases=True)
+    mlp = pip.PairMLP(params)
+    U0 = host(pip.pair_embed(g(p4), g(mask), mlp))
+    bad = p4.copy()
+    bad[mask == 0] = np.nan
+    bad[2, 30] = [1e30, -1e30, 3e29, -7e29]
+    U1 = host(pip.pair_embed(g(bad), g(mask), mlp))
+    np.testing.assert_array_equal(U1.view(np.uint32), U0.view(np.uint32))
+
+
+# ---------------------------------------------------------------- attention
+def rand_qkv(B, H, P, mask, seed, dtype="f32"):
+    return synth.make_qkv(B, H, P, 16, mask, rng=np.random.default_rng(seed), dtype=dtype)
+
+
+@pytest.mark.parametrize("B,H,P,ns", [(2, 8, 16, (11, 16)), (5, 3, 48, (48, 33, 1, 0, 17)),
+                                      (2, 8, 256, (256, 77))])
+def test_attention_f32_ragged(B, H, P, ns):
+    _, mask = ragged_jets(B, P, ns, seed=P)
+    q, k, v = rand_qkv(B, H, P, mask, seed=P)
+    u = np.random.default_rng(P + 1).normal(0, 1.5, size=(B, H, P, P)).astype(np.float32)
+    O = host(pip.pair_bias_attention(g(q), g(k), g(v), g(u), g(mask)))
+    ref = oracle.attention(q, k, v, u, mask)
+    assert_close(O, ref, TOL32, "O f32")
+    assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "O padded rows")
+
+
+def test_attention_f32_kernel_workload_with_oracle_bias():
+    d = synth.make_workload("kernel")
+    U = oracle.pair_embed(d["p4"], d["mask"], d["mlp"]).astype(np.float32)
+    O = host(pip.pair_bias_attention(g(d["q"]), g(d["k"]), g(d["v"]), g(U), g(d["mask"])))
+    ref = oracle.attention(d["q"], d["k"], d["v"], U, d["mask"])
+    assert_close(O, ref, TOL32, "O f32 (B=128, P=128)")
+    assert_zero_bits(O.transpose(0, 2, 1, 3), d["mask"] == 0, "O padded rows")
+
+
+def test_attention_bf16_large_workload():
+    d = synth.make_workload("large_bf16")
+    U = synth.bf16_round(oracle.pair_embed(d["p4"], d["mask"], d["mlp"]).astype(np.float32))
+    bf = torch.bfloat16
+    O = host(pip.pair_bias_attention(g(d["q"], bf), g(d["k"], bf), g(d["v"], bf), g(U, bf),
+                                     g(d["mask"])))
+    ref = oracle.attention(d["q"], d["k"], d["v"], U, d["mask"])
+    assert_close(O, ref, TOLBF, "O bf16 (B=64, P=256)")
+    assert_zero_bits(O.transpose(0, 2, 1, 3), d["mask"] == 0, "O bf16 padded rows")
+
+
+def test_attention_ignores_padding_values_and_empty_jets():
+    B, H, P = 3, 8, 32
+    _, mask = ragged_jets(B, P, (20, 0, 9), seed=5)
+    q, k, v = rand_qkv(B, H, P, mask, seed=5)
+    u = np.random.default_rng(6).normal(0, 1, size=(B, H, P, P)).astype(np.float32)
+    O0 = host(pip.pair_bias_attention(g(q), g(k), g(v), g(u), g(mask)))
+    q2, k2, v2, u2 = (x.copy() for x in (q, k, v, u))
+    pad = mask == 0
+    for x in (q2, k2, v2):
+        x[pad[:, None, :, None].repeat(H, 1).repeat(16, 3)] = np.nan
+    u2[np.broadcast_to(pad[:, None, None, :], u2.shape)] = 1e30
+    u2[np.broadcast_to(pad[:, None, :, None], u2.shape)] = np.nan
+    O1 = host(pip.pair_bias_attention(g(q2), g(k2), g(v2), g(u2), g(mask)))
+    np.testing.assert_array_equal(O1.view(np.uint32), O0.view(np.uint32))
+    assert np.all(O0.view(np.uint32)[1] == 0)  # the all-padded jet
+
+
+def test_embed_then_attention_chain_f32():
+    d = synth.make_workload("tiny")
+    mlp = pip.PairMLP(d["mlp"])
+    U = pip.pair_embed(g(d["p4"]), g(d["mask"]), mlp)
+    O = host(pip.pair_bias_attention(g(d["q"]), g(d["k"]), g(d["v"]), U, g(d["mask"])))
+    ref = oracle.pair_embed_attention(d["p4"], d["mask"], d["mlp"], d["q"], d["k"], d["v"])
+    assert_close(O, ref, TOL32, "embed -> attention (tiny)")
+
+
+def test_empty_batch_is_a_noop():
+    mlp = pip.PairMLP(mlp_for(1))
+    p4 = torch.zeros((0, 16, 4), device=dev())
+    mask = torch.zeros((0, 16), device=dev(), dtype=torch.uint8)
+    U = pip.pair_embed(p4, mask, mlp)
+    assert U.shape == (0, 8, 16, 16)
