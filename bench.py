@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the pair-interaction hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic jets at the kernel
+benchmark shape of the ml4sci_cms_e2e26 README ("Results", table "ParT
+Kernels": N=128 jets, P=128 slots, H=8, D=16): pair_embed (features + pair MLP
+-> U, float32) then pair_bias_attention (masked softmax(QK^T/sqrt(D) + U) V).
+Inputs are resident on the GPU before the timed region.  Prints ONE JSON line.
+
+  value            = B * P^2 slot pairs per second of the whole step
+  roofline         = the pair-embed kernel (the dominant one) against the
+                     float32 MFMA peak, algorithmic flops = unique real pairs
+                     n(n+1)/2 per jet x 17,920 flop
+  cpu_baseline     = the CPU oracle on the same workload (host threads)
+  workloads        = the other workloads (fused batch-512, bf16 large jets,
+                     8-layer block stack) timed the same way
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("pairs/s fused PairEmbed+MLP and µs biased attn at B=128 P=128 H=8 D=16; "
+          "%roofline")
+MLP_FLOP_PER_PAIR = 2 * (4 * 64 + 64 * 64 + 64 * 64 + 64 * 8)  # 17,920
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pair_embed_f32_kernel_B128_P128_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "pair_interaction_particle_amd", "csrc", f)
+                  for f in ("pair_embed.hip", "pip_device.h")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per pair-embed launch from the committed rocprofv3 --pmc
+    summary, or None when absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def pair_counts(mask):
+    import numpy as np
+    n = (mask != 0).sum(axis=1).astype(np.int64)
+    return int((n * (n + 1) // 2).sum()), int((n * n).sum()), n
+
+
+def attention_bytes(mask, H, P, D, elt):
+    """Algorithmic bytes of one attention launch: real Q/K/V rows and real U
+    pairs read, the full O written (padding zeros are part of the result)."""
+    import numpy as np
+    n = (mask != 0).sum(axis=1).astype(np.int64)
+    B = mask.shape[0]
+    return int(H * (3 * n.sum() * D + (n * n).sum()) * elt + B * H * P * D * elt)
+
+
+def time_events(fns, reps, warmup):
+    """Average device time (ms) of each callable in fns, measured with events
+    recorded on the current stream around each launch."""
+    import torch
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+          for _ in range(reps)]
+    t0 = time.perf_counter()
+    for r in range(reps):
+        ev[r][0].record()
+        for i, f in enumerate(fns):
+            f()
+            ev[r][i + 1].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / reps
+    per = [sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
+           for i in range(len(fns))]
+    return per, wall_ms
+
+
+def to_dev(x, dtype=None):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def cpu_baseline(d, budget_s):
+    """The oracle (fp64, OpenMP over jets) on the same workload, repeated
+    until about budget_s seconds of wall time have passed."""
+    import oracle
+    B, P = d["mask"].shape
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 1000:
+        t = time.perf_counter()
+        U = oracle.pair_embed(d["p4"], d["mask"], d["mlp"])
+        oracle.attention(d["q"], d["k"], d["v"], U, d["mask"])
+        t_total += time.perf_counter() - t
+        reps += 1
+    return {"value": B * P * P * reps / t_total, "unit": "slot-pairs/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "whole kernel workload (B=128 jets, P=128) run %d time(s): float64 pair "
+                      "embed + attention, %.1f s wall" % (reps, t_total)}
+
+
+def bench_extra(pip, synth, reps, warmup):
+    """Time the other workloads' entries (parity for them is in tests/)."""
+    import torch
+    out = {}
+    # bf16 large jets: pair_embed (bf16 MLP) + attention (bf16)
+    d = synth.make_workload("large_bf16")
+    B, P = d["mask"].shape
+    p4, mask = to_dev(d["p4"]), to_dev(d["mask"])
+    bf = torch.bfloat16
+    q, k, v = (to_dev(d[x], bf) for x in ("q", "k", "v"))
+    mlp = pip.PairMLP(d["mlp"])
+    U = torch.empty((B, 8, P, P), device="cuda", dtype=bf)
+    O = torch.empty_like(q)
+    (te, ta), _ = time_events([lambda: pip.pair_embed(p4, mask, mlp, "bf16", out=U),
+                               lambda: pip.pair_bias_attention(q, k, v, U, mask, out=O)],
+                              reps, warmup)
+    uniq, ordered, _ = pair_counts(d["mask"])
+    ab = attention_bytes(d["mask"], 8, P, 16, 2)
+    out["large_bf16"] = {
+        "shape": "B=64 P=256 n~U{60..256} H=8 D=16 bf16",
+        "pair_embed_us": te * 1e3, "attention_us": ta * 1e3,
+        "pair_embed_slot_pairs_per_s": B * P * P / (te * 1e-3),
+        "pair_embed_mfma_tflops": uniq * MLP_FLOP_PER_PAIR / (te * 1e-3) / 1e12,
+        "attention_gbs": ab / (ta * 1e-3) / 1e9,
+        "attention_hbm_frac": ab / (ta * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del U, O, q, k, v
+    # fused batch-512
+    d = synth.make_workload("fused512")
+    B, P = d["mask"].shape
+    p4, mask = to_dev(d["p4"]), to_dev(d["mask"])
+    q, k, v = (to_dev(d[x]) for x in ("q", "k", "v"))
+    mlp = pip.PairMLP(d["mlp"])
+    O = torch.empty_like(q)
+    try:
+        (tf,), _ = time_events([lambda: pip.pair_embed_attention(p4, mask, mlp, q, k, v, out=O)],
+                               reps, warmup)
+        uniq, ordered, _ = pair_counts(d["mask"])
+        flops = uniq * MLP_FLOP_PER_PAIR + ordered * 8 * 64
+        out["fused512"] = {"shape": "B=512 P=128 n~U{20..128} H=8 D=16 fp32, 5% massive",
+                           "pair_embed_attention_us": tf * 1e3,
+                           "slot_pairs_per_s": B * P * P / (tf * 1e-3),
+                           "mfma_tflops": flops / (tf * 1e-3) / 1e12,
+                           "mfma_frac": flops / (tf * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
+    except pip.PipError as e:
+        out["fused512"] = {"error": str(e)}
+    del O, q, k, v
+    # block stack: 8 layers reusing U
+    d = synth.make_workload("stack8")
+    B, P = d["mask"].shape
+    mask = to_dev(d["mask"])
+    mlp = pip.PairMLP(d["mlp"])
+    U = pip.pair_embed(to_dev(d["p4"]), mask, mlp)
+    x0 = to_dev(d["x0"])
+    X = x0.clone()
+    w = [to_dev(d[x]) for x in ("wq", "wk", "wv", "wo")]
+    ws = torch.empty(pip.block_stack_workspace_bytes(B, P, 128) // 4, device="cuda")
+    try:
+        # X is updated in place; re-applying the stack to the running X does
+        # the same work every time (the path has no data-dependent work).
+        (tb,), _ = time_events([lambda: pip.block_stack(X, *w, U, mask, workspace=ws)],
+                               reps, warmup)
+        nr = int((d["mask"] != 0).sum())
+        _, ordered, _ = pair_counts(d["mask"])
+        flops = 8 * (nr * 128 * 128 * 2 * 4 + ordered * 8 * 64)
+        out["stack8"] = {"shape": "B=128 P=128 C=128 H=8 D=16 L=8 fp32",
+                         "block_stack_us": tb * 1e3,
+                         "mfma_tflops": flops / (tb * 1e-3) / 1e12,
+                         "mfma_frac": flops / (tb * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
+    except pip.PipError as e:
+        out["stack8"] = {"error": str(e)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path shards over jets with no exchange, "
+              "and this build runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from pair_interaction_particle_amd import binding as pip
+    from pair_interaction_particle_amd import synth
+
+    torch.cuda.set_device(0)
+    d = synth.make_workload("kernel")
+    B, P = d["mask"].shape
+    H, D = 8, 16
+    p4, mask = to_dev(d["p4"]), to_dev(d["mask"])
+    q, k, v = (to_dev(d[x]) for x in ("q", "k", "v"))
+    mlp = pip.PairMLP(d["mlp"])
+    U = torch.empty((B, H, P, P), device="cuda", dtype=torch.float32)
+    O = torch.empty_like(q)
+
+    def embed():
+        pip.pair_embed(p4, mask, mlp, out=U)
+
+    def attn():
+        pip.pair_bias_attention(q, k, v, U, mask, out=O)
+
+    (t_embed, t_attn), wall_ms = time_events([embed, attn], args.steps, args.warmup)
+    ms_per_step = wall_ms
+    slot_pairs = B * P * P
+    uniq, ordered, n = pair_counts(d["mask"])
+    flops = uniq * MLP_FLOP_PER_PAIR
+    achieved = flops / (t_embed * 1e-3) / 1e12
+    traffic = measured_traffic()
+    ab = attention_bytes(d["mask"], H, P, D, 4)
+    res = {
+        "metric": METRIC,
+        "value": slot_pairs / (ms_per_step * 1e-3),
+        "unit": "slot-pairs/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "kernel: B=128 jets, P=128 slots, real n~U{20..128}, H=8, "
+                               "D=16, fp32; step = pair_embed + pair_bias_attention",
+                   "B": B, "P": P, "H": H, "D": D, "global_batch": B, "seq_len": P,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+                     "traffic": traffic, "kernel": "pair_embed_kernel<false> (fp32)",
+                     "algorithmic_flop_per_launch": flops,
+                     "unique_real_pairs": uniq},
+        "pair_embed_us": t_embed * 1e3,
+        "pair_embed_slot_pairs_per_s": slot_pairs / (t_embed * 1e-3),
+        "attention_us": t_attn * 1e3,
+        "attention_roofline": {"bound": "hbm", "achieved": ab / (t_attn * 1e-3) / 1e9,
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": ab / (t_attn * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               "algorithmic_bytes_per_launch": ab},
+        "real_ordered_pairs": ordered,
+    }
+    if not args.no_extra:
+        res["workloads"] = bench_extra(pip, synth, max(10, args.steps // 2), 3)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

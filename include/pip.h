@@ -141,8 +141,12 @@ pip_status pip_pair_bias_attention(const void *Q, const void *K, const void *V, 
 
 /* Fused pair embedding + attention with H = 8: the same O as pip_pair_embed
  * followed by pip_pair_bias_attention, but U only ever lives on chip.
- * Q, K, V, O are (B, 8, P, D) in `dtype`.  Requires D == 16, P % 16 == 0,
- * 16 <= P <= 256.  Errors: NULL, SHAPE, ALIGN, DTYPE, UNSUPPORTED, HIP. */
+ * Q, K, V, O are (B, 8, P, D) in `dtype` (PIP_BF16: the MLP as in
+ * pip_pair_embed's bf16 mode, U kept in float32 on chip, attention as in
+ * pip_pair_bias_attention's bf16 mode).  Unlike the other entries it also
+ * requires `mask` to be 16-byte aligned (rows are read as 16-byte vectors).
+ * Requires D == 16, P % 16 == 0, 16 <= P <= 256.  Errors: NULL, SHAPE,
+ * ALIGN, DTYPE, UNSUPPORTED, HIP. */
 pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
                                     const pip_pair_mlp *mlp, const void *Q, const void *K,
                                     const void *V, int64_t B, int64_t P, int64_t D, void *O,
@@ -160,7 +164,7 @@ size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C);
  * X (B, P, C) is updated in place; Wq, Wk, Wv, Wo are (L, C, C) applied as
  * X @ W.  Padded rows of X are left unchanged (their O is 0).  workspace
  * must hold pip_block_stack_workspace_bytes(B, P, C) bytes.
- * Requires C == 16 * H, H >= 1, C <= 256, P % 16 == 0, 16 <= P <= 256.
+ * Requires C == 16 * H, 1 <= H <= 16, P % 16 == 0, 16 <= P <= 256.
  * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, HIP. */
 pip_status pip_block_stack(float *X, const float *Wq, const float *Wk, const float *Wv,
                            const float *Wo, const float *U, const uint8_t *mask, int64_t B,

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "pip_internal.h"
+#include "pip_mlp.h"
 
 namespace {
 
@@ -120,28 +121,29 @@ pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **ou
     if (st != PIP_OK) return st;
     const float *W1 = w.data(), *W2 = W1 + 256, *W3 = W2 + 4096, *W4 = W3 + 4096;
 
-    // float32 operands (layouts in pip_internal.h)
-    std::vector<float> p32(pip::kW32Ops * 64);
+    // float32 operands, grouped by four per lane (layouts in pip_mlp.h):
+    // operand op of lane l lives at ((op / 4) * 64 + l) * 4 + op % 4.
+    std::vector<float> p32(pip::kW32Floats);
+    auto at32 = [&](int op, int l) -> float & { return p32[((op / 4) * 64 + l) * 4 + op % 4]; };
     for (int c = 0; c < 4; ++c)
-        for (int l = 0; l < 64; ++l) p32[pip::kW32L1 + c * 64 + l] = W1[(16 * c + l % 16) * 4 + l / 16];
+        for (int l = 0; l < 64; ++l) at32(c, l) = W1[(16 * c + l % 16) * 4 + l / 16];
     const float *Wh[2] = {W2, W3};
-    const int offs[2] = {pip::kW32L2, pip::kW32L3};
     for (int t = 0; t < 2; ++t)
         for (int co = 0; co < 4; ++co)
             for (int ci = 0; ci < 4; ++ci)
                 for (int r = 0; r < 4; ++r)
                     for (int l = 0; l < 64; ++l)
-                        p32[offs[t] + ((co * 4 + ci) * 4 + r) * 64 + l] =
+                        at32(4 + 64 * t + (co * 4 + ci) * 4 + r, l) =
                             Wh[t][(16 * co + l % 16) * 64 + 16 * ci + 4 * (l / 16) + r];
     for (int ci = 0; ci < 4; ++ci)
         for (int r = 0; r < 4; ++r)
             for (int l = 0; l < 64; ++l)
-                p32[pip::kW32L4 + (ci * 4 + r) * 64 + l] =
+                at32(132 + ci * 4 + r, l) =
                     (l % 16 < 8) ? W4[(l % 16) * 64 + 16 * ci + 4 * (l / 16) + r] : 0.0f;
 
     // bfloat16 operands: 8 values per lane; slot j < 4 -> channel 32s + 4g + j,
     // slot j >= 4 -> channel 32s + 16 + 4g + (j - 4)
-    std::vector<uint16_t> p16(pip::kW16Ops * 64 * 8);
+    std::vector<uint16_t> p16(pip::kW16Elems);
     auto chan = [](int s, int g, int j) { return 32 * s + (j < 4 ? 0 : 16) + 4 * g + (j & 3); };
     const int offs16[2] = {pip::kW16L2, pip::kW16L3};
     for (int t = 0; t < 2; ++t)
@@ -245,7 +247,8 @@ pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
     if (st != PIP_OK || B == 0 || P == 0) return st;
     if (!p4 || !mask || !mlp || !Q || !K || !V || !O) return PIP_ERR_NULL;
     if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
-    if (!aligned16(p4) || !aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    if (!aligned16(p4) || !aligned16(mask) || !aligned16(Q) || !aligned16(K) ||
+        !aligned16(V) || !aligned16(O))
         return PIP_ERR_ALIGN;
     if ((st = check_device(mlp)) != PIP_OK) return st;
     hipStream_t s = (hipStream_t)stream;
@@ -273,7 +276,7 @@ pip_status pip_block_stack(float *X, const float *Wq, const float *Wk, const flo
     if (B == 0 || P == 0 || L == 0) return PIP_OK;
     if (!X || !Wq || !Wk || !Wv || !Wo || !U || !mask) return PIP_ERR_NULL;
     if (H == 0 || C != (int64_t)PIP_HEAD_DIM * H) return PIP_ERR_SHAPE;
-    if (C > 256 || C % 64 != 0) return PIP_ERR_UNSUPPORTED;
+    if (H > 16) return PIP_ERR_UNSUPPORTED;
     if (!workspace) return PIP_ERR_NULL;
     if (workspace_bytes < pip_block_stack_workspace_bytes(B, P, C)) return PIP_ERR_SHAPE;
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||

@@ -1,17 +1,430 @@
-// fused.hip -- placeholder until the fused kernel lands.
+// fused.hip -- pair embedding and biased attention in one kernel: U only ever
+// lives on chip ("Fusion 2" and "Fusion 3" of the ml4sci_cms_e2e26 README,
+// "How the Kernel Fusion Works", composed).
+//
+// Jet kernel (P <= 128).  One 512-thread workgroup per jet walks the lower
+// triangle of 16x16 tiles in rounds.  In each round the 8 waves push the
+// tile's pair blocks through the MFMA MLP chain into an LDS tile of U (8
+// heads), then wave h applies head h of that tile twice: to query block I
+// against key block J, and (transposed) to query block J against key block I.
+// So every unique pair goes through the MLP once, as in pair_embed.  Each
+// wave owns the online-softmax state (O, running max, running sum) of its
+// head for every query block, kept in LDS, so no two waves ever update the
+// same state and one barrier per round suffices (the U tile is double
+// buffered).  Jets are taken largest first: every workgroup ranks the jets
+// by real multiplicity (from the mask) and takes the one whose rank is its
+// block index, so the hardware dispatcher schedules longest-job-first.
+//
+// Row kernel (any P <= 256).  One 256-thread workgroup per (jet, query block
+// I) computes the U tiles (I, J) for every key block J and consumes them at
+// once; each wave owns two heads.  It recomputes the MLP for the mirrored
+// pairs and is used only where the jet kernel's LDS state does not fit.
+#include <type_traits>
+
+#include "pip_attn.h"
 #include "pip_internal.h"
+#include "pip_mlp.h"
+
 namespace pip {
-hipError_t launch_embed_attention_f32(const float *, const uint8_t *, int, int, const pip_pair_mlp *,
-                                      const float *, const float *, const float *, float *, hipStream_t) {
-    return hipErrorNotSupported;
+
+__device__ __forceinline__ int tri_row_f(int t) {
+    int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    while (i * (i + 1) / 2 > t) --i;
+    return i;
 }
-hipError_t launch_embed_attention_bf16(const float *, const uint8_t *, int, int, const pip_pair_mlp *,
-                                       const uint16_t *, const uint16_t *, const uint16_t *, uint16_t *,
-                                       hipStream_t) {
-    return hipErrorNotSupported;
+
+__device__ __forceinline__ bool block_pair_f(bool diag, int k, int nblk, int lane, int &i,
+                                             int &j) {
+    if (k >= nblk) {
+        i = j = 0;
+        return false;
+    }
+    if (!diag) {
+        i = k;
+        j = lane & 15;
+        return true;
+    }
+    int p = 16 * k + (lane & 15);
+    const bool valid = p < 136;
+    p = valid ? p : 0;
+    i = tri_row_f(p);
+    j = p - i * (i + 1) / 2;
+    return valid;
 }
-hipError_t launch_block_stack(float *, const float *, const float *, const float *, const float *,
-                              const float *, const uint8_t *, int, int, int, int, int, float *, hipStream_t) {
-    return hipErrorNotSupported;
+
+// number of nonzero bytes in a 32-bit word
+__device__ __forceinline__ int nz_bytes(uint32_t w) {
+    uint32_t t = w | (w >> 4);
+    t |= t >> 2;
+    t |= t >> 1;
+    return __popc(t & 0x01010101u);
 }
+
+// Element type of Q/K/V/O.
+template <bool kBf16>
+using QkvT = typename std::conditional<kBf16, uint16_t, float>::type;
+
+template <bool kBf16>
+__device__ __forceinline__ v4f scores(const QkvT<kBf16> *Qh, const QkvT<kBf16> *Kh, int q0,
+                                      int k0) {
+    if constexpr (kBf16) return scores_bf16(Qh, Kh, q0, k0);
+    else return scores_f32(Qh, Kh, q0, k0);
+}
+template <bool kBf16>
+__device__ __forceinline__ v4f pv(const QkvT<kBf16> *Vh, int k0, const v4f &p,
+                                  const int (&kreal)[4], v4f acc) {
+    if constexpr (kBf16) return pv_bf16(Vh, k0, p, kreal, acc);
+    else return pv_f32(Vh, k0, p, kreal, acc);
+}
+template <bool kBf16>
+__device__ __forceinline__ void store_o(QkvT<kBf16> *Orow, const v4f &o) {
+    if constexpr (kBf16)
+        *(uint2 *)Orow = make_uint2((uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16),
+                                    (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16));
+    else *(float4 *)Orow = make_float4(o[0], o[1], o[2], o[3]);
+}
+
+// Stage the MLP weights of the chosen precision into LDS.
+template <bool kBf16, int kThreads>
+__device__ inline void stage_mlp(float4 *wl, v8bf *wl16, float *bl, const float4 *w32,
+                                 const v8bf *w16, const float *bias) {
+    stage_weights<kThreads>(wl, bl, w32, bias, kBf16 ? 64 : kW32Groups * 64);
+    if constexpr (kBf16)
+        for (int i = threadIdx.x; i < kW16Ops * 64; i += kThreads) wl16[i] = w16[i];
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void mlp2(const float4 *wl, const v8bf *wl16, const float *bl,
+                                     float fA, float fB, v4f &uA, v4f &uB) {
+    if constexpr (kBf16) mlp2_bf16(wl, wl16, bl, fA, fB, uA, uB);
+    else mlp2_f32(wl, bl, fA, fB, uA, uB);
+}
+
+// ------------------------------------------------------------ jet kernel
+constexpr int kJetThreads = 512;
+constexpr int kJetMaxP = 128;
+constexpr int kJetMaxT = kJetMaxP / kTile;
+constexpr int kSortMaxB = 2048;
+
+template <bool kBf16>
+__global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
+    const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B, int P, int sort,
+    const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
+    const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
+    const QkvT<kBf16> *__restrict__ K, const QkvT<kBf16> *__restrict__ V,
+    QkvT<kBf16> *__restrict__ O) {
+    constexpr int kW4 = kBf16 ? 64 : kW32Groups * 64;
+    __shared__ float4 wl[kW4];
+    __shared__ v8bf wl16[kBf16 ? kW16Ops * 64 : 1];
+    __shared__ float bl[kBiasFloats];
+    __shared__ PartLds<kJetMaxP> L;
+    __shared__ float us[2][kHeads][16][17];
+    __shared__ float4 Ost[kHeads][kJetMaxT][64];  // O^T accumulators, lane layout
+    __shared__ float mst[kHeads][kJetMaxT][16], lst[kHeads][kJetMaxT][16];
+    __shared__ int blkAny[kJetMaxT];
+    __shared__ uint16_t nj[kSortMaxB];
+    __shared__ int hist[kJetMaxP + 2];
+    __shared__ int scanbuf[kJetThreads];
+    __shared__ int jetSel;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int T = P / kTile;
+
+    // ---- which jet: rank blockIdx.x in the order (n descending, index ascending)
+    if (sort) {
+        for (int i = tid; i <= P + 1; i += kJetThreads) hist[i] = 0;
+        __syncthreads();
+        for (int b = tid; b < B; b += kJetThreads) {
+            const uint4 *row = (const uint4 *)(mask + (size_t)b * P);
+            int n = 0;
+            for (int w = 0; w < P / 16; ++w) {
+                const uint4 v = row[w];
+                n += nz_bytes(v.x) + nz_bytes(v.y) + nz_bytes(v.z) + nz_bytes(v.w);
+            }
+            nj[b] = (uint16_t)n;
+            atomicAdd(&hist[n], 1);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            // bin of rank r: bins in descending n; find n* and the rank within it
+            int r = blockIdx.x, n = P;
+            while (r >= hist[n]) {
+                r -= hist[n];
+                --n;
+            }
+            hist[P + 1] = n;  // n*
+            scanbuf[0] = r;   // k: position among the jets with n == n*
+        }
+        __syncthreads();
+        const int nstar = hist[P + 1], k = scanbuf[0];
+        // k-th jet (index order) with n == nstar: contiguous ranges per thread
+        const int per = (B + kJetThreads - 1) / kJetThreads;
+        const int b0 = tid * per, b1 = min(b0 + per, B);
+        int cnt = 0;
+        for (int b = b0; b < b1; ++b) cnt += nj[b] == nstar;
+        __syncthreads();
+        scanbuf[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < kJetThreads; off <<= 1) {  // inclusive scan
+            const int v = (tid >= off) ? scanbuf[tid - off] : 0;
+            __syncthreads();
+            scanbuf[tid] += v;
+            __syncthreads();
+        }
+        const int excl = scanbuf[tid] - cnt;
+        if (k >= excl && k < excl + cnt) {
+            int seen = excl;
+            for (int b = b0; b < b1; ++b)
+                if (nj[b] == nstar) {
+                    if (seen == k) jetSel = b;
+                    ++seen;
+                }
+        }
+        __syncthreads();
+    } else if (tid == 0) {
+        jetSel = blockIdx.x;
+    }
+    if (!sort) __syncthreads();
+    const int jet = jetSel;
+
+    // ---- stage particles, weights, state
+    for (int s = tid; s < P; s += kJetThreads) {
+        const size_t idx = (size_t)jet * P + s;
+        const int real = mask[idx] != 0;
+        stage_particle(L, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+    }
+    stage_mlp<kBf16, kJetThreads>(wl, wl16, bl, w32, w16, bias);
+    for (int i = tid; i < kHeads * T * 64; i += kJetThreads)
+        (&Ost[0][0][0])[(i / (T * 64)) * kJetMaxT * 64 + i % (T * 64)] =
+            make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = tid; i < kHeads * kJetMaxT * 16; i += kJetThreads) {
+        (&mst[0][0][0])[i] = -INFINITY;
+        (&lst[0][0][0])[i] = 0.0f;
+    }
+    __syncthreads();
+    if (tid < T) {
+        int a = 0;
+        for (int i = 0; i < kTile; ++i) a |= L.real[tid * kTile + i];
+        blkAny[tid] = a;
+    }
+    __syncthreads();
+
+    const int h = wave;  // this wave's head
+    const size_t hb = ((size_t)jet * kHeads + h) * P;
+    const QkvT<kBf16> *Qh = Q + hb * 16, *Kh = K + hb * 16, *Vh = V + hb * 16;
+
+    // one attention unit: query block qb against key block kb of head h, U
+    // element (query q, key k) = Ut[q][k] (or Ut[k][q] when transposed)
+    auto unit = [&](const float (*Ut)[17], bool transposed, int qb, int kb) {
+        const int q0 = qb * kTile, k0 = kb * kTile;
+        v4f s = scores<kBf16>(Qh, Kh, q0, k0);
+        int kreal[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            kreal[r] = L.real[k0 + 4 * g + r];
+            const float u = transposed ? Ut[4 * g + r][c] : Ut[c][4 * g + r];
+            s[r] = kreal[r] ? fmaf(s[r], kQkScale2, u * kLog2e) : -INFINITY;
+        }
+        float m = mst[h][qb][c], l = lst[h][qb][c];
+        const float corr = online_softmax(s, m, l);
+        const float4 a4 = Ost[h][qb][lane];
+        v4f acc = {a4.x * corr, a4.y * corr, a4.z * corr, a4.w * corr};
+        acc = pv<kBf16>(Vh, k0, s, kreal, acc);
+        Ost[h][qb][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if (g == 0) {
+            mst[h][qb][c] = m;
+            lst[h][qb][c] = l;
+        }
+    };
+
+    const int ntri = T * (T + 1) / 2;
+    int round = 0;
+    for (int t = 0; t < ntri; ++t) {
+        const int I = tri_row_f(t), J = t - I * (I + 1) / 2;
+        if (!(blkAny[I] && blkAny[J])) continue;
+        const int buf = round & 1;
+        ++round;
+        const bool diag = (I == J);
+        const int nblk = diag ? 9 : 16;
+        const int r0 = I * kTile, c0 = J * kTile;
+        int iA, jA, iB, jB;
+        const bool vA = block_pair_f(diag, 2 * wave, nblk, lane, iA, jA);
+        const bool vB = block_pair_f(diag, 2 * wave + 1, nblk, lane, iB, jB);
+        const bool realA = vA && L.real[r0 + iA] && L.real[c0 + jA];
+        const bool realB = vB && L.real[r0 + iB] && L.real[c0 + jB];
+        if (__ballot(realA || realB) != 0) {
+            const int k = lane >> 4;
+            const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, k) : 0.0f;
+            const float fB = realB ? pair_feature(L, r0 + iB, c0 + jB, k) : 0.0f;
+            v4f uA, uB;
+            mlp2<kBf16>(wl, wl16, bl, fA, fB, uA, uB);
+            if (lane < 32) {
+                const int h0 = (lane >> 4) * 4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (vA) {
+                        us[buf][h0 + r][iA][jA] = uA[r];
+                        if (diag) us[buf][h0 + r][jA][iA] = uA[r];
+                    }
+                    if (vB) {
+                        us[buf][h0 + r][iB][jB] = uB[r];
+                        if (diag) us[buf][h0 + r][jB][iB] = uB[r];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        unit(us[buf][h], false, I, J);
+        if (!diag) unit(us[buf][h], true, J, I);
+    }
+
+    // ---- finalise this head: O = acc / l on real queries, exact 0 elsewhere
+    for (int qb = 0; qb < T; ++qb) {
+        const int q = qb * kTile + c;
+        const bool rq = blkAny[qb] && L.real[q];
+        v4f o = {0.f, 0.f, 0.f, 0.f};
+        if (rq) {
+            const float4 a4 = Ost[h][qb][lane];
+            const float inv = 1.0f / lst[h][qb][c];
+            o = (v4f){a4.x * inv, a4.y * inv, a4.z * inv, a4.w * inv};
+        }
+        store_o<kBf16>(O + (hb + q) * 16 + 4 * g, o);
+    }
+}
+
+// ------------------------------------------------------------ row kernel
+constexpr int kRowThreads = 256;
+
+template <bool kBf16>
+__global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
+    const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
+    const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
+    const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
+    const QkvT<kBf16> *__restrict__ K, const QkvT<kBf16> *__restrict__ V,
+    QkvT<kBf16> *__restrict__ O) {
+    constexpr int kW4 = kBf16 ? 64 : kW32Groups * 64;
+    __shared__ float4 wl[kW4];
+    __shared__ v8bf wl16[kBf16 ? kW16Ops * 64 : 1];
+    __shared__ float bl[kBiasFloats];
+    __shared__ PartLds<kMaxP> L;
+    __shared__ float us[kHeads][16][17];
+    __shared__ int blkAny[kMaxP / kTile];
+
+    const int T = P / kTile;
+    const int jet = blockIdx.x / T, I = blockIdx.x - jet * T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int r0 = I * kTile;
+
+    for (int s = tid; s < P; s += kRowThreads) {
+        const size_t idx = (size_t)jet * P + s;
+        const int real = mask[idx] != 0;
+        stage_particle(L, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+    }
+    __syncthreads();
+    if (tid < T) {
+        int a = 0;
+        for (int i = 0; i < kTile; ++i) a |= L.real[tid * kTile + i];
+        blkAny[tid] = a;
+    }
+    __syncthreads();
+    if (!blkAny[I]) {  // no real query in this block: zeros
+        for (int i = tid; i < kHeads * 16 * 4; i += kRowThreads) {
+            const int hh = i >> 6, q = (i >> 2) & 15, d4 = (i & 3) * 4;
+            store_o<kBf16>(O + ((((size_t)jet * kHeads + hh) * P) + r0 + q) * 16 + d4,
+                           (v4f){0.f, 0.f, 0.f, 0.f});
+        }
+        return;
+    }
+    stage_mlp<kBf16, kRowThreads>(wl, wl16, bl, w32, w16, bias);
+    __syncthreads();
+
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int J = 0; J < T; ++J) {
+        if (!blkAny[J]) continue;
+        const int c0 = J * kTile;
+        for (int pass = 0; pass < 2; ++pass) {  // rows 8 pass + 2 wave + {0, 1}
+            const int iA = 8 * pass + 2 * wave, iB = iA + 1, j = lane & 15;
+            const bool realA = L.real[r0 + iA] && L.real[c0 + j];
+            const bool realB = L.real[r0 + iB] && L.real[c0 + j];
+            if (__ballot(realA || realB) == 0) continue;
+            const int k = lane >> 4;
+            const float fA = realA ? pair_feature(L, r0 + iA, c0 + j, k) : 0.0f;
+            const float fB = realB ? pair_feature(L, r0 + iB, c0 + j, k) : 0.0f;
+            v4f uA, uB;
+            mlp2<kBf16>(wl, wl16, bl, fA, fB, uA, uB);
+            if (lane < 32) {
+                const int h0 = (lane >> 4) * 4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    us[h0 + r][iA][j] = uA[r];
+                    us[h0 + r][iB][j] = uB[r];
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int h = 2 * wave + hh;
+            const size_t hb = ((size_t)jet * kHeads + h) * P;
+            v4f s = scores<kBf16>(Q + hb * 16, K + hb * 16, r0, c0);
+            int kreal[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                kreal[r] = L.real[c0 + 4 * g + r];
+                s[r] = kreal[r] ? fmaf(s[r], kQkScale2, us[h][c][4 * g + r] * kLog2e)
+                                : -INFINITY;
+            }
+            const float corr = online_softmax(s, m[hh], l[hh]);
+            acc[hh] *= corr;
+            acc[hh] = pv<kBf16>(V + hb * 16, c0, s, kreal, acc[hh]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int h = 2 * wave + hh;
+        const size_t hb = ((size_t)jet * kHeads + h) * P;
+        const int q = r0 + c;
+        const bool rq = L.real[q];
+        const float inv = rq ? 1.0f / l[hh] : 0.0f;
+        v4f o = rq ? acc[hh] * inv : (v4f){0.f, 0.f, 0.f, 0.f};
+        store_o<kBf16>(O + (hb + q) * 16 + 4 * g, o);
+    }
+}
+
+template <bool kBf16>
+static hipError_t launch_fused(const float *p4, const uint8_t *mask, int B, int P,
+                               const pip_pair_mlp *m, const QkvT<kBf16> *Q,
+                               const QkvT<kBf16> *K, const QkvT<kBf16> *V, QkvT<kBf16> *O,
+                               hipStream_t s) {
+    if (P <= kJetMaxP) {
+        const int sort = B <= kSortMaxB ? 1 : 0;
+        hipLaunchKernelGGL(embed_attention_jet_kernel<kBf16>, dim3(B), dim3(kJetThreads), 0, s,
+                           (const float4 *)p4, mask, B, P, sort, (const float4 *)m->w32,
+                           (const v8bf *)m->w16, m->bias, Q, K, V, O);
+    } else {
+        hipLaunchKernelGGL(embed_attention_row_kernel<kBf16>, dim3(B * (P / kTile)),
+                           dim3(kRowThreads), 0, s, (const float4 *)p4, mask, P,
+                           (const float4 *)m->w32, (const v8bf *)m->w16, m->bias, Q, K, V, O);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_embed_attention_f32(const float *p4, const uint8_t *mask, int B, int P,
+                                      const pip_pair_mlp *m, const float *Q, const float *K,
+                                      const float *V, float *O, hipStream_t s) {
+    return launch_fused<false>(p4, mask, B, P, m, Q, K, V, O, s);
+}
+
+hipError_t launch_embed_attention_bf16(const float *p4, const uint8_t *mask, int B, int P,
+                                       const pip_pair_mlp *m, const uint16_t *Q,
+                                       const uint16_t *K, const uint16_t *V, uint16_t *O,
+                                       hipStream_t s) {
+    return launch_fused<true>(p4, mask, B, P, m, Q, K, V, O, s);
+}
+
 }  // namespace pip

@@ -1,0 +1,51 @@
+"""Fit the polynomial of the device GELU and print it as C++ constants.
+
+GELU(x) = x Phi(x) = max(x, 0) - |x| Phi(-|x|), and for a >= 0
+Phi(-a) = 2^(-Q(a)) with Q(a) = -log2 Phi(-a), a smooth function that grows
+like a^2 / (2 ln 2).  Q is fitted on [0, A] by a polynomial of degree n with
+iteratively reweighted least squares towards the minimax of the GELU error
+|x| ln2 Phi(-a) |dQ| (Chebyshev nodes); beyond A the argument is clamped,
+where |x| Phi(-A) is below 1e-8 |x|.  The device then needs n FMAs, one
+v_exp_f32 and three more VALU ops per element, with no branch.
+
+Run:  python gen_gelu_coeffs.py   (prints the tables pasted into pip_device.h)
+"""
+import numpy as np
+from scipy.special import log_ndtr, ndtr
+
+A = 6.0
+
+
+def fit(deg, A=A, nodes=6000, iters=40):
+    k = np.arange(nodes)
+    a = (A / 2) * (1 - np.cos(np.pi * (k + 0.5) / nodes))
+    Q = -log_ndtr(-a) / np.log(2)
+    w = np.maximum(a, 0.02) * ndtr(-a) * np.log(2)
+    V = np.vander(a, deg + 1, increasing=True)
+    ww = w.copy()
+    for _ in range(iters):
+        c, *_ = np.linalg.lstsq(V * ww[:, None], Q * ww, rcond=None)
+        err = np.abs((V @ c - Q) * w)
+        ww = w * (err / err.max()) ** 0.6 + 1e-30
+    return c
+
+
+def max_error(c, A=A):
+    xs = np.linspace(-12, 12, 600001)
+    x32 = xs.astype(np.float32)
+    ax = np.minimum(np.abs(x32), np.float32(A))
+    c32 = c.astype(np.float32)
+    p = np.full_like(ax, c32[-1])
+    for cc in c32[-2::-1]:
+        p = (p * ax + cc).astype(np.float32)
+    g = (np.maximum(x32, 0) - np.abs(x32) * np.exp2(-p).astype(np.float32)).astype(np.float32)
+    return float(np.abs(g.astype(np.float64) - xs * ndtr(xs)).max())
+
+
+if __name__ == "__main__":
+    for deg, name in ((6, "kGeluQ"), (3, "kGeluQ3")):
+        c = fit(deg)
+        print("// degree %d on [0, %.1f]: max |GELU error| %.2e (float32 evaluation)"
+              % (deg, A, max_error(c)))
+        print("constexpr float %s[%d] = {%s};" % (
+            name, deg + 1, ", ".join("%.9ef" % v for v in c.astype(np.float32))))

@@ -1,0 +1,102 @@
+// pip_attn.h -- pieces of the flash-style biased attention shared by the
+// attention, fused and block-stack kernels.
+//
+// "Fusion 3" of the ml4sci_cms_e2e26 README ("How the Kernel Fusion Works"):
+// softmax(Q K^T / sqrt(d) + bias) V with an online softmax.  Scores are
+// computed transposed, S^T = K Q^T, so that lane l holds the scores of query
+// l%16 against keys 4(l/16)+r: the row max / sum need an in-lane reduction
+// over r and two cross-lane steps (l^16, l^32), and the probabilities are
+// already the B operand of O^T += V^T P^T.  Scores are kept in base-2 units.
+#pragma once
+
+#include "pip_device.h"
+
+namespace pip {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kQkScale2 = 1.4426950408889634f * 0.25f;  // log2(e) / sqrt(16)
+
+__device__ __forceinline__ float xmax16(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float xsum16(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+// Online-softmax update of one key block for the lane's query: s[r] are the
+// base-2 scores (-inf for padded keys) and become the probabilities; m, l are
+// the running max and sum; returns the factor that rescales the accumulator.
+__device__ __forceinline__ float online_softmax(v4f &s, float &m, float &l) {
+    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    bm = xmax16(bm);
+    const float mn = fmaxf(m, bm);
+    const float corr = __builtin_amdgcn_exp2f(m - mn);  // m = -inf on the first block -> 0
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - mn);
+    float ps = (s[0] + s[1]) + (s[2] + s[3]);
+    ps = xsum16(ps);
+    l = l * corr + ps;
+    m = mn;
+    return corr;
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t f2bf(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ v4f mfma16bf(v4s a, v4s b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// S^T tile (keys x queries) of one head: lane l gets the scores of query
+// q0 + l%16 against keys k0 + 4(l/16) + r.  Qh / Kh point at the head's
+// (P, 16) rows.  The reduction over d pairs lane group g, step s with d = 4g+s.
+__device__ __forceinline__ v4f scores_f32(const float *__restrict__ Qh,
+                                          const float *__restrict__ Kh, int q0, int k0) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const float4 qv = *(const float4 *)(Qh + (size_t)(q0 + c) * 16 + 4 * g);
+    const float4 kv = *(const float4 *)(Kh + (size_t)(k0 + c) * 16 + 4 * g);
+    v4f s = {0.f, 0.f, 0.f, 0.f};
+    s = mfma4(kv.x, qv.x, s);
+    s = mfma4(kv.y, qv.y, s);
+    s = mfma4(kv.z, qv.z, s);
+    return mfma4(kv.w, qv.w, s);
+}
+__device__ __forceinline__ v4f scores_bf16(const uint16_t *__restrict__ Qh,
+                                           const uint16_t *__restrict__ Kh, int q0, int k0) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    const v4s qv = *(const v4s *)(Qh + (size_t)(q0 + c) * 16 + 4 * g);
+    const v4s kv = *(const v4s *)(Kh + (size_t)(k0 + c) * 16 + 4 * g);
+    return mfma16bf(kv, qv, (v4f){0.f, 0.f, 0.f, 0.f});
+}
+
+// acc (O^T: lane l holds O[q0 + l%16][4(l/16) + r]) += V^T P^T for key block
+// k0; p[r] is the probability of key k0 + 4(l/16) + r.  V rows of padded keys
+// are selected to 0 (a NaN there must not meet p = 0 inside the MFMA).
+__device__ __forceinline__ v4f pv_f32(const float *__restrict__ Vh, int k0, const v4f &p,
+                                      const int (&kreal)[4], v4f acc) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float vv = kreal[r] ? Vh[(size_t)(k0 + 4 * g + r) * 16 + c] : 0.f;
+        acc = mfma4(vv, p[r], acc);
+    }
+    return acc;
+}
+__device__ __forceinline__ v4f pv_bf16(const uint16_t *__restrict__ Vh, int k0, const v4f &p,
+                                       const int (&kreal)[4], v4f acc) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    v4s vv, pv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        vv[r] = kreal[r] ? (short)Vh[(size_t)(k0 + 4 * g + r) * 16 + c] : (short)0;
+        pv[r] = (short)f2bf(p[r]);
+    }
+    return mfma16bf(vv, pv, acc);
+}
+
+}  // namespace pip

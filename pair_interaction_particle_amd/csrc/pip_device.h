@@ -26,6 +26,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 constexpr int kHid = 64;
 constexpr int kHeads = 8;
 constexpr int kTile = 16;
+constexpr int kMaxP = 256;
 // ln(1e-8) and 1e-8: the feature clamp (PIP_FEATURE_EPS).
 constexpr double kEps = 1e-8;
 constexpr float kLnEps = -18.420680743952367f;
@@ -37,23 +38,20 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// GELU(x) = x * Phi(x), Phi the standard normal CDF (exact erf form).
-__device__ __forceinline__ float gelu(float x) {
-    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
-}
-
 // ------------------------------------------------------------ kinematics
 // Per-particle record staged in LDS (struct of arrays, one slot per particle).
+template <int N>
 struct PartLds {
-    double E[32], px[32], py[32], pz[32], y[32], phi[32];
-    float lnpt[32], pt[32];
-    int real[32];
+    double E[N], px[N], py[N], pz[N], y[N], phi[N];
+    float lnpt[N], pt[N];
+    int real[N];
 };
 
 // Fill LDS slot `s` from the energy-first 4-vector (E, px, py, pz):
 // pT = sqrt(px^2 + py^2), y = 1/2 ln((E+pz)/(E-pz)) with both arguments
 // floored at 1e-300, phi = atan2(py, px); all in float64.
-__device__ inline void stage_particle(PartLds& L, int s, float4 p, int real) {
+template <class PL>
+__device__ inline void stage_particle(PL& L, int s, float4 p, int real) {
     double E = p.x, px = p.y, py = p.z, pz = p.w;
     double num = E + pz, den = E - pz;
     num = (num > kRapFloor) ? num : kRapFloor;
@@ -75,7 +73,8 @@ __device__ inline void stage_particle(PartLds& L, int s, float4 p, int real) {
 // pair's invariant mass squared (E_a+E_b)^2 - |p_a+p_b|^2, in float64 with
 // every product and difference rounded separately (no contraction), so that
 // near-collinear pairs, where m^2 cancels, are reproducible bit for bit.
-__device__ __forceinline__ void pair_geometry(const PartLds& L, int ia, int ib, double& dr2,
+template <class PL>
+__device__ __forceinline__ void pair_geometry(const PL& L, int ia, int ib, double& dr2,
                                               double& m2) {
 #pragma clang fp contract(off)
     double dy = L.y[ia] - L.y[ib];
@@ -95,7 +94,8 @@ __device__ __forceinline__ void pair_geometry(const PartLds& L, int ia, int ib, 
 //   ln z  = max(ln ptmin - ln max(pT_a + pT_b, eps), ln eps)
 //   ln dR = max(ln(dR^2)/2, ln eps)
 //   ln m2 = ln max(m2, eps)
-__device__ __forceinline__ float pair_feature(const PartLds& L, int ia, int ib, int k) {
+template <class PL>
+__device__ __forceinline__ float pair_feature(const PL& L, int ia, int ib, int k) {
     double dr2, m2;
     pair_geometry(L, ia, ib, dr2, m2);
     float lnptmin = fminf(L.lnpt[ia], L.lnpt[ib]);

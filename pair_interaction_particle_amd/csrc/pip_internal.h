@@ -6,18 +6,12 @@
 
 #include "../../include/pip.h"
 
-// Device-resident folded pair MLP.  Packed operand layouts (each operand is 64
-// lane values, one per lane of a wave):
-//  float32 (w32), operands in this order:
-//   L1  c = 0..3:                 lane l -> W1'[16c + l%16][l/16]
-//   L2  (co, ci, r) 4x4x4:        lane l -> W2'[16co + l%16][16ci + 4(l/16) + r]
-//   L3  (co, ci, r) 4x4x4:        same with W3'
-//   L4  (ci, r) 4x4:              lane l -> W4[l%16][16ci + 4(l/16) + r] (rows >= 8: 0)
-//  bfloat16 (w16), 8 values per lane per operand:
-//   L2, L3  (co, s) 4x2:  slot j<4 -> W'[16co + l%16][32s + 4(l/16) + j]
-//                         slot j>=4 -> W'[16co + l%16][32s + 16 + 4(l/16) + j-4]
-//   L4      s = 0..1:     same with W4 (rows >= 8: 0)
-//  bias: b1' (64) | b2' (64) | b3' (64) | b4 (8), plain.
+// Device-resident folded pair MLP: w32 holds the float32 MFMA operands of all
+// four layers, w16 the bfloat16 operands of layers 2..4, bias the folded
+// biases b1' | b2' | b3' | b4.  Operand layouts are documented in pip_mlp.h;
+// the bf16 operand (layer 2 or 3, co, s) of lane l holds, in slot j,
+// W'[16co + l%16][32s + (j < 4 ? 0 : 16) + 4(l/16) + (j & 3)], stored at
+// ((layer * 8 + co * 2 + s) * 64 + l) * 8 + j; layer 4 uses operands 16 + s.
 struct pip_pair_mlp {
     int device;
     float *w32;
@@ -26,11 +20,7 @@ struct pip_pair_mlp {
 };
 
 namespace pip {
-constexpr int kW32Ops = 4 + 64 + 64 + 16;  // 148
-constexpr int kW32L1 = 0, kW32L2 = 4 * 64, kW32L3 = 68 * 64, kW32L4 = 132 * 64;
-constexpr int kW16Ops = 8 + 8 + 2;         // 18, each 64 lanes x 8 bf16
-constexpr int kW16L2 = 0, kW16L3 = 8 * 512, kW16L4 = 16 * 512;
-constexpr int kBiasL1 = 0, kBiasL2 = 64, kBiasL3 = 128, kBiasL4 = 192;
+constexpr int kW16L2 = 0, kW16L3 = 8 * 512, kW16L4 = 16 * 512;  // bf16 element offsets
 
 hipError_t launch_pair_features(const float *p4, const uint8_t *mask, int B, int P, float *F,
                                 hipStream_t s);

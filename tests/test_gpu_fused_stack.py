@@ -1,0 +1,105 @@
+"""GPU parity of the fused pair_embed_attention entry and of the block stack
+against the float64 oracle (through the C ABI).  Bars as in
+test_gpu_parity.py: float32 |err| <= 1e-4 (1 + |ref|), bfloat16
+<= 2e-2 (1 + |ref|), padded outputs exactly +0.0."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from pair_interaction_particle_amd import binding as pip
+from pair_interaction_particle_amd import synth
+from test_gpu_parity import (TOL32, TOLBF, assert_close, assert_zero_bits, g, host, mlp_for,
+                             ragged_jets, rand_qkv)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,P,ns", [
+    (2, 16, (11, 16)),                 # jet kernel
+    (6, 64, (64, 50, 17, 16, 1, 0)),   # jet kernel, ragged, empty jet, hole
+    (3, 128, (128, 20, 77)),           # jet kernel at its largest P
+    (3, 256, (256, 131, 0)),           # row kernel (P > 128)
+    (2, 144, (144, 40)),               # row kernel, odd block count
+])
+def test_fused_f32(B, P, ns):
+    p4, mask = ragged_jets(B, P, ns, seed=P + B)
+    params = mlp_for(P, biases=True, input_bn=(P == 64))
+    q, k, v = rand_qkv(B, 8, P, mask, seed=P)
+    mlp = pip.PairMLP(params)
+    O = host(pip.pair_embed_attention(g(p4), g(mask), mlp, g(q), g(k), g(v)))
+    ref = oracle.pair_embed_attention(p4, mask, params, q, k, v)
+    assert_close(O, ref, TOL32, "fused O f32 P=%d" % P)
+    assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "fused O padded rows")
+
+
+@pytest.mark.parametrize("B,P,ns", [(4, 128, (128, 60, 9, 100)), (2, 256, (256, 90))])
+def test_fused_bf16(B, P, ns):
+    p4, mask = ragged_jets(B, P, ns, seed=P + 7, sigma=0.8)
+    params = mlp_for(P + 1)
+    q, k, v = rand_qkv(B, 8, P, mask, seed=P + 1, dtype="bf16")
+    mlp = pip.PairMLP(params)
+    bf = torch.bfloat16
+    O = host(pip.pair_embed_attention(g(p4), g(mask), mlp, g(q, bf), g(k, bf), g(v, bf)))
+    ref = oracle.pair_embed_attention(p4, mask, params, q, k, v)
+    assert_close(O, ref, TOLBF, "fused O bf16 P=%d" % P)
+    assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "fused bf16 padded rows")
+
+
+def test_fused_batch512_workload():
+    d = synth.make_workload("fused512")
+    mlp = pip.PairMLP(d["mlp"])
+    O = host(pip.pair_embed_attention(g(d["p4"]), g(d["mask"]), mlp, g(d["q"]), g(d["k"]),
+                                      g(d["v"])))
+    ref = oracle.pair_embed_attention(d["p4"], d["mask"], d["mlp"], d["q"], d["k"], d["v"])
+    assert_close(O, ref, TOL32, "fused O (B=512, P=128)")
+    assert_zero_bits(O.transpose(0, 2, 1, 3), d["mask"] == 0, "fused O padded rows")
+
+
+def test_fused_matches_unfused_and_ignores_padding():
+    B, P = 3, 64
+    p4, mask = ragged_jets(B, P, (64, 33, 5), seed=11)
+    params = mlp_for(11, biases=True)
+    q, k, v = rand_qkv(B, 8, P, mask, seed=11)
+    mlp = pip.PairMLP(params)
+    O0 = host(pip.pair_embed_attention(g(p4), g(mask), mlp, g(q), g(k), g(v)))
+    pad = mask == 0
+    p4b = p4.copy()
+    p4b[pad] = np.nan
+    qb, kb, vb = (x.copy() for x in (q, k, v))
+    for x in (qb, kb, vb):
+        x[np.broadcast_to(pad[:, None, :, None], x.shape)] = np.nan
+    O1 = host(pip.pair_embed_attention(g(p4b), g(mask), mlp, g(qb), g(kb), g(vb)))
+    np.testing.assert_array_equal(O1.view(np.uint32), O0.view(np.uint32))
+    U = pip.pair_embed(g(p4), g(mask), mlp)
+    O2 = host(pip.pair_bias_attention(g(q), g(k), g(v), U, g(mask)))
+    np.testing.assert_allclose(O0, O2, rtol=0, atol=2e-5)
+
+
+def test_block_stack_workload():
+    d = synth.make_workload("stack8")
+    U = oracle.pair_embed(d["p4"], d["mask"], d["mlp"]).astype(np.float32)
+    X = g(d["x0"])
+    pip.block_stack(X, g(d["wq"]), g(d["wk"]), g(d["wv"]), g(d["wo"]), g(U), g(d["mask"]))
+    got = host(X)
+    ref = oracle.block_stack(d["x0"], d["wq"], d["wk"], d["wv"], d["wo"], U, d["mask"])
+    assert_close(got, ref, TOL32, "block stack X (B=128, P=128, C=128, L=8)")
+    assert_zero_bits(got, d["mask"] == 0, "padded rows of X")
+
+
+@pytest.mark.parametrize("B,P,C,L,ns", [(3, 48, 32, 3, (48, 17, 0)), (2, 32, 256, 2, (30, 32))])
+def test_block_stack_ragged_padded_rows_untouched(B, P, C, L, ns):
+    rng = np.random.default_rng(C + L)
+    _, mask = ragged_jets(B, P, ns, seed=C)
+    x0, wq, wk, wv, wo = synth.make_block_stack(B, P, C, L, mask, rng=rng)
+    x0 = x0.copy()
+    x0[mask == 0] = rng.normal(0, 5, size=(int((mask == 0).sum()), C))  # junk padding
+    H = C // 16
+    U = rng.normal(0, 1, size=(B, H, P, P)).astype(np.float32)
+    X = g(x0)
+    pip.block_stack(X, g(wq), g(wk), g(wv), g(wo), g(U), g(mask))
+    got = host(X)
+    ref = oracle.block_stack(x0, wq, wk, wv, wo, U, mask)
+    real = mask != 0
+    assert_close(got[real], ref[real], TOL32, "block stack X C=%d" % C)
+    np.testing.assert_array_equal(got[~real].view(np.uint32), x0[~real].view(np.uint32))
