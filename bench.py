@@ -209,7 +209,20 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device-to-device copies of MIB MiB (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path shards over jets with no exchange, "
               "and this build runs on a single MI355X (use --gpus 1).", file=sys.stderr)

@@ -123,6 +123,7 @@ pip_status pip_pair_features(const float *p4, const uint8_t *mask, int64_t B, in
  * symmetric in (a, c).  Pairs touching a padded slot are exactly 0.
  * u_dtype PIP_F32: float32 MLP.  PIP_BF16: layer 1 float32, hidden layers
  * 2..4 bfloat16 operands with float32 accumulation, U stored as bfloat16.
+ * `mask` must be 16-byte aligned too (its rows are read as 16-byte vectors).
  * Requires P % 16 == 0, 16 <= P <= 256.  Errors: NULL, SHAPE, ALIGN, DTYPE,
  * UNSUPPORTED, HIP. */
 pip_status pip_pair_embed(const float *p4, const uint8_t *mask, int64_t B, int64_t P,

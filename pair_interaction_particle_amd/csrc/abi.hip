@@ -206,7 +206,7 @@ pip_status pip_pair_embed(const float *p4, const uint8_t *mask, int64_t B, int64
     pip_status st = check_pair_grid(B, P);
     if (st != PIP_OK || B == 0 || P == 0) return st;
     if (!p4 || !mask || !mlp || !U) return PIP_ERR_NULL;
-    if (!aligned16(p4) || !aligned16(U)) return PIP_ERR_ALIGN;
+    if (!aligned16(p4) || !aligned16(mask) || !aligned16(U)) return PIP_ERR_ALIGN;
     if ((st = check_device(mlp)) != PIP_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     if (u_dtype == PIP_F32)

@@ -8,15 +8,18 @@
 // Work decomposition (gfx950).  U is symmetric in (a, b) because every
 // feature is, so only the lower triangle of 16x16 tiles (I >= J) is computed
 // and every off-diagonal tile is written twice (direct and transposed) from
-// an LDS staging buffer.  A 512-thread workgroup owns a chunk of consecutive
-// tiles of one jet (triangle order t = I(I+1)/2 + J): it stages the jet's
-// particle kinematics (float64) and the packed MLP weights in LDS once, then
-// walks its tiles.  Inside a tile the unit of work is a pair block of 16 pairs
-// = the 16 columns of one 16x16 MFMA: off-diagonal tiles have 16 (one per
-// row), diagonal tiles pack their 136 unique pairs into 9.  Each of the 8
-// waves pushes two pair blocks at a time through the MFMA layer chain; hidden
-// activations never leave registers.  Tiles without a real pair only write
-// zeros; rows of padded particles are skipped.
+// an LDS staging buffer.  The kernel is persistent: two 512-thread
+// workgroups per CU, each staging the packed MLP weights in LDS once and
+// taking an equal contiguous share of the real tiles of the batch (counted
+// from the mask in-kernel) plus an equal share of the all-padding tiles,
+// which only get zeros.  When its range enters a new jet a workgroup stages
+// that jet's particle kinematics (float64) in LDS.  Inside a tile the unit of
+// work is a pair block of 16 pairs = the 16 columns of one 16x16 MFMA:
+// off-diagonal tiles have 16 (one per row), diagonal tiles pack their 136
+// unique pairs into 9.  Each of the 8 waves pushes two pair blocks at a time
+// through the MFMA layer chain; hidden activations never leave registers.
+// The U tile is double buffered in LDS, so a tile costs one barrier.
+#include <algorithm>
 #include <type_traits>
 
 #include "pip_internal.h"
@@ -87,30 +90,15 @@ __device__ __forceinline__ void store4(uint16_t *U, size_t off, const float (&v)
 constexpr int kEmbedThreads = 512;
 constexpr int kEmbedWaves = kEmbedThreads / 64;
 
-// Write tile (I, J) of every head and, if I != J, its transpose (J, I), from
-// the LDS tile us[h][i][j]; pairs with a padded end are written as 0 (select).
-template <typename OutT, class PL>
-__device__ inline void write_tile(const PL &L, const float (*us)[16][17], OutT *U, int P, int I,
-                                  int J, bool zero) {
+// Zero tile (I, J) of every head and, if I != J, its transpose (J, I): one
+// 16-byte store per thread and direction.
+template <typename OutT>
+__device__ inline void zero_tile(OutT *U, int P, int I, int J) {
     const int tid = threadIdx.x;
-    const int r0 = I * kTile, c0 = J * kTile;
-    {
-        const int h = tid >> 6, i = (tid >> 2) & 15, j0 = (tid & 3) * 4;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            v[e] = (!zero && L.real[r0 + i] && L.real[c0 + j0 + e]) ? us[h][i][j0 + e] : 0.0f;
-        store4(U, ((size_t)h * P + r0 + i) * P + c0 + j0, v);
-    }
-    if (I == J) return;
-    {
-        const int h = tid >> 6, j = (tid >> 2) & 15, i0 = (tid & 3) * 4;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            v[e] = (!zero && L.real[c0 + j] && L.real[r0 + i0 + e]) ? us[h][i0 + e][j] : 0.0f;
-        store4(U, ((size_t)h * P + c0 + j) * P + r0 + i0, v);
-    }
+    const float z[4] = {0.f, 0.f, 0.f, 0.f};
+    const int h = tid >> 6, i = (tid >> 2) & 15, j0 = (tid & 3) * 4;
+    store4(U, ((size_t)h * P + I * kTile + i) * P + J * kTile + j0, z);
+    if (I != J) store4(U, ((size_t)h * P + J * kTile + i) * P + I * kTile + j0, z);
 }
 
 // Pair (i, j) (tile-local) that lane `lane` of pair block k computes.
@@ -132,102 +120,269 @@ __device__ __forceinline__ bool block_pair(bool diag, int k, int nblk, int lane,
     return valid;
 }
 
+// Bit t set when 16-block t of a mask row holds a real particle (row 16-byte
+// aligned, read as T 16-byte vectors).
+__device__ __forceinline__ uint32_t jet_activity(const uint8_t *__restrict__ mrow, int T) {
+    uint32_t act = 0;
+    for (int t = 0; t < T; ++t) {
+        const uint4 v = ((const uint4 *)mrow)[t];
+        if (v.x | v.y | v.z | v.w) act |= 1u << t;
+    }
+    return act;
+}
+
+// index of the k-th set bit of act (k < popcount(act))
+__device__ __forceinline__ int nth_bit(uint32_t act, int k) {
+    for (int i = 0; i < k; ++i) act &= act - 1;
+    return __builtin_ctz(act);
+}
+
+// Pair blocks of a jet's active-tile triangle, in tile order: tile (ia, ja)
+// of the active blocks (ja <= ia) has 16 blocks off the diagonal and 10 on
+// it (9 hold its 136 unique pairs, the 10th is empty so that every tile has
+// an even count and a wave's two blocks are always rows 2m, 2m+1 of one
+// tile), so the blocks before row ia number 8 ia (ia - 1) + 10 ia.
+__device__ __forceinline__ int blocks_before_row(int ia) { return 8 * ia * (ia - 1) + 10 * ia; }
+__device__ __forceinline__ int blocks_before(int kt) {
+    const int ia = tri_row(kt), ja = kt - ia * (ia + 1) / 2;
+    return blocks_before_row(ia) + 16 * ja;
+}
+
+// Flat pair block q of the jet with activity act -> tile (I, J) and the pair
+// (i, j) lane `lane` computes; false for the unused slots of a diagonal tile.
+__device__ __forceinline__ bool flat_pair(uint32_t act, int q, int lane, int &I, int &J, int &i,
+                                          int &j) {
+    int ia = (int)((sqrtf(4.0f + 32.0f * (float)q) - 2.0f) * 0.0625f);
+    while (blocks_before_row(ia + 1) <= q) ++ia;
+    while (blocks_before_row(ia) > q) --ia;
+    const int rem = q - blocks_before_row(ia);
+    const int ja = min(rem / 16, ia);
+    I = nth_bit(act, ia);
+    J = nth_bit(act, ja);
+    return block_pair(ia == ja, rem - 16 * ja, ia == ja ? 10 : 16, lane, i, j);
+}
+
+__device__ __forceinline__ int active_tiles(uint32_t act) {
+    const int a = __popc(act);
+    return a * (a + 1) / 2;
+}
+
+__device__ __forceinline__ void store_u(float *U, size_t off, float v) { U[off] = v; }
+__device__ __forceinline__ void store_u(uint16_t *U, size_t off, float v) {
+    U[off] = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Write the result of one pair block from registers: lane l < 32 holds the
+// values of heads 4(l/16) + q for the pair (i, j) of tile (I, J); each value
+// goes to U[h][a][b] and to its mirror U[h][b][a] (once when a == b), as
+// exact 0 when a or b is padded.
+template <typename OutT, class PL>
+__device__ __forceinline__ void write_block(const PL &L, OutT *U, int P, int I, int J, bool valid,
+                                           int i, int j, const v4f &u, bool zero) {
+    const int lane = threadIdx.x & 63;
+    if (lane >= 32 || !valid) return;
+    const int a = I * kTile + i, b = J * kTile + j;
+    const bool real = !zero && L.real[a] && L.real[b];
+    const int h0 = (lane >> 4) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float v = real ? u[q] : 0.0f;
+        const size_t hp = (size_t)(h0 + q) * P;
+        store_u(U, (hp + a) * P + b, v);
+        if (a != b) store_u(U, (hp + b) * P + a, v);
+    }
+}
+
+__device__ __forceinline__ void store_u2(float *U, size_t off, float a, float b) {
+    *(float2 *)(U + off) = make_float2(a, b);
+}
+__device__ __forceinline__ void store_u2(uint16_t *U, size_t off, float a, float b) {
+    *(uint32_t *)(U + off) = bf16_pair(a, b);
+}
+
+// Write two blocks that are rows a0 = I*16 + 2m and a0 + 1 of off-diagonal
+// tile (I, J): lane l < 32 holds heads 4(l/16) + q for column b = J*16 + l%16.
+// Direct rows are 64-byte segments across the lanes; the mirrored pair
+// U[h][b][a0..a0+1] is one 8-byte store per lane.
+template <typename OutT, class PL>
+__device__ __forceinline__ void write_row_pair(const PL &L, OutT *U, int P, int a0, int b,
+                                              const v4f &uA, const v4f &uB, bool zero) {
+    const int lane = threadIdx.x & 63;
+    if (lane >= 32) return;
+    const bool rb = !zero && L.real[b];
+    const bool rA = rb && L.real[a0], rB = rb && L.real[a0 + 1];
+    const int h0 = (lane >> 4) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float vA = rA ? uA[q] : 0.0f, vB = rB ? uB[q] : 0.0f;
+        const size_t hp = (size_t)(h0 + q) * P;
+        store_u(U, (hp + a0) * P + b, vA);
+        store_u(U, (hp + a0 + 1) * P + b, vB);
+        store_u2(U, (hp + b) * P + a0, vA, vB);
+    }
+}
+
+// Persistent pair-embed kernel.  Real tiles (both blocks hold a real
+// particle) are counted per jet from the mask; a block-wide scan gives every
+// workgroup an equal contiguous range of them.  All-padding tiles are split
+// evenly too and only get zeros.  Within a jet the workgroup's tiles are
+// dealt to its 8 waves round robin; each wave runs its tiles alone (no
+// barrier between tiles) and writes U straight from registers, so waves
+// drift apart and hide each other's latencies.  Workgroup w is remapped so
+// that the workgroups of one XCD (dispatch is round-robin over 8 XCDs) hold
+// adjacent ranges and thus write neighbouring parts of U.
 template <bool kBf16>
 __global__ __launch_bounds__(kEmbedThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
-                       int ntri, int nchunk, int G, const float4 *__restrict__ w32,
-                       const v8bf *__restrict__ w16, const float *__restrict__ bias,
-                       void *__restrict__ Uout) {
+void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B,
+                       int P, const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
+                       const float *__restrict__ bias, void *__restrict__ Uout) {
     constexpr int kW4 = kBf16 ? 64 : kW32Groups * 64;  // float4 operand groups in LDS
     __shared__ float4 wl[kW4];
     __shared__ v8bf wl16[kBf16 ? kW16Ops * 64 : 1];
     __shared__ float bl[kBiasFloats];
     __shared__ PartLds<kMaxP> L;
-    __shared__ float us[kHeads][16][17];
-    __shared__ int blkAny[kMaxP / kTile];
+    __shared__ int scan[kEmbedThreads];
 
-    const int jet = blockIdx.x / nchunk;
-    const int t0 = (blockIdx.x - jet * nchunk) * G;
-    const int t1 = min(t0 + G, ntri);
+    typedef typename std::conditional<kBf16, uint16_t, float>::type OutT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = P / kTile, ntri = T * (T + 1) / 2;
+    const int W = gridDim.x;
+    const int w = (W % 8 == 0) ? (blockIdx.x % 8) * (W / 8) + blockIdx.x / 8 : blockIdx.x;
 
-    for (int s = tid; s < P; s += kEmbedThreads) {
-        const size_t idx = (size_t)jet * P + s;
-        const int real = mask[idx] != 0;
-        stage_particle(L, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+    // ---- this workgroup's range of real tiles
+    const int per = (B + kEmbedThreads - 1) / kEmbedThreads;
+    const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
+    int cnt = 0;
+    for (int b = b0; b < b1; ++b) cnt += active_tiles(jet_activity(mask + (size_t)b * P, T));
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kEmbedThreads; off <<= 1) {  // inclusive scan
+        const int v = (tid >= off) ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
     }
+    const long R = scan[kEmbedThreads - 1];
+    const int r0 = (int)(R * w / W), r1 = (int)(R * (w + 1) / W);
+    if (r0 < r1) {
+    // the jet holding real tile r0 and its local index (uniform in the block)
+    int c = 0;
+    while (scan[c] <= r0) ++c;
+    int b = c * per, k = r0 - (c ? scan[c - 1] : 0);
+    uint32_t act = jet_activity(mask + (size_t)b * P, T);
+    while (k >= active_tiles(act)) {
+        k -= active_tiles(act);
+        ++b;
+        act = jet_activity(mask + (size_t)b * P, T);
+    }
+
     stage_weights<kEmbedThreads>(wl, bl, w32, bias, kW4);
     if constexpr (kBf16)
         for (int i = tid; i < kW16Ops * 64; i += kEmbedThreads) wl16[i] = w16[i];
-    __syncthreads();
-    if (tid < P / kTile) {
-        int a = 0;
-        for (int i = 0; i < kTile; ++i) a |= L.real[tid * kTile + i];
-        blkAny[tid] = a;
-    }
-    __syncthreads();
 
-    typedef typename std::conditional<kBf16, uint16_t, float>::type OutT;
-    OutT *U = (OutT *)Uout + (size_t)jet * kHeads * P * P;
-    for (int t = t0; t < t1; ++t) {
-        const int I = tri_row(t), J = t - I * (I + 1) / 2;
-        if (!(blkAny[I] && blkAny[J])) {  // no real pair: zeros only
-            write_tile<OutT>(L, us, U, P, I, J, true);
-            continue;
-        }
-        const bool diag = (I == J);
-        const int nblk = diag ? 9 : 16;
-        const int r0 = I * kTile, c0 = J * kTile;
-        int iA, jA, iB, jB;
-        const bool vA = block_pair(diag, 2 * wave, nblk, lane, iA, jA);
-        const bool vB = block_pair(diag, 2 * wave + 1, nblk, lane, iB, jB);
-        const bool realA = vA && L.real[r0 + iA] && L.real[c0 + jA];
-        const bool realB = vB && L.real[r0 + iB] && L.real[c0 + jB];
-        if (__ballot(realA || realB) != 0) {
-            const int k = lane >> 4;
-            const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, k) : 0.0f;
-            const float fB = realB ? pair_feature(L, r0 + iB, c0 + jB, k) : 0.0f;
-            v4f uA, uB;
-            if constexpr (kBf16) mlp2_bf16(wl, wl16, bl, fA, fB, uA, uB);
-            else mlp2_f32(wl, bl, fA, fB, uA, uB);
-            if (lane < 32) {
-                const int h0 = (lane >> 4) * 4;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (vA) {
-                        us[h0 + r][iA][jA] = uA[r];
-                        if (diag) us[h0 + r][jA][iA] = uA[r];
-                    }
-                    if (vB) {
-                        us[h0 + r][iB][jB] = uB[r];
-                        if (diag) us[h0 + r][jB][iB] = uB[r];
-                    }
+    int r = r0;
+    while (r < r1) {
+        const int nt = active_tiles(act);
+        const int kend = min(nt, k + (r1 - r));  // this jet's tiles in the range: [k, kend)
+        if (kend > k) {
+            __syncthreads();  // every wave is done with the previous jet's particles
+            for (int s = tid; s < P; s += kEmbedThreads) {
+                const size_t idx = (size_t)b * P + s;
+                const int real = mask[idx] != 0;
+                stage_particle(L, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+            }
+            __syncthreads();
+            OutT *U = (OutT *)Uout + (size_t)b * kHeads * P * P;
+            // the range's pair blocks, flattened, dealt to the waves in pairs
+            const int q0 = blocks_before(k), q1 = blocks_before(kend);
+            for (int q = q0 + 2 * wave; q < q1; q += 2 * kEmbedWaves) {
+                int IA, JA, iA, jA, IB, JB, iB, jB;
+                const bool vA = flat_pair(act, q, lane, IA, JA, iA, jA);
+                const bool vB = flat_pair(act, q + 1, lane, IB, JB, iB, jB);
+                const bool realA = vA && L.real[IA * kTile + iA] && L.real[JA * kTile + jA];
+                const bool realB = vB && L.real[IB * kTile + iB] && L.real[JB * kTile + jB];
+                v4f uA = {0.f, 0.f, 0.f, 0.f}, uB = uA;
+                const bool any = __ballot(realA || realB) != 0;
+                if (any) {
+                    const int f = lane >> 4;
+                    const float fA =
+                        realA ? pair_feature(L, IA * kTile + iA, JA * kTile + jA, f) : 0.0f;
+                    const float fB =
+                        realB ? pair_feature(L, IB * kTile + iB, JB * kTile + jB, f) : 0.0f;
+                    if constexpr (kBf16) mlp2_bf16(wl, wl16, bl, fA, fB, uA, uB);
+                    else mlp2_f32(wl, bl, fA, fB, uA, uB);
+                }
+                if (IA != JA) {  // rows iA, iA + 1 (= iB) of one off-diagonal tile
+                    write_row_pair<OutT>(L, U, P, IA * kTile + iA, JA * kTile + jA, uA, uB, !any);
+                } else {
+                    write_block<OutT>(L, U, P, IA, JA, vA, iA, jA, uA, !any);
+                    write_block<OutT>(L, U, P, IB, JB, vB, iB, jB, uB, !any);
                 }
             }
+            r += kend - k;
         }
-        __syncthreads();
-        write_tile<OutT>(L, us, U, P, I, J, false);
-        __syncthreads();
+        if (r < r1) {
+            ++b;
+            k = 0;
+            act = jet_activity(mask + (size_t)b * P, T);
+        }
+    }
+    }  // real tiles
+
+    // ---- tiles without a real pair: zeros (after the real tiles, so these
+    // stores overlap the other workgroups' work; jet activity read once per jet)
+    {
+        const long tot = (long)B * ntri;
+        const long z1 = tot * (w + 1) / W;
+        int bz = -1;
+        uint32_t actz = 0;
+        for (long z = tot * w / W; z < z1; ++z) {
+            const int bb = (int)(z / ntri), t = (int)(z - (long)bb * ntri);
+            if (bb != bz) {
+                bz = bb;
+                actz = jet_activity(mask + (size_t)bb * P, T);
+            }
+            const int I = tri_row(t), J = t - I * (I + 1) / 2;
+            if ((actz >> I & 1) && (actz >> J & 1)) continue;
+            zero_tile<OutT>((OutT *)Uout + (size_t)bb * kHeads * P * P, P, I, J);
+        }
     }
 }
 
-// Tiles per workgroup: enough workgroups to fill 256 CUs twice over, few
-// enough that staging the jet and the weights is amortised.
-static int chunk_tiles(int B, int ntri) {
-    int G = 4;
-    while (G > 1 && (long)B * ((ntri + G - 1) / G) < 2048) --G;
-    return G;
+// Two resident 512-thread workgroups per CU (the LDS budget allows two).
+static int persistent_grid(int B, int P) {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    const long T = P / kTile, tiles = (long)B * T * (T + 1) / 2;
+    return (int)std::min<long>(2L * cus[dev], std::max<long>(tiles, 1));
 }
 
+// Batches are cut into segments of at most 65,536 jets so that tile counts
+// stay far inside int range.
 template <bool kBf16>
 static hipError_t launch_embed(const float *p4, const uint8_t *mask, int B, int P,
                                const pip_pair_mlp *m, void *U, hipStream_t s) {
-    const int T = P / kTile, ntri = T * (T + 1) / 2;
-    const int G = chunk_tiles(B, ntri), nchunk = (ntri + G - 1) / G;
-    hipLaunchKernelGGL(pair_embed_kernel<kBf16>, dim3(B * nchunk), dim3(kEmbedThreads), 0, s,
-                       (const float4 *)p4, mask, P, ntri, nchunk, G, (const float4 *)m->w32,
-                       (const v8bf *)m->w16, m->bias, U);
-    return hipGetLastError();
+    typedef typename std::conditional<kBf16, uint16_t, float>::type OutT;
+    constexpr int kSeg = 65536;
+    for (int b0 = 0; b0 < B; b0 += kSeg) {
+        const int nb = std::min(kSeg, B - b0);
+        hipLaunchKernelGGL(pair_embed_kernel<kBf16>, dim3(persistent_grid(nb, P)),
+                           dim3(kEmbedThreads), 0, s, (const float4 *)p4 + (size_t)b0 * P,
+                           mask + (size_t)b0 * P, nb, P, (const float4 *)m->w32,
+                           (const v8bf *)m->w16, m->bias,
+                           (void *)((OutT *)U + (size_t)b0 * kHeads * P * P));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_pair_embed_f32(const float *p4, const uint8_t *mask, int B, int P,

@@ -13,35 +13,40 @@
 namespace pip {
 
 // ------------------------------------------------------------ GELU
-// GELU(x) = x Phi(x) = max(x, 0) - |x| Phi(-|x|) with Phi(-a) = 2^-Q(a), Q a
-// polynomial fitted by gen_gelu_coeffs.py (weighted least squares towards the
-// minimax of the GELU error) on a in [0, 6]; beyond 6, |x| Phi(-6) < 1e-8 |x|.
-// Degree 6: |error| <= 5.6e-7 in float32 evaluation; degree 3: <= 9.3e-5.
-constexpr float kGeluQ[7] = {9.999959469e-01f, 1.151174664e+00f, 4.588546455e-01f,
-                             5.329676718e-02f, -8.003029972e-03f, 7.443534560e-04f,
-                             -3.008377280e-05f};
-constexpr float kGeluQ3[4] = {1.005243897e+00f, 1.122994184e+00f, 5.049490333e-01f,
-                              2.317943610e-02f};
+// GELU(x) = x Phi(x) = max(x, 0) - |x| Phi(-|x|) with Phi(-a) = 2^-Q(a) and Q
+// a polynomial fitted by gen_gelu_coeffs.py (weighted least squares towards
+// the minimax of the GELU error, a in [0, 7]).  Q has a positive leading
+// coefficient and keeps growing beyond the fit range, so 2^-Q underflows to 0
+// for large |x| and no clamp is needed.  max(x, 0) is taken on the bit
+// pattern (an integer max), exact for every finite x, -0 included.
+// Degree 5 (float32 path): |error| <= 8.9e-7 on [-40, 40]; degree 3 (bf16
+// path): <= 9.6e-5.  Each costs its degree in FMAs, one v_exp_f32, one
+// v_max_i32 and one FMA, with no branch.
+constexpr float kGeluQ[6] = {1.000067353e+00f, 1.150599599e+00f, 4.603779614e-01f,
+                             5.149073154e-02f, -6.955113262e-03f, 4.553909530e-04f};
+constexpr float kGeluQ3[4] = {1.005338550e+00f, 1.122809887e+00f, 5.050402880e-01f,
+                              2.316968702e-02f};
+
+__device__ __forceinline__ float relu_bits(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
 
 __device__ __forceinline__ float gelu_f32(float x) {
-    const float a = fminf(fabsf(x), 6.0f);
-    float p = kGeluQ[6];
-    p = fmaf(p, a, kGeluQ[5]);
-    p = fmaf(p, a, kGeluQ[4]);
+    const float a = fabsf(x);
+    float p = fmaf(kGeluQ[5], a, kGeluQ[4]);
     p = fmaf(p, a, kGeluQ[3]);
     p = fmaf(p, a, kGeluQ[2]);
     p = fmaf(p, a, kGeluQ[1]);
     p = fmaf(p, a, kGeluQ[0]);
-    return fmaf(-fabsf(x), __builtin_amdgcn_exp2f(-p), fmaxf(x, 0.0f));
+    return fmaf(-a, __builtin_amdgcn_exp2f(-p), relu_bits(x));
 }
 
 __device__ __forceinline__ float gelu_lo(float x) {  // the bf16 path's GELU
-    const float a = fminf(fabsf(x), 6.0f);
-    float p = kGeluQ3[3];
-    p = fmaf(p, a, kGeluQ3[2]);
+    const float a = fabsf(x);
+    float p = fmaf(kGeluQ3[3], a, kGeluQ3[2]);
     p = fmaf(p, a, kGeluQ3[1]);
     p = fmaf(p, a, kGeluQ3[0]);
-    return fmaf(-fabsf(x), __builtin_amdgcn_exp2f(-p), fmaxf(x, 0.0f));
+    return fmaf(-a, __builtin_amdgcn_exp2f(-p), relu_bits(x));
 }
 
 // ------------------------------------------------------------ weight layout
