@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <cmath>
 #include <vector>
 
 #include "pip_internal.h"
@@ -159,18 +160,59 @@ pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **ou
                 p16[pip::kW16L4 + (s * 64 + l) * 8 + j] =
                     (l % 16 < 8) ? host_bf16(W4[(l % 16) * 64 + chan(s, l / 16, j)]) : 0;
 
+    // fp16 hi / lo operands (same slot layout as the bf16 ones): hi = fp16(w),
+    // lo = fp16(w - hi), both round to nearest even.  The fp16 x 2 chain is
+    // used only when every layer's folded weights are well scaled for fp16:
+    // 2^-8 <= max |W'| <= 2^14 per layer (finite), so products carry at most
+    // ~2^-22 relative error plus ~2^-25 absolute per factor in fp16's
+    // subnormal range; otherwise the exact float32 chain runs.
+    std::vector<uint16_t> px2(2 * pip::kW16Elems);
+    bool f16ok = true;
+    for (const float *Wl : {W2, W3, W4}) {
+        const int n = (Wl == W4) ? 8 * 64 : 64 * 64;
+        float mx = 0.0f;
+        for (int i = 0; i < n; ++i) {
+            if (!std::isfinite(Wl[i])) f16ok = false;
+            mx = fmaxf(mx, fabsf(Wl[i]));
+        }
+        if (!(mx >= 0.00390625f && mx <= 16384.0f)) f16ok = false;
+    }
+    auto put_x2 = [&](size_t at, float wv) {
+        const _Float16 hi = (_Float16)wv;
+        const _Float16 lo = (_Float16)(wv - (float)hi);
+        px2[at] = __builtin_bit_cast(uint16_t, hi);
+        px2[pip::kW16Elems + at] = __builtin_bit_cast(uint16_t, lo);
+    };
+    for (int t = 0; t < 2; ++t)
+        for (int co = 0; co < 4; ++co)
+            for (int s = 0; s < 2; ++s)
+                for (int l = 0; l < 64; ++l)
+                    for (int j = 0; j < 8; ++j)
+                        put_x2(offs16[t] + ((co * 2 + s) * 64 + l) * 8 + j,
+                               Wh[t][(16 * co + l % 16) * 64 + chan(s, l / 16, j)]);
+    for (int s = 0; s < 2; ++s)
+        for (int l = 0; l < 64; ++l)
+            for (int j = 0; j < 8; ++j)
+                put_x2(pip::kW16L4 + (s * 64 + l) * 8 + j,
+                       (l % 16 < 8) ? W4[(l % 16) * 64 + chan(s, l / 16, j)] : 0.0f);
+
     pip_pair_mlp *m = new pip_pair_mlp();
+    m->f16ok = f16ok ? 1 : 0;
     m->w32 = nullptr;
     m->w16 = nullptr;
+    m->wx2 = nullptr;
     m->bias = nullptr;
     hipError_t e = hipGetDevice(&m->device);
     if (e == hipSuccess) e = hipMalloc((void **)&m->w32, p32.size() * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void **)&m->w16, p16.size() * sizeof(uint16_t));
+    if (e == hipSuccess) e = hipMalloc((void **)&m->wx2, px2.size() * sizeof(uint16_t));
     if (e == hipSuccess) e = hipMalloc((void **)&m->bias, b.size() * sizeof(float));
     if (e == hipSuccess)
         e = hipMemcpy(m->w32, p32.data(), p32.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(m->w16, p16.data(), p16.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(m->wx2, px2.data(), px2.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(m->bias, b.data(), b.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
@@ -186,6 +228,7 @@ pip_status pip_pair_mlp_destroy(pip_pair_mlp *m) {
     hipError_t e = hipSuccess, e2;
     if (m->w32 && (e2 = hipFree(m->w32)) != hipSuccess) e = e2;
     if (m->w16 && (e2 = hipFree(m->w16)) != hipSuccess) e = e2;
+    if (m->wx2 && (e2 = hipFree(m->wx2)) != hipSuccess) e = e2;
     if (m->bias && (e2 = hipFree(m->bias)) != hipSuccess) e = e2;
     delete m;
     return hip_status(e);

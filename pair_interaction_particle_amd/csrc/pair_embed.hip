@@ -162,6 +162,16 @@ __device__ __forceinline__ bool flat_pair(uint32_t act, int q, int lane, int &I,
     return block_pair(ia == ja, rem - 16 * ja, ia == ja ? 10 : 16, lane, i, j);
 }
 
+constexpr uint8_t kNoPair = 0x0f;
+
+// Active block indices of a jet, 4 bits each (entry k = k-th set bit of act).
+__device__ __forceinline__ uint64_t active_index(uint32_t act) {
+    uint64_t idx = 0;
+    for (int k = 0; act; ++k, act &= act - 1) idx |= (uint64_t)__builtin_ctz(act) << (4 * k);
+    return idx;
+}
+__device__ __forceinline__ int nth_active(uint64_t idx, int k) { return (int)(idx >> (4 * k)) & 15; }
+
 __device__ __forceinline__ int active_tiles(uint32_t act) {
     const int a = __popc(act);
     return a * (a + 1) / 2;
@@ -231,20 +241,28 @@ __device__ __forceinline__ void write_row_pair(const PL &L, OutT *U, int P, int 
 // drift apart and hide each other's latencies.  Workgroup w is remapped so
 // that the workgroups of one XCD (dispatch is round-robin over 8 XCDs) hold
 // adjacent ranges and thus write neighbouring parts of U.
-template <bool kBf16>
+template <int kMode>
 __global__ __launch_bounds__(kEmbedThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B,
                        int P, const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
-                       const float *__restrict__ bias, void *__restrict__ Uout) {
-    constexpr int kW4 = kBf16 ? 64 : kW32Groups * 64;  // float4 operand groups in LDS
-    __shared__ float4 wl[kW4];
-    __shared__ v8bf wl16[kBf16 ? kW16Ops * 64 : 1];
-    __shared__ float bl[kBiasFloats];
+                       const v8h *__restrict__ wx2, const float *__restrict__ bias,
+                       void *__restrict__ Uout) {
+    MlpLds<kMode> M;
     __shared__ PartLds<kMaxP> L;
     __shared__ int scan[kEmbedThreads];
 
-    typedef typename std::conditional<kBf16, uint16_t, float>::type OutT;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // pair (i, j), j <= i, of slot p of a diagonal tile's triangle packing
+    // as i << 4 | j; the unused slots 136..159 hold kNoPair (i = 0, j = 15),
+    // which no valid entry can equal since j <= i
+    __shared__ uint8_t diagPair[160];
+
+    typedef typename std::conditional<kMode == kMlpBf16, uint16_t, float>::type OutT;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid < 160) {
+        const int i = tri_row(tid);
+        diagPair[tid] = tid < 136 ? (uint8_t)(i << 4 | (tid - i * (i + 1) / 2)) : kNoPair;
+    }
     const int T = P / kTile, ntri = T * (T + 1) / 2;
     const int W = gridDim.x;
     const int w = (W % 8 == 0) ? (blockIdx.x % 8) * (W / 8) + blockIdx.x / 8 : blockIdx.x;
@@ -276,9 +294,7 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         act = jet_activity(mask + (size_t)b * P, T);
     }
 
-    stage_weights<kEmbedThreads>(wl, bl, w32, bias, kW4);
-    if constexpr (kBf16)
-        for (int i = tid; i < kW16Ops * 64; i += kEmbedThreads) wl16[i] = w16[i];
+    M.template stage<kEmbedThreads>(w32, w16, wx2, bias);
 
     int r = r0;
     while (r < r1) {
@@ -293,32 +309,65 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             }
             __syncthreads();
             OutT *U = (OutT *)Uout + (size_t)b * kHeads * P * P;
-            // the range's pair blocks, flattened, dealt to the waves in pairs
+            // the range's pair blocks, flattened, dealt to the waves in pairs;
+            // the tile walk is wave-uniform (scalar registers)
+            const uint64_t aidx = active_index(act);
             const int q0 = blocks_before(k), q1 = blocks_before(kend);
-            for (int q = q0 + 2 * wave; q < q1; q += 2 * kEmbedWaves) {
-                int IA, JA, iA, jA, IB, JB, iB, jB;
-                const bool vA = flat_pair(act, q, lane, IA, JA, iA, jA);
-                const bool vB = flat_pair(act, q + 1, lane, IB, JB, iB, jB);
-                const bool realA = vA && L.real[IA * kTile + iA] && L.real[JA * kTile + jA];
-                const bool realB = vB && L.real[IB * kTile + iB] && L.real[JB * kTile + jB];
-                v4f uA = {0.f, 0.f, 0.f, 0.f}, uB = uA;
-                const bool any = __ballot(realA || realB) != 0;
-                if (any) {
-                    const int f = lane >> 4;
-                    const float fA =
-                        realA ? pair_feature(L, IA * kTile + iA, JA * kTile + jA, f) : 0.0f;
-                    const float fB =
-                        realB ? pair_feature(L, IB * kTile + iB, JB * kTile + jB, f) : 0.0f;
-                    if constexpr (kBf16) mlp2_bf16(wl, wl16, bl, fA, fB, uA, uB);
-                    else mlp2_f32(wl, bl, fA, fB, uA, uB);
+            auto sweep = [&](auto exact_t) {
+                constexpr bool kExact = decltype(exact_t)::value;
+                bool ok = true;
+                int q = q0 + 2 * wv;
+                int ia = tri_row(k), rem = q - blocks_before_row(ia);
+                for (; q < q1; q += 2 * kEmbedWaves, rem += 2 * kEmbedWaves) {
+                    // Compiler-only memory barrier (emits nothing): keeps the
+                    // loop-invariant LDS weight reads inside the loop instead
+                    // of hoisting 144+ registers of operands out of it.
+                    __asm__ volatile("" ::: "memory");
+                    while (rem >= 16 * ia + 10) {  // rows have 16 ia + 10 blocks
+                        rem -= 16 * ia + 10;
+                        ++ia;
+                    }
+                    const int ja = min(rem >> 4, ia), kb = rem - 16 * ja;
+                    const int I = nth_active(aidx, ia), J = nth_active(aidx, ja);
+                    const bool diag = ia == ja;
+                    // this lane's pairs (tile-local rows / columns) of blocks kb, kb+1
+                    int iA = kb, jA = lane & 15, iB = kb + 1, jB = lane & 15;
+                    bool vA = true, vB = true;
+                    if (diag) {
+                        const int eA = diagPair[16 * kb + (lane & 15)];
+                        const int eB = diagPair[16 * kb + 16 + (lane & 15)];
+                        vA = eA != kNoPair;
+                        vB = eB != kNoPair;
+                        iA = vA ? eA >> 4 : 0;
+                        jA = vA ? eA & 15 : 0;
+                        iB = vB ? eB >> 4 : 0;
+                        jB = vB ? eB & 15 : 0;
+                    }
+                    const int aA = I * kTile + iA, bA = J * kTile + jA;
+                    const int aB = I * kTile + iB, bB = J * kTile + jB;
+                    const bool realA = vA && L.real[aA] && L.real[bA];
+                    const bool realB = vB && L.real[aB] && L.real[bB];
+                    v4f uA = {0.f, 0.f, 0.f, 0.f}, uB = uA;
+                    const bool any = __ballot(realA || realB) != 0;
+                    if (any) {
+                        const int f = lane >> 4;
+                        const float fA = realA ? pair_feature(L, aA, bA, f) : 0.0f;
+                        const float fB = realB ? pair_feature(L, aB, bB, f) : 0.0f;
+                        if constexpr (kExact) M.run_exact(w32, fA, fB, uA, uB);
+                        else ok = M.run(fA, fB, uA, uB) && ok;
+                    }
+                    if (!diag) {  // rows kb, kb + 1 of one off-diagonal tile
+                        write_row_pair<OutT>(L, U, P, aA, bA, uA, uB, !any);
+                    } else {
+                        write_block<OutT>(L, U, P, I, J, vA, iA, jA, uA, !any);
+                        write_block<OutT>(L, U, P, I, J, vB, iB, jB, uB, !any);
+                    }
                 }
-                if (IA != JA) {  // rows iA, iA + 1 (= iB) of one off-diagonal tile
-                    write_row_pair<OutT>(L, U, P, IA * kTile + iA, JA * kTile + jA, uA, uB, !any);
-                } else {
-                    write_block<OutT>(L, U, P, IA, JA, vA, iA, jA, uA, !any);
-                    write_block<OutT>(L, U, P, IB, JB, vB, iB, jB, uB, !any);
-                }
-            }
+                return ok;
+            };
+            // A wave whose fp16 x 2 results were not all finite redoes its
+            // share of this jet exactly (its later stores replace the earlier).
+            if (!sweep(std::false_type{})) sweep(std::true_type{});
             r += kend - k;
         }
         if (r < r1) {
@@ -367,17 +416,17 @@ static int persistent_grid(int B, int P) {
 
 // Batches are cut into segments of at most 65,536 jets so that tile counts
 // stay far inside int range.
-template <bool kBf16>
+template <int kMode>
 static hipError_t launch_embed(const float *p4, const uint8_t *mask, int B, int P,
                                const pip_pair_mlp *m, void *U, hipStream_t s) {
-    typedef typename std::conditional<kBf16, uint16_t, float>::type OutT;
+    typedef typename std::conditional<kMode == kMlpBf16, uint16_t, float>::type OutT;
     constexpr int kSeg = 65536;
     for (int b0 = 0; b0 < B; b0 += kSeg) {
         const int nb = std::min(kSeg, B - b0);
-        hipLaunchKernelGGL(pair_embed_kernel<kBf16>, dim3(persistent_grid(nb, P)),
+        hipLaunchKernelGGL(pair_embed_kernel<kMode>, dim3(persistent_grid(nb, P)),
                            dim3(kEmbedThreads), 0, s, (const float4 *)p4 + (size_t)b0 * P,
                            mask + (size_t)b0 * P, nb, P, (const float4 *)m->w32,
-                           (const v8bf *)m->w16, m->bias,
+                           (const v8bf *)m->w16, (const v8h *)m->wx2, m->bias,
                            (void *)((OutT *)U + (size_t)b0 * kHeads * P * P));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -387,12 +436,13 @@ static hipError_t launch_embed(const float *p4, const uint8_t *mask, int B, int 
 
 hipError_t launch_pair_embed_f32(const float *p4, const uint8_t *mask, int B, int P,
                                  const pip_pair_mlp *m, float *U, hipStream_t s) {
-    return launch_embed<false>(p4, mask, B, P, m, U, s);
+    return m->f16ok ? launch_embed<kMlpF16x2>(p4, mask, B, P, m, U, s)
+                    : launch_embed<kMlpF32>(p4, mask, B, P, m, U, s);
 }
 
 hipError_t launch_pair_embed_bf16(const float *p4, const uint8_t *mask, int B, int P,
                                   const pip_pair_mlp *m, uint16_t *U, hipStream_t s) {
-    return launch_embed<true>(p4, mask, B, P, m, U, s);
+    return launch_embed<kMlpBf16>(p4, mask, B, P, m, U, s);
 }
 
 }  // namespace pip

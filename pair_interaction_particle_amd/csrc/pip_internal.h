@@ -12,10 +12,15 @@
 // the bf16 operand (layer 2 or 3, co, s) of lane l holds, in slot j,
 // W'[16co + l%16][32s + (j < 4 ? 0 : 16) + 4(l/16) + (j & 3)], stored at
 // ((layer * 8 + co * 2 + s) * 64 + l) * 8 + j; layer 4 uses operands 16 + s.
+// wx2 holds the fp16 hi operands of layers 2..4 followed by the fp16 lo
+// operands (same layout as w16); f16ok is set when every folded weight of
+// layers 2..4 lies inside the fp16 range, which the fp16 x 2 chain needs.
 struct pip_pair_mlp {
     int device;
+    int f16ok;
     float *w32;
     uint16_t *w16;
+    uint16_t *wx2;
     float *bias;
 };
 

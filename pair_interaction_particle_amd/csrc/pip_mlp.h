@@ -58,7 +58,10 @@ __device__ __forceinline__ float gelu_lo(float x) {  // the bf16 path's GELU
 // layer 4 rows >= 8 are zero).
 constexpr int kW32Groups = 37;
 constexpr int kW32Floats = kW32Groups * 64 * 4;  // 9,472
-// bfloat16 operands (layers 2..4): 18 operands of 8 bf16 per lane, [op][lane].
+// 16-bit operands of layers 2..4 (bf16, or fp16 hi and lo halves): 18
+// operands of 8 values per lane, [op][lane]; operand (layer 2 or 3, co, s) of
+// lane l holds in slot j the weight W'[16co + l%16][32s + (j < 4 ? 0 : 16) +
+// 4(l/16) + (j & 3)], operands 16 + s are layer 4 (rows >= 8 zero).
 constexpr int kW16Ops = 18;
 constexpr int kW16Elems = kW16Ops * 64 * 8;      // 9,216
 constexpr int kBiasFloats = 200;                 // b1' | b2' | b3' | b4
@@ -226,5 +229,244 @@ __device__ __forceinline__ void mlp2_bf16(const float4 *__restrict__ wl,
     uA = mfma32bf(w1, pack_bf16(hA[2], hA[3]), mfma32bf(w0, pack_bf16(hA[0], hA[1]), b4));
     uB = mfma32bf(w1, pack_bf16(hB[2], hB[3]), mfma32bf(w0, pack_bf16(hB[0], hB[1]), b4));
 }
+
+
+// ------------------------------------------------------------ fp16 x 2 chain
+// Float32-faithful products on the fp16 matrix cores: every float32 operand x
+// is carried as hi = fp16(x) and lo = fp16(x - hi) (11 + 11 significand
+// bits, |x - hi - lo| <= 2^-22 |x| in the normal range), and
+// x w = x_hi w_hi + x_hi w_lo + x_lo w_hi up to a dropped x_lo w_lo term of
+// relative size 2^-22; accumulation is float32.  The weights are split on
+// the host, the activations after every GELU.  An activation beyond the fp16
+// range turns into inf and so into a non-finite U, which the caller detects
+// and recomputes with the exact float32 chain.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v4f mfma32h(v8h a, v8h b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// hi / lo fp16 B operands for K = 32 (slots 0..3 from channel block `lo_blk`,
+// 4..7 from `hi_blk`, as in pack_bf16).
+__device__ __forceinline__ void split_f16(v4f b0, v4f b1, v8h &hi, v8h &lo) {
+#pragma unroll
+    for (int r = 0; r < 4; r += 2) {
+        const v2h h0 = __builtin_convertvector((v2f){b0[r], b0[r + 1]}, v2h);
+        const v2h h1 = __builtin_convertvector((v2f){b1[r], b1[r + 1]}, v2h);
+        const v2h l0 = __builtin_convertvector(
+            (v2f){b0[r] - (float)h0[0], b0[r + 1] - (float)h0[1]}, v2h);
+        const v2h l1 = __builtin_convertvector(
+            (v2f){b1[r] - (float)h1[0], b1[r + 1] - (float)h1[1]}, v2h);
+        hi[r] = h0[0];
+        hi[r + 1] = h0[1];
+        hi[r + 4] = h1[0];
+        hi[r + 5] = h1[1];
+        lo[r] = l0[0];
+        lo[r + 1] = l0[1];
+        lo[r + 4] = l1[0];
+        lo[r + 5] = l1[1];
+    }
+}
+
+// t += W x over K = 64 (two K = 32 halves) with the three-term split.
+__device__ __forceinline__ v4f mfma_x2(const v8h *__restrict__ wh, const v8h *__restrict__ wl,
+                                       int op0, int lane, const v8h (&xh)[2],
+                                       const v8h (&xl)[2], v4f t) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const v8h a = wh[(op0 + s) * 64 + lane], b = wl[(op0 + s) * 64 + lane];
+        t = mfma32h(a, xl[s], t);
+        t = mfma32h(b, xh[s], t);
+        t = mfma32h(a, xh[s], t);
+    }
+    return t;
+}
+
+// Two pair blocks through the fp16 x 2 chain: layer 1 on the float32 MFMA
+// (K = 4, float32 features), layers 2..4 as above.  wl holds the float32
+// layer-1 group (64 float4); wh / wlo the fp16 hi / lo operands [op][lane].
+__device__ __forceinline__ void mlp2_f16x2(const float4 *__restrict__ wl,
+                                           const v8h *__restrict__ wh,
+                                           const v8h *__restrict__ wlo,
+                                           const float *__restrict__ bl, float vA, float vB,
+                                           v4f &uA, v4f &uB) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    v4f hA[4], hB[4];
+    {
+        const float4 w = wl[lane];
+        const float w1[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const v4f b = bias4(bl, 16 * c + 4 * g);
+            hA[c] = mfma4(w1[c], vA, b);
+            hB[c] = mfma4(w1[c], vB, b);
+        }
+    }
+#pragma unroll
+    for (int layer = 0; layer < 3; ++layer) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hA[c][r] = gelu_f32(hA[c][r]);
+                hB[c][r] = gelu_f32(hB[c][r]);
+            }
+        v8h xhA[2], xlA[2], xhB[2], xlB[2];
+        split_f16(hA[0], hA[1], xhA[0], xlA[0]);
+        split_f16(hA[2], hA[3], xhA[1], xlA[1]);
+        split_f16(hB[0], hB[1], xhB[0], xlB[0]);
+        split_f16(hB[2], hB[3], xhB[1], xlB[1]);
+        if (layer < 2) {
+#pragma unroll
+            for (int co = 0; co < 4; ++co) {
+                const v4f b = bias4(bl, 64 * (layer + 1) + 16 * co + 4 * g);
+                const int op0 = layer * 8 + co * 2;
+                hA[co] = mfma_x2(wh, wlo, op0, lane, xhA, xlA, b);
+                hB[co] = mfma_x2(wh, wlo, op0, lane, xhB, xlB, b);
+            }
+        } else {
+            v4f b4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b4[r] = (4 * g + r < kHeads) ? bl[192 + 4 * g + r] : 0.0f;
+            uA = mfma_x2(wh, wlo, 16, lane, xhA, xlA, b4);
+            uB = mfma_x2(wh, wlo, 16, lane, xhB, xlB, b4);
+        }
+    }
+}
+
+// One pair block through the float32 chain (weights through any pointer):
+// the exact fall back of the fp16 x 2 chain, which runs only for the rare
+// block whose fp16 x 2 result was not finite.  One block at a time keeps its
+// register footprint below that of the hot path it is inlined into.
+__device__ inline v4f mlp1_f32(const float4 *__restrict__ wl, const float *__restrict__ bl,
+                               float v) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    v4f h[4], t[4];
+    {
+        const float4 w = wl[lane];
+        const float w1[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) h[c] = mfma4(w1[c], v, bias4(bl, 16 * c + 4 * g));
+    }
+    for (int layer = 0; layer < 2; ++layer) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[c][r] = gelu_f32(h[c][r]);
+#pragma unroll
+        for (int co = 0; co < 4; ++co) t[co] = bias4(bl, 64 * (layer + 1) + 16 * co + 4 * g);
+        const int gbase = 1 + 16 * layer;
+#pragma unroll
+        for (int ci = 0; ci < 4; ++ci)
+#pragma unroll
+            for (int co = 0; co < 4; ++co) {
+                const float4 w = wl[(gbase + co * 4 + ci) * 64 + lane];
+                t[co] = mfma4(w.x, h[ci][0], t[co]);
+                t[co] = mfma4(w.y, h[ci][1], t[co]);
+                t[co] = mfma4(w.z, h[ci][2], t[co]);
+                t[co] = mfma4(w.w, h[ci][3], t[co]);
+            }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) h[c] = t[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[c][r] = gelu_f32(h[c][r]);
+    v4f u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u[r] = (4 * g + r < kHeads) ? bl[192 + 4 * g + r] : 0.0f;
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci) {
+        const float4 w = wl[(33 + ci) * 64 + lane];
+        u = mfma4(w.x, h[ci][0], u);
+        u = mfma4(w.y, h[ci][1], u);
+        u = mfma4(w.z, h[ci][2], u);
+        u = mfma4(w.w, h[ci][3], u);
+    }
+    return u;
+}
+
+__device__ __forceinline__ bool all_finite(const v4f &a, const v4f &b) {
+    bool ok = true;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        ok = ok && __builtin_isfinite(a[r]) && __builtin_isfinite(b[r]);
+    return ok;
+}
+
+
+// ------------------------------------------------------------ mode dispatch
+// kMlpF32: every layer on the float32 MFMA (weights 37 KB in LDS).
+// kMlpF16x2: layer 1 float32, layers 2..4 fp16 x 2 (float32-faithful), with
+//   a per-block-pair fall back to the float32 chain (weights from global
+//   memory) when an activation left the fp16 range.
+// kMlpBf16: layer 1 float32, layers 2..4 bf16 operands, GELU degree 3.
+constexpr int kMlpF32 = 0, kMlpF16x2 = 1, kMlpBf16 = 2;
+
+template <int kMode>
+struct MlpLds {
+    static constexpr int kW4 = kMode == kMlpF32 ? kW32Groups * 64 : 64;
+    static constexpr int kOps16 = kMode == kMlpF32 ? 1 : kW16Ops * 64;
+    float4 *wl;
+    v8h *wh;
+    v8h *wlo;
+    v8bf *wb;
+    float *bl;
+
+    __device__ MlpLds() {
+        __shared__ float4 s_wl[kW4];
+        __shared__ v8h s_wh[kMode == kMlpF16x2 ? kOps16 : 1];
+        __shared__ v8h s_wlo[kMode == kMlpF16x2 ? kOps16 : 1];
+        __shared__ v8bf s_wb[kMode == kMlpBf16 ? kOps16 : 1];
+        __shared__ float s_bl[kBiasFloats];
+        wl = s_wl;
+        wh = s_wh;
+        wlo = s_wlo;
+        wb = s_wb;
+        bl = s_bl;
+    }
+
+    // Copy this mode's operands and the biases into LDS (all threads; the
+    // caller synchronises before use).
+    template <int kThreads>
+    __device__ void stage(const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
+                          const v8h *__restrict__ wx2, const float *__restrict__ bias) {
+        stage_weights<kThreads>(wl, bl, w32, bias, kW4);
+        if constexpr (kMode == kMlpF16x2)
+            for (int i = threadIdx.x; i < kOps16; i += kThreads) {
+                wh[i] = wx2[i];
+                wlo[i] = wx2[kOps16 + i];
+            }
+        if constexpr (kMode == kMlpBf16)
+            for (int i = threadIdx.x; i < kOps16; i += kThreads) wb[i] = w16[i];
+    }
+
+    // Two pair blocks through this mode's chain.  Returns false (for the
+    // whole wave) when the fp16 x 2 chain produced a non-finite value, i.e.
+    // an activation may have left the fp16 range: the caller then redoes its
+    // work with run_exact.  The other modes always return true.
+    __device__ __forceinline__ bool run(float fA, float fB, v4f &uA, v4f &uB) const {
+        if constexpr (kMode == kMlpF32) {
+            mlp2_f32(wl, bl, fA, fB, uA, uB);
+            return true;
+        } else if constexpr (kMode == kMlpF16x2) {
+            mlp2_f16x2(wl, wh, wlo, bl, fA, fB, uA, uB);
+            return __ballot(!all_finite(uA, uB)) == 0;
+        } else {
+            mlp2_bf16(wl, wb, bl, fA, fB, uA, uB);
+            return true;
+        }
+    }
+
+    // The exact float32 chain with the float32 operands w32 in global memory.
+    __device__ __forceinline__ void run_exact(const float4 *__restrict__ w32, float fA, float fB,
+                                              v4f &uA, v4f &uB) const {
+        uA = mlp1_f32(w32, bl, fA);
+        uB = mlp1_f32(w32, bl, fB);
+    }
+};
 
 }  // namespace pip

@@ -119,6 +119,40 @@ def test_pair_embed_bf16_large_workload():
     assert_zero_bits(U.transpose(0, 2, 3, 1), ~pair_mask(d["mask"]), "U bf16 padding")
 
 
+def test_pair_embed_fp16_overflow_redoes_exactly():
+    # One hidden channel of layer 1 is driven to ~8e4 (beyond fp16) through a
+    # large bias but read out through tiny layer-2 weights, so the problem
+    # stays well conditioned while the fp16 x 2 chain overflows; the folded
+    # weights are well scaled, so that chain is the one chosen.  The affected
+    # waves must redo their share with the exact float32 chain.
+    p4, mask = ragged_jets(3, 48, (48, 30, 17), seed=21)
+    params = mlp_for(21, biases=True)
+    params["b1"] = params["b1"].copy()
+    params["b1"][5] = 8.0e4
+    params["w2"] = params["w2"].copy()
+    params["w2"][:, 5] = 1.0e-5
+    ws = pip.fold(params)[0]
+    assert all(2 ** -8 <= np.abs(w).max() <= 2 ** 14 for w in ws[1:])
+    assert np.abs(ws[0][5]).max() < 1.0 and pip.fold(params)[1][0][5] > 65504.0 / 3
+    mlp = pip.PairMLP(params)
+    U = host(pip.pair_embed(g(p4), g(mask), mlp))
+    ref = oracle.pair_embed(p4, mask, params)
+    assert_close(U, ref, TOL32, "U f32 with an fp16-overflowing hidden channel")
+
+
+def test_pair_embed_badly_scaled_weights_use_exact_chain():
+    # layer 3 x 1e5 and layer 4 x 1e-5: far outside the well-scaled range, so
+    # the exact float32 chain runs; U stays O(1) and well conditioned.
+    p4, mask = ragged_jets(2, 32, (32, 19), seed=22)
+    params = mlp_for(22)
+    params["w3"] = (params["w3"] * 1e5).astype(np.float32)
+    params["w4"] = (params["w4"] * 1e-5).astype(np.float32)
+    mlp = pip.PairMLP(params)
+    U = host(pip.pair_embed(g(p4), g(mask), mlp))
+    ref = oracle.pair_embed(p4, mask, params)
+    assert_close(U, ref, TOL32, "U f32 with badly scaled weights")
+
+
 def test_pair_embed_ignores_padding_values():
     p4, mask = ragged_jets(3, 32, (20, 32, 9), seed=3)
     params = mlp_for(3, biases=True)
