@@ -85,20 +85,13 @@ __device__ __forceinline__ void store_o(QkvT<kBf16> *Orow, const v4f &o) {
     else *(float4 *)Orow = make_float4(o[0], o[1], o[2], o[3]);
 }
 
-// Stage the MLP weights of the chosen precision into LDS.
-template <bool kBf16, int kThreads>
-__device__ inline void stage_mlp(float4 *wl, v8bf *wl16, float *bl, const float4 *w32,
-                                 const v8bf *w16, const float *bias) {
-    stage_weights<kThreads>(wl, bl, w32, bias, kBf16 ? 64 : kW32Groups * 64);
-    if constexpr (kBf16)
-        for (int i = threadIdx.x; i < kW16Ops * 64; i += kThreads) wl16[i] = w16[i];
-}
-
-template <bool kBf16>
-__device__ __forceinline__ void mlp2(const float4 *wl, const v8bf *wl16, const float *bl,
-                                     float fA, float fB, v4f &uA, v4f &uB) {
-    if constexpr (kBf16) mlp2_bf16(wl, wl16, bl, fA, fB, uA, uB);
-    else mlp2_f32(wl, bl, fA, fB, uA, uB);
+// Two pair blocks through the chain of mode kMode; a non-finite fp16 x 2
+// result (an activation beyond fp16) is recomputed with the exact chain.
+template <int kMode>
+__device__ __forceinline__ void mlp_pair_blocks(const MlpLds<kMode> &M,
+                                                const float4 *__restrict__ w32, float fA,
+                                                float fB, v4f &uA, v4f &uB) {
+    if (!M.run(fA, fB, uA, uB)) M.run_exact(w32, fA, fB, uA, uB);
 }
 
 // ------------------------------------------------------------ jet kernel
@@ -107,17 +100,14 @@ constexpr int kJetMaxP = 128;
 constexpr int kJetMaxT = kJetMaxP / kTile;
 constexpr int kSortMaxB = 2048;
 
-template <bool kBf16>
+template <int kMode, bool kBf16 = (kMode == kMlpBf16)>
 __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
     const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B, int P, int sort,
-    const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
+    const float4 *__restrict__ w32, const v8bf *__restrict__ w16, const v8h *__restrict__ wx2,
     const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
     const QkvT<kBf16> *__restrict__ K, const QkvT<kBf16> *__restrict__ V,
     QkvT<kBf16> *__restrict__ O) {
-    constexpr int kW4 = kBf16 ? 64 : kW32Groups * 64;
-    __shared__ float4 wl[kW4];
-    __shared__ v8bf wl16[kBf16 ? kW16Ops * 64 : 1];
-    __shared__ float bl[kBiasFloats];
+    MlpLds<kMode> M;
     __shared__ PartLds<kJetMaxP> L;
     __shared__ float us[2][kHeads][16][17];
     __shared__ float4 Ost[kHeads][kJetMaxT][64];  // O^T accumulators, lane layout
@@ -195,7 +185,7 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
         const int real = mask[idx] != 0;
         stage_particle(L, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
     }
-    stage_mlp<kBf16, kJetThreads>(wl, wl16, bl, w32, w16, bias);
+    M.template stage<kJetThreads>(w32, w16, wx2, bias);
     for (int i = tid; i < kHeads * T * 64; i += kJetThreads)
         (&Ost[0][0][0])[(i / (T * 64)) * kJetMaxT * 64 + i % (T * 64)] =
             make_float4(0.f, 0.f, 0.f, 0.f);
@@ -259,7 +249,7 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
             const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, k) : 0.0f;
             const float fB = realB ? pair_feature(L, r0 + iB, c0 + jB, k) : 0.0f;
             v4f uA, uB;
-            mlp2<kBf16>(wl, wl16, bl, fA, fB, uA, uB);
+            mlp_pair_blocks<kMode>(M, w32, fA, fB, uA, uB);
             if (lane < 32) {
                 const int h0 = (lane >> 4) * 4;
 #pragma unroll
@@ -297,17 +287,14 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
 // ------------------------------------------------------------ row kernel
 constexpr int kRowThreads = 256;
 
-template <bool kBf16>
+template <int kMode, bool kBf16 = (kMode == kMlpBf16)>
 __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
     const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
-    const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
+    const float4 *__restrict__ w32, const v8bf *__restrict__ w16, const v8h *__restrict__ wx2,
     const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
     const QkvT<kBf16> *__restrict__ K, const QkvT<kBf16> *__restrict__ V,
     QkvT<kBf16> *__restrict__ O) {
-    constexpr int kW4 = kBf16 ? 64 : kW32Groups * 64;
-    __shared__ float4 wl[kW4];
-    __shared__ v8bf wl16[kBf16 ? kW16Ops * 64 : 1];
-    __shared__ float bl[kBiasFloats];
+    MlpLds<kMode> M;
     __shared__ PartLds<kMaxP> L;
     __shared__ float us[kHeads][16][17];
     __shared__ int blkAny[kMaxP / kTile];
@@ -338,7 +325,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
         }
         return;
     }
-    stage_mlp<kBf16, kRowThreads>(wl, wl16, bl, w32, w16, bias);
+    M.template stage<kRowThreads>(w32, w16, wx2, bias);
     __syncthreads();
 
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
@@ -355,7 +342,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
             const float fA = realA ? pair_feature(L, r0 + iA, c0 + j, k) : 0.0f;
             const float fB = realB ? pair_feature(L, r0 + iB, c0 + j, k) : 0.0f;
             v4f uA, uB;
-            mlp2<kBf16>(wl, wl16, bl, fA, fB, uA, uB);
+            mlp_pair_blocks<kMode>(M, w32, fA, fB, uA, uB);
             if (lane < 32) {
                 const int h0 = (lane >> 4) * 4;
 #pragma unroll
@@ -396,20 +383,21 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
     }
 }
 
-template <bool kBf16>
+template <int kMode, bool kBf16 = (kMode == kMlpBf16)>
 static hipError_t launch_fused(const float *p4, const uint8_t *mask, int B, int P,
                                const pip_pair_mlp *m, const QkvT<kBf16> *Q,
                                const QkvT<kBf16> *K, const QkvT<kBf16> *V, QkvT<kBf16> *O,
                                hipStream_t s) {
     if (P <= kJetMaxP) {
         const int sort = B <= kSortMaxB ? 1 : 0;
-        hipLaunchKernelGGL(embed_attention_jet_kernel<kBf16>, dim3(B), dim3(kJetThreads), 0, s,
+        hipLaunchKernelGGL(embed_attention_jet_kernel<kMode>, dim3(B), dim3(kJetThreads), 0, s,
                            (const float4 *)p4, mask, B, P, sort, (const float4 *)m->w32,
-                           (const v8bf *)m->w16, m->bias, Q, K, V, O);
+                           (const v8bf *)m->w16, (const v8h *)m->wx2, m->bias, Q, K, V, O);
     } else {
-        hipLaunchKernelGGL(embed_attention_row_kernel<kBf16>, dim3(B * (P / kTile)),
+        hipLaunchKernelGGL(embed_attention_row_kernel<kMode>, dim3(B * (P / kTile)),
                            dim3(kRowThreads), 0, s, (const float4 *)p4, mask, P,
-                           (const float4 *)m->w32, (const v8bf *)m->w16, m->bias, Q, K, V, O);
+                           (const float4 *)m->w32, (const v8bf *)m->w16, (const v8h *)m->wx2,
+                           m->bias, Q, K, V, O);
     }
     return hipGetLastError();
 }
@@ -417,14 +405,15 @@ static hipError_t launch_fused(const float *p4, const uint8_t *mask, int B, int 
 hipError_t launch_embed_attention_f32(const float *p4, const uint8_t *mask, int B, int P,
                                       const pip_pair_mlp *m, const float *Q, const float *K,
                                       const float *V, float *O, hipStream_t s) {
-    return launch_fused<false>(p4, mask, B, P, m, Q, K, V, O, s);
+    return m->f16ok ? launch_fused<kMlpF16x2>(p4, mask, B, P, m, Q, K, V, O, s)
+                    : launch_fused<kMlpF32>(p4, mask, B, P, m, Q, K, V, O, s);
 }
 
 hipError_t launch_embed_attention_bf16(const float *p4, const uint8_t *mask, int B, int P,
                                        const pip_pair_mlp *m, const uint16_t *Q,
                                        const uint16_t *K, const uint16_t *V, uint16_t *O,
                                        hipStream_t s) {
-    return launch_fused<true>(p4, mask, B, P, m, Q, K, V, O, s);
+    return launch_fused<kMlpBf16>(p4, mask, B, P, m, Q, K, V, O, s);
 }
 
 }  // namespace pip

@@ -46,6 +46,27 @@ def test_fused_bf16(B, P, ns):
     assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "fused bf16 padded rows")
 
 
+@pytest.mark.parametrize("P,ns", [(48, (48, 30, 17)), (160, (160, 70, 17))])
+def test_fused_f32_mlp_modes(P, ns):
+    # The fp16 x 2 chain with a hidden channel beyond fp16 (redone exactly),
+    # then the exact chain chosen for badly scaled weights; jet and row kernel.
+    p4, mask = ragged_jets(3, P, ns, seed=P + 21)
+    q, k, v = rand_qkv(3, 8, P, mask, seed=P + 21)
+    over = mlp_for(21, biases=True)
+    over["b1"] = over["b1"].copy()
+    over["b1"][5] = 8.0e4
+    over["w2"] = over["w2"].copy()
+    over["w2"][:, 5] = 1.0e-5
+    scaled = mlp_for(22)
+    scaled["w3"] = (scaled["w3"] * 1e5).astype(np.float32)
+    scaled["w4"] = (scaled["w4"] * 1e-5).astype(np.float32)
+    for name, params in (("overflow", over), ("badly scaled", scaled)):
+        mlp = pip.PairMLP(params)
+        O = host(pip.pair_embed_attention(g(p4), g(mask), mlp, g(q), g(k), g(v)))
+        ref = oracle.pair_embed_attention(p4, mask, params, q, k, v)
+        assert_close(O, ref, TOL32, "fused O f32, %s weights, P=%d" % (name, P))
+
+
 def test_fused_batch512_workload():
     d = synth.make_workload("fused512")
     mlp = pip.PairMLP(d["mlp"])
