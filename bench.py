@@ -36,7 +36,7 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pair_embed_f32_kernel_B128_P128_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "pair_interaction_particle_amd", "csrc", f)
-                  for f in ("pair_embed.hip", "pip_device.h")]
+                  for f in ("pair_embed.hip", "pip_device.h", "pip_mlp.h")]
 
 
 def kernel_source_hash():
@@ -272,7 +272,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-                     "traffic": traffic, "kernel": "pair_embed_kernel<false> (fp32)",
+                     "traffic": traffic, "kernel": "pair_embed_kernel<kMlpF16x2> (fp32 path)",
                      "algorithmic_flop_per_launch": flops,
                      "unique_real_pairs": uniq},
         "pair_embed_us": t_embed * 1e3,
