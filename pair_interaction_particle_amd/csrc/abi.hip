@@ -267,7 +267,8 @@ pip_status pip_pair_bias_attention(const void *Q, const void *K, const void *V, 
     if (B == 0 || P == 0 || H == 0) return PIP_OK;
     if (!Q || !K || !V || !U || !mask || !O) return PIP_ERR_NULL;
     if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
-    if (B * H > ((int64_t)1 << 31) - 1) return PIP_ERR_UNSUPPORTED;
+    if (B * H * pip::attention_chunks((int)P) > ((int64_t)1 << 31) - 1)
+        return PIP_ERR_UNSUPPORTED;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(O))
         return PIP_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;

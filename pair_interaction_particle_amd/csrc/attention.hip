@@ -2,207 +2,488 @@
 //
 // "Event Classification with Masked Transformer Autoencoders"
 // (ml4sci_cms_e2e26 README), "How the Kernel Fusion Works", Fusion 3:
-// softmax(Q K^T / sqrt(d) + bias) V in one pass with a FlashAttention-style
-// online softmax, never materialising the (B*H, P, P) score matrix.
+// softmax(Q K^T / sqrt(d) + bias) V in one pass, never materialising the
+// (B*H, P, P) score matrix in HBM.
 //
-// gfx950 design: one 256-thread workgroup per (jet, head); wave w owns query
-// blocks w, w+4, ... of 16 queries.  For each key block of 16 keys that holds
-// a real key, the scores are computed transposed, S^T = K Q^T, with MFMA so
-// that lane l ends up with the 4 scores of query l%16 against keys 4(l/16)+r:
-// the row max / row sum need an in-lane reduction over r plus two cross-lane
-// steps (lanes l^16 and l^32), and the probabilities are already the B operand
-// of O^T += V^T P^T.  The U tile is read with one 16-byte load per lane
-// (query row, 4 consecutive keys).  Key blocks without a real key and query
-// blocks without a real query are skipped; padded query rows store 0.
-#include "pip_device.h"
+// The kernel reads U once and is bound by HBM, so the design is about bytes in
+// flight: every workgroup of the launch should be resident at once, issue all
+// of its loads early and have little work left once the data is there.  One
+// workgroup per (jet, head, group of up to 8 query blocks of 16 queries); each
+// wave owns kQ query blocks (2 for P <= 128, which keeps the register count
+// low enough for four workgroups per CU, 1 for larger P).
+//   1. Each wave takes the jet's real-slot bits with ballots (wave-uniform,
+//      no LDS), then issues the loads of its U strips (16 queries x every key
+//      block that holds a real key) and of its Q rows into registers.
+//   2. While those are in flight the workgroup stages K and V^T in LDS for
+//      the key blocks up to an even count; padded key rows and blocks without
+//      a real key are written as 0 (a NaN there must not meet a zero
+//      probability inside the MFMA).
+//   3. One barrier, then per query block: U of padded keys is replaced by
+//      -inf; scores S^T = K Q^T on the matrix cores, transposed so that lane l
+//      holds query l%16 against keys 4(l/16)+r, over pairs of key blocks; an
+//      exact two-pass softmax over the strip held in registers (row max and
+//      row sum need an in-lane reduction and two cross-lane steps); then
+//      O^T += V^T P^T with one K = 32 product per pair of key blocks, the
+//      probabilities already in the B-operand layout.
+// Query blocks without a real query store zeros; padded queries store 0.
+//
+// float32 inputs run on the fp16 matrix cores with split operands: every
+// float32 x is carried as hi + lo (two fp16, 22 significand bits).  Scores
+// take all four products, (K_hi + K_lo)(Q_hi + Q_lo), in two 16x16x32 MFMAs
+// whose reduction index runs over [hi | lo] x d; P V takes three
+// (V_hi P_hi + V_hi P_lo + V_lo P_hi).  The products are exact in fp32 and
+// accumulated in fp32, so the result is float32-faithful (relative product
+// error about 2^-22).  K and V are split once when staged.  When a real Q, K
+// or V value is beyond the fp16 range (or not finite) the query block takes a
+// float32 MFMA path instead.  bfloat16 inputs use the bf16 matrix cores.
+#include "pip_attn.h"
 #include "pip_internal.h"
 
 namespace pip {
 
-__device__ __forceinline__ float xmax16(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ __forceinline__ float xsum16(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
-}
+constexpr int kAttnQBlocks = 8;  // query blocks per workgroup
+constexpr float kF16Safe = 65504.0f;
+constexpr uint32_t kBf16NegInf = 0xff80ff80u;  // two bf16 -inf
 
-// log2(e) / sqrt(16) and log2(e): scores are kept in base-2 units.
-constexpr float kLog2e = 1.4426950408889634f;
+template <bool kBf16>
+using AttnElt = typename std::conditional<kBf16, uint16_t, float>::type;
 
-// Online-softmax update of one key block for the lane's query (l%16).  s[r]
-// are base-2 scores for keys 4(l/16)+r (-inf for padded keys); returns the
-// probabilities p[r] and updates m (running max), l (running sum) and the
-// rescale factor of the accumulator.
-__device__ __forceinline__ float online_softmax(v4f &s, float &m, float &l) {
-    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    bm = xmax16(bm);
-    const float mn = fmaxf(m, bm);
-    const float corr = exp2f(m - mn);  // m = -inf on the first block -> 0
+// Real-slot bits of one jet: bit k of word k/64, the same in every lane.
+template <int kWords>
+struct SlotBits {
+    uint64_t w[kWords];
+
+    // every byte load is issued (address clamped into the row) before the
+    // first ballot, so the loads overlap
+    __device__ __forceinline__ void load(const uint8_t *__restrict__ mrow, int P) {
+        const int lane = threadIdx.x & 63;
+        uint8_t b[kWords];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = exp2f(s[r] - mn);
-    float ps = (s[0] + s[1]) + (s[2] + s[3]);
-    ps = xsum16(ps);
-    l = l * corr + ps;
-    m = mn;
-    return corr;
-}
-
-__global__ __launch_bounds__(256) void attention_f32_kernel(
-    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
-    const float *__restrict__ U, const uint8_t *__restrict__ mask, int H, int P,
-    float *__restrict__ O) {
-    __shared__ int realS[kTile * 16];
-    __shared__ int blkAny[16];
-    const int bh = blockIdx.x, jet = bh / H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, c = lane & 15;
-    const int T = P / kTile;
-    for (int i = tid; i < P; i += 256) realS[i] = mask[(size_t)jet * P + i] != 0;
-    __syncthreads();
-    if (tid < T) {
-        int a = 0;
-        for (int i = 0; i < kTile; ++i) a |= realS[tid * kTile + i];
-        blkAny[tid] = a;
+        for (int i = 0; i < kWords; ++i) b[i] = mrow[min(64 * i + lane, P - 1)];
+#pragma unroll
+        for (int i = 0; i < kWords; ++i) w[i] = __ballot(64 * i + lane < P && b[i] != 0);
     }
-    __syncthreads();
+    // word i for a run-time i (selects, no indexed register access)
+    __device__ __forceinline__ uint64_t word(int i) const {
+        uint64_t r = w[0];
+#pragma unroll
+        for (int j = 1; j < kWords; ++j) r = i == j ? w[j] : r;
+        return r;
+    }
+    // the 16 bits of block kb (compile-time kb)
+    __device__ __forceinline__ uint32_t block(int kb) const {
+        return (uint32_t)(w[kb >> 2] >> (16 * (kb & 3))) & 0xffffu;
+    }
+    __device__ __forceinline__ uint32_t block_rt(int kb) const {
+        return (uint32_t)(word(kb >> 2) >> (16 * (kb & 3))) & 0xffffu;
+    }
+    __device__ __forceinline__ bool slot(int k) const { return (word(k >> 6) >> (k & 63)) & 1; }
+};
 
-    const size_t base = (size_t)bh * P;
-    const float qk_scale = kLog2e * 0.25f;  // log2(e) / sqrt(16)
-    for (int qb = wave; qb < T; qb += 4) {
-        const int q = qb * kTile + c;
-        float4 *orow = (float4 *)(O + (base + q) * 16 + 4 * g);
-        if (!blkAny[qb]) {
-            *orow = make_float4(0.f, 0.f, 0.f, 0.f);
-            continue;
-        }
-        const float4 qv = *(const float4 *)(Q + (base + q) * 16 + 4 * g);
-        float m = -INFINITY, l = 0.f;
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = 0; kb < T; ++kb) {
-            if (!blkAny[kb]) continue;
-            const int k0 = kb * kTile;
-            const float4 kv = *(const float4 *)(K + (base + k0 + c) * 16 + 4 * g);
-            v4f s = {0.f, 0.f, 0.f, 0.f};
-            s = mfma4(kv.x, qv.x, s);
-            s = mfma4(kv.y, qv.y, s);
-            s = mfma4(kv.z, qv.z, s);
-            s = mfma4(kv.w, qv.w, s);
-            const float4 u = *(const float4 *)(U + (base + q) * P + k0 + 4 * g);
-            const float uu[4] = {u.x, u.y, u.z, u.w};
+// LDS row stride (elements) of V^T: the key range plus a pad that spreads the
+// 16 rows over the banks.
+constexpr int vt_stride(int kT) { return kT * 16 + 8; }
+
+// Position of key k inside a V^T row: keys are grouped by pairs of key
+// blocks so that lane group g finds keys 4g..4g+3 of both blocks of a pair
+// in 8 consecutive entries (one 16-byte LDS read per operand).
+__device__ __forceinline__ int vt_pos(int k) {
+    return (k & ~31) + ((k >> 2) & 3) * 8 + ((k >> 4) & 1) * 4 + (k & 3);
+}
+
+__device__ __forceinline__ bool f16_safe(float4 x) {
+    return fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))) <= kF16Safe &&
+           x.x == x.x && x.y == x.y && x.z == x.z && x.w == x.w;
+}
+
+__device__ __forceinline__ float max8(const float (&a)[4], const float (&b)[4]) {
+    return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+                 fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+}
+
+// Is either block of the pair (kb, kb + 1) a block with a real key?
+template <int kWords>
+__device__ __forceinline__ bool pair_real(const SlotBits<kWords> &real, int kb, int T) {
+    return (kb < T && real.block(kb)) || (kb + 1 < T && real.block(kb + 1));
+}
+
+// ------------------------------------------------------------ float32
+// One query block (rows q0 .. q0+15) of a float32 head.  u is the U strip
+// (-inf for key blocks without a real key), qa / qc are this lane's Q row
+// entries 8(g&1) .. +3 and +4 .. +7 (0 for padded queries).
+template <int kT, int kWords>
+__device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc, bool rq,
+                                           bool kvbad, const SlotBits<kWords> &real, int T,
+                                           const uint16_t *Ks, const uint16_t *Vth,
+                                           const uint16_t *Vtl, const float *__restrict__ Qh,
+                                           const float *__restrict__ Kh,
+                                           const float *__restrict__ Vh,
+                                           const float *__restrict__ urow, int q0,
+                                           float *__restrict__ orow) {
+    constexpr int kVt = vt_stride(kT);
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    float m = -INFINITY, lsum = 0.f;
+    v4f o = {0.f, 0.f, 0.f, 0.f};
+    if (!(kvbad || __any(rq && !(f16_safe(qa) && f16_safe(qc))))) {
+        // U of padded keys -> -inf, so that every score is an FMA result
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                s[r] = realS[k0 + 4 * g + r] ? fmaf(s[r], qk_scale, uu[r] * kLog2e) : -INFINITY;
-            const float corr = online_softmax(s, m, l);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= corr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // select, not multiply: a NaN in a padded V row must not meet p = 0
-                const float vv = realS[k0 + 4 * g + r] ? V[(base + k0 + 4 * g + r) * 16 + c] : 0.f;
-                acc = mfma4(vv, s[r], acc);
+        for (int kb = 0; kb < kT; ++kb) {
+            const uint32_t bits = real.block(kb);
+            if (kb < T && bits != 0 && bits != 0xffffu) {
+                const uint32_t kbits = bits >> (4 * g);
+                u[kb].x = (kbits & 1) ? u[kb].x : -INFINITY;
+                u[kb].y = (kbits & 2) ? u[kb].y : -INFINITY;
+                u[kb].z = (kbits & 4) ? u[kb].z : -INFINITY;
+                u[kb].w = (kbits & 8) ? u[kb].w : -INFINITY;
             }
         }
-        const float inv = realS[q] ? 1.0f / l : 0.0f;
-        float4 o;
-        o.x = realS[q] ? acc[0] * inv : 0.f;
-        o.y = realS[q] ? acc[1] * inv : 0.f;
-        o.z = realS[q] ? acc[2] * inv : 0.f;
-        o.w = realS[q] ? acc[3] * inv : 0.f;
-        *orow = o;
-    }
-}
-
-// ------------------------------------------------------------ bf16
-__device__ __forceinline__ float bf2f(uint16_t b) {
-    return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
-__device__ __forceinline__ uint16_t f2bf(float x) {
-    __bf16 h = (__bf16)x;
-    return __builtin_bit_cast(uint16_t, h);
-}
-__device__ __forceinline__ v4f mfma16bf(v4s a, v4s b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-__global__ __launch_bounds__(256) void attention_bf16_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const uint16_t *__restrict__ U,
-    const uint8_t *__restrict__ mask, int H, int P, uint16_t *__restrict__ O) {
-    __shared__ int realS[kTile * 16];
-    __shared__ int blkAny[16];
-    const int bh = blockIdx.x, jet = bh / H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, c = lane & 15;
-    const int T = P / kTile;
-    for (int i = tid; i < P; i += 256) realS[i] = mask[(size_t)jet * P + i] != 0;
-    __syncthreads();
-    if (tid < T) {
-        int a = 0;
-        for (int i = 0; i < kTile; ++i) a |= realS[tid * kTile + i];
-        blkAny[tid] = a;
-    }
-    __syncthreads();
-
-    const size_t base = (size_t)bh * P;
-    const float qk_scale = kLog2e * 0.25f;
-    for (int qb = wave; qb < T; qb += 4) {
-        const int q = qb * kTile + c;
-        uint2 *orow = (uint2 *)(O + (base + q) * 16 + 4 * g);
-        if (!blkAny[qb]) {
-            *orow = make_uint2(0u, 0u);
-            continue;
+        v8h qh, ql;
+        {
+            v4h h0, l0, h1, l1;
+            split4_f16(qa, h0, l0);
+            split4_f16(qc, h1, l1);
+            qh = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+            ql = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        const v4s qv = *(const v4s *)(Q + (base + q) * 16 + 4 * g);
-        float m = -INFINITY, l = 0.f;
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = 0; kb < T; ++kb) {
-            if (!blkAny[kb]) continue;
-            const int k0 = kb * kTile;
-            const v4s kv = *(const v4s *)(K + (base + k0 + c) * 16 + 4 * g);
-            v4f s = {0.f, 0.f, 0.f, 0.f};
-            s = mfma16bf(kv, qv, s);
-            const uint2 uw = *(const uint2 *)(U + (base + q) * P + k0 + 4 * g);
-            const float uu[4] = {bf2f(uw.x & 0xffff), bf2f(uw.x >> 16), bf2f(uw.y & 0xffff),
-                                 bf2f(uw.y >> 16)};
+        // scores over pairs of key blocks; a block without a real key has
+        // zero K rows in LDS and U = -inf, so its scores are -inf
+        float s[kT][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                s[r] = realS[k0 + 4 * g + r] ? fmaf(s[r], qk_scale, uu[r] * kLog2e) : -INFINITY;
-            const float corr = online_softmax(s, m, l);
+        for (int kb = 0; kb < kT; kb += 2) {
+            if (!pair_real(real, kb, T)) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= corr;
-            v4s vv, pv;
+                for (int r = 0; r < 4; ++r) s[kb][r] = s[kb + 1][r] = -INFINITY;
+                continue;
+            }
+            // lane group g holds reduction entries [hi | lo][8(g & 1) .. + 7]
+            const v8h ka0 = *(const v8h *)(Ks + (kb * kTile + c) * 32 + 8 * g);
+            const v8h ka1 = *(const v8h *)(Ks + ((kb + 1) * kTile + c) * 32 + 8 * g);
+            v4f a0 = mfma32h(ka0, qh, (v4f){0.f, 0.f, 0.f, 0.f});
+            v4f a1 = mfma32h(ka1, qh, (v4f){0.f, 0.f, 0.f, 0.f});
+            a0 = mfma32h(ka0, ql, a0);
+            a1 = mfma32h(ka1, ql, a1);
+            s[kb][0] = fmaf(a0[0], 0.25f, u[kb].x);
+            s[kb][1] = fmaf(a0[1], 0.25f, u[kb].y);
+            s[kb][2] = fmaf(a0[2], 0.25f, u[kb].z);
+            s[kb][3] = fmaf(a0[3], 0.25f, u[kb].w);
+            s[kb + 1][0] = fmaf(a1[0], 0.25f, u[kb + 1].x);
+            s[kb + 1][1] = fmaf(a1[1], 0.25f, u[kb + 1].y);
+            s[kb + 1][2] = fmaf(a1[2], 0.25f, u[kb + 1].z);
+            s[kb + 1][3] = fmaf(a1[3], 0.25f, u[kb + 1].w);
+            m = fmaxf(m, max8(s[kb], s[kb + 1]));
+        }
+        m = xmax16(m);
+        const float mb = m * kLog2e;
+        // P V over the same pairs; V rows of blocks without a real key are 0
+#pragma unroll
+        for (int kb = 0; kb < kT; kb += 2) {
+            if (!pair_real(real, kb, T)) continue;
+            v8f p;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                vv[r] = realS[k0 + 4 * g + r] ? (short)V[(base + k0 + 4 * g + r) * 16 + c] : 0;
-                pv[r] = (short)f2bf(s[r]);
+                p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], kLog2e, -mb));
+                p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][r], kLog2e, -mb));
             }
-            acc = mfma16bf(vv, pv, acc);
+            lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            const int off = c * kVt + kb * kTile + 8 * g;
+            const v8h vh = *(const v8h *)(Vth + off);
+            const v8h vl = *(const v8h *)(Vtl + off);
+            const v8h ph = __builtin_convertvector(p, v8h);
+            const v8h pl = __builtin_convertvector(p - __builtin_convertvector(ph, v8f), v8h);
+            o = mfma32h(vh, pl, o);
+            o = mfma32h(vl, ph, o);
+            o = mfma32h(vh, ph, o);
         }
-        const bool rq = realS[q];
-        const float inv = rq ? 1.0f / l : 0.0f;
-        uint2 o;
-        o.x = rq ? ((uint32_t)f2bf(acc[0] * inv) | ((uint32_t)f2bf(acc[1] * inv) << 16)) : 0u;
-        o.y = rq ? ((uint32_t)f2bf(acc[2] * inv) | ((uint32_t)f2bf(acc[3] * inv) << 16)) : 0u;
-        *orow = o;
+    } else {
+        // A real Q, K or V value beyond the fp16 range: float32 MFMA with an
+        // online softmax, everything re-read from global memory (rare path).
+        const float4 qv = rq ? *(const float4 *)(Qh + (size_t)(q0 + c) * 16 + 4 * g)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int kb = 0; kb < T; ++kb) {
+            const uint32_t bits = real.block_rt(kb);
+            if (!bits) continue;
+            const uint32_t kbits = bits >> (4 * g);
+            const int kr = kb * kTile + c;
+            const float4 kv = real.slot(kr) ? *(const float4 *)(Kh + (size_t)kr * 16 + 4 * g)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mfma4(kv.x, qv.x, acc);
+            acc = mfma4(kv.y, qv.y, acc);
+            acc = mfma4(kv.z, qv.z, acc);
+            acc = mfma4(kv.w, qv.w, acc);
+            const float4 uv = *(const float4 *)(urow + kb * kTile);
+            const float uu[4] = {uv.x, uv.y, uv.z, uv.w};
+            float sb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sb[r] = ((kbits >> r) & 1) ? fmaf(acc[r], 0.25f, uu[r]) : -INFINITY;
+            const float bm = xmax16(fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
+            const float mn = fmaxf(m, bm);
+            const float corr = __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+            m = mn;
+            lsum *= corr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] *= corr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f((sb[r] - m) * kLog2e);
+                lsum += p;
+                const int kk = kb * kTile + 4 * g + r;
+                const float vv = ((kbits >> r) & 1) ? Vh[(size_t)kk * 16 + c] : 0.f;
+                o = mfma4(vv, p, o);
+            }
+        }
     }
+    const float inv = 1.0f / xsum16(lsum);
+    *(float4 *)orow = rq ? make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// ------------------------------------------------------------ bfloat16
+// One query block of a bf16 head.  u holds bf16 pairs (-inf for key blocks
+// without a real key), qv this lane's Q row entries 4g .. 4g+3.
+template <int kT, int kWords>
+__device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
+                                            const SlotBits<kWords> &real, int T,
+                                            const uint16_t *Ks, const uint16_t *Vth,
+                                            uint16_t *__restrict__ orow) {
+    constexpr int kVt = vt_stride(kT);
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    // U of padded keys -> -inf (bit patterns), so that every score is an FMA result
+#pragma unroll
+    for (int kb = 0; kb < kT; ++kb) {
+        const uint32_t bits = real.block(kb);
+        if (kb < T && bits != 0 && bits != 0xffffu) {
+            const uint32_t kbits = bits >> (4 * g);
+            const uint32_t k0 = ((kbits & 1) ? 0xffffu : 0u) | ((kbits & 2) ? 0xffff0000u : 0u);
+            const uint32_t k1 = ((kbits & 4) ? 0xffffu : 0u) | ((kbits & 8) ? 0xffff0000u : 0u);
+            u[kb].x = (u[kb].x & k0) | (kBf16NegInf & ~k0);
+            u[kb].y = (u[kb].y & k1) | (kBf16NegInf & ~k1);
+        }
+    }
+    float s[kT][4];
+    float m = -INFINITY, lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kT; kb += 2) {
+        if (!pair_real(real, kb, T)) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[kb][r] = s[kb + 1][r] = -INFINITY;
+            continue;
+        }
+        const v4s k0 = *(const v4s *)(Ks + (kb * kTile + c) * 16 + 4 * g);
+        const v4s k1 = *(const v4s *)(Ks + ((kb + 1) * kTile + c) * 16 + 4 * g);
+        const v4f a0 = mfma16bf(k0, qv, (v4f){0.f, 0.f, 0.f, 0.f});
+        const v4f a1 = mfma16bf(k1, qv, (v4f){0.f, 0.f, 0.f, 0.f});
+        s[kb][0] = fmaf(a0[0], 0.25f, bf2f(u[kb].x & 0xffff));
+        s[kb][1] = fmaf(a0[1], 0.25f, bf2f(u[kb].x >> 16));
+        s[kb][2] = fmaf(a0[2], 0.25f, bf2f(u[kb].y & 0xffff));
+        s[kb][3] = fmaf(a0[3], 0.25f, bf2f(u[kb].y >> 16));
+        s[kb + 1][0] = fmaf(a1[0], 0.25f, bf2f(u[kb + 1].x & 0xffff));
+        s[kb + 1][1] = fmaf(a1[1], 0.25f, bf2f(u[kb + 1].x >> 16));
+        s[kb + 1][2] = fmaf(a1[2], 0.25f, bf2f(u[kb + 1].y & 0xffff));
+        s[kb + 1][3] = fmaf(a1[3], 0.25f, bf2f(u[kb + 1].y >> 16));
+        m = fmaxf(m, max8(s[kb], s[kb + 1]));
+    }
+    m = xmax16(m);
+    const float mb = m * kLog2e;
+    v4f o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < kT; kb += 2) {
+        if (!pair_real(real, kb, T)) continue;
+        v8f p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], kLog2e, -mb));
+            p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][r], kLog2e, -mb));
+        }
+        lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        const v8bf vt = *(const v8bf *)(Vth + c * kVt + kb * kTile + 8 * g);
+        o = mfma32bf(vt, __builtin_convertvector(p, v8bf), o);
+    }
+    const float inv = 1.0f / xsum16(lsum);
+    *(uint2 *)orow =
+        rq ? make_uint2((uint32_t)f2bf(o[0] * inv) | ((uint32_t)f2bf(o[1] * inv) << 16),
+                        (uint32_t)f2bf(o[2] * inv) | ((uint32_t)f2bf(o[3] * inv) << 16))
+           : make_uint2(0u, 0u);
+}
+
+// ------------------------------------------------------------ kernel
+template <bool kBf16, int kT, int kQ>
+__global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
+    const AttnElt<kBf16> *__restrict__ Q, const AttnElt<kBf16> *__restrict__ K,
+    const AttnElt<kBf16> *__restrict__ V, const AttnElt<kBf16> *__restrict__ U,
+    const uint8_t *__restrict__ mask, int H, int P, int chunks, AttnElt<kBf16> *__restrict__ O) {
+    using E = AttnElt<kBf16>;
+    constexpr int kWaves = kAttnQBlocks / kQ, kThreads = 64 * kWaves;
+    constexpr int kWords = (kT * 16 + 63) / 64;
+    constexpr int kVt = vt_stride(kT);
+    // fp32: K rows as 32 fp16 [hi d0..15 | lo d0..15], V^T hi and lo;
+    // bf16: K rows of 16 bf16 and V^T.  V^T rows use the vt_pos order.
+    constexpr int kKRow = kBf16 ? 16 : 32;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[kT * 16 * kKRow];
+    __shared__ __attribute__((aligned(16))) uint16_t Vth[16 * kVt];
+    __shared__ __attribute__((aligned(16))) uint16_t Vtl[kBf16 ? 1 : 16 * kVt];
+    __shared__ int badw[kWaves];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int chunk = blockIdx.x % chunks, bh = blockIdx.x / chunks, jet = bh / H;
+    const int T = P / kTile;
+    const size_t base = (size_t)bh * P;
+    const E *Qh = Q + base * 16, *Kh = K + base * 16, *Vh = V + base * 16;
+
+    // ---- 1. K and V rows this thread stages, issued before the mask is known
+    // (blocks below an even block count; the mask only decides what is kept),
+    // then the mask, then the U strips and Q rows of this wave's query blocks.
+    // The wait counter drains in issue order, so the barrier waits for K and V
+    // alone.  Nothing else loaded here is looked at before the barrier.
+    constexpr int kItems = (kT * 16 * 4 + kThreads - 1) / kThreads;
+    using KVec = typename std::conditional<kBf16, uint2, float4>::type;
+    const int nst = 16 * (T + (T & 1));
+    KVec kk[kItems], vv[kItems];
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        const int i = tid + it * kThreads, k = i >> 2, d0 = (i & 3) * 4;
+        const size_t off = (i < nst * 4 && k < P) ? (size_t)k * 16 + d0 : 0;
+        kk[it] = *(const KVec *)(Kh + off);
+        vv[it] = *(const KVec *)(Vh + off);
+    }
+
+    SlotBits<kWords> real;
+    real.load(mask + (size_t)jet * P, P);
+
+    using UVec = typename std::conditional<kBf16, uint2, float4>::type;
+    UVec u[kQ][kT];
+    float4 qa[kQ], qc[kQ];  // fp32: Q[q0 + c][8(g & 1) .. + 7]
+    v4s qb16[kQ];           // bf16: Q[q0 + c][4g .. 4g + 3]
+    // a zero the compiler cannot see (P <= 256): the unneeded strip loads
+    // read the row start, and must not be merged with the load of block 0
+    const int zero = P >> 16;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+        const int qb = chunk * kAttnQBlocks + wave + j * kWaves;
+        const bool act = qb < T && real.block_rt(qb) != 0;
+        const int qr = act ? qb * kTile + c : 0;  // query row read
+        const E *urow = U + (base + qr) * P + 4 * g;
+#pragma unroll
+        for (int kb = 0; kb < kT; ++kb) {
+            const bool need = act && kb < T && real.block(kb);
+            u[j][kb] = *(const UVec *)(urow + (need ? kb : kb * zero) * kTile);
+        }
+        if constexpr (kBf16) {
+            qb16[j] = *(const v4s *)(Qh + (size_t)qr * 16 + 4 * g);
+        } else {
+            const float4 *qp = (const float4 *)(Qh + (size_t)qr * 16 + 8 * (g & 1));
+            qa[j] = qp[0];
+            qc[j] = qp[1];
+        }
+    }
+
+    // ---- 2. K and V^T into LDS
+    bool bad = false;  // a real K or V value outside the fp16-safe range
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        const int i = tid + it * kThreads, k = i >> 2, d0 = (i & 3) * 4;
+        if (i >= nst * 4) continue;
+        const bool rb = k < P && real.block_rt(k >> 4);
+        const bool rk = rb && real.slot(k);
+        const int kp = vt_pos(k);
+        if constexpr (kBf16) {
+            const uint2 kz = rk ? kk[it] : make_uint2(0u, 0u);
+            const uint2 vz = rk ? vv[it] : make_uint2(0u, 0u);
+            *(uint2 *)(Ks + k * 16 + d0) = kz;
+            Vth[(d0 + 0) * kVt + kp] = (uint16_t)(vz.x & 0xffff);
+            Vth[(d0 + 1) * kVt + kp] = (uint16_t)(vz.x >> 16);
+            Vth[(d0 + 2) * kVt + kp] = (uint16_t)(vz.y & 0xffff);
+            Vth[(d0 + 3) * kVt + kp] = (uint16_t)(vz.y >> 16);
+        } else {
+            const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 kz = rk ? kk[it] : zero, vz = rk ? vv[it] : zero;
+            bad |= !(f16_safe(kz) && f16_safe(vz));
+            v4h kh, kl, vh, vl;
+            split4_f16(kz, kh, kl);
+            split4_f16(vz, vh, vl);
+            *(v4h *)(Ks + k * 32 + d0) = kh;
+            *(v4h *)(Ks + k * 32 + 16 + d0) = kl;
+            // bit-cast whole vectors: clang mis-lowers a bit_cast of one
+            // vector element (it reads element 0)
+            const v4s vhb = __builtin_bit_cast(v4s, vh), vlb = __builtin_bit_cast(v4s, vl);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                Vth[(d0 + jj) * kVt + kp] = (uint16_t)vhb[jj];
+                Vtl[(d0 + jj) * kVt + kp] = (uint16_t)vlb[jj];
+            }
+        }
+    }
+    // one flag word per wave; __syncthreads() (not a workgroup-reduction
+    // primitive) is what orders the LDS stores above before the reads below
+    if (lane == 0) badw[wave] = __any(bad);
+    __syncthreads();
+    bool kvbad = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) kvbad |= badw[w] != 0;
+
+    // ---- 3. per query block
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+        const int qb = chunk * kAttnQBlocks + wave + j * kWaves;
+        const int q0 = qb * kTile;
+        if (qb >= T) continue;
+        E *orow = O + (base + q0 + c) * 16 + 4 * g;
+        if (real.block_rt(qb) == 0) {
+            if constexpr (kBf16) *(uint2 *)orow = make_uint2(0u, 0u);
+            else *(float4 *)orow = make_float4(0.f, 0.f, 0.f, 0.f);
+            continue;
+        }
+        // U of key blocks without a real key -> -inf, Q rows of padded
+        // queries -> 0 (only now: a select on a loaded value before the
+        // barrier would wait for every load)
+#pragma unroll
+        for (int kb = 0; kb < kT; ++kb) {
+            if (kb < T && real.block(kb)) continue;
+            if constexpr (kBf16) u[j][kb] = make_uint2(kBf16NegInf, kBf16NegInf);
+            else u[j][kb] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
+        const bool rq = real.slot(q0 + c);
+        if constexpr (kBf16) {
+            attend_bf16<kT>(u[j], rq ? qb16[j] : (v4s){0, 0, 0, 0}, rq, real, T, Ks, Vth, orow);
+        } else {
+            const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+            attend_f32<kT>(u[j], rq ? qa[j] : zero, rq ? qc[j] : zero, rq, kvbad, real, T, Ks,
+                           Vth, Vtl, Qh, Kh, Vh, U + (base + q0 + c) * P + 4 * g, q0, orow);
+        }
+    }
+}
+
+int attention_chunks(int P) { return (P / kTile + kAttnQBlocks - 1) / kAttnQBlocks; }
+
+template <bool kBf16>
+static hipError_t launch_attention(const AttnElt<kBf16> *Q, const AttnElt<kBf16> *K,
+                                   const AttnElt<kBf16> *V, const AttnElt<kBf16> *U,
+                                   const uint8_t *mask, int B, int H, int P,
+                                   AttnElt<kBf16> *O, hipStream_t s) {
+    const int chunks = attention_chunks(P);
+    const dim3 grid((unsigned)((size_t)B * H * chunks));
+    if (P <= 128)
+        hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1>), grid, dim3(64 * kAttnQBlocks), 0,
+                           s, Q, K, V, U, mask, H, P, chunks, O);
+    else
+        hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1>), grid, dim3(64 * kAttnQBlocks), 0, s,
+                           Q, K, V, U, mask, H, P, chunks, O);
+    return hipGetLastError();
 }
 
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V,
                                 const float *U, const uint8_t *mask, int B, int H, int P,
                                 float *O, hipStream_t s) {
-    hipLaunchKernelGGL(attention_f32_kernel, dim3(B * H), dim3(256), 0, s, Q, K, V, U, mask, H,
-                       P, O);
-    return hipGetLastError();
+    return launch_attention<false>(Q, K, V, U, mask, B, H, P, O, s);
 }
 
 hipError_t launch_attention_bf16(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                  const uint16_t *U, const uint8_t *mask, int B, int H, int P,
                                  uint16_t *O, hipStream_t s) {
-    hipLaunchKernelGGL(attention_bf16_kernel, dim3(B * H), dim3(256), 0, s, Q, K, V, U, mask,
-                       H, P, O);
-    return hipGetLastError();
+    return launch_attention<true>(Q, K, V, U, mask, B, H, P, O, s);
 }
 
 }  // namespace pip

@@ -16,13 +16,25 @@ namespace pip {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kQkScale2 = 1.4426950408889634f * 0.25f;  // log2(e) / sqrt(16)
 
+// Reductions over the four lanes l, l^16, l^32, l^48 with the gfx950 row
+// swaps: v_permlane16_swap of x with itself gives {x[l], x[l^16]} (in some
+// order) and v_permlane32_swap {x[l], x[l^32]}; no LDS round trip.  Both
+// lanes of a pair add the same two operands in the same order.
 __device__ __forceinline__ float xmax16(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float xsum16(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned v = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Online-softmax update of one key block for the lane's query: s[r] are the

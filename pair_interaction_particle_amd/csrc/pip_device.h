@@ -22,6 +22,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v8f __attribute__((ext_vector_type(8)));
 
 constexpr int kHid = 64;
 constexpr int kHeads = 8;
@@ -36,6 +41,24 @@ constexpr double kRapFloor = 1e-300;
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma32bf(v8bf a, v8bf b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma32h(v8h a, v8h b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// x = hi + lo with hi = fp16(x), lo = fp16(x - hi), both rounded to nearest:
+// 22 significand bits, |x - hi - lo| <= 2^-22 |x| while x and x - hi stay in
+// the normal fp16 range (|x| <= 65504; below 2^-14 the error is absolute,
+// at most 2^-25).
+__device__ __forceinline__ void split4_f16(float4 x, v4h &hi, v4h &lo) {
+    const v4f v = {x.x, x.y, x.z, x.w};
+    hi = __builtin_convertvector(v, v4h);
+    lo = __builtin_convertvector(v - __builtin_convertvector(hi, v4f), v4h);
 }
 
 // ------------------------------------------------------------ kinematics

@@ -33,6 +33,8 @@ hipError_t launch_pair_embed_f32(const float *p4, const uint8_t *mask, int B, in
                                  const pip_pair_mlp *m, float *U, hipStream_t s);
 hipError_t launch_pair_embed_bf16(const float *p4, const uint8_t *mask, int B, int P,
                                   const pip_pair_mlp *m, uint16_t *U, hipStream_t s);
+// workgroups per (jet, head) of the attention kernel
+int attention_chunks(int P);
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V,
                                 const float *U, const uint8_t *mask, int B, int H, int P,
                                 float *O, hipStream_t s);

@@ -155,9 +155,6 @@ __device__ __forceinline__ void mlp2_f32(const float4 *__restrict__ wl,
 }
 
 // ------------------------------------------------------------ bf16 chain
-__device__ __forceinline__ v4f mfma32bf(v8bf a, v8bf b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // bf16 B operand for K = 32: slots 0..3 from channel block lo, 4..7 from hi.
 __device__ __forceinline__ v8bf pack_bf16(v4f lo, v4f hi) {
@@ -240,14 +237,6 @@ __device__ __forceinline__ void mlp2_bf16(const float4 *__restrict__ wl,
 // the host, the activations after every GELU.  An activation beyond the fp16
 // range turns into inf and so into a non-finite U, which the caller detects
 // and recomputes with the exact float32 chain.
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ v4f mfma32h(v8h a, v8h b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
 // hi / lo fp16 B operands for K = 32 (slots 0..3 from channel block `lo_blk`,
 // 4..7 from `hi_blk`, as in pack_bf16).
 __device__ __forceinline__ void split_f16(v4f b0, v4f b1, v8h &hi, v8h &lo) {

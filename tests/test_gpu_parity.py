@@ -202,6 +202,25 @@ def test_attention_bf16_large_workload():
     assert_zero_bits(O.transpose(0, 2, 1, 3), d["mask"] == 0, "O bf16 padded rows")
 
 
+def test_attention_f32_values_beyond_fp16_range():
+    # jet 0: K x 1e5 and Q x 1e-5 (scores unchanged); jet 1: V x 1e5; jet 2:
+    # Q x 1e5 and K x 1e-5.  Each puts a real Q, K or V value beyond the fp16
+    # range, so those query blocks take the float32 path.
+    B, H, P = 3, 2, 48
+    _, mask = ragged_jets(B, P, (48, 30, 17), seed=31)
+    q, k, v = rand_qkv(B, H, P, mask, seed=31)
+    k[0] *= 1e5
+    q[0] *= 1e-5
+    v[1] *= 1e5
+    q[2] *= 1e5
+    k[2] *= 1e-5
+    u = np.random.default_rng(32).normal(0, 1.5, size=(B, H, P, P)).astype(np.float32)
+    O = host(pip.pair_bias_attention(g(q), g(k), g(v), g(u), g(mask)))
+    ref = oracle.attention(q, k, v, u, mask)
+    assert_close(O, ref, TOL32, "O f32 with values beyond fp16")
+    assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "O padded rows")
+
+
 def test_attention_ignores_padding_values_and_empty_jets():
     B, H, P = 3, 8, 32
     _, mask = ragged_jets(B, P, (20, 0, 9), seed=5)
