@@ -183,7 +183,7 @@ def bench_extra(pip, synth, reps, warmup):
     x0 = to_dev(d["x0"])
     X = x0.clone()
     w = [to_dev(d[x]) for x in ("wq", "wk", "wv", "wo")]
-    ws = torch.empty(pip.block_stack_workspace_bytes(B, P, 128) // 4, device="cuda")
+    ws = torch.empty(pip.block_stack_workspace_bytes(B, P, 128, 8) // 4, device="cuda")
     try:
         # X is updated in place; re-applying the stack to the running X does
         # the same work every time (the path has no data-dependent work).

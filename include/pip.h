@@ -153,8 +153,11 @@ pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
                                     const void *V, int64_t B, int64_t P, int64_t D, void *O,
                                     int dtype, void *stream);
 
-/* Bytes of device workspace pip_block_stack needs (B * P * C floats). */
-size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C);
+/* Bytes of device workspace pip_block_stack needs for L layers: the attention
+ * output of a layer (B * P * C floats) plus every layer's weights packed as
+ * split fp16 matrix-core operands (L * 4 * C^2 * 2 * 2 bytes for C a multiple
+ * of 32) and their column scales.  0 for sizes the stack does not take. */
+size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C, int64_t L);
 
 /* L attention layers reusing one bias U (the ParT encoder's attention
  * sublayer with embed C and H heads, "Architecture Comparison"), float32:
@@ -164,7 +167,11 @@ size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C);
  *   X <- X + O Wo[l]
  * X (B, P, C) is updated in place; Wq, Wk, Wv, Wo are (L, C, C) applied as
  * X @ W.  Padded rows of X are left unchanged (their O is 0).  workspace
- * must hold pip_block_stack_workspace_bytes(B, P, C) bytes.
+ * must hold pip_block_stack_workspace_bytes(B, P, C, L) bytes; its contents
+ * are scratch (overwritten by every call; calls that share a workspace on
+ * different streams race).  The products run on the fp16 matrix cores with
+ * split operands (hi + lo per float32 value, each row and weight column
+ * scaled by an exact power of two first), float32-faithful to ~1e-6.
  * Requires C == 16 * H, 1 <= H <= 16, P % 16 == 0, 16 <= P <= 256.
  * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, HIP. */
 pip_status pip_block_stack(float *X, const float *Wq, const float *Wk, const float *Wv,

@@ -72,7 +72,7 @@ def lib():
         L.pip_pair_embed.argtypes = [vp, vp, i64, i64, vp, vp, i, vp]
         L.pip_pair_bias_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i, vp]
         L.pip_pair_embed_attention.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i, vp]
-        L.pip_block_stack_workspace_bytes.argtypes = [i64, i64, i64]
+        L.pip_block_stack_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.pip_block_stack_workspace_bytes.restype = C.c_size_t
         L.pip_block_stack.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
                                       C.c_size_t, vp]
@@ -246,8 +246,8 @@ def pair_embed_attention(p4, mask, mlp: PairMLP, q, k, v, out=None):
     return out
 
 
-def block_stack_workspace_bytes(B, P, C_):
-    return int(lib().pip_block_stack_workspace_bytes(B, P, C_))
+def block_stack_workspace_bytes(B, P, C_, L_):
+    return int(lib().pip_block_stack_workspace_bytes(B, P, C_, L_))
 
 
 def block_stack(x, wq, wk, wv, wo, u, mask, workspace=None):
@@ -256,7 +256,7 @@ def block_stack(x, wq, wk, wv, wo, u, mask, workspace=None):
     B, P, Cw = x.shape
     L = wq.shape[0]
     H = u.shape[1]
-    nbytes = block_stack_workspace_bytes(B, P, Cw)
+    nbytes = block_stack_workspace_bytes(B, P, Cw, L)
     if workspace is None:
         workspace = torch.empty(max(nbytes // 4, 1), device=x.device, dtype=torch.float32)
     st = lib().pip_block_stack(

@@ -305,9 +305,11 @@ pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
         (const uint16_t *)V, (uint16_t *)O, s));
 }
 
-size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C) {
-    if (B <= 0 || P <= 0 || C <= 0) return 0;
-    return (size_t)B * (size_t)P * (size_t)C * sizeof(float);
+size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C, int64_t L) {
+    if (B <= 0 || P <= 0 || C <= 0 || L <= 0) return 0;
+    if (check_pair_grid(B, P) != PIP_OK || C % 16 != 0 || C > 16 * 16 || L > (1 << 20))
+        return 0;
+    return pip::block_stack_workspace((int)B, (int)P, (int)C, (int)L);
 }
 
 pip_status pip_block_stack(float *X, const float *Wq, const float *Wk, const float *Wv,
@@ -322,12 +324,13 @@ pip_status pip_block_stack(float *X, const float *Wq, const float *Wk, const flo
     if (H == 0 || C != (int64_t)PIP_HEAD_DIM * H) return PIP_ERR_SHAPE;
     if (H > 16) return PIP_ERR_UNSUPPORTED;
     if (!workspace) return PIP_ERR_NULL;
-    if (workspace_bytes < pip_block_stack_workspace_bytes(B, P, C)) return PIP_ERR_SHAPE;
+    if (L > (1 << 20)) return PIP_ERR_UNSUPPORTED;
+    if (workspace_bytes < pip_block_stack_workspace_bytes(B, P, C, L)) return PIP_ERR_SHAPE;
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
         !aligned16(Wo) || !aligned16(U) || !aligned16(workspace))
         return PIP_ERR_ALIGN;
     return hip_status(pip::launch_block_stack(X, Wq, Wk, Wv, Wo, U, mask, (int)B, (int)P,
-                                              (int)C, (int)H, (int)L, (float *)workspace,
+                                              (int)C, (int)H, (int)L, workspace,
                                               (hipStream_t)stream));
 }
 

@@ -36,77 +36,12 @@
 // error about 2^-22).  K and V are split once when staged.  When a real Q, K
 // or V value is beyond the fp16 range (or not finite) the query block takes a
 // float32 MFMA path instead.  bfloat16 inputs use the bf16 matrix cores.
-#include "pip_attn.h"
+#include "pip_attn_core.h"
 #include "pip_internal.h"
 
 namespace pip {
 
 constexpr int kAttnQBlocks = 8;  // query blocks per workgroup
-constexpr float kF16Safe = 65504.0f;
-constexpr uint32_t kBf16NegInf = 0xff80ff80u;  // two bf16 -inf
-
-template <bool kBf16>
-using AttnElt = typename std::conditional<kBf16, uint16_t, float>::type;
-
-// Real-slot bits of one jet: bit k of word k/64, the same in every lane.
-template <int kWords>
-struct SlotBits {
-    uint64_t w[kWords];
-
-    // every byte load is issued (address clamped into the row) before the
-    // first ballot, so the loads overlap
-    __device__ __forceinline__ void load(const uint8_t *__restrict__ mrow, int P) {
-        const int lane = threadIdx.x & 63;
-        uint8_t b[kWords];
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) b[i] = mrow[min(64 * i + lane, P - 1)];
-#pragma unroll
-        for (int i = 0; i < kWords; ++i) w[i] = __ballot(64 * i + lane < P && b[i] != 0);
-    }
-    // word i for a run-time i (selects, no indexed register access)
-    __device__ __forceinline__ uint64_t word(int i) const {
-        uint64_t r = w[0];
-#pragma unroll
-        for (int j = 1; j < kWords; ++j) r = i == j ? w[j] : r;
-        return r;
-    }
-    // the 16 bits of block kb (compile-time kb)
-    __device__ __forceinline__ uint32_t block(int kb) const {
-        return (uint32_t)(w[kb >> 2] >> (16 * (kb & 3))) & 0xffffu;
-    }
-    __device__ __forceinline__ uint32_t block_rt(int kb) const {
-        return (uint32_t)(word(kb >> 2) >> (16 * (kb & 3))) & 0xffffu;
-    }
-    __device__ __forceinline__ bool slot(int k) const { return (word(k >> 6) >> (k & 63)) & 1; }
-};
-
-// LDS row stride (elements) of V^T: the key range plus a pad that spreads the
-// 16 rows over the banks.
-constexpr int vt_stride(int kT) { return kT * 16 + 8; }
-
-// Position of key k inside a V^T row: keys are grouped by pairs of key
-// blocks so that lane group g finds keys 4g..4g+3 of both blocks of a pair
-// in 8 consecutive entries (one 16-byte LDS read per operand).
-__device__ __forceinline__ int vt_pos(int k) {
-    return (k & ~31) + ((k >> 2) & 3) * 8 + ((k >> 4) & 1) * 4 + (k & 3);
-}
-
-__device__ __forceinline__ bool f16_safe(float4 x) {
-    return fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))) <= kF16Safe &&
-           x.x == x.x && x.y == x.y && x.z == x.z && x.w == x.w;
-}
-
-__device__ __forceinline__ float max8(const float (&a)[4], const float (&b)[4]) {
-    return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
-                 fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
-}
-
-// Is either block of the pair (kb, kb + 1) a block with a real key?
-template <int kWords>
-__device__ __forceinline__ bool pair_real(const SlotBits<kWords> &real, int kb, int T) {
-    return (kb < T && real.block(kb)) || (kb + 1 < T && real.block(kb + 1));
-}
-
 // ------------------------------------------------------------ float32
 // One query block (rows q0 .. q0+15) of a float32 head.  u is the U strip
 // (-inf for key blocks without a real key), qa / qc are this lane's Q row
@@ -120,23 +55,10 @@ __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc
                                            const float *__restrict__ Vh,
                                            const float *__restrict__ urow, int q0,
                                            float *__restrict__ orow) {
-    constexpr int kVt = vt_stride(kT);
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     float m = -INFINITY, lsum = 0.f;
     v4f o = {0.f, 0.f, 0.f, 0.f};
     if (!(kvbad || __any(rq && !(f16_safe(qa) && f16_safe(qc))))) {
-        // U of padded keys -> -inf, so that every score is an FMA result
-#pragma unroll
-        for (int kb = 0; kb < kT; ++kb) {
-            const uint32_t bits = real.block(kb);
-            if (kb < T && bits != 0 && bits != 0xffffu) {
-                const uint32_t kbits = bits >> (4 * g);
-                u[kb].x = (kbits & 1) ? u[kb].x : -INFINITY;
-                u[kb].y = (kbits & 2) ? u[kb].y : -INFINITY;
-                u[kb].z = (kbits & 4) ? u[kb].z : -INFINITY;
-                u[kb].w = (kbits & 8) ? u[kb].w : -INFINITY;
-            }
-        }
         v8h qh, ql;
         {
             v4h h0, l0, h1, l1;
@@ -145,55 +67,7 @@ __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc
             qh = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
             ql = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        // scores over pairs of key blocks; a block without a real key has
-        // zero K rows in LDS and U = -inf, so its scores are -inf
-        float s[kT][4];
-#pragma unroll
-        for (int kb = 0; kb < kT; kb += 2) {
-            if (!pair_real(real, kb, T)) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) s[kb][r] = s[kb + 1][r] = -INFINITY;
-                continue;
-            }
-            // lane group g holds reduction entries [hi | lo][8(g & 1) .. + 7]
-            const v8h ka0 = *(const v8h *)(Ks + (kb * kTile + c) * 32 + 8 * g);
-            const v8h ka1 = *(const v8h *)(Ks + ((kb + 1) * kTile + c) * 32 + 8 * g);
-            v4f a0 = mfma32h(ka0, qh, (v4f){0.f, 0.f, 0.f, 0.f});
-            v4f a1 = mfma32h(ka1, qh, (v4f){0.f, 0.f, 0.f, 0.f});
-            a0 = mfma32h(ka0, ql, a0);
-            a1 = mfma32h(ka1, ql, a1);
-            s[kb][0] = fmaf(a0[0], 0.25f, u[kb].x);
-            s[kb][1] = fmaf(a0[1], 0.25f, u[kb].y);
-            s[kb][2] = fmaf(a0[2], 0.25f, u[kb].z);
-            s[kb][3] = fmaf(a0[3], 0.25f, u[kb].w);
-            s[kb + 1][0] = fmaf(a1[0], 0.25f, u[kb + 1].x);
-            s[kb + 1][1] = fmaf(a1[1], 0.25f, u[kb + 1].y);
-            s[kb + 1][2] = fmaf(a1[2], 0.25f, u[kb + 1].z);
-            s[kb + 1][3] = fmaf(a1[3], 0.25f, u[kb + 1].w);
-            m = fmaxf(m, max8(s[kb], s[kb + 1]));
-        }
-        m = xmax16(m);
-        const float mb = m * kLog2e;
-        // P V over the same pairs; V rows of blocks without a real key are 0
-#pragma unroll
-        for (int kb = 0; kb < kT; kb += 2) {
-            if (!pair_real(real, kb, T)) continue;
-            v8f p;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], kLog2e, -mb));
-                p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][r], kLog2e, -mb));
-            }
-            lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            const int off = c * kVt + kb * kTile + 8 * g;
-            const v8h vh = *(const v8h *)(Vth + off);
-            const v8h vl = *(const v8h *)(Vtl + off);
-            const v8h ph = __builtin_convertvector(p, v8h);
-            const v8h pl = __builtin_convertvector(p - __builtin_convertvector(ph, v8f), v8h);
-            o = mfma32h(vh, pl, o);
-            o = mfma32h(vl, ph, o);
-            o = mfma32h(vh, ph, o);
-        }
+        attend_split<kT>(u, qh, ql, 0.25f, real, T, Ks, Vth, Vtl, o, lsum);
     } else {
         // A real Q, K or V value beyond the fp16 range: float32 MFMA with an
         // online softmax, everything re-read from global memory (rare path).
@@ -233,8 +107,9 @@ __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc
                 o = mfma4(vv, p, o);
             }
         }
+        lsum = xsum16(lsum);
     }
-    const float inv = 1.0f / xsum16(lsum);
+    const float inv = 1.0f / lsum;
     *(float4 *)orow = rq ? make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
 }

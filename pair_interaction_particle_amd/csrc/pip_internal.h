@@ -48,7 +48,9 @@ hipError_t launch_embed_attention_bf16(const float *p4, const uint8_t *mask, int
                                        const pip_pair_mlp *m, const uint16_t *Q,
                                        const uint16_t *K, const uint16_t *V, uint16_t *O,
                                        hipStream_t s);
+// bytes of workspace the block stack needs
+size_t block_stack_workspace(int B, int P, int C, int L);
 hipError_t launch_block_stack(float *X, const float *Wq, const float *Wk, const float *Wv,
                               const float *Wo, const float *U, const uint8_t *mask, int B,
-                              int P, int C, int H, int L, float *ws, hipStream_t s);
+                              int P, int C, int H, int L, void *ws, hipStream_t s);
 }  // namespace pip

@@ -81,8 +81,13 @@ def test_attention_validation(L):
 
 def test_block_stack_validation(L):
     f = L.pip_block_stack
-    ws = L.pip_block_stack_workspace_bytes(2, 16, 128)
-    assert ws == 2 * 16 * 128 * 4
+    ws = L.pip_block_stack_workspace_bytes(2, 16, 128, 1)
+    # O (B*P*C floats) + split fp16 hi/lo operands of the four (C, C) weights
+    # + 4 C column scales, each section 256-byte aligned
+    assert ws == 2 * 16 * 128 * 4 + 2 * (4 * 128 * 128 * 2) + 4 * 128 * 4
+    assert L.pip_block_stack_workspace_bytes(2, 16, 128, 8) > ws
+    assert L.pip_block_stack_workspace_bytes(2, 16, 100, 1) == 0
+    assert L.pip_block_stack_workspace_bytes(2, 16, 128, 0) == 0
     w = [A16] * 7
     assert f(*w, 2, 16, 128, 8, 1, None, ws, None) == NULL
     assert f(*w, 2, 16, 128, 8, 1, A16, ws - 4, None) == SHAPE
