@@ -124,3 +124,18 @@ def test_block_stack_ragged_padded_rows_untouched(B, P, C, L, ns):
     real = mask != 0
     assert_close(got[real], ref[real], TOL32, "block stack X C=%d" % C)
     np.testing.assert_array_equal(got[~real].view(np.uint32), x0[~real].view(np.uint32))
+
+
+def test_fused_many_jets_unsorted_path():
+    # more jets than the in-kernel ranking takes: workgroups take jets in index order
+    B, P = 2100, 16
+    rng = np.random.default_rng(70)
+    ns = tuple(int(x) for x in rng.integers(0, 17, size=B))
+    p4, mask = ragged_jets(B, P, ns, seed=70, hole=False)
+    params = mlp_for(70)
+    q, k, v = rand_qkv(B, 8, P, mask, seed=70)
+    mlp = pip.PairMLP(params)
+    O = host(pip.pair_embed_attention(g(p4), g(mask), mlp, g(q), g(k), g(v)))
+    ref = oracle.pair_embed_attention(p4, mask, params, q, k, v)
+    assert_close(O, ref, TOL32, "fused O B=2100")
+    assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "fused O padded rows")

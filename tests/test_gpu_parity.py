@@ -1,8 +1,15 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle on
 the same seeded inputs, element by element.
 
-Bars: float32 |err| <= 1e-4 (1 + |ref|); bfloat16 |err| <= 2e-2 (1 + |ref|);
-every output that involves a padded slot is +0.0 bit for bit.  The oracle's
+Bars: float32 |err| <= 1e-4 (1 + |ref|); bfloat16 attention outputs
+|err| <= 2e-2 (1 + |ref|); bfloat16 U |err| <= 3e-2 (1 + |ref|); every output
+that involves a padded slot is +0.0 bit for bit.
+
+The bf16 U bar follows from the bf16 arithmetic itself: layers 2-4 take bf16
+operands (unit roundoff 2^-9), and on the diagonal pairs three of the four
+features sit at the ln(eps) clamp (-18.4), which drives large first-layer
+activations.  Emulating exactly those roundings in float64 on a full P = 256
+jet reaches 2.4e-2 (1 + |ref|) on diagonal pairs (below 0.9e-2 elsewhere).  The oracle's
 inputs are always the synthetic inputs themselves (bf16 workloads: the
 bf16-rounded values), never anything the GPU produced.
 """
@@ -18,7 +25,7 @@ from pair_interaction_particle_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-TOL32, TOLBF = 1e-4, 2e-2
+TOL32, TOLBF, TOLBF_U = 1e-4, 2e-2, 3e-2
 
 
 def dev():
@@ -115,7 +122,7 @@ def test_pair_embed_bf16_large_workload():
     mlp = pip.PairMLP(d["mlp"])
     U = host(pip.pair_embed(g(d["p4"]), g(d["mask"]), mlp, dtype="bf16"))
     ref = oracle.pair_embed(d["p4"], d["mask"], d["mlp"])
-    assert_close(U, ref, TOLBF, "U bf16 (B=64, P=256)")
+    assert_close(U, ref, TOLBF_U, "U bf16 (B=64, P=256)")
     assert_zero_bits(U.transpose(0, 2, 3, 1), ~pair_mask(d["mask"]), "U bf16 padding")
 
 
@@ -253,3 +260,42 @@ def test_empty_batch_is_a_noop():
     mask = torch.zeros((0, 16), device=dev(), dtype=torch.uint8)
     U = pip.pair_embed(p4, mask, mlp)
     assert U.shape == (0, 8, 16, 16)
+
+
+# ---------------------------------------------------------------- edge shapes
+@pytest.mark.parametrize("H", [1, 5, 16])
+def test_attention_f32_head_counts(H):
+    B, P = 3, 32
+    _, mask = ragged_jets(B, P, (32, 17, 3), seed=40 + H)
+    q, k, v = rand_qkv(B, H, P, mask, seed=40 + H)
+    u = np.random.default_rng(41 + H).normal(0, 1, size=(B, H, P, P)).astype(np.float32)
+    O = host(pip.pair_bias_attention(g(q), g(k), g(v), g(u), g(mask)))
+    ref = oracle.attention(q, k, v, u, mask)
+    assert_close(O, ref, TOL32, "O f32 H=%d" % H)
+    assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "O padded rows")
+
+
+@pytest.mark.parametrize("B,P,ns", [(3, 48, (48, 20, 1)), (1, 256, (256,)), (2, 144, (144, 0))])
+def test_pair_embed_bf16_ragged(B, P, ns):
+    p4, mask = ragged_jets(B, P, ns, seed=50 + P)
+    params = mlp_for(50 + P, biases=True)
+    mlp = pip.PairMLP(params)
+    U = host(pip.pair_embed(g(p4), g(mask), mlp, dtype="bf16"))
+    ref = oracle.pair_embed(p4, mask, params)
+    assert_close(U, ref, TOLBF_U, "U bf16 P=%d" % P)
+    assert_zero_bits(U.transpose(0, 2, 3, 1), ~pair_mask(mask), "U bf16 padding")
+
+
+def test_single_full_jet_at_max_p_every_entry():
+    B, P = 1, 256
+    p4, mask = ragged_jets(B, P, (256,), seed=60, hole=False)
+    params = mlp_for(60)
+    mlp = pip.PairMLP(params)
+    q, k, v = rand_qkv(B, 8, P, mask, seed=60)
+    U = host(pip.pair_embed(g(p4), g(mask), mlp))
+    assert_close(U, oracle.pair_embed(p4, mask, params), TOL32, "U P=256")
+    O = host(pip.pair_bias_attention(g(q), g(k), g(v), g(U), g(mask)))
+    ref = oracle.pair_embed_attention(p4, mask, params, q, k, v)
+    assert_close(O, ref, TOL32, "O P=256")
+    O2 = host(pip.pair_embed_attention(g(p4), g(mask), mlp, g(q), g(k), g(v)))
+    assert_close(O2, ref, TOL32, "fused O P=256")
