@@ -76,14 +76,14 @@ hipError_t launch_pair_features(const float *p4, const uint8_t *mask, int B, int
 }
 
 // ------------------------------------------------------------ U stores
-__device__ __forceinline__ void store4(float *U, size_t off, const float (&v)[4]) {
+__device__ __forceinline__ void store4(float *U, uint32_t off, const float (&v)[4]) {
     *(float4 *)(U + off) = make_float4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
-__device__ __forceinline__ void store4(uint16_t *U, size_t off, const float (&v)[4]) {
+__device__ __forceinline__ void store4(uint16_t *U, uint32_t off, const float (&v)[4]) {
     *(uint2 *)(U + off) = make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
 }
 
@@ -97,8 +97,8 @@ __device__ inline void zero_tile(OutT *U, int P, int I, int J) {
     const int tid = threadIdx.x;
     const float z[4] = {0.f, 0.f, 0.f, 0.f};
     const int h = tid >> 6, i = (tid >> 2) & 15, j0 = (tid & 3) * 4;
-    store4(U, ((size_t)h * P + I * kTile + i) * P + J * kTile + j0, z);
-    if (I != J) store4(U, ((size_t)h * P + J * kTile + i) * P + I * kTile + j0, z);
+    store4(U, ((uint32_t)h * P + I * kTile + i) * P + J * kTile + j0, z);
+    if (I != J) store4(U, ((uint32_t)h * P + J * kTile + i) * P + I * kTile + j0, z);
 }
 
 // Pair (i, j) (tile-local) that lane `lane` of pair block k computes.
@@ -177,8 +177,10 @@ __device__ __forceinline__ int active_tiles(uint32_t act) {
     return a * (a + 1) / 2;
 }
 
-__device__ __forceinline__ void store_u(float *U, size_t off, float v) { U[off] = v; }
-__device__ __forceinline__ void store_u(uint16_t *U, size_t off, float v) {
+// Offsets inside one jet's U block (8 P^2 <= 2^19 elements) are 32-bit, so
+// the stores take the jet base from scalar registers plus a 32-bit lane offset.
+__device__ __forceinline__ void store_u(float *U, uint32_t off, float v) { U[off] = v; }
+__device__ __forceinline__ void store_u(uint16_t *U, uint32_t off, float v) {
     U[off] = __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
@@ -193,20 +195,21 @@ __device__ __forceinline__ void write_block(const PL &L, OutT *U, int P, int I, 
     if (lane >= 32 || !valid) return;
     const int a = I * kTile + i, b = J * kTile + j;
     const bool real = !zero && L.real[a] && L.real[b];
-    const int h0 = (lane >> 4) * 4;
+    const uint32_t pp = (uint32_t)P * P;
+    const uint32_t h0 = (lane >> 4) * 4 * pp;
+    const uint32_t oab = h0 + (uint32_t)a * P + b, oba = h0 + (uint32_t)b * P + a;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const float v = real ? u[q] : 0.0f;
-        const size_t hp = (size_t)(h0 + q) * P;
-        store_u(U, (hp + a) * P + b, v);
-        if (a != b) store_u(U, (hp + b) * P + a, v);
+        store_u(U, oab + q * pp, v);
+        if (a != b) store_u(U, oba + q * pp, v);
     }
 }
 
-__device__ __forceinline__ void store_u2(float *U, size_t off, float a, float b) {
+__device__ __forceinline__ void store_u2(float *U, uint32_t off, float a, float b) {
     *(float2 *)(U + off) = make_float2(a, b);
 }
-__device__ __forceinline__ void store_u2(uint16_t *U, size_t off, float a, float b) {
+__device__ __forceinline__ void store_u2(uint16_t *U, uint32_t off, float a, float b) {
     *(uint32_t *)(U + off) = bf16_pair(a, b);
 }
 
@@ -221,14 +224,15 @@ __device__ __forceinline__ void write_row_pair(const PL &L, OutT *U, int P, int 
     if (lane >= 32) return;
     const bool rb = !zero && L.real[b];
     const bool rA = rb && L.real[a0], rB = rb && L.real[a0 + 1];
-    const int h0 = (lane >> 4) * 4;
+    const uint32_t pp = (uint32_t)P * P;
+    const uint32_t h0 = (lane >> 4) * 4 * pp;
+    const uint32_t oab = h0 + (uint32_t)a0 * P + b, oba = h0 + (uint32_t)b * P + a0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const float vA = rA ? uA[q] : 0.0f, vB = rB ? uB[q] : 0.0f;
-        const size_t hp = (size_t)(h0 + q) * P;
-        store_u(U, (hp + a0) * P + b, vA);
-        store_u(U, (hp + a0 + 1) * P + b, vB);
-        store_u2(U, (hp + b) * P + a0, vA, vB);
+        store_u(U, oab + q * pp, vA);
+        store_u(U, oab + q * pp + P, vB);
+        store_u2(U, oba + q * pp, vA, vB);
     }
 }
 
