@@ -126,14 +126,18 @@ __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     // U of padded keys -> -inf (bit patterns), so that every score is an FMA result
 #pragma unroll
-    for (int kb = 0; kb < kT; ++kb) {
-        const uint32_t bits = real.block(kb);
-        if (kb < T && bits != 0 && bits != 0xffffu) {
-            const uint32_t kbits = bits >> (4 * g);
-            const uint32_t k0 = ((kbits & 1) ? 0xffffu : 0u) | ((kbits & 2) ? 0xffff0000u : 0u);
-            const uint32_t k1 = ((kbits & 4) ? 0xffffu : 0u) | ((kbits & 8) ? 0xffff0000u : 0u);
-            u[kb].x = (u[kb].x & k0) | (kBf16NegInf & ~k0);
-            u[kb].y = (u[kb].y & k1) | (kBf16NegInf & ~k1);
+    for (int kb = 0; kb < kT; kb += 2) {
+        const uint32_t bits = real.pair(kb >> 1);
+        if (kb < T && bits != 0 && bits != 0xffffffffu) {
+            const uint32_t lb = bits >> (8 * g);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t kbits = lb >> (4 * t);
+                const uint32_t k0 = ((kbits & 1) ? 0xffffu : 0u) | ((kbits & 2) ? 0xffff0000u : 0u);
+                const uint32_t k1 = ((kbits & 4) ? 0xffffu : 0u) | ((kbits & 8) ? 0xffff0000u : 0u);
+                u[kb + t].x = (u[kb + t].x & k0) | (kBf16NegInf & ~k0);
+                u[kb + t].y = (u[kb + t].y & k1) | (kBf16NegInf & ~k1);
+            }
         }
     }
     float s[kT][4];
@@ -193,7 +197,8 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
     constexpr int kWords = (kT * 16 + 63) / 64;
     constexpr int kVt = vt_stride(kT);
     // fp32: K rows as 32 fp16 [hi d0..15 | lo d0..15], V^T hi and lo;
-    // bf16: K rows of 16 bf16 and V^T.  V^T rows use the vt_pos order.
+    // bf16: K rows of 16 bf16 and V^T.  K rows in key_row order, V^T in plain
+    // key order.
     constexpr int kKRow = kBf16 ? 16 : 32;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kT * 16 * kKRow];
     __shared__ __attribute__((aligned(16))) uint16_t Vth[16 * kVt];
@@ -240,11 +245,22 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
         const int qb = chunk * kAttnQBlocks + wave + j * kWaves;
         const bool act = qb < T && real.block_rt(qb) != 0;
         const int qr = act ? qb * kTile + c : 0;  // query row read
-        const E *urow = U + (base + qr) * P + 4 * g;
+        const E *urow = U + (base + qr) * P;
 #pragma unroll
-        for (int kb = 0; kb < kT; ++kb) {
-            const bool need = act && kb < T && real.block(kb);
-            u[j][kb] = *(const UVec *)(urow + (need ? kb : kb * zero) * kTile);
+        for (int kb = 0; kb < kT; kb += 2) {
+            // lane group g's 8 keys of the pair: one contiguous run
+            // (a pair past an odd block count is half outside the row:
+            // clamped, and those keys are masked)
+            const bool need = act && kb < T && real.pair(kb >> 1) != 0;
+            const int off = min(need ? u_col(kb, g) : u_col(kb, g) * zero, P - 8);
+            if constexpr (kBf16) {
+                const uint4 v = *(const uint4 *)(urow + off);
+                u[j][kb] = make_uint2(v.x, v.y);
+                u[j][kb + 1] = make_uint2(v.z, v.w);
+            } else {
+                u[j][kb] = *(const float4 *)(urow + off);
+                u[j][kb + 1] = *(const float4 *)(urow + off + 4);
+            }
         }
         if constexpr (kBf16) {
             qb16[j] = *(const v4s *)(Qh + (size_t)qr * 16 + 4 * g);
@@ -261,17 +277,16 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
     for (int it = 0; it < kItems; ++it) {
         const int i = tid + it * kThreads, k = i >> 2, d0 = (i & 3) * 4;
         if (i >= nst * 4) continue;
-        const bool rb = k < P && real.block_rt(k >> 4);
-        const bool rk = rb && real.slot(k);
-        const int kp = vt_pos(k);
+        const bool rk = k < P && real.slot(k);
+        const int kr = key_row(k);
         if constexpr (kBf16) {
             const uint2 kz = rk ? kk[it] : make_uint2(0u, 0u);
             const uint2 vz = rk ? vv[it] : make_uint2(0u, 0u);
-            *(uint2 *)(Ks + k * 16 + d0) = kz;
-            Vth[(d0 + 0) * kVt + kp] = (uint16_t)(vz.x & 0xffff);
-            Vth[(d0 + 1) * kVt + kp] = (uint16_t)(vz.x >> 16);
-            Vth[(d0 + 2) * kVt + kp] = (uint16_t)(vz.y & 0xffff);
-            Vth[(d0 + 3) * kVt + kp] = (uint16_t)(vz.y >> 16);
+            *(uint2 *)(Ks + kr * 16 + d0) = kz;
+            Vth[(d0 + 0) * kVt + k] = (uint16_t)(vz.x & 0xffff);
+            Vth[(d0 + 1) * kVt + k] = (uint16_t)(vz.x >> 16);
+            Vth[(d0 + 2) * kVt + k] = (uint16_t)(vz.y & 0xffff);
+            Vth[(d0 + 3) * kVt + k] = (uint16_t)(vz.y >> 16);
         } else {
             const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
             const float4 kz = rk ? kk[it] : zero, vz = rk ? vv[it] : zero;
@@ -279,15 +294,15 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
             v4h kh, kl, vh, vl;
             split4_f16(kz, kh, kl);
             split4_f16(vz, vh, vl);
-            *(v4h *)(Ks + k * 32 + d0) = kh;
-            *(v4h *)(Ks + k * 32 + 16 + d0) = kl;
+            *(v4h *)(Ks + kr * 32 + d0) = kh;
+            *(v4h *)(Ks + kr * 32 + 16 + d0) = kl;
             // bit-cast whole vectors: clang mis-lowers a bit_cast of one
             // vector element (it reads element 0)
             const v4s vhb = __builtin_bit_cast(v4s, vh), vlb = __builtin_bit_cast(v4s, vl);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                Vth[(d0 + jj) * kVt + kp] = (uint16_t)vhb[jj];
-                Vtl[(d0 + jj) * kVt + kp] = (uint16_t)vlb[jj];
+                Vth[(d0 + jj) * kVt + k] = (uint16_t)vhb[jj];
+                Vtl[(d0 + jj) * kVt + k] = (uint16_t)vlb[jj];
             }
         }
     }
@@ -316,7 +331,7 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
         // barrier would wait for every load)
 #pragma unroll
         for (int kb = 0; kb < kT; ++kb) {
-            if (kb < T && real.block(kb)) continue;
+            if (pair_real(real, kb & ~1, T)) continue;
             if constexpr (kBf16) u[j][kb] = make_uint2(kBf16NegInf, kBf16NegInf);
             else u[j][kb] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }

@@ -461,11 +461,14 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
     float4 u[kT];
     {
         const int zero = P >> 16;  // 0, opaque to the compiler (P <= 256)
-        const float *urow = U + (base + (qact ? q0 + c : 0)) * P + 4 * g;
+        const float *urow = U + (base + (qact ? q0 + c : 0)) * P;
 #pragma unroll
-        for (int kb = 0; kb < kT; ++kb) {
-            const bool need = qact && kb < T && real.block(kb);
-            u[kb] = *(const float4 *)(urow + (need ? kb : kb * zero) * kTile);
+        for (int kb = 0; kb < kT; kb += 2) {
+            // (half a pair lies past an odd block count: clamped, masked)
+            const bool need = qact && kb < T && real.pair(kb >> 1) != 0;
+            const int off = min(need ? u_col(kb, g) : u_col(kb, g) * zero, P - 8);
+            u[kb] = *(const float4 *)(urow + off);
+            u[kb + 1] = *(const float4 *)(urow + off + 4);
         }
     }
 
@@ -499,15 +502,15 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
         v4h kh, kl, vh, vl;
         split4_f16(kk, kh, kl);
         split4_f16(vv, vh, vl);
-        *(v4h *)(Ks + k * 32 + 4 * g) = kh;
-        *(v4h *)(Ks + k * 32 + 16 + 4 * g) = kl;
+        const int kr = key_row(k);
+        *(v4h *)(Ks + kr * 32 + 4 * g) = kh;
+        *(v4h *)(Ks + kr * 32 + 16 + 4 * g) = kl;
         // bit-cast whole vectors (clang mis-lowers a bit_cast of one element)
         const v4s vhb = __builtin_bit_cast(v4s, vh), vlb = __builtin_bit_cast(v4s, vl);
-        const int kp = vt_pos(k);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            Vth[(4 * g + r) * kVt + kp] = (uint16_t)vhb[r];
-            Vtl[(4 * g + r) * kVt + kp] = (uint16_t)vlb[r];
+            Vth[(4 * g + r) * kVt + k] = (uint16_t)vhb[r];
+            Vtl[(4 * g + r) * kVt + k] = (uint16_t)vlb[r];
         }
     }
     float qinv = 1.f;
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
     }
 #pragma unroll
     for (int kb = 0; kb < kT; ++kb)
-        if (!(kb < T && real.block(kb))) u[kb] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (!pair_real(real, kb & ~1, T)) u[kb] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     v8h qh, ql;
     {
         const float4 a = *(const float4 *)&Qs[wave][c][8 * (g & 1)];

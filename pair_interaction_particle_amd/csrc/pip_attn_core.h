@@ -2,8 +2,8 @@
 // fp16 operands, shared by the attention kernel and the block stack.
 //
 // "Fusion 3" of the ml4sci_cms_e2e26 README ("How the Kernel Fusion Works"):
-// softmax(Q K^T / sqrt(d) + bias) V.  K (as [key][hi d0..15 | lo d0..15]
-// fp16) and V^T (hi and lo, keys in vt_pos order) sit in LDS; the bias rows
+// softmax(Q K^T / sqrt(d) + bias) V.  K (as [key_row(key)][hi d0..15 | lo
+// d0..15] fp16) and V^T (hi and lo, plain key order) sit in LDS; the bias rows
 // of one query block (the "U strip") sit in registers.  Scores are computed
 // transposed, S^T = K Q^T, so that lane l holds query l%16 against keys
 // 4(l/16)+r; the softmax is exact (two passes over the strip); P V takes one
@@ -51,17 +51,31 @@ struct SlotBits {
         return (uint32_t)(word(kb >> 2) >> (16 * (kb & 3))) & 0xffffu;
     }
     __device__ __forceinline__ bool slot(int k) const { return (word(k >> 6) >> (k & 63)) & 1; }
+    // the 32 bits of key-block pair p (keys 32p .. 32p+31; compile-time p)
+    __device__ __forceinline__ uint32_t pair(int p) const {
+        return (uint32_t)(w[p >> 1] >> (32 * (p & 1)));
+    }
+    __device__ __forceinline__ uint32_t pair_rt(int p) const {
+        return (uint32_t)(word(p >> 1) >> (32 * (p & 1)));
+    }
 };
 
 // LDS row stride (elements) of V^T: the key range plus a pad that spreads the
 // 16 rows over the banks.
 constexpr int vt_stride(int kT) { return kT * 16 + 8; }
 
-// Position of key k inside a V^T row: keys are grouped by pairs of key
-// blocks so that lane group g finds keys 4g..4g+3 of both blocks of a pair
-// in 8 consecutive entries (one 16-byte LDS read per operand).
-__device__ __forceinline__ int vt_pos(int k) {
-    return (k & ~31) + ((k >> 2) & 3) * 8 + ((k >> 4) & 1) * 4 + (k & 3);
+// Key order inside a pair of key blocks (keys 32p .. 32p+31): the score MFMA
+// of block t = 0, 1 of the pair puts key 32p + 8g + 4t + r in lane group g,
+// register r.  Lane group g's keys of both blocks are then the 8 consecutive
+// keys 32p + 8g .. +7: one contiguous U read per lane and pair, and V^T in
+// plain key order for P V.  key_row(k) is the K row (score A-operand row
+// 16 (2p + t) + 4g + r) that holds key k.
+__device__ __forceinline__ int key_row(int k) {
+    return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+}
+// Offset inside a U row of lane group g's 4 keys of key block kb.
+__device__ __forceinline__ int u_col(int kb, int g) {
+    return 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
 }
 
 __device__ __forceinline__ bool f16_safe(float4 x) {
@@ -74,19 +88,21 @@ __device__ __forceinline__ float max8(const float (&a)[4], const float (&b)[4]) 
                  fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
 }
 
-// Is either block of the pair (kb, kb + 1) a block with a real key?
+// Does the pair of key blocks (kb, kb + 1) (kb even) hold a real key?  (Bits
+// of slots at or past P are 0.)
 template <int kWords>
 __device__ __forceinline__ bool pair_real(const SlotBits<kWords> &real, int kb, int T) {
-    return (kb < T && real.block(kb)) || (kb + 1 < T && real.block(kb + 1));
+    return kb < T && real.pair(kb >> 1) != 0;
 }
 
 // Scores, exact softmax and P V of one query block:
 //   s = qk_mul (k . q) + u   (u = -inf for keys to exclude),
 //   p = exp(s - max s),  o = sum_k p v_k (lane layout of O^T), l = sum_k p.
 // qh / ql are this lane's split Q entries 8(g&1) .. +7 of query l%16; u is
-// the strip (U of padded keys inside a real block is replaced here; blocks
-// without a real key must already hold -inf).  K and V rows of keys that are
-// not real must be 0 in LDS for every block below an even block count.
+// the strip in the pair key order of key_row / u_col (U of padded keys inside
+// a pair with a real key is replaced here; pairs without a real key must
+// already hold -inf).  K and V rows of keys that are not real must be 0 in LDS
+// for every pair below an even block count.
 template <int kT, int kWords>
 __device__ __forceinline__ void attend_split(float4 (&u)[kT], v8h qh, v8h ql, float qk_mul,
                                              const SlotBits<kWords> &real, int T,
@@ -96,14 +112,18 @@ __device__ __forceinline__ void attend_split(float4 (&u)[kT], v8h qh, v8h ql, fl
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     // U of padded keys -> -inf, so that every score is an FMA result
 #pragma unroll
-    for (int kb = 0; kb < kT; ++kb) {
-        const uint32_t bits = real.block(kb);
-        if (kb < T && bits != 0 && bits != 0xffffu) {
-            const uint32_t kbits = bits >> (4 * g);
-            u[kb].x = (kbits & 1) ? u[kb].x : -INFINITY;
-            u[kb].y = (kbits & 2) ? u[kb].y : -INFINITY;
-            u[kb].z = (kbits & 4) ? u[kb].z : -INFINITY;
-            u[kb].w = (kbits & 8) ? u[kb].w : -INFINITY;
+    for (int kb = 0; kb < kT; kb += 2) {
+        const uint32_t bits = real.pair(kb >> 1);
+        if (kb < T && bits != 0 && bits != 0xffffffffu) {
+            const uint32_t lb = bits >> (8 * g);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t kbits = lb >> (4 * t);
+                u[kb + t].x = (kbits & 1) ? u[kb + t].x : -INFINITY;
+                u[kb + t].y = (kbits & 2) ? u[kb + t].y : -INFINITY;
+                u[kb + t].z = (kbits & 4) ? u[kb + t].z : -INFINITY;
+                u[kb + t].w = (kbits & 8) ? u[kb + t].w : -INFINITY;
+            }
         }
     }
     // scores over pairs of key blocks; a block without a real key has zero K
