@@ -9,8 +9,7 @@
 // flight: every workgroup of the launch should be resident at once, issue all
 // of its loads early and have little work left once the data is there.  One
 // workgroup per (jet, head, group of up to 8 query blocks of 16 queries); each
-// wave owns kQ query blocks (2 for P <= 128, which keeps the register count
-// low enough for four workgroups per CU, 1 for larger P).
+// wave owns one query block.
 //   1. Each wave takes the jet's real-slot bits with ballots (wave-uniform,
 //      no LDS), then issues the loads of its U strips (16 queries x every key
 //      block that holds a real key) and of its Q rows into registers.
@@ -20,11 +19,14 @@
 //      probability inside the MFMA).
 //   3. One barrier, then per query block: U of padded keys is replaced by
 //      -inf; scores S^T = K Q^T on the matrix cores, transposed so that lane l
-//      holds query l%16 against keys 4(l/16)+r, over pairs of key blocks; an
-//      exact two-pass softmax over the strip held in registers (row max and
-//      row sum need an in-lane reduction and two cross-lane steps); then
-//      O^T += V^T P^T with one K = 32 product per pair of key blocks, the
-//      probabilities already in the B-operand layout.
+//      holds query l%16 against keys 4(l/16)+r, over pairs of key blocks.
+//      float32: an exact two-pass softmax over the scores held in registers;
+//      bfloat16: a running max and sum per pair of key blocks (the rescale
+//      costs one exp2 per pair and keeps no score array, so the kernel stays
+//      within 64 registers at P = 256).  Row max and row sum take an in-lane
+//      reduction and two cross-lane swaps.  Then O^T += V^T P^T with one
+//      K = 32 product per pair of key blocks, the probabilities already in
+//      the B-operand layout.
 // Query blocks without a real query store zeros; padded queries store 0.
 //
 // float32 inputs run on the fp16 matrix cores with split operands: every
@@ -140,42 +142,38 @@ __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
             }
         }
     }
-    float s[kT][4];
+    // online softmax over pairs of key blocks: the running max m is the same
+    // in the 4 lane groups of a query (cross-lane max per pair)
     float m = -INFINITY, lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < kT; kb += 2) {
-        if (!pair_real(real, kb, T)) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[kb][r] = s[kb + 1][r] = -INFINITY;
-            continue;
-        }
-        const v4s k0 = *(const v4s *)(Ks + (kb * kTile + c) * 16 + 4 * g);
-        const v4s k1 = *(const v4s *)(Ks + ((kb + 1) * kTile + c) * 16 + 4 * g);
-        const v4f a0 = mfma16bf(k0, qv, (v4f){0.f, 0.f, 0.f, 0.f});
-        const v4f a1 = mfma16bf(k1, qv, (v4f){0.f, 0.f, 0.f, 0.f});
-        s[kb][0] = fmaf(a0[0], 0.25f, bf2f(u[kb].x & 0xffff));
-        s[kb][1] = fmaf(a0[1], 0.25f, bf2f(u[kb].x >> 16));
-        s[kb][2] = fmaf(a0[2], 0.25f, bf2f(u[kb].y & 0xffff));
-        s[kb][3] = fmaf(a0[3], 0.25f, bf2f(u[kb].y >> 16));
-        s[kb + 1][0] = fmaf(a1[0], 0.25f, bf2f(u[kb + 1].x & 0xffff));
-        s[kb + 1][1] = fmaf(a1[1], 0.25f, bf2f(u[kb + 1].x >> 16));
-        s[kb + 1][2] = fmaf(a1[2], 0.25f, bf2f(u[kb + 1].y & 0xffff));
-        s[kb + 1][3] = fmaf(a1[3], 0.25f, bf2f(u[kb + 1].y >> 16));
-        m = fmaxf(m, max8(s[kb], s[kb + 1]));
-    }
-    m = xmax16(m);
-    const float mb = m * kLog2e;
     v4f o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < kT; kb += 2) {
         if (!pair_real(real, kb, T)) continue;
+        const v4s k0 = *(const v4s *)(Ks + (kb * kTile + c) * 16 + 4 * g);
+        const v4s k1 = *(const v4s *)(Ks + ((kb + 1) * kTile + c) * 16 + 4 * g);
+        const v4f a0 = mfma16bf(k0, qv, (v4f){0.f, 0.f, 0.f, 0.f});
+        const v4f a1 = mfma16bf(k1, qv, (v4f){0.f, 0.f, 0.f, 0.f});
+        float s0[4], s1[4];
+        s0[0] = fmaf(a0[0], 0.25f, bf2f(u[kb].x & 0xffff));
+        s0[1] = fmaf(a0[1], 0.25f, bf2f(u[kb].x >> 16));
+        s0[2] = fmaf(a0[2], 0.25f, bf2f(u[kb].y & 0xffff));
+        s0[3] = fmaf(a0[3], 0.25f, bf2f(u[kb].y >> 16));
+        s1[0] = fmaf(a1[0], 0.25f, bf2f(u[kb + 1].x & 0xffff));
+        s1[1] = fmaf(a1[1], 0.25f, bf2f(u[kb + 1].x >> 16));
+        s1[2] = fmaf(a1[2], 0.25f, bf2f(u[kb + 1].y & 0xffff));
+        s1[3] = fmaf(a1[3], 0.25f, bf2f(u[kb + 1].y >> 16));
+        const float mn = fmaxf(m, xmax16(max8(s0, s1)));
+        const float corr = __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+        m = mn;
+        const float mb = mn * kLog2e;
         v8f p;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], kLog2e, -mb));
-            p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][r], kLog2e, -mb));
+            p[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], kLog2e, -mb));
+            p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], kLog2e, -mb));
         }
-        lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        lsum = fmaf(lsum, corr, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        o = o * corr;
         const v8bf vt = *(const v8bf *)(Vth + c * kVt + kb * kTile + 8 * g);
         o = mfma32bf(vt, __builtin_convertvector(p, v8bf), o);
     }

@@ -36,12 +36,20 @@ struct SlotBits {
 #pragma unroll
         for (int i = 0; i < kWords; ++i) w[i] = __ballot(64 * i + lane < P && b[i] != 0);
     }
-    // word i for a run-time i (selects, no indexed register access)
+    // word i for a run-time i.  The words pass through readfirstlane (free:
+    // they are wave-uniform) so that the selects act on values; a select
+    // between two fields would otherwise be folded into an indexed load,
+    // which keeps the struct in memory (moved to LDS or scratch).
     __device__ __forceinline__ uint64_t word(int i) const {
-        uint64_t r = w[0];
+        uint64_t r = uniform(w[0]);
 #pragma unroll
-        for (int j = 1; j < kWords; ++j) r = i == j ? w[j] : r;
+        for (int j = 1; j < kWords; ++j) r = i == j ? uniform(w[j]) : r;
         return r;
+    }
+    static __device__ __forceinline__ uint64_t uniform(uint64_t x) {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+        return ((uint64_t)hi << 32) | lo;
     }
     // the 16 bits of block kb (compile-time kb)
     __device__ __forceinline__ uint32_t block(int kb) const {
