@@ -121,13 +121,18 @@ __device__ __forceinline__ bool block_pair(bool diag, int k, int nblk, int lane,
 }
 
 // Bit t set when 16-block t of a mask row holds a real particle (row 16-byte
-// aligned, read as T 16-byte vectors).
+// aligned, read as T 16-byte vectors).  All loads are issued before the
+// first is looked at (addresses clamped into the row): one memory round trip
+// instead of T.
 __device__ __forceinline__ uint32_t jet_activity(const uint8_t *__restrict__ mrow, int T) {
+    constexpr int kMaxT = kMaxP / kTile;
+    uint4 v[kMaxT];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) v[t] = ((const uint4 *)mrow)[min(t, T - 1)];
     uint32_t act = 0;
-    for (int t = 0; t < T; ++t) {
-        const uint4 v = ((const uint4 *)mrow)[t];
-        if (v.x | v.y | v.z | v.w) act |= 1u << t;
-    }
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t)
+        if (t < T && (v[t].x | v[t].y | v[t].z | v[t].w)) act |= 1u << t;
     return act;
 }
 
@@ -287,9 +292,10 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     const long R = scan[kEmbedThreads - 1];
     const int r0 = (int)(R * w / W), r1 = (int)(R * (w + 1) / W);
     if (r0 < r1) {
-    // the jet holding real tile r0 and its local index (uniform in the block)
-    int c = 0;
-    while (scan[c] <= r0) ++c;
+    // the jet holding real tile r0 and its local index (uniform in the block):
+    // the first thread whose inclusive count exceeds r0 (the scan does not
+    // decrease, so that is the number of counts at or below r0)
+    const int c = __syncthreads_count(scan[tid] <= r0);
     int b = c * per, k = r0 - (c ? scan[c - 1] : 0);
     uint32_t act = jet_activity(mask + (size_t)b * P, T);
     while (k >= active_tiles(act)) {
