@@ -113,8 +113,7 @@ __device__ __forceinline__ void b_operand(const float *Xs, const float *rsc, int
     const float4 a = *(const float4 *)src, b = *(const float4 *)(src + 4);
     const float sc = rsc[16 * i + c];
     const v8f x = {a.x * sc, a.y * sc, a.z * sc, a.w * sc, b.x * sc, b.y * sc, b.z * sc, b.w * sc};
-    bh = __builtin_convertvector(x, v8h);
-    bl = __builtin_convertvector(x - __builtin_convertvector(bh, v8f), v8h);
+    split_f16<8>(x, bh, bl);
 }
 
 // Row scales of the kRows rows in Xs (all kStackThreads threads; the caller
@@ -419,8 +418,8 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
             v8f x;
 #pragma unroll
             for (int j = 0; j < 8; ++j) x[j] = 32 * s + 8 * g + j < C ? xv[t2][s][j] * rs : 0.f;
-            const v8h bh = __builtin_convertvector(x, v8h);
-            const v8h bl = __builtin_convertvector(x - __builtin_convertvector(bh, v8f), v8h);
+            v8h bh, bl;
+            split_f16<8>(x, bh, bl);
             const size_t ok = ((size_t)(1 * NT + h) * KS + s) * 64 + lane;
             const size_t ov = ((size_t)(2 * NT + h) * KS + s) * 64 + lane;
             const v8h kh = Ahi[ok], kl = Alo[ok], vh = Ahi[ov], vl = Alo[ov];

@@ -180,8 +180,8 @@ __device__ __forceinline__ void attend_split(float4 (&u)[kT], v8h qh, v8h ql, fl
         const int off = c * kVt + kb * kTile + 8 * g;
         const v8h vh = *(const v8h *)(Vth + off);
         const v8h vl = *(const v8h *)(Vtl + off);
-        const v8h ph = __builtin_convertvector(p, v8h);
-        const v8h pl = __builtin_convertvector(p - __builtin_convertvector(ph, v8f), v8h);
+        v8h ph, pl;
+        split_f16<8>(p, ph, pl);
         o = mfma32h(vh, pl, o);
         o = mfma32h(vl, ph, o);
         o = mfma32h(vh, ph, o);

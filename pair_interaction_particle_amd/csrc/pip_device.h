@@ -55,10 +55,30 @@ __device__ __forceinline__ v4f mfma32h(v8h a, v8h b, v4f c) {
 // 22 significand bits, |x - hi - lo| <= 2^-22 |x| while x and x - hi stay in
 // the normal fp16 range (|x| <= 65504; below 2^-14 the error is absolute,
 // at most 2^-25).
+// The residual x - hi is formed as fma(hi, -1, x) with the -1 in a scalar
+// register the optimiser cannot see through: the FMA then stays an FMA and
+// reads its fp16 operand in place (v_fma_mix_f32), one instruction instead of
+// a conversion and a subtraction.  The value is the same: x - hi is exact.
+__device__ __forceinline__ float opaque_neg_one() {
+    float m;
+    __asm__("s_mov_b32 %0, -1.0" : "=s"(m));
+    return m;
+}
+template <int N>
+__device__ __forceinline__ void split_f16(const float __attribute__((ext_vector_type(N))) &x,
+                                          _Float16 __attribute__((ext_vector_type(N))) &hi,
+                                          _Float16 __attribute__((ext_vector_type(N))) &lo) {
+    typedef float VF __attribute__((ext_vector_type(N)));
+    hi = __builtin_convertvector(x, _Float16 __attribute__((ext_vector_type(N))));
+    const float m1 = opaque_neg_one();
+    VF r;
+#pragma unroll
+    for (int j = 0; j < N; ++j) r[j] = fmaf((float)hi[j], m1, x[j]);
+    lo = __builtin_convertvector(r, _Float16 __attribute__((ext_vector_type(N))));
+}
 __device__ __forceinline__ void split4_f16(float4 x, v4h &hi, v4h &lo) {
     const v4f v = {x.x, x.y, x.z, x.w};
-    hi = __builtin_convertvector(v, v4h);
-    lo = __builtin_convertvector(v - __builtin_convertvector(hi, v4f), v4h);
+    split_f16<4>(v, hi, lo);
 }
 
 // ------------------------------------------------------------ kinematics

@@ -240,23 +240,8 @@ __device__ __forceinline__ void mlp2_bf16(const float4 *__restrict__ wl,
 // hi / lo fp16 B operands for K = 32 (slots 0..3 from channel block `lo_blk`,
 // 4..7 from `hi_blk`, as in pack_bf16).
 __device__ __forceinline__ void split_f16(v4f b0, v4f b1, v8h &hi, v8h &lo) {
-#pragma unroll
-    for (int r = 0; r < 4; r += 2) {
-        const v2h h0 = __builtin_convertvector((v2f){b0[r], b0[r + 1]}, v2h);
-        const v2h h1 = __builtin_convertvector((v2f){b1[r], b1[r + 1]}, v2h);
-        const v2h l0 = __builtin_convertvector(
-            (v2f){b0[r] - (float)h0[0], b0[r + 1] - (float)h0[1]}, v2h);
-        const v2h l1 = __builtin_convertvector(
-            (v2f){b1[r] - (float)h1[0], b1[r + 1] - (float)h1[1]}, v2h);
-        hi[r] = h0[0];
-        hi[r + 1] = h0[1];
-        hi[r + 4] = h1[0];
-        hi[r + 5] = h1[1];
-        lo[r] = l0[0];
-        lo[r + 1] = l0[1];
-        lo[r + 4] = l1[0];
-        lo[r + 5] = l1[1];
-    }
+    const v8f x = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    split_f16<8>(x, hi, lo);
 }
 
 // t += W x over K = 64 (two K = 32 halves) with the three-term split.
