@@ -351,11 +351,20 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
     constexpr int kWords = (kT * 16 + 63) / 64;
     constexpr int kVt = vt_stride(kT);
     constexpr int kRbw = (kT + kSaWaves - 1) / kSaWaves;  // row blocks per wave
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kT * 16 * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t Vth[16 * kVt];
-    __shared__ __attribute__((aligned(16))) uint16_t Vtl[16 * kVt];
-    __shared__ __attribute__((aligned(16))) float Qs[kSaWaves][16][20];
+    // LDS: during the projections the head's packed Q/K/V weight operands
+    // ([m][hi, lo][s][lane], read by all 8 waves); afterwards, in the same
+    // bytes, K, V^T and the Q tiles of the attention.
+    constexpr int kKsB = kT * 16 * 32 * 2, kVtB = 16 * kVt * 2, kQsB = kSaWaves * 16 * 20 * 4;
+    constexpr int kWB = 3 * 2 * kKS * 64 * 16;
+    constexpr int kAttnB = kKsB + 2 * kVtB + kQsB;
+    static_assert(kKsB % 16 == 0 && kVtB % 16 == 0, "LDS sections stay 16-byte aligned");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kAttnB > kWB ? kAttnB : kWB];
     __shared__ float kvmax[2][kSaWaves];
+    uint16_t *Ks = (uint16_t *)smem;
+    uint16_t *Vth = (uint16_t *)(smem + kKsB);
+    uint16_t *Vtl = (uint16_t *)(smem + kKsB + kVtB);
+    float (*Qs)[16][20] = (float (*)[16][20])(smem + kKsB + 2 * kVtB);
+    v8h *Ws = (v8h *)smem;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -392,6 +401,28 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
     const int qb = chunk * kSaWaves + wave, q0 = qb * kTile;
     const bool qact = qb < T && real.block_rt(qb) != 0;
 
+    // the head's weight operands into LDS, every load issued before the first
+    // store (one L2 round trip per workgroup instead of one per K step and wave)
+    {
+        constexpr int kW = 3 * 2 * kKS * 64;  // v8h operands
+        constexpr int kIt = (kW + kSaThreads - 1) / kSaThreads;
+        v8h wv[kIt];
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int i = min(tid + it * kSaThreads, kW - 1);
+            const int m = i / (2 * kKS * 64), hl = (i / (kKS * 64)) & 1;
+            const int s = (i / 64) % kKS, l = i & 63;
+            const size_t o = ((size_t)(m * NT + h) * KS + min(s, KS - 1)) * 64 + l;
+            wv[it] = hl ? Alo[o] : Ahi[o];
+        }
+#pragma unroll
+        for (int it = 0; it < kIt; ++it)
+            if (tid + it * kSaThreads < kW) Ws[tid + it * kSaThreads] = wv[it];
+    }
+    __syncthreads();
+    // operand (m, hi / lo, s) of this lane
+    auto wop = [&](int m, int hl, int s) { return Ws[((m * 2 + hl) * kKS + s) * 64 + lane]; };
+
     // ---- 2. projections
     v4f kt[kRbw], vt[kRbw], qt = {0.f, 0.f, 0.f, 0.f};
     float kmx = 0.f, vmx = 0.f;
@@ -420,9 +451,7 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
             for (int j = 0; j < 8; ++j) x[j] = 32 * s + 8 * g + j < C ? xv[t2][s][j] * rs : 0.f;
             v8h bh, bl;
             split_f16<8>(x, bh, bl);
-            const size_t ok = ((size_t)(1 * NT + h) * KS + s) * 64 + lane;
-            const size_t ov = ((size_t)(2 * NT + h) * KS + s) * 64 + lane;
-            const v8h kh = Ahi[ok], kl = Alo[ok], vh = Ahi[ov], vl = Alo[ov];
+            const v8h kh = wop(1, 0, s), kl = wop(1, 1, s), vh = wop(2, 0, s), vl = wop(2, 1, s);
             ak = mfma32h(kh, bl, ak);
             av = mfma32h(vh, bl, av);
             ak = mfma32h(kl, bh, ak);
@@ -430,8 +459,7 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
             ak = mfma32h(kh, bh, ak);
             av = mfma32h(vh, bh, av);
             if (isq) {
-                const size_t oq = ((size_t)h * KS + s) * 64 + lane;
-                const v8h qh = Ahi[oq], ql = Alo[oq];
+                const v8h qh = wop(0, 0, s), ql = wop(0, 1, s);
                 aq = mfma32h(qh, bl, aq);
                 aq = mfma32h(ql, bh, aq);
                 aq = mfma32h(qh, bh, aq);
