@@ -319,9 +319,9 @@ __global__ __launch_bounds__(kStackThreads) void stack_out_kernel(
 // One workgroup per (jet, head, group of 8 query blocks), 8 waves; the H x
 // chunks workgroups of a jet share one XCD (block index modulo 8), so the
 // jet's X rows are read from HBM once per layer.
-//   1. Wave w loads the X rows of row blocks w and w + 8 (every block below an
-//      even block count that holds a real row), then the U strip of its
-//      query block.  The loads of the strip run while the projections do.
+//   1. The head's packed Q/K/V weight operands go to LDS (one load round
+//      for the workgroup); wave w loads the X rows of row blocks w and w + 8
+//      (every block below an even block count that holds a real row).
 //   2. K_h, V_h (and Q_h of its own query block) of those rows on the fp16
 //      matrix cores with split operands, every X row scaled by its own power
 //      of two first.  Padded rows give 0.
@@ -331,7 +331,9 @@ __global__ __launch_bounds__(kStackThreads) void stack_out_kernel(
 //      relative accuracy, and the scales are undone exactly on the scores
 //      and the output.  K and V^T go to LDS, Q through LDS into the
 //      B-operand layout.
-//   4. The attention core of pair_bias_attention on the strip; O goes to the
+//   4. The U strip of the wave's query block is loaded once the projections
+//      no longer hold registers; the attention core of pair_bias_attention
+//      runs on it; O goes to the
 //      head-major (B, H, P, 16) buffer the Wo step reads.
 constexpr int kSaWaves = 8;
 constexpr int kSaThreads = 64 * kSaWaves;
@@ -634,11 +636,11 @@ hipError_t launch_block_stack(float *X, const float *Wq, const float *Wk, const 
                                0, s, X, o.hi, o.lo, o.ci, U, mask, B, H, P, C, chunks, O);
         // X += O Wo[l]
         if (KS <= 4)
-            hipLaunchKernelGGL((stack_out_kernel<4, 4>), dim3((unsigned)((R + 63) / 64)),
+            hipLaunchKernelGGL((stack_out_kernel<4, 1>), dim3((unsigned)((R + 15) / 16)),
                                dim3(kStackThreads), 0, s, X, O, o.hi, o.lo, o.ci, mask, R, P, C,
                                H);
         else
-            hipLaunchKernelGGL((stack_out_kernel<8, 2>), dim3((unsigned)((R + 31) / 32)),
+            hipLaunchKernelGGL((stack_out_kernel<8, 1>), dim3((unsigned)((R + 15) / 16)),
                                dim3(kStackThreads), 0, s, X, O, o.hi, o.lo, o.ci, mask, R, P, C,
                                H);
     }
