@@ -241,10 +241,123 @@ __device__ __forceinline__ void write_row_pair(const PL &L, OutT *U, int P, int 
     }
 }
 
-// Persistent pair-embed kernel.  Real tiles (both blocks hold a real
-// particle) are counted per jet from the mask; a block-wide scan gives every
-// workgroup an equal contiguous range of them.  All-padding tiles are split
-// evenly too and only get zeros.  Within a jet the workgroup's tiles are
+// ---- work estimate for the balanced split
+// A CU's time follows the wave iterations (pairs of blocks) it runs: one that
+// holds a real pair runs the MLP, an all-padding one only stores zeros but
+// still costs its features, branches and stores (the weights below were fitted
+// to per-wave timings).  The estimate takes the real slots of a jet to come
+// first (the usual layout):
+// the ia-th active block then holds r = min(16, n - 16 ia) real rows (at least
+// 1), an off-diagonal tile of its rows has ceil(r / 2) real iterations of 8,
+// and its diagonal tile min(5, ceil(r (r + 1) / 64)) of 5.  Any other layout
+// only moves the split points; every iteration is still done exactly once.
+template <int kMode>
+struct WorkCost {  // relative cost of a real and of an all-padding iteration
+    static constexpr int kReal = kMode == kMlpBf16 ? 3 : 5, kPad = 2;
+};
+
+struct JetInfo {
+    uint32_t act;  // bit t: block t holds a real slot
+    int n;         // real slots
+};
+// bit k set when byte k of x is nonzero (k < 4)
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+    x |= x >> 4;
+    x |= x >> 2;
+    x |= x >> 1;
+    x &= 0x01010101u;
+    return (x | (x >> 7) | (x >> 14) | (x >> 21)) & 0xfu;
+}
+// Every load is issued before the first is looked at (addresses clamped into
+// the row): one memory round trip.
+__device__ __forceinline__ JetInfo jet_info(const uint8_t *__restrict__ mrow, int T) {
+    constexpr int kMaxT = kMaxP / kTile;
+    uint4 v[kMaxT];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) v[t] = ((const uint4 *)mrow)[min(t, T - 1)];
+    JetInfo j = {0u, 0};
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) {
+        const int c = __popc(nonzero_bytes(v[t].x) | nonzero_bytes(v[t].y) << 4 |
+                             nonzero_bytes(v[t].z) << 8 | nonzero_bytes(v[t].w) << 12);
+        if (t < T && c) {
+            j.act |= 1u << t;
+            j.n += c;
+        }
+    }
+    return j;
+}
+__device__ __forceinline__ int est_rows(int n, int ia) { return max(1, min(16, n - 16 * ia)); }
+__device__ __forceinline__ int est_diag_real(int r) { return min(5, (r * (r + 1) / 2 + 31) >> 5); }
+template <class C>
+__device__ __forceinline__ int est_off_cost(int r) {
+    return 8 * C::kPad + (C::kReal - C::kPad) * ((r + 1) >> 1);
+}
+template <class C>
+__device__ __forceinline__ int est_diag_cost(int r) {
+    return 5 * C::kPad + (C::kReal - C::kPad) * est_diag_real(r);
+}
+template <class C>
+__device__ __forceinline__ int est_row_cost(int n, int ia) {
+    const int r = est_rows(n, ia);
+    return ia * est_off_cost<C>(r) + est_diag_cost<C>(r);
+}
+template <class C>
+__device__ __forceinline__ int jet_cost(JetInfo j) {
+    int c = 0;
+    const int a = __popc(j.act);
+    for (int ia = 0; ia < a; ++ia) c += est_row_cost<C>(j.n, ia);
+    return c;
+}
+// The flat block index (even) of the first iteration of the jet whose cost
+// prefix reaches tl (0 <= tl < jet_cost(j)).
+template <class C>
+__device__ __forceinline__ int jet_split(JetInfo j, int tl) {
+    int ia = 0, acc = 0;
+    for (;; ++ia) {
+        const int rc = est_row_cost<C>(j.n, ia);
+        if (tl < acc + rc) break;
+        acc += rc;
+    }
+    const int r = est_rows(j.n, ia), oc = est_off_cost<C>(r);
+    int rem = tl - acc, first, n;
+    bool diag;
+    if (rem < ia * oc) {
+        const int ja = rem / oc;
+        rem -= ja * oc;
+        first = blocks_before_row(ia) + 16 * ja;
+        n = 8;
+        diag = false;
+    } else {
+        rem -= ia * oc;
+        first = blocks_before_row(ia) + 16 * ia;
+        n = 5;
+        diag = true;
+    }
+    // the smallest iteration whose cost prefix inside the tile reaches rem
+    const int dr = est_diag_real(r);
+    int k = 0, pre = 0;
+    while (k < n && pre < rem) {
+        pre += (diag ? k < dr : 2 * k < r) ? C::kReal : C::kPad;
+        ++k;
+    }
+    return first + 2 * k;
+}
+// The tile row ia that holds flat pair block q.
+__device__ __forceinline__ int block_row(int q) {
+    int ia = (int)((sqrtf(4.0f + 32.0f * (float)q) - 2.0f) * 0.0625f);
+    while (blocks_before_row(ia + 1) <= q) ++ia;
+    while (ia > 0 && blocks_before_row(ia) > q) --ia;
+    return ia;
+}
+// Pair blocks of a jet (the blocks before the row past its last active tile).
+__device__ __forceinline__ int jet_blocks(uint32_t act) { return blocks_before_row(__popc(act)); }
+
+// Persistent pair-embed kernel.  The work of every jet (its pair blocks in
+// tile order, weighted by the estimate above) is counted from the mask; a
+// block-wide scan gives every workgroup an equal contiguous share, split at
+// pair-block granularity (the two workgroups of a CU then carry a like load).
+// All-padding tiles are split evenly too and only get zeros.  Within a jet the workgroup's tiles are
 // dealt to its 8 waves round robin; each wave runs its tiles alone (no
 // barrier between tiles) and writes U straight from registers, so waves
 // drift apart and hide each other's latencies.  Workgroup w is remapped so
@@ -257,8 +370,9 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
                        const v8h *__restrict__ wx2, const float *__restrict__ bias,
                        void *__restrict__ Uout) {
     MlpLds<kMode> M;
-    __shared__ PartLds<kMaxP> L;
+    __shared__ PartLds<kMaxP> Ls[2];  // the particles of two jets
     __shared__ int scan[kEmbedThreads];
+    __shared__ JetInfo jinfo[kEmbedThreads];
 
     // pair (i, j), j <= i, of slot p of a diagonal tile's triangle packing
     // as i << 4 | j; the unused slots 136..159 hold kNoPair (i = 0, j = 15),
@@ -276,58 +390,117 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     const int W = gridDim.x;
     const int w = (W % 8 == 0) ? (blockIdx.x % 8) * (W / 8) + blockIdx.x / 8 : blockIdx.x;
 
-    // ---- this workgroup's range of real tiles
+    // ---- this workgroup's equal share of the estimated work: a block scan of
+    // the per-jet costs (each thread sums the jets of its range), split at
+    // iteration granularity
     const int per = (B + kEmbedThreads - 1) / kEmbedThreads;
     const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
     int cnt = 0;
-    for (int b = b0; b < b1; ++b) cnt += active_tiles(jet_activity(mask + (size_t)b * P, T));
-    scan[tid] = cnt;
+    JetInfo mine = {0u, 0};  // the thread's jet when it has one (per == 1)
+    for (int b = b0; b < b1; ++b) {
+        mine = jet_info(mask + (size_t)b * P, T);
+        cnt += jet_cost<WorkCost<kMode>>(mine);
+    }
+    jinfo[tid] = mine;
+    // inclusive scan of the counts: within each wave, then the wave totals
+    int inc = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(inc, off);
+        inc += lane >= off ? v : 0;
+    }
+    if (lane == 63) scan[wv] = inc;
     __syncthreads();
-    for (int off = 1; off < kEmbedThreads; off <<= 1) {  // inclusive scan
-        const int v = (tid >= off) ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+    int before = 0, totw = 0;
+#pragma unroll
+    for (int k = 0; k < kEmbedWaves; ++k) {
+        const int v = scan[k];
+        before += k < wv ? v : 0;
+        totw += v;
     }
-    const long R = scan[kEmbedThreads - 1];
-    const int r0 = (int)(R * w / W), r1 = (int)(R * (w + 1) / W);
-    if (r0 < r1) {
-    // the jet holding real tile r0 and its local index (uniform in the block):
-    // the first thread whose inclusive count exceeds r0 (the scan does not
-    // decrease, so that is the number of counts at or below r0)
-    const int c = __syncthreads_count(scan[tid] <= r0);
-    int b = c * per, k = r0 - (c ? scan[c - 1] : 0);
-    uint32_t act = jet_activity(mask + (size_t)b * P, T);
-    while (k >= active_tiles(act)) {
-        k -= active_tiles(act);
-        ++b;
-        act = jet_activity(mask + (size_t)b * P, T);
+    __syncthreads();
+    scan[tid] = before + inc;
+    __syncthreads();
+    const long total = totw;
+    // split point i: the first iteration whose cost prefix reaches
+    // total (w + i) / W, as the jet and the cost left inside it; jet B at the end
+    int sb[2], st[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = (int)(total * (w + i) / W);
+        sb[i] = B;
+        st[i] = 0;
+        if (t >= total) continue;
+        // the first thread whose inclusive prefix exceeds t (the prefix does
+        // not decrease, so that is the number of prefixes at or below t)
+        const int c = __syncthreads_count(scan[tid] <= t);
+        sb[i] = c * per;
+        st[i] = t - (c ? scan[c - 1] : 0);
     }
+    // the jets at the split points: from LDS when every thread has one jet,
+    // else walked from the first jet of the split thread's range
+    JetInfo js = {0u, 0}, je = {0u, 0};
+    if (per == 1) {
+        if (sb[0] < B) js = jinfo[sb[0]];
+        if (sb[1] < B) je = jinfo[sb[1]];
+    } else {
+        js = sb[0] < B ? jet_info(mask + (size_t)sb[0] * P, T) : JetInfo{0u, 0};
+        je = sb[1] < B ? jet_info(mask + (size_t)sb[1] * P, T) : JetInfo{0u, 0};
+        for (int jc = jet_cost<WorkCost<kMode>>(js); sb[0] < B && st[0] >= jc;
+             jc = jet_cost<WorkCost<kMode>>(js)) {
+            st[0] -= jc;
+            ++sb[0];
+            js = jet_info(mask + (size_t)min(sb[0], B - 1) * P, T);
+        }
+        for (int jc = jet_cost<WorkCost<kMode>>(je); sb[1] < B && st[1] >= jc;
+             jc = jet_cost<WorkCost<kMode>>(je)) {
+            st[1] -= jc;
+            ++sb[1];
+            je = jet_info(mask + (size_t)min(sb[1], B - 1) * P, T);
+        }
+    }
+    const int bS = sb[0], bE = sb[1];
+    const int qS = bS < B ? jet_split<WorkCost<kMode>>(js, st[0]) : 0;
+    const int qE = bE < B ? jet_split<WorkCost<kMode>>(je, st[1]) : 0;
 
-    M.template stage<kEmbedThreads>(w32, w16, wx2, bias);
+    if (bS < B) M.template stage<kEmbedThreads>(w32, w16, wx2, bias);
+    const int nj = bE - bS + (qE > 0 ? 1 : 0);  // jets this workgroup visits
 
-    int r = r0;
-    while (r < r1) {
-        const int nt = active_tiles(act);
-        const int kend = min(nt, k + (r1 - r));  // this jet's tiles in the range: [k, kend)
-        if (kend > k) {
-            __syncthreads();  // every wave is done with the previous jet's particles
-            for (int s = tid; s < P; s += kEmbedThreads) {
-                const size_t idx = (size_t)b * P + s;
-                const int real = mask[idx] != 0;
-                stage_particle(L, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
-            }
+    // the particles of jet j of the range into slot j & 1 (all threads)
+    auto stage_jet = [&](int j) {
+        const int b = bS + j;
+        PartLds<kMaxP> &Lj = Ls[j & 1];
+        for (int s = tid; s < P; s += kEmbedThreads) {
+            const size_t idx = (size_t)b * P + s;
+            const int real = mask[idx] != 0;
+            stage_particle(Lj, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+        }
+    };
+    // the first two jets at once, so that no barrier separates them
+    for (int j = 0; j < min(nj, 2); ++j) stage_jet(j);
+    __syncthreads();
+
+    for (int j = 0; j < nj; ++j) {
+        const int b = bS + j;
+        if (j >= 2) {  // a third jet reuses slot j & 1: wait for jet j - 2
             __syncthreads();
+            stage_jet(j);
+            __syncthreads();
+        }
+        const PartLds<kMaxP> &L = Ls[j & 1];
+        const uint32_t act = b == bS ? js.act : b == bE ? je.act : jet_activity(mask + (size_t)b * P, T);
+        const int q0 = b == bS ? qS : 0, q1 = b == bE ? qE : jet_blocks(act);
+        if (q1 <= q0) continue;
+        {
             OutT *U = (OutT *)Uout + (size_t)b * kHeads * P * P;
             // the range's pair blocks, flattened, dealt to the waves in pairs;
             // the tile walk is wave-uniform (scalar registers)
             const uint64_t aidx = active_index(act);
-            const int q0 = blocks_before(k), q1 = blocks_before(kend);
             auto sweep = [&](auto exact_t) {
                 constexpr bool kExact = decltype(exact_t)::value;
                 bool ok = true;
                 int q = q0 + 2 * wv;
-                int ia = tri_row(k), rem = q - blocks_before_row(ia);
+                int ia = block_row(q0), rem = q - blocks_before_row(ia);
                 for (; q < q1; q += 2 * kEmbedWaves, rem += 2 * kEmbedWaves) {
                     // Compiler-only memory barrier (emits nothing): keeps the
                     // loop-invariant LDS weight reads inside the loop instead
@@ -378,15 +551,8 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             // A wave whose fp16 x 2 results were not all finite redoes its
             // share of this jet exactly (its later stores replace the earlier).
             if (!sweep(std::false_type{})) sweep(std::true_type{});
-            r += kend - k;
-        }
-        if (r < r1) {
-            ++b;
-            k = 0;
-            act = jet_activity(mask + (size_t)b * P, T);
         }
     }
-    }  // real tiles
 
     // ---- tiles without a real pair: zeros (after the real tiles, so these
     // stores overlap the other workgroups' work; jet activity read once per jet)
