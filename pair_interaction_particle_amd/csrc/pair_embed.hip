@@ -89,6 +89,7 @@ __device__ __forceinline__ void store4(uint16_t *U, uint32_t off, const float (&
 
 constexpr int kEmbedThreads = 512;
 constexpr int kEmbedWaves = kEmbedThreads / 64;
+static_assert((kEmbedWaves & (kEmbedWaves - 1)) == 0, "the sweep rotates waves modulo a power of two");
 
 // Zero tile (I, J) of every head and, if I != J, its transpose (J, I): one
 // 16-byte store per thread and direction.
@@ -499,9 +500,16 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             auto sweep = [&](auto exact_t) {
                 constexpr bool kExact = decltype(exact_t)::value;
                 bool ok = true;
-                int q = q0 + 2 * wv;
-                int ia = block_row(q0), rem = q - blocks_before_row(ia);
-                for (; q < q1; q += 2 * kEmbedWaves, rem += 2 * kEmbedWaves) {
+                // round r gives wave w iteration 8 r + (w - r) mod 8: the
+                // position inside a tile rotates, so no wave keeps taking the
+                // all-padding rows at the end of partly real tiles
+                const int nit = (q1 - q0) >> 1;
+                int ia = block_row(q0);
+                for (int r = 0; 8 * r < nit; ++r) {
+                    const int it = 8 * r + ((wv - r) & (kEmbedWaves - 1));
+                    if (it >= nit) continue;
+                    const int q = q0 + 2 * it;
+                    int rem = q - blocks_before_row(ia);
                     // Compiler-only memory barrier (emits nothing): keeps the
                     // loop-invariant LDS weight reads inside the loop instead
                     // of hoisting 144+ registers of operands out of it.
