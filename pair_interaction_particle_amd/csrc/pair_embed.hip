@@ -394,6 +394,9 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // ---- this workgroup's equal share of the estimated work: a block scan of
     // the per-jet costs (each thread sums the jets of its range), split at
     // iteration granularity
+    // the MLP weights: loads issued now, stored to LDS once the split is known
+    typename MlpLds<kMode>::template Staging<kEmbedThreads> wst;
+    wst.load(w32, w16, wx2, bias);
     const int per = (B + kEmbedThreads - 1) / kEmbedThreads;
     const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
     int cnt = 0;
@@ -464,7 +467,7 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     const int qS = bS < B ? jet_split<WorkCost<kMode>>(js, st[0]) : 0;
     const int qE = bE < B ? jet_split<WorkCost<kMode>>(je, st[1]) : 0;
 
-    if (bS < B) M.template stage<kEmbedThreads>(w32, w16, wx2, bias);
+    wst.store(M);
     const int nj = bE - bS + (qE > 0 ? 1 : 0);  // jets this workgroup visits
 
     // the particles of jet j of the range into slot j & 1 (all threads)

@@ -66,14 +66,25 @@ constexpr int kW16Ops = 18;
 constexpr int kW16Elems = kW16Ops * 64 * 8;      // 9,216
 constexpr int kBiasFloats = 200;                 // b1' | b2' | b3' | b4
 
-// Copy the packed weights and biases from global memory into LDS (all threads
-// of the block; caller synchronises).
-template <int kThreads>
-__device__ inline void stage_weights(float4 *wl, float *bl, const float4 *__restrict__ w,
-                                     const float *__restrict__ b, int nw4) {
-    for (int i = threadIdx.x; i < nw4; i += kThreads) wl[i] = w[i];
-    for (int i = threadIdx.x; i < kBiasFloats; i += kThreads) bl[i] = b[i];
-}
+// This thread's share of an N-element copy into LDS, split into a load step
+// and a store step so that a caller can issue every load of several copies
+// before the first store, and keep them in flight across other work.
+template <int kThreads, int N, class T>
+struct LdsCopy {
+    static constexpr int kIt = (N + kThreads - 1) / kThreads;
+    T v[kIt];
+    __device__ __forceinline__ void load(const T *__restrict__ src) {
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) v[it] = src[min((int)threadIdx.x + it * kThreads, N - 1)];
+    }
+    __device__ __forceinline__ void store(T *dst) const {
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int i = threadIdx.x + it * kThreads;
+            if (i < N) dst[i] = v[it];
+        }
+    }
+};
 
 __device__ __forceinline__ v4f bias4(const float *bl, int off) {
     return *(const v4f *)(bl + off);
@@ -405,17 +416,42 @@ struct MlpLds {
 
     // Copy this mode's operands and the biases into LDS (all threads; the
     // caller synchronises before use).
+    // This thread's share of the staging as a load step and a store step
+    // (the caller synchronises before the weights are used).
+    template <int kThreads>
+    struct Staging {
+        LdsCopy<kThreads, kW4, float4> c32;
+        LdsCopy<kThreads, kBiasFloats, float> cb;
+        LdsCopy<kThreads, kMode == kMlpF16x2 ? kOps16 : 1, v8h> chi, clo;
+        LdsCopy<kThreads, kMode == kMlpBf16 ? kOps16 : 1, v8bf> c16;
+        __device__ __forceinline__ void load(const float4 *__restrict__ w32,
+                                             const v8bf *__restrict__ w16,
+                                             const v8h *__restrict__ wx2,
+                                             const float *__restrict__ bias) {
+            c32.load(w32);
+            cb.load(bias);
+            if constexpr (kMode == kMlpF16x2) {
+                chi.load(wx2);
+                clo.load(wx2 + kOps16);
+            }
+            if constexpr (kMode == kMlpBf16) c16.load(w16);
+        }
+        __device__ __forceinline__ void store(const MlpLds &M) const {
+            c32.store(M.wl);
+            cb.store(M.bl);
+            if constexpr (kMode == kMlpF16x2) {
+                chi.store(M.wh);
+                clo.store(M.wlo);
+            }
+            if constexpr (kMode == kMlpBf16) c16.store(M.wb);
+        }
+    };
     template <int kThreads>
     __device__ void stage(const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
                           const v8h *__restrict__ wx2, const float *__restrict__ bias) {
-        stage_weights<kThreads>(wl, bl, w32, bias, kW4);
-        if constexpr (kMode == kMlpF16x2)
-            for (int i = threadIdx.x; i < kOps16; i += kThreads) {
-                wh[i] = wx2[i];
-                wlo[i] = wx2[kOps16 + i];
-            }
-        if constexpr (kMode == kMlpBf16)
-            for (int i = threadIdx.x; i < kOps16; i += kThreads) wb[i] = w16[i];
+        Staging<kThreads> st;
+        st.load(w32, w16, wx2, bias);
+        st.store(*this);
     }
 
     // Two pair blocks through this mode's chain.  Returns false (for the
