@@ -480,8 +480,17 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             stage_particle(Lj, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
         }
     };
-    // the first two jets at once, so that no barrier separates them
-    for (int j = 0; j < min(nj, 2); ++j) stage_jet(j);
+    // the first two jets at once, so that no barrier separates them: thread t
+    // takes particle t % kMaxP of jet t / kMaxP
+    static_assert(kEmbedThreads == 2 * kMaxP, "one particle per thread for two jets");
+    {
+        const int j = tid / kMaxP, sl = tid % kMaxP;
+        if (j < nj && sl < P) {
+            const size_t idx = (size_t)(bS + j) * P + sl;
+            const int real = mask[idx] != 0;
+            stage_particle(Ls[j], sl, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+        }
+    }
     __syncthreads();
 
     for (int j = 0; j < nj; ++j) {
