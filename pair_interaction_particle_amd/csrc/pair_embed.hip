@@ -288,6 +288,24 @@ __device__ __forceinline__ JetInfo jet_info(const uint8_t *__restrict__ mrow, in
     }
     return j;
 }
+// The jet of a 16-lane group: lane t of the group holds 16-byte block t of the
+// mask row (t < T); every lane of the group returns the jet's info.  Call with
+// the whole wave active.
+__device__ __forceinline__ JetInfo jet_info16(uint4 v, int T) {
+    const int lane = threadIdx.x & 63, t = lane & 15;
+    const int c = t < T ? __popc(nonzero_bytes(v.x) | nonzero_bytes(v.y) << 4 |
+                                 nonzero_bytes(v.z) << 8 | nonzero_bytes(v.w) << 12)
+                        : 0;
+    JetInfo j;
+    j.act = (uint32_t)(__ballot(c != 0) >> (lane & ~15)) & 0xffffu;
+    int n = c;
+    n += __shfl_xor(n, 1);
+    n += __shfl_xor(n, 2);
+    n += __shfl_xor(n, 4);
+    n += __shfl_xor(n, 8);
+    j.n = n;
+    return j;
+}
 __device__ __forceinline__ int est_rows(int n, int ia) { return max(1, min(16, n - 16 * ia)); }
 __device__ __forceinline__ int est_diag_real(int r) { return min(5, (r * (r + 1) / 2 + 31) >> 5); }
 template <class C>
@@ -397,15 +415,39 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // the MLP weights: loads issued now, stored to LDS once the split is known
     typename MlpLds<kMode>::template Staging<kEmbedThreads> wst;
     wst.load(w32, w16, wx2, bias);
+    // Per-jet info from the mask by 16-lane groups (group g of the block takes
+    // jets g, g + 32, ..., four per round with every load of a round issued
+    // first; each load instruction reads four whole rows).  With one jet per
+    // thread (per == 1) the info goes to jinfo[jet]; else the costs are summed
+    // per thread range in scan[].
     const int per = (B + kEmbedThreads - 1) / kEmbedThreads;
-    const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
-    int cnt = 0;
-    JetInfo mine = {0u, 0};  // the thread's jet when it has one (per == 1)
-    for (int b = b0; b < b1; ++b) {
-        mine = jet_info(mask + (size_t)b * P, T);
-        cnt += jet_cost<WorkCost<kMode>>(mine);
+    jinfo[tid] = JetInfo{0u, 0};
+    scan[tid] = 0;
+    __syncthreads();
+    {
+        constexpr int kJ = 4;
+        const int grp = tid >> 4;  // 0 .. 31
+        for (int r0 = 0; r0 < B; r0 += 32 * kJ) {
+            uint4 v[kJ];
+#pragma unroll
+            for (int k = 0; k < kJ; ++k) {
+                const int b = min(r0 + grp + 32 * k, B - 1);
+                v[k] = ((const uint4 *)(mask + (size_t)b * P))[min(lane & 15, T - 1)];
+            }
+#pragma unroll
+            for (int k = 0; k < kJ; ++k) {
+                const int b = r0 + grp + 32 * k;
+                const JetInfo ji = jet_info16(v[k], T);
+                if ((lane & 15) == 0 && b < B) {
+                    if (per == 1) jinfo[b] = ji;
+                    else atomicAdd(&scan[b / per], jet_cost<WorkCost<kMode>>(ji));
+                }
+            }
+        }
     }
-    jinfo[tid] = mine;
+    __syncthreads();
+    const int cnt = per == 1 ? jet_cost<WorkCost<kMode>>(jinfo[tid]) : scan[tid];
+    __syncthreads();
     // inclusive scan of the counts: within each wave, then the wave totals
     int inc = cnt;
 #pragma unroll
