@@ -7,18 +7,17 @@
 //
 // Work decomposition (gfx950).  U is symmetric in (a, b) because every
 // feature is, so only the lower triangle of 16x16 tiles (I >= J) is computed
-// and every off-diagonal tile is written twice (direct and transposed) from
-// an LDS staging buffer.  The kernel is persistent: two 512-thread
-// workgroups per CU, each staging the packed MLP weights in LDS once and
-// taking an equal contiguous share of the real tiles of the batch (counted
-// from the mask in-kernel) plus an equal share of the all-padding tiles,
-// which only get zeros.  When its range enters a new jet a workgroup stages
-// that jet's particle kinematics (float64) in LDS.  Inside a tile the unit of
-// work is a pair block of 16 pairs = the 16 columns of one 16x16 MFMA:
-// off-diagonal tiles have 16 (one per row), diagonal tiles pack their 136
-// unique pairs into 9.  Each of the 8 waves pushes two pair blocks at a time
-// through the MFMA layer chain; hidden activations never leave registers.
-// The U tile is double buffered in LDS, so a tile costs one barrier.
+// and every value is written twice (U[a][b] and U[b][a]) straight from
+// registers.  The kernel is persistent: two 512-thread workgroups per CU, each
+// staging the packed MLP weights in LDS once and taking an equal share of the
+// batch's estimated work (counted from the mask in-kernel) plus an equal share
+// of the all-padding tiles, which only get zeros.  A workgroup stages the
+// particle kinematics (float64) of the jets its share touches in LDS, two jets
+// at a time.  Inside a tile the unit of work is a pair block of 16 pairs = the
+// 16 columns of one 16x16 MFMA: off-diagonal tiles have 16 (one per row),
+// diagonal tiles pack their 136 unique pairs into 9 (plus an empty 10th).
+// Each of the 8 waves pushes two pair blocks at a time through the MFMA layer
+// chain; hidden activations never leave registers.
 #include <algorithm>
 #include <type_traits>
 
@@ -376,10 +375,10 @@ __device__ __forceinline__ int jet_blocks(uint32_t act) { return blocks_before_r
 // tile order, weighted by the estimate above) is counted from the mask; a
 // block-wide scan gives every workgroup an equal contiguous share, split at
 // pair-block granularity (the two workgroups of a CU then carry a like load).
-// All-padding tiles are split evenly too and only get zeros.  Within a jet the workgroup's tiles are
-// dealt to its 8 waves round robin; each wave runs its tiles alone (no
-// barrier between tiles) and writes U straight from registers, so waves
-// drift apart and hide each other's latencies.  Workgroup w is remapped so
+// All-padding tiles are split evenly too and only get zeros.  The 8 waves
+// claim the iterations (pairs of blocks) of each jet from a counter in LDS and
+// run them alone (no barrier between iterations, none between the first two
+// jets), writing U straight from registers.  Workgroup w is remapped so
 // that the workgroups of one XCD (dispatch is round-robin over 8 XCDs) hold
 // adjacent ranges and thus write neighbouring parts of U.
 template <int kMode>
@@ -392,6 +391,8 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     __shared__ PartLds<kMaxP> Ls[2];  // the particles of two jets
     __shared__ int scan[kEmbedThreads];
     __shared__ JetInfo jinfo[kEmbedThreads];
+    __shared__ int work_next[2];  // next unclaimed iteration of the jet in each slot
+    __shared__ int work_fail;     // a wave's fp16 x 2 results were not all finite
 
     // pair (i, j), j <= i, of slot p of a diagonal tile's triangle packing
     // as i << 4 | j; the unused slots 136..159 hold kNoPair (i = 0, j = 15),
@@ -522,6 +523,10 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             stage_particle(Lj, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
         }
     };
+    if (tid == 0) {
+        work_next[0] = work_next[1] = kEmbedWaves;  // iteration w opens wave w's claims
+        work_fail = 0;
+    }
     // the first two jets at once, so that no barrier separates them: thread t
     // takes particle t % kMaxP of jet t / kMaxP
     static_assert(kEmbedThreads == 2 * kMaxP, "one particle per thread for two jets");
@@ -535,84 +540,101 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     }
     __syncthreads();
 
-    for (int j = 0; j < nj; ++j) {
+    // One jet of the range: its pair blocks [q0, q1), flattened into wave
+    // iterations of two blocks; the tile walk is wave-uniform (scalar
+    // registers).  Fast pass (fp16 x 2 or bf16): iterations claimed from the
+    // slot's counter, so the waves finish together; exact pass: a fixed deal
+    // in which round r gives wave w iteration 8 r + (w - r) mod 8.
+    auto run_jet = [&](int j, auto exact_t) {
+        constexpr bool kExact = decltype(exact_t)::value;
         const int b = bS + j;
-        if (j >= 2) {  // a third jet reuses slot j & 1: wait for jet j - 2
-            __syncthreads();
-            stage_jet(j);
-            __syncthreads();
-        }
         const PartLds<kMaxP> &L = Ls[j & 1];
         const uint32_t act = b == bS ? js.act : b == bE ? je.act : jet_activity(mask + (size_t)b * P, T);
         const int q0 = b == bS ? qS : 0, q1 = b == bE ? qE : jet_blocks(act);
-        if (q1 <= q0) continue;
-        {
-            OutT *U = (OutT *)Uout + (size_t)b * kHeads * P * P;
-            // the range's pair blocks, flattened, dealt to the waves in pairs;
-            // the tile walk is wave-uniform (scalar registers)
-            const uint64_t aidx = active_index(act);
-            auto sweep = [&](auto exact_t) {
-                constexpr bool kExact = decltype(exact_t)::value;
-                bool ok = true;
-                // round r gives wave w iteration 8 r + (w - r) mod 8: the
-                // position inside a tile rotates, so no wave keeps taking the
-                // all-padding rows at the end of partly real tiles
-                const int nit = (q1 - q0) >> 1;
-                int ia = block_row(q0);
-                for (int r = 0; 8 * r < nit; ++r) {
-                    const int it = 8 * r + ((wv - r) & (kEmbedWaves - 1));
-                    if (it >= nit) continue;
-                    const int q = q0 + 2 * it;
-                    int rem = q - blocks_before_row(ia);
-                    // Compiler-only memory barrier (emits nothing): keeps the
-                    // loop-invariant LDS weight reads inside the loop instead
-                    // of hoisting 144+ registers of operands out of it.
-                    __asm__ volatile("" ::: "memory");
-                    while (rem >= 16 * ia + 10) {  // rows have 16 ia + 10 blocks
-                        rem -= 16 * ia + 10;
-                        ++ia;
-                    }
-                    const int ja = min(rem >> 4, ia), kb = rem - 16 * ja;
-                    const int I = nth_active(aidx, ia), J = nth_active(aidx, ja);
-                    const bool diag = ia == ja;
-                    // this lane's pairs (tile-local rows / columns) of blocks kb, kb+1
-                    int iA = kb, jA = lane & 15, iB = kb + 1, jB = lane & 15;
-                    bool vA = true, vB = true;
-                    if (diag) {
-                        const int eA = diagPair[16 * kb + (lane & 15)];
-                        const int eB = diagPair[16 * kb + 16 + (lane & 15)];
-                        vA = eA != kNoPair;
-                        vB = eB != kNoPair;
-                        iA = vA ? eA >> 4 : 0;
-                        jA = vA ? eA & 15 : 0;
-                        iB = vB ? eB >> 4 : 0;
-                        jB = vB ? eB & 15 : 0;
-                    }
-                    const int aA = I * kTile + iA, bA = J * kTile + jA;
-                    const int aB = I * kTile + iB, bB = J * kTile + jB;
-                    const bool realA = vA && L.real[aA] && L.real[bA];
-                    const bool realB = vB && L.real[aB] && L.real[bB];
-                    v4f uA = {0.f, 0.f, 0.f, 0.f}, uB = uA;
-                    const bool any = __ballot(realA || realB) != 0;
-                    if (any) {
-                        const int f = lane >> 4;
-                        const float fA = realA ? pair_feature(L, aA, bA, f) : 0.0f;
-                        const float fB = realB ? pair_feature(L, aB, bB, f) : 0.0f;
-                        if constexpr (kExact) M.run_exact(w32, fA, fB, uA, uB);
-                        else ok = M.run(fA, fB, uA, uB) && ok;
-                    }
-                    if (!diag) {  // rows kb, kb + 1 of one off-diagonal tile
-                        write_row_pair<OutT>(L, U, P, aA, bA, uA, uB, !any);
-                    } else {
-                        write_block<OutT>(L, U, P, I, J, vA, iA, jA, uA, !any);
-                        write_block<OutT>(L, U, P, I, J, vB, iB, jB, uB, !any);
-                    }
-                }
-                return ok;
-            };
-            // A wave whose fp16 x 2 results were not all finite redoes its
-            // share of this jet exactly (its later stores replace the earlier).
-            if (!sweep(std::false_type{})) sweep(std::true_type{});
+        const int nit = max(0, (q1 - q0) >> 1);
+        OutT *U = (OutT *)Uout + (size_t)b * kHeads * P * P;
+        const uint64_t aidx = active_index(act);
+        bool ok = true;
+        int ia = block_row(max(q0, 0));
+        int it = wv, r = 0;
+        while (kExact ? 8 * r < nit : it < nit) {
+            int itn = 0;
+            if constexpr (kExact) {
+                it = 8 * r + ((wv - r) & (kEmbedWaves - 1));
+                ++r;
+                if (it >= nit) continue;
+            } else if (lane == 0) {
+                itn = atomicAdd(&work_next[j & 1], 1);  // the next claim, early
+            }
+            const int q = q0 + 2 * it;
+            int rem = q - blocks_before_row(ia);
+            // Compiler-only memory barrier (emits nothing): keeps the
+            // loop-invariant LDS weight reads inside the loop instead of
+            // hoisting 144+ registers of operands out of it.
+            __asm__ volatile("" ::: "memory");
+            while (rem >= 16 * ia + 10) {  // rows have 16 ia + 10 blocks
+                rem -= 16 * ia + 10;
+                ++ia;
+            }
+            const int ja = min(rem >> 4, ia), kb = rem - 16 * ja;
+            const int I = nth_active(aidx, ia), J = nth_active(aidx, ja);
+            const bool diag = ia == ja;
+            // this lane's pairs (tile-local rows / columns) of blocks kb, kb+1
+            int iA = kb, jA = lane & 15, iB = kb + 1, jB = lane & 15;
+            bool vA = true, vB = true;
+            if (diag) {
+                const int eA = diagPair[16 * kb + (lane & 15)];
+                const int eB = diagPair[16 * kb + 16 + (lane & 15)];
+                vA = eA != kNoPair;
+                vB = eB != kNoPair;
+                iA = vA ? eA >> 4 : 0;
+                jA = vA ? eA & 15 : 0;
+                iB = vB ? eB >> 4 : 0;
+                jB = vB ? eB & 15 : 0;
+            }
+            const int aA = I * kTile + iA, bA = J * kTile + jA;
+            const int aB = I * kTile + iB, bB = J * kTile + jB;
+            const bool realA = vA && L.real[aA] && L.real[bA];
+            const bool realB = vB && L.real[aB] && L.real[bB];
+            v4f uA = {0.f, 0.f, 0.f, 0.f}, uB = uA;
+            const bool any = __ballot(realA || realB) != 0;
+            if (any) {
+                const int f = lane >> 4;
+                const float fA = realA ? pair_feature(L, aA, bA, f) : 0.0f;
+                const float fB = realB ? pair_feature(L, aB, bB, f) : 0.0f;
+                if constexpr (kExact) M.run_exact(w32, fA, fB, uA, uB);
+                else ok = M.run(fA, fB, uA, uB) && ok;
+            }
+            if (!diag) {  // rows kb, kb + 1 of one off-diagonal tile
+                write_row_pair<OutT>(L, U, P, aA, bA, uA, uB, !any);
+            } else {
+                write_block<OutT>(L, U, P, I, J, vA, iA, jA, uA, !any);
+                write_block<OutT>(L, U, P, I, J, vB, iB, jB, uB, !any);
+            }
+            if constexpr (!kExact) it = __builtin_amdgcn_readfirstlane(itn);
+        }
+        return ok;
+    };
+    bool ok = true;
+    for (int j = 0; j < nj; ++j) {
+        if (j >= 2) {  // a third jet reuses slot j & 1: wait for jet j - 2
+            __syncthreads();
+            stage_jet(j);
+            if (tid == 0) work_next[j & 1] = kEmbedWaves;
+            __syncthreads();
+        }
+        ok = run_jet(j, std::false_type{}) && ok;
+    }
+    // When a wave's fp16 x 2 results were not all finite, the workgroup redoes
+    // its range exactly (the later stores replace the earlier ones).
+    if (!ok && lane == 0) work_fail = 1;
+    __syncthreads();
+    if (work_fail) {
+        for (int j = 0; j < nj; ++j) {
+            __syncthreads();
+            stage_jet(j);
+            __syncthreads();
+            run_jet(j, std::true_type{});
         }
     }
 
