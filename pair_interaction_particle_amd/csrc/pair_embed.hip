@@ -549,7 +549,10 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         constexpr bool kExact = decltype(exact_t)::value;
         const int b = bS + j;
         const PartLds<kMaxP> &L = Ls[j & 1];
-        const uint32_t act = b == bS ? js.act : b == bE ? je.act : jet_activity(mask + (size_t)b * P, T);
+        const uint32_t act = b == bS   ? js.act
+                             : b == bE ? je.act
+                             : per == 1 ? jinfo[b].act
+                                        : jet_activity(mask + (size_t)b * P, T);
         const int q0 = b == bS ? qS : 0, q1 = b == bE ? qE : jet_blocks(act);
         const int nit = max(0, (q1 - q0) >> 1);
         OutT *U = (OutT *)Uout + (size_t)b * kHeads * P * P;
@@ -649,7 +652,7 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             const int bb = (int)(z / ntri), t = (int)(z - (long)bb * ntri);
             if (bb != bz) {
                 bz = bb;
-                actz = jet_activity(mask + (size_t)bb * P, T);
+                actz = per == 1 ? jinfo[bb].act : jet_activity(mask + (size_t)bb * P, T);
             }
             const int I = tri_row(t), J = t - I * (I + 1) / 2;
             if ((actz >> I & 1) && (actz >> J & 1)) continue;
