@@ -292,9 +292,11 @@ __device__ __forceinline__ JetInfo jet_info(const uint8_t *__restrict__ mrow, in
 // the whole wave active.
 __device__ __forceinline__ JetInfo jet_info16(uint4 v, int T) {
     const int lane = threadIdx.x & 63, t = lane & 15;
-    const int c = t < T ? __popc(nonzero_bytes(v.x) | nonzero_bytes(v.y) << 4 |
-                                 nonzero_bytes(v.z) << 8 | nonzero_bytes(v.w) << 12)
-                        : 0;
+    // (computed for every lane and then scaled, so that the load it depends on
+    // is not sunk into a branch, which would make the wait counter drain)
+    const int c = __popc(nonzero_bytes(v.x) | nonzero_bytes(v.y) << 4 | nonzero_bytes(v.z) << 8 |
+                         nonzero_bytes(v.w) << 12) *
+                  (int)(t < T);
     JetInfo j;
     j.act = (uint32_t)(__ballot(c != 0) >> (lane & ~15)) & 0xffffu;
     int n = c;
@@ -413,14 +415,14 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // ---- this workgroup's equal share of the estimated work: a block scan of
     // the per-jet costs (each thread sums the jets of its range), split at
     // iteration granularity
-    // the MLP weights: loads issued now, stored to LDS once the split is known
-    typename MlpLds<kMode>::template Staging<kEmbedThreads> wst;
-    wst.load(w32, w16, wx2, bias);
     // Per-jet info from the mask by 16-lane groups (group g of the block takes
     // jets g, g + 32, ..., four per round with every load of a round issued
     // first; each load instruction reads four whole rows).  With one jet per
     // thread (per == 1) the info goes to jinfo[jet]; else the costs are summed
-    // per thread range in scan[].
+    // per thread range in scan[].  The MLP weight loads are issued right after
+    // the first round's mask loads (the wait counter drains in order, so the
+    // mask values need not wait for them) and stored to LDS after the split.
+    typename MlpLds<kMode>::template Staging<kEmbedThreads> wst;
     const int per = (B + kEmbedThreads - 1) / kEmbedThreads;
     jinfo[tid] = JetInfo{0u, 0};
     scan[tid] = 0;
@@ -428,13 +430,14 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     {
         constexpr int kJ = 4;
         const int grp = tid >> 4;  // 0 .. 31
-        for (int r0 = 0; r0 < B; r0 += 32 * kJ) {
-            uint4 v[kJ];
+        auto round_loads = [&](int r0, uint4 (&v)[kJ]) {
 #pragma unroll
             for (int k = 0; k < kJ; ++k) {
                 const int b = min(r0 + grp + 32 * k, B - 1);
                 v[k] = ((const uint4 *)(mask + (size_t)b * P))[min(lane & 15, T - 1)];
             }
+        };
+        auto round_info = [&](int r0, const uint4 (&v)[kJ]) {
 #pragma unroll
             for (int k = 0; k < kJ; ++k) {
                 const int b = r0 + grp + 32 * k;
@@ -444,6 +447,15 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
                     else atomicAdd(&scan[b / per], jet_cost<WorkCost<kMode>>(ji));
                 }
             }
+        };
+        uint4 v[kJ];
+        round_loads(0, v);
+        __asm__ volatile("" ::: "memory");  // (issue order: mask rows, then weights)
+        wst.load(w32, w16, wx2, bias);
+        round_info(0, v);
+        for (int r0 = 32 * kJ; r0 < B; r0 += 32 * kJ) {
+            round_loads(r0, v);
+            round_info(r0, v);
         }
     }
     __syncthreads();
