@@ -531,8 +531,13 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         PartLds<kMaxP> &Lj = Ls[j & 1];
         for (int s = tid; s < P; s += kEmbedThreads) {
             const size_t idx = (size_t)b * P + s;
-            const int real = mask[idx] != 0;
-            stage_particle(Lj, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+            // both loads issued before either is used (a load under the mask
+            // test would be a second round trip)
+            const float4 pv = p4[idx];
+            const uint8_t mb = mask[idx];
+            __asm__ volatile("" ::: "memory");
+            const int real = mb != 0;
+            stage_particle(Lj, s, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
         }
     };
     if (tid == 0) {
@@ -546,8 +551,11 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         const int j = tid / kMaxP, sl = tid % kMaxP;
         if (j < nj && sl < P) {
             const size_t idx = (size_t)(bS + j) * P + sl;
-            const int real = mask[idx] != 0;
-            stage_particle(Ls[j], sl, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+            const float4 pv = p4[idx];  // both loads issued before either is used
+            const uint8_t mb = mask[idx];
+            __asm__ volatile("" ::: "memory");
+            const int real = mb != 0;
+            stage_particle(Ls[j], sl, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
         }
     }
     __syncthreads();
