@@ -182,8 +182,11 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
     // ---- stage particles, weights, state
     for (int s = tid; s < P; s += kJetThreads) {
         const size_t idx = (size_t)jet * P + s;
-        const int real = mask[idx] != 0;
-        stage_particle(L, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+        const float4 pv = p4[idx];  // both loads issued before either is used
+        const uint8_t mb = mask[idx];
+        __asm__ volatile("" ::: "memory");
+        const int real = mb != 0;
+        stage_particle(L, s, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
     }
     M.template stage<kJetThreads>(w32, w16, wx2, bias);
     for (int i = tid; i < kHeads * T * 64; i += kJetThreads)
@@ -307,8 +310,11 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
 
     for (int s = tid; s < P; s += kRowThreads) {
         const size_t idx = (size_t)jet * P + s;
-        const int real = mask[idx] != 0;
-        stage_particle(L, s, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+        const float4 pv = p4[idx];  // both loads issued before either is used
+        const uint8_t mb = mask[idx];
+        __asm__ volatile("" ::: "memory");
+        const int real = mb != 0;
+        stage_particle(L, s, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
     }
     __syncthreads();
     if (tid < T) {

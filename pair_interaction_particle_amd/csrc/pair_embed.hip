@@ -44,8 +44,11 @@ __device__ inline void stage_tile(PartLds<32> &L, const float4 *__restrict__ p4,
     if (t < 32) {
         const int part = (t < 16) ? (I * kTile + t) : (J * kTile + t - 16);
         const size_t idx = (size_t)jet * P + part;
-        const int real = mask[idx] != 0;
-        stage_particle(L, t, real ? p4[idx] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+        const float4 pv = p4[idx];  // both loads issued before either is used
+        const uint8_t mb = mask[idx];
+        __asm__ volatile("" ::: "memory");
+        const int real = mb != 0;
+        stage_particle(L, t, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
     }
 }
 
