@@ -127,12 +127,18 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
         for (int i = tid; i <= P + 1; i += kJetThreads) hist[i] = 0;
         __syncthreads();
         for (int b = tid; b < B; b += kJetThreads) {
+            // every load of the row issued before the first is used
+            // (addresses clamped into the row; blocks past P / 16 not counted)
             const uint4 *row = (const uint4 *)(mask + (size_t)b * P);
+            uint4 v[kJetMaxT];
+#pragma unroll
+            for (int w = 0; w < kJetMaxT; ++w) v[w] = row[min(w, P / 16 - 1)];
             int n = 0;
-            for (int w = 0; w < P / 16; ++w) {
-                const uint4 v = row[w];
-                n += nz_bytes(v.x) + nz_bytes(v.y) + nz_bytes(v.z) + nz_bytes(v.w);
-            }
+#pragma unroll
+            for (int w = 0; w < kJetMaxT; ++w)
+                n += w < P / 16
+                         ? nz_bytes(v[w].x) + nz_bytes(v[w].y) + nz_bytes(v[w].z) + nz_bytes(v[w].w)
+                         : 0;
             nj[b] = (uint16_t)n;
             atomicAdd(&hist[n], 1);
         }
