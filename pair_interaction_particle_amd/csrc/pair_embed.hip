@@ -483,16 +483,20 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     __syncthreads();
     scan[tid] = before + inc;
     __syncthreads();
-    const long total = totw;
     // split point i: the first iteration whose cost prefix reaches
-    // total (w + i) / W, as the jet and the cost left inside it; jet B at the end
+    // floor(totw (w + i) / W), as the jet and the cost left inside it; jet B
+    // at the end.  (totw = W qt + rt, so the floor is qt (w + i) + floor(rt
+    // (w + i) / W) in 32 bits; a 64-bit division here costs a long scalar
+    // sequence and a register spill whose reload waits for every load in
+    // flight.)
+    const int qt = totw / W, rt = totw - qt * W;
     int sb[2], st[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int t = (int)(total * (w + i) / W);
+        const int t = qt * (w + i) + rt * (w + i) / W;
         sb[i] = B;
         st[i] = 0;
-        if (t >= total) continue;
+        if (t >= totw) continue;
         // the first thread whose inclusive prefix exceeds t (the prefix does
         // not decrease, so that is the number of prefixes at or below t)
         const int c = __syncthreads_count(scan[tid] <= t);
@@ -667,12 +671,13 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // ---- tiles without a real pair: zeros (after the real tiles, so these
     // stores overlap the other workgroups' work; jet activity read once per jet)
     {
-        const long tot = (long)B * ntri;
-        const long z1 = tot * (w + 1) / W;
+        // tiles [tot w / W, tot (w + 1) / W), floors taken in 32 bits as above
+        const int tot = B * ntri, qz = tot / W, rz = tot - qz * W;
+        const int z1 = qz * (w + 1) + rz * (w + 1) / W;
         int bz = -1;
         uint32_t actz = 0;
-        for (long z = tot * w / W; z < z1; ++z) {
-            const int bb = (int)(z / ntri), t = (int)(z - (long)bb * ntri);
+        for (int z = qz * w + rz * w / W; z < z1; ++z) {
+            const int bb = z / ntri, t = z - bb * ntri;
             if (bb != bz) {
                 bz = bb;
                 actz = per == 1 ? jinfo[bb].act : jet_activity(mask + (size_t)bb * P, T);
