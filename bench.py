@@ -204,8 +204,11 @@ def bench_extra(pip, synth, reps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU needs ~40 ms of continuous load to reach its steady clocks
+    # (pair_embed runs ~75 us per call in the first milliseconds, ~64 us
+    # after); 500 warmup steps are ~45 ms.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -285,7 +288,8 @@ def main():
         "real_ordered_pairs": ordered,
     }
     if not args.no_extra:
-        res["workloads"] = bench_extra(pip, synth, max(10, args.steps // 2), 3)
+        res["workloads"] = bench_extra(pip, synth, max(10, args.steps // 2),
+                                       max(3, args.warmup // 2))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
     else:
