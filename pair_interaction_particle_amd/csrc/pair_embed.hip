@@ -91,13 +91,13 @@ __device__ __forceinline__ void store4(uint16_t *U, uint32_t off, const float (&
 
 constexpr int kEmbedThreads = 512;
 constexpr int kEmbedWaves = kEmbedThreads / 64;
+constexpr int kWgPerCu = 1024 / kEmbedThreads;
 static_assert((kEmbedWaves & (kEmbedWaves - 1)) == 0, "the sweep rotates waves modulo a power of two");
 
-// Zero tile (I, J) of every head and, if I != J, its transpose (J, I): one
-// 16-byte store per thread and direction.
+// Zero tile (I, J) of every head and, if I != J, its transpose (J, I), by
+// 512 threads (t = 0 .. 511): one 16-byte store per thread and direction.
 template <typename OutT>
-__device__ inline void zero_tile(OutT *U, int P, int I, int J) {
-    const int tid = threadIdx.x;
+__device__ inline void zero_tile(OutT *U, int P, int I, int J, int tid) {
     const float z[4] = {0.f, 0.f, 0.f, 0.f};
     const int h = tid >> 6, i = (tid >> 2) & 15, j0 = (tid & 3) * 4;
     store4(U, ((uint32_t)h * P + I * kTile + i) * P + J * kTile + j0, z);
@@ -432,18 +432,19 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     __syncthreads();
     {
         constexpr int kJ = 4;
-        const int grp = tid >> 4;  // 0 .. 31
+        constexpr int kGroups = kEmbedThreads / 16;
+        const int grp = tid >> 4;  // 0 .. kGroups - 1
         auto round_loads = [&](int r0, uint4 (&v)[kJ]) {
 #pragma unroll
             for (int k = 0; k < kJ; ++k) {
-                const int b = min(r0 + grp + 32 * k, B - 1);
+                const int b = min(r0 + grp + kGroups * k, B - 1);
                 v[k] = ((const uint4 *)(mask + (size_t)b * P))[min(lane & 15, T - 1)];
             }
         };
         auto round_info = [&](int r0, const uint4 (&v)[kJ]) {
 #pragma unroll
             for (int k = 0; k < kJ; ++k) {
-                const int b = r0 + grp + 32 * k;
+                const int b = r0 + grp + kGroups * k;
                 const JetInfo ji = jet_info16(v[k], T);
                 if ((lane & 15) == 0 && b < B) {
                     if (per == 1) jinfo[b] = ji;
@@ -456,7 +457,7 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         __asm__ volatile("" ::: "memory");  // (issue order: mask rows, then weights)
         wst.load(w32, w16, wx2, bias);
         round_info(0, v);
-        for (int r0 = 32 * kJ; r0 < B; r0 += 32 * kJ) {
+        for (int r0 = kGroups * kJ; r0 < B; r0 += kGroups * kJ) {
             round_loads(r0, v);
             round_info(r0, v);
         }
@@ -553,10 +554,10 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     }
     // the first two jets at once, so that no barrier separates them: thread t
     // takes particle t % kMaxP of jet t / kMaxP
-    static_assert(kEmbedThreads == 2 * kMaxP, "one particle per thread for two jets");
+    static_assert(kEmbedThreads >= 2 * kMaxP, "one particle per thread for two jets");
     {
         const int j = tid / kMaxP, sl = tid % kMaxP;
-        if (j < nj && sl < P) {
+        if (j < min(nj, 2) && sl < P) {
             const size_t idx = (size_t)(bS + j) * P + sl;
             const float4 pv = p4[idx];  // both loads issued before either is used
             const uint8_t mb = mask[idx];
@@ -571,7 +572,8 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // iterations of two blocks; the tile walk is wave-uniform (scalar
     // registers).  Fast pass (fp16 x 2 or bf16): iterations claimed from the
     // slot's counter, so the waves finish together; exact pass: a fixed deal
-    // in which round r gives wave w iteration 8 r + (w - r) mod 8.
+    // in which round r gives wave w iteration kEmbedWaves r + (w - r) mod
+    // kEmbedWaves.
     auto run_jet = [&](int j, auto exact_t) {
         constexpr bool kExact = decltype(exact_t)::value;
         const int b = bS + j;
@@ -587,10 +589,10 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         bool ok = true;
         int ia = block_row(max(q0, 0));
         int it = wv, r = 0;
-        while (kExact ? 8 * r < nit : it < nit) {
+        while (kExact ? kEmbedWaves * r < nit : it < nit) {
             int itn = 0;
             if constexpr (kExact) {
-                it = 8 * r + ((wv - r) & (kEmbedWaves - 1));
+                it = kEmbedWaves * r + ((wv - r) & (kEmbedWaves - 1));
                 ++r;
                 if (it >= nit) continue;
             } else if (lane == 0) {
@@ -674,9 +676,14 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         // tiles [tot w / W, tot (w + 1) / W), floors taken in 32 bits as above
         const int tot = B * ntri, qz = tot / W, rz = tot - qz * W;
         const int z1 = qz * (w + 1) + rz * (w + 1) / W;
+        // each 512 threads take one tile per step (the half is wave-uniform)
+        constexpr int kZPar = kEmbedThreads / 512;
+        static_assert(kEmbedThreads % 512 == 0, "zero tiles are written by 512 threads");
         int bz = -1;
         uint32_t actz = 0;
-        for (int z = qz * w + rz * w / W; z < z1; ++z) {
+        for (int z0 = qz * w + rz * w / W; z0 < z1; z0 += kZPar) {
+            const int z = z0 + tid / 512;
+            if (z >= z1) continue;
             const int bb = z / ntri, t = z - bb * ntri;
             if (bb != bz) {
                 bz = bb;
@@ -684,12 +691,13 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             }
             const int I = tri_row(t), J = t - I * (I + 1) / 2;
             if ((actz >> I & 1) && (actz >> J & 1)) continue;
-            zero_tile<OutT>((OutT *)Uout + (size_t)bb * kHeads * P * P, P, I, J);
+            zero_tile<OutT>((OutT *)Uout + (size_t)bb * kHeads * P * P, P, I, J, tid % 512);
         }
     }
 }
 
-// Two resident 512-thread workgroups per CU (the LDS budget allows two).
+// kWgPerCu resident workgroups per CU (16 waves: 4 per SIMD at the kernel's
+// register budget).
 static int persistent_grid(int B, int P) {
     static int cus[64];
     int dev = 0;
@@ -702,7 +710,7 @@ static int persistent_grid(int B, int P) {
         cus[dev] = n;
     }
     const long T = P / kTile, tiles = (long)B * T * (T + 1) / 2;
-    return (int)std::min<long>(2L * cus[dev], std::max<long>(tiles, 1));
+    return (int)std::min<long>((long)kWgPerCu * cus[dev], std::max<long>(tiles, 1));
 }
 
 // Batches are cut into segments of at most 65,536 jets so that tile counts
