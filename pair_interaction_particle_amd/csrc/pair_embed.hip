@@ -398,6 +398,8 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     __shared__ JetInfo jinfo[kEmbedThreads];
     __shared__ int work_next[2];  // next unclaimed iteration of the jet in each slot
     __shared__ int work_fail;     // a wave's fp16 x 2 results were not all finite
+    __shared__ int split_out[4];  // first and end jet, first and end pair block
+    __shared__ JetInfo split_jet[2];
 
     // pair (i, j), j <= i, of slot p of a diagonal tile's triangle packing
     // as i << 4 | j; the unused slots 136..159 hold kNoPair (i = 0, j = 15),
@@ -463,74 +465,92 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         }
     }
     __syncthreads();
-    const int cnt = per == 1 ? jet_cost<WorkCost<kMode>>(jinfo[tid]) : scan[tid];
+    // the cost of each thread's entry (its jet, or its range of jets)
+    if (per == 1) scan[tid] = jet_cost<WorkCost<kMode>>(jinfo[tid]);
     __syncthreads();
-    // inclusive scan of the counts: within each wave, then the wave totals
-    int inc = cnt;
+    // Wave 0 scans the kEmbedThreads entry costs (kPerLane per lane) and finds
+    // both split points; the other waves store the MLP weights meanwhile.
+    // Split point i: the first iteration whose cost prefix reaches
+    // floor(totw (w + i) / W), as the jet and the cost left inside it (jet B
+    // at the end).  With totw = W qt + rt that floor is qt (w + i) +
+    // floor(rt (w + i) / W), exact in 32 bits (a 64-bit division costs a long
+    // scalar sequence and a register spill whose reload waits for every load
+    // in flight).
+    if (wv == 0) {
+        constexpr int kPerLane = kEmbedThreads / 64;
+        int cst[kPerLane], sum = 0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(inc, off);
-        inc += lane >= off ? v : 0;
-    }
-    if (lane == 63) scan[wv] = inc;
-    __syncthreads();
-    int before = 0, totw = 0;
-#pragma unroll
-    for (int k = 0; k < kEmbedWaves; ++k) {
-        const int v = scan[k];
-        before += k < wv ? v : 0;
-        totw += v;
-    }
-    __syncthreads();
-    scan[tid] = before + inc;
-    __syncthreads();
-    // split point i: the first iteration whose cost prefix reaches
-    // floor(totw (w + i) / W), as the jet and the cost left inside it; jet B
-    // at the end.  (totw = W qt + rt, so the floor is qt (w + i) + floor(rt
-    // (w + i) / W) in 32 bits; a 64-bit division here costs a long scalar
-    // sequence and a register spill whose reload waits for every load in
-    // flight.)
-    const int qt = totw / W, rt = totw - qt * W;
-    int sb[2], st[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int t = qt * (w + i) + rt * (w + i) / W;
-        sb[i] = B;
-        st[i] = 0;
-        if (t >= totw) continue;
-        // the first thread whose inclusive prefix exceeds t (the prefix does
-        // not decrease, so that is the number of prefixes at or below t)
-        const int c = __syncthreads_count(scan[tid] <= t);
-        sb[i] = c * per;
-        st[i] = t - (c ? scan[c - 1] : 0);
-    }
-    // the jets at the split points: from LDS when every thread has one jet,
-    // else walked from the first jet of the split thread's range
-    JetInfo js = {0u, 0}, je = {0u, 0};
-    if (per == 1) {
-        if (sb[0] < B) js = jinfo[sb[0]];
-        if (sb[1] < B) je = jinfo[sb[1]];
-    } else {
-        js = sb[0] < B ? jet_info(mask + (size_t)sb[0] * P, T) : JetInfo{0u, 0};
-        je = sb[1] < B ? jet_info(mask + (size_t)sb[1] * P, T) : JetInfo{0u, 0};
-        for (int jc = jet_cost<WorkCost<kMode>>(js); sb[0] < B && st[0] >= jc;
-             jc = jet_cost<WorkCost<kMode>>(js)) {
-            st[0] -= jc;
-            ++sb[0];
-            js = jet_info(mask + (size_t)min(sb[0], B - 1) * P, T);
+        for (int e = 0; e < kPerLane; ++e) {
+            cst[e] = scan[kPerLane * lane + e];
+            sum += cst[e];
         }
-        for (int jc = jet_cost<WorkCost<kMode>>(je); sb[1] < B && st[1] >= jc;
-             jc = jet_cost<WorkCost<kMode>>(je)) {
-            st[1] -= jc;
-            ++sb[1];
-            je = jet_info(mask + (size_t)min(sb[1], B - 1) * P, T);
+        int inc = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(inc, off);
+            inc += lane >= off ? v : 0;
+        }
+        const int totw = __shfl(inc, 63), excl = inc - sum;
+        const int qt = totw / W, rt = totw - qt * W;
+        int sb[2], st[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = qt * (w + i) + rt * (w + i) / W;
+            // entries of this lane whose inclusive prefix is at most t (the
+            // prefix does not decrease, so they come first), and the prefix
+            // before the next one
+            int k = 0, pre = excl, run = excl;
+#pragma unroll
+            for (int e = 0; e < kPerLane; ++e) {
+                run += cst[e];
+                const bool below = run <= t;
+                k += below;
+                pre = below ? run : pre;
+            }
+            // the first lane whose inclusive prefix exceeds t holds the entry
+            const int L = __popcll(__ballot(inc <= t));
+            sb[i] = B;
+            st[i] = 0;
+            if (t < totw) {
+                sb[i] = (kPerLane * L + __shfl(k, L)) * per;
+                st[i] = t - __shfl(pre, L);
+            }
+        }
+        // the jets at the split points: from LDS when every thread has one
+        // jet, else walked from the first jet of the split entry's range
+        JetInfo js = {0u, 0}, je = {0u, 0};
+        if (per == 1) {
+            if (sb[0] < B) js = jinfo[sb[0]];
+            if (sb[1] < B) je = jinfo[sb[1]];
+        } else {
+            js = sb[0] < B ? jet_info(mask + (size_t)sb[0] * P, T) : JetInfo{0u, 0};
+            je = sb[1] < B ? jet_info(mask + (size_t)sb[1] * P, T) : JetInfo{0u, 0};
+            for (int jc = jet_cost<WorkCost<kMode>>(js); sb[0] < B && st[0] >= jc;
+                 jc = jet_cost<WorkCost<kMode>>(js)) {
+                st[0] -= jc;
+                ++sb[0];
+                js = jet_info(mask + (size_t)min(sb[0], B - 1) * P, T);
+            }
+            for (int jc = jet_cost<WorkCost<kMode>>(je); sb[1] < B && st[1] >= jc;
+                 jc = jet_cost<WorkCost<kMode>>(je)) {
+                st[1] -= jc;
+                ++sb[1];
+                je = jet_info(mask + (size_t)min(sb[1], B - 1) * P, T);
+            }
+        }
+        if (lane == 0) {
+            split_out[0] = sb[0];
+            split_out[1] = sb[1];
+            split_out[2] = sb[0] < B ? jet_split<WorkCost<kMode>>(js, st[0]) : 0;
+            split_out[3] = sb[1] < B ? jet_split<WorkCost<kMode>>(je, st[1]) : 0;
+            split_jet[0] = js;
+            split_jet[1] = je;
         }
     }
-    const int bS = sb[0], bE = sb[1];
-    const int qS = bS < B ? jet_split<WorkCost<kMode>>(js, st[0]) : 0;
-    const int qE = bE < B ? jet_split<WorkCost<kMode>>(je, st[1]) : 0;
-
     wst.store(M);
+    __syncthreads();
+    const int bS = split_out[0], bE = split_out[1], qS = split_out[2], qE = split_out[3];
+    const JetInfo js = split_jet[0], je = split_jet[1];
     const int nj = bE - bS + (qE > 0 ? 1 : 0);  // jets this workgroup visits
 
     // the particles of jet j of the range into slot j & 1 (all threads)
