@@ -391,7 +391,7 @@ __global__ __launch_bounds__(kEmbedThreads) __attribute__((amdgpu_waves_per_eu(4
 void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B,
                        int P, const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
                        const v8h *__restrict__ wx2, const float *__restrict__ bias,
-                       void *__restrict__ Uout) {
+                       void *__restrict__ Uout, int wz) {
     MlpLds<kMode> M;
     __shared__ PartLds<kMaxP> Ls[2];  // the particles of two jets
     __shared__ int scan[kEmbedThreads];
@@ -691,17 +691,20 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     }
 
     // ---- tiles without a real pair: zeros (after the real tiles, so these
-    // stores overlap the other workgroups' work; jet activity read once per jet)
-    {
-        // tiles [tot w / W, tot (w + 1) / W), floors taken in 32 bits as above
-        const int tot = B * ntri, qz = tot / W, rz = tot - qz * W;
-        const int z1 = qz * (w + 1) + rz * (w + 1) / W;
+    // stores overlap the other workgroups' work; jet activity read once per
+    // jet).  Only the first wz workgroups (one per CU: workgroups i and
+    // i + wz share a CU, and the older one finishes first) write them.
+    if ((int)blockIdx.x < wz) {
+        // tiles [tot zw / wz, tot (zw + 1) / wz), floors taken in 32 bits as above
+        const int zw = blockIdx.x;
+        const int tot = B * ntri, qz = tot / wz, rz = tot - qz * wz;
+        const int z1 = qz * (zw + 1) + rz * (zw + 1) / wz;
         // each 512 threads take one tile per step (the half is wave-uniform)
         constexpr int kZPar = kEmbedThreads / 512;
         static_assert(kEmbedThreads % 512 == 0, "zero tiles are written by 512 threads");
         int bz = -1;
         uint32_t actz = 0;
-        for (int z0 = qz * w + rz * w / W; z0 < z1; z0 += kZPar) {
+        for (int z0 = qz * zw + rz * zw / wz; z0 < z1; z0 += kZPar) {
             const int z = z0 + tid / 512;
             if (z >= z1) continue;
             const int bb = z / ntri, t = z - bb * ntri;
@@ -716,9 +719,8 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     }
 }
 
-// kWgPerCu resident workgroups per CU (16 waves: 4 per SIMD at the kernel's
-// register budget).
-static int persistent_grid(int B, int P) {
+// Compute units of the current device (cached per device).
+static int cu_count() {
     static int cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -729,8 +731,14 @@ static int persistent_grid(int B, int P) {
             n = 256;
         cus[dev] = n;
     }
+    return cus[dev];
+}
+
+// kWgPerCu resident workgroups per CU (16 waves: 4 per SIMD at the kernel's
+// register budget).
+static int persistent_grid(int B, int P) {
     const long T = P / kTile, tiles = (long)B * T * (T + 1) / 2;
-    return (int)std::min<long>((long)kWgPerCu * cus[dev], std::max<long>(tiles, 1));
+    return (int)std::min<long>((long)kWgPerCu * cu_count(), std::max<long>(tiles, 1));
 }
 
 // Batches are cut into segments of at most 65,536 jets so that tile counts
@@ -742,11 +750,13 @@ static hipError_t launch_embed(const float *p4, const uint8_t *mask, int B, int 
     constexpr int kSeg = 65536;
     for (int b0 = 0; b0 < B; b0 += kSeg) {
         const int nb = std::min(kSeg, B - b0);
-        hipLaunchKernelGGL(pair_embed_kernel<kMode>, dim3(persistent_grid(nb, P)),
-                           dim3(kEmbedThreads), 0, s, (const float4 *)p4 + (size_t)b0 * P,
-                           mask + (size_t)b0 * P, nb, P, (const float4 *)m->w32,
-                           (const v8bf *)m->w16, (const v8h *)m->wx2, m->bias,
-                           (void *)((OutT *)U + (size_t)b0 * kHeads * P * P));
+        const int grid = persistent_grid(nb, P);
+        // zero tiles: the workgroups that are first on their CU
+        const int wz = std::max(1, std::min(grid, cu_count()));
+        hipLaunchKernelGGL(pair_embed_kernel<kMode>, dim3(grid), dim3(kEmbedThreads), 0, s,
+                           (const float4 *)p4 + (size_t)b0 * P, mask + (size_t)b0 * P, nb, P,
+                           (const float4 *)m->w32, (const v8bf *)m->w16, (const v8h *)m->wx2,
+                           m->bias, (void *)((OutT *)U + (size_t)b0 * kHeads * P * P), wz);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
