@@ -245,18 +245,22 @@ __device__ __forceinline__ void write_row_pair(const PL &L, OutT *U, int P, int 
 }
 
 // ---- work estimate for the balanced split
-// A CU's time follows the wave iterations (pairs of blocks) it runs: one that
-// holds a real pair runs the MLP, an all-padding one only stores zeros but
-// still costs its features, branches and stores (the weights below were fitted
-// to per-wave timings).  The estimate takes the real slots of a jet to come
-// first (the usual layout):
+// A CU's time follows the wave iterations (pairs of blocks) it runs and the
+// jets it starts: an iteration that holds a real pair runs the MLP, an
+// all-padding one only walks the tile and stores zeros, and every jet costs
+// a staging round (particles, barriers).  The weights below are a least-
+// squares fit of per-CU end times (s_memtime) to those counts: float32
+// 0.51 us per real iteration, ~0 per padding one and 1.6 us per jet; bf16
+// 0.63, 0.15 and 0.67 us.  The estimate takes the real slots of a jet to
+// come first (the usual layout):
 // the ia-th active block then holds r = min(16, n - 16 ia) real rows (at least
 // 1), an off-diagonal tile of its rows has ceil(r / 2) real iterations of 8,
 // and its diagonal tile min(5, ceil(r (r + 1) / 64)) of 5.  Any other layout
 // only moves the split points; every iteration is still done exactly once.
 template <int kMode>
-struct WorkCost {  // relative cost of a real and of an all-padding iteration
-    static constexpr int kReal = kMode == kMlpBf16 ? 3 : 5, kPad = 2;
+struct WorkCost {  // relative cost of a real and an all-padding iteration, and of a jet
+    static constexpr int kReal = kMode == kMlpBf16 ? 4 : 5, kPad = 1,
+                         kJet = kMode == kMlpBf16 ? 4 : 15;
 };
 
 struct JetInfo {
@@ -330,12 +334,13 @@ __device__ __forceinline__ int jet_cost(JetInfo j) {
     int c = 0;
     const int a = __popc(j.act);
     for (int ia = 0; ia < a; ++ia) c += est_row_cost<C>(j.n, ia);
-    return c;
+    return a ? c + C::kJet : 0;
 }
 // The flat block index (even) of the first iteration of the jet whose cost
-// prefix reaches tl (0 <= tl < jet_cost(j)).
+// prefix reaches tl (0 <= tl < jet_cost(j); the jet's own cost comes first).
 template <class C>
 __device__ __forceinline__ int jet_split(JetInfo j, int tl) {
+    tl = max(tl - C::kJet, 0);
     int ia = 0, acc = 0;
     for (;; ++ia) {
         const int rc = est_row_cost<C>(j.n, ia);
