@@ -10,8 +10,9 @@
 // and every value is written twice (U[a][b] and U[b][a]) straight from
 // registers.  The kernel is persistent: two 512-thread workgroups per CU, each
 // staging the packed MLP weights in LDS once and taking an equal share of the
-// batch's estimated work (counted from the mask in-kernel) plus an equal share
-// of the all-padding tiles, which only get zeros.  A workgroup stages the
+// batch's estimated work (counted from the mask in-kernel); the first
+// workgroup of each CU also takes a share of the all-padding tiles, which only
+// get zeros.  A workgroup stages the
 // particle kinematics (float64) of the jets its share touches in LDS, two jets
 // at a time.  Inside a tile the unit of work is a pair block of 16 pairs = the
 // 16 columns of one 16x16 MFMA: off-diagonal tiles have 16 (one per row),
@@ -382,10 +383,12 @@ __device__ __forceinline__ int block_row(int q) {
 __device__ __forceinline__ int jet_blocks(uint32_t act) { return blocks_before_row(__popc(act)); }
 
 // Persistent pair-embed kernel.  The work of every jet (its pair blocks in
-// tile order, weighted by the estimate above) is counted from the mask; a
-// block-wide scan gives every workgroup an equal contiguous share, split at
-// pair-block granularity (the two workgroups of a CU then carry a like load).
-// All-padding tiles are split evenly too and only get zeros.  The 8 waves
+// tile order, weighted by the estimate above) is counted from the mask; one
+// wave scans the per-jet costs and gives every workgroup an equal contiguous
+// share, split at pair-block granularity (the two workgroups of a CU then
+// carry a like load).  All-padding tiles are split evenly over the first
+// workgroup of each CU (the older one, which finishes its share first) and
+// only get zeros.  The 8 waves
 // claim the iterations (pairs of blocks) of each jet from a counter in LDS and
 // run them alone (no barrier between iterations, none between the first two
 // jets), writing U straight from registers.  Workgroup w is remapped so
