@@ -498,7 +498,8 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             const int v = __shfl_up(inc, off);
             inc += lane >= off ? v : 0;
         }
-        const int totw = __shfl(inc, 63), excl = inc - sum;
+        // (readlane: a uniform source lane needs no LDS round trip)
+        const int totw = __builtin_amdgcn_readlane(inc, 63), excl = inc - sum;
         const int qt = totw / W, rt = totw - qt * W;
         int sb[2], st[2];
 #pragma unroll
@@ -520,8 +521,8 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             sb[i] = B;
             st[i] = 0;
             if (t < totw) {
-                sb[i] = (kPerLane * L + __shfl(k, L)) * per;
-                st[i] = t - __shfl(pre, L);
+                sb[i] = (kPerLane * L + __builtin_amdgcn_readlane(k, L)) * per;
+                st[i] = t - __builtin_amdgcn_readlane(pre, L);
             }
         }
         // the jets at the split points: from LDS when every thread has one
