@@ -13,7 +13,7 @@
 //   1. Each wave takes the jet's real-slot bits with ballots (wave-uniform,
 //      no LDS), then issues the loads of its U strips (16 queries x every key
 //      block that holds a real key) and of its Q rows into registers.
-//   2. While those are in flight the workgroup stages K and V^T in LDS for
+//   2. While those are in flight the workgroup stages K and V in LDS for
 //      the key blocks up to an even count; padded key rows and blocks without
 //      a real key are written as 0 (a NaN there must not meet a zero
 //      probability inside the MFMA).
@@ -26,7 +26,8 @@
 //      within 64 registers at P = 256).  Row max and row sum take an in-lane
 //      reduction and two cross-lane swaps.  Then O^T += V^T P^T with one
 //      K = 32 product per pair of key blocks, the probabilities already in
-//      the B-operand layout.
+//      the B-operand layout.  V is staged row-major with 8-byte stores and
+//      read as V^T by the gfx950 LDS transpose load (ds_read_b64_tr_b16).
 // Query blocks without a real query store zeros; padded queries store 0.
 //
 // float32 inputs run on the fp16 matrix cores with split operands: every
@@ -51,8 +52,8 @@ constexpr int kAttnQBlocks = 8;  // query blocks per workgroup
 template <int kT, int kWords>
 __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc, bool rq,
                                            bool kvbad, const SlotBits<kWords> &real, int T,
-                                           const uint16_t *Ks, const uint16_t *Vth,
-                                           const uint16_t *Vtl, const float *__restrict__ Qh,
+                                           const uint16_t *Ks, const uint16_t *Vsh,
+                                           const uint16_t *Vsl, const float *__restrict__ Qh,
                                            const float *__restrict__ Kh,
                                            const float *__restrict__ Vh,
                                            const float *__restrict__ urow, int q0,
@@ -69,7 +70,7 @@ __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc
             qh = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
             ql = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        attend_split<kT>(u, qh, ql, 0.25f, real, T, Ks, Vth, Vtl, o, lsum);
+        attend_split<kT>(u, qh, ql, 0.25f, real, T, Ks, Vsh, Vsl, o, lsum);
     } else {
         // A real Q, K or V value beyond the fp16 range: float32 MFMA with an
         // online softmax, everything re-read from global memory (rare path).
@@ -122,9 +123,8 @@ __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc
 template <int kT, int kWords>
 __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
                                             const SlotBits<kWords> &real, int T,
-                                            const uint16_t *Ks, const uint16_t *Vth,
+                                            const uint16_t *Ks, const uint16_t *Vsh,
                                             uint16_t *__restrict__ orow) {
-    constexpr int kVt = vt_stride(kT);
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     // U of padded keys -> -inf (bit patterns), so that every score is an FMA result
 #pragma unroll
@@ -174,7 +174,7 @@ __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
         }
         lsum = fmaf(lsum, corr, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
         o = o * corr;
-        const v8bf vt = *(const v8bf *)(Vth + c * kVt + kb * kTile + 8 * g);
+        const v8bf vt = __builtin_bit_cast(v8bf, v_operand(Vsh, kb * kTile));
         o = mfma32bf(vt, __builtin_convertvector(p, v8bf), o);
     }
     const float inv = 1.0f / xsum16(lsum);
@@ -185,22 +185,24 @@ __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
 }
 
 // ------------------------------------------------------------ kernel
+// (float32 at P <= 128: held to 6 waves per SIMD, i.e. at most 80 VGPRs, so
+// that three workgroups stay resident per CU)
 template <bool kBf16, int kT, int kQ>
-__global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
+__global__ __launch_bounds__(64 * kAttnQBlocks / kQ)
+__attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_kernel(
     const AttnElt<kBf16> *__restrict__ Q, const AttnElt<kBf16> *__restrict__ K,
     const AttnElt<kBf16> *__restrict__ V, const AttnElt<kBf16> *__restrict__ U,
     const uint8_t *__restrict__ mask, int H, int P, int chunks, AttnElt<kBf16> *__restrict__ O) {
     using E = AttnElt<kBf16>;
     constexpr int kWaves = kAttnQBlocks / kQ, kThreads = 64 * kWaves;
     constexpr int kWords = (kT * 16 + 63) / 64;
-    constexpr int kVt = vt_stride(kT);
-    // fp32: K rows as 32 fp16 [hi d0..15 | lo d0..15], V^T hi and lo;
-    // bf16: K rows of 16 bf16 and V^T.  K rows in key_row order, V^T in plain
-    // key order.
+    // fp32: K rows as 32 fp16 [hi d0..15 | lo d0..15], V hi and lo;
+    // bf16: K rows of 16 bf16 and V.  K rows in key_row order, V row-major in
+    // plain key order (read transposed as the P V operand).
     constexpr int kKRow = kBf16 ? 16 : 32;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kT * 16 * kKRow];
-    __shared__ __attribute__((aligned(16))) uint16_t Vth[16 * kVt];
-    __shared__ __attribute__((aligned(16))) uint16_t Vtl[kBf16 ? 1 : 16 * kVt];
+    __shared__ __attribute__((aligned(16))) uint16_t Vsh[kT * 16 * kVRow];
+    __shared__ __attribute__((aligned(16))) uint16_t Vsl[kBf16 ? 1 : kT * 16 * kVRow];
     __shared__ int badw[kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
         }
     }
 
-    // ---- 2. K and V^T into LDS
+    // ---- 2. K and V into LDS
     bool bad = false;  // a real K or V value outside the fp16-safe range
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
@@ -281,10 +283,7 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
             const uint2 kz = rk ? kk[it] : make_uint2(0u, 0u);
             const uint2 vz = rk ? vv[it] : make_uint2(0u, 0u);
             *(uint2 *)(Ks + kr * 16 + d0) = kz;
-            Vth[(d0 + 0) * kVt + k] = (uint16_t)(vz.x & 0xffff);
-            Vth[(d0 + 1) * kVt + k] = (uint16_t)(vz.x >> 16);
-            Vth[(d0 + 2) * kVt + k] = (uint16_t)(vz.y & 0xffff);
-            Vth[(d0 + 3) * kVt + k] = (uint16_t)(vz.y >> 16);
+            *(uint2 *)(Vsh + k * kVRow + d0) = vz;
         } else {
             const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
             const float4 kz = rk ? kk[it] : zero, vz = rk ? vv[it] : zero;
@@ -294,14 +293,8 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
             split4_f16(vz, vh, vl);
             *(v4h *)(Ks + kr * 32 + d0) = kh;
             *(v4h *)(Ks + kr * 32 + 16 + d0) = kl;
-            // bit-cast whole vectors: clang mis-lowers a bit_cast of one
-            // vector element (it reads element 0)
-            const v4s vhb = __builtin_bit_cast(v4s, vh), vlb = __builtin_bit_cast(v4s, vl);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                Vth[(d0 + jj) * kVt + k] = (uint16_t)vhb[jj];
-                Vtl[(d0 + jj) * kVt + k] = (uint16_t)vlb[jj];
-            }
+            *(v4h *)(Vsh + k * kVRow + d0) = vh;
+            *(v4h *)(Vsl + k * kVRow + d0) = vl;
         }
     }
     // one flag word per wave; __syncthreads() (not a workgroup-reduction
@@ -335,11 +328,11 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ) void attention_kernel(
         }
         const bool rq = real.slot(q0 + c);
         if constexpr (kBf16) {
-            attend_bf16<kT>(u[j], rq ? qb16[j] : (v4s){0, 0, 0, 0}, rq, real, T, Ks, Vth, orow);
+            attend_bf16<kT>(u[j], rq ? qb16[j] : (v4s){0, 0, 0, 0}, rq, real, T, Ks, Vsh, orow);
         } else {
             const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
             attend_f32<kT>(u[j], rq ? qa[j] : zero, rq ? qc[j] : zero, rq, kvbad, real, T, Ks,
-                           Vth, Vtl, Qh, Kh, Vh, U + (base + q0 + c) * P + 4 * g, q0, orow);
+                           Vsh, Vsl, Qh, Kh, Vh, U + (base + q0 + c) * P + 4 * g, q0, orow);
         }
     }
 }

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kStackThreads) void stack_out_kernel(
 //      power-of-two scales that put them into [2^13, 2^14): the split fp16
 //      operands of the attention can then neither overflow nor lose
 //      relative accuracy, and the scales are undone exactly on the scores
-//      and the output.  K and V^T go to LDS, Q through LDS into the
+//      and the output.  K and V go to LDS, Q through LDS into the
 //      B-operand layout.
 //   4. The U strip of the wave's query block is loaded once the projections
 //      no longer hold registers; the attention core of pair_bias_attention
@@ -351,20 +351,19 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
     const float *__restrict__ ci, const float *__restrict__ U, const uint8_t *__restrict__ mask,
     int B, int H, int P, int C, int chunks, float *__restrict__ O) {
     constexpr int kWords = (kT * 16 + 63) / 64;
-    constexpr int kVt = vt_stride(kT);
     constexpr int kRbw = (kT + kSaWaves - 1) / kSaWaves;  // row blocks per wave
     // LDS: during the projections the head's packed Q/K/V weight operands
     // ([m][hi, lo][s][lane], read by all 8 waves); afterwards, in the same
-    // bytes, K, V^T and the Q tiles of the attention.
-    constexpr int kKsB = kT * 16 * 32 * 2, kVtB = 16 * kVt * 2, kQsB = kSaWaves * 16 * 20 * 4;
+    // bytes, K, V and the Q tiles of the attention.
+    constexpr int kKsB = kT * 16 * 32 * 2, kVtB = kT * 16 * kVRow * 2, kQsB = kSaWaves * 16 * 20 * 4;
     constexpr int kWB = 3 * 2 * kKS * 64 * 16;
     constexpr int kAttnB = kKsB + 2 * kVtB + kQsB;
     static_assert(kKsB % 16 == 0 && kVtB % 16 == 0, "LDS sections stay 16-byte aligned");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kAttnB > kWB ? kAttnB : kWB];
     __shared__ float kvmax[2][kSaWaves];
     uint16_t *Ks = (uint16_t *)smem;
-    uint16_t *Vth = (uint16_t *)(smem + kKsB);
-    uint16_t *Vtl = (uint16_t *)(smem + kKsB + kVtB);
+    uint16_t *Vsh = (uint16_t *)(smem + kKsB);  // V hi / lo, row-major
+    uint16_t *Vsl = (uint16_t *)(smem + kKsB + kVtB);
     float (*Qs)[16][20] = (float (*)[16][20])(smem + kKsB + 2 * kVtB);
     v8h *Ws = (v8h *)smem;
 
@@ -509,7 +508,7 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
     }
     __syncthreads();
 
-    // ---- 3. head scales; K, V^T to LDS; Q through LDS
+    // ---- 3. head scales; K, V to LDS; Q through LDS
     float km = 0.f, vm = 0.f;
 #pragma unroll
     for (int w = 0; w < kSaWaves; ++w) {
@@ -534,13 +533,8 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
         const int kr = key_row(k);
         *(v4h *)(Ks + kr * 32 + 4 * g) = kh;
         *(v4h *)(Ks + kr * 32 + 16 + 4 * g) = kl;
-        // bit-cast whole vectors (clang mis-lowers a bit_cast of one element)
-        const v4s vhb = __builtin_bit_cast(v4s, vh), vlb = __builtin_bit_cast(v4s, vl);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            Vth[(4 * g + r) * kVt + k] = (uint16_t)vhb[r];
-            Vtl[(4 * g + r) * kVt + k] = (uint16_t)vlb[r];
-        }
+        *(v4h *)(Vsh + k * kVRow + 4 * g) = vh;
+        *(v4h *)(Vsl + k * kVRow + 4 * g) = vl;
     }
     float qinv = 1.f;
     if (qact) {
@@ -575,7 +569,7 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
     }
     v4f o;
     float l;
-    attend_split<kT>(u, qh, ql, 0.25f * kinv * qinv, real, T, Ks, Vth, Vtl, o, l);
+    attend_split<kT>(u, qh, ql, 0.25f * kinv * qinv, real, T, Ks, Vsh, Vsl, o, l);
     const float inv = vinv / l;
     *(float4 *)orow = real.slot(q0 + c)
                           ? make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv)

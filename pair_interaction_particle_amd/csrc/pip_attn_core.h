@@ -3,7 +3,7 @@
 //
 // "Fusion 3" of the ml4sci_cms_e2e26 README ("How the Kernel Fusion Works"):
 // softmax(Q K^T / sqrt(d) + bias) V.  K (as [key_row(key)][hi d0..15 | lo
-// d0..15] fp16) and V^T (hi and lo, plain key order) sit in LDS; the bias rows
+// d0..15] fp16) and V (hi and lo, row-major in plain key order) sit in LDS; the bias rows
 // of one query block (the "U strip") sit in registers.  Scores are computed
 // transposed, S^T = K Q^T, so that lane l holds query l%16 against keys
 // 4(l/16)+r; the softmax is exact (two passes over the strip); P V takes one
@@ -68,14 +68,29 @@ struct SlotBits {
     }
 };
 
-// LDS row stride (elements) of V^T: the key range plus a pad that spreads the
-// 16 rows over the banks.
-constexpr int vt_stride(int kT) { return kT * 16 + 8; }
+// V in LDS: row-major, one row of kVRow 16-bit elements (d = 0 .. 15) per
+// key, written with one 8-byte store per 4 values.
+constexpr int kVRow = 16;
+
+// The P V A operand (V^T: row d = lane % 16, reduction slots 8 (lane / 16) ..
+// + 7 = keys k0 + 8 (lane / 16) .. + 7, k0 = 32 p for pair p) from row-major V
+// with two gfx950 LDS transpose reads.  Within a 16-lane group,
+// ds_read_b64_tr_b16 gives lane 4c + d, slot e, element d of the 4-element
+// block addressed by lane 4e + c; so lane j addresses V[k + j / 4][4 (j % 4)]
+// and lane i receives V[k .. k + 3][i].
+__device__ __forceinline__ v8h v_operand(const uint16_t *Vr, int k0) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    typedef __attribute__((address_space(3))) v4s *LdsV4s;
+    const uint16_t *p = Vr + (k0 + 8 * g + (c >> 2)) * kVRow + 4 * (c & 3);
+    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4s)p);
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4s)(p + 4 * kVRow));
+    return __builtin_bit_cast(v8h, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // Key order inside a pair of key blocks (keys 32p .. 32p+31): the score MFMA
 // of block t = 0, 1 of the pair puts key 32p + 8g + 4t + r in lane group g,
 // register r.  Lane group g's keys of both blocks are then the 8 consecutive
-// keys 32p + 8g .. +7: one contiguous U read per lane and pair, and V^T in
+// keys 32p + 8g .. +7: one contiguous U read per lane and pair, and V in
 // plain key order for P V.  key_row(k) is the K row (score A-operand row
 // 16 (2p + t) + 4g + r) that holds key k.
 __device__ __forceinline__ int key_row(int k) {
@@ -110,13 +125,12 @@ __device__ __forceinline__ bool pair_real(const SlotBits<kWords> &real, int kb, 
 // the strip in the pair key order of key_row / u_col (U of padded keys inside
 // a pair with a real key is replaced here; pairs without a real key must
 // already hold -inf).  K and V rows of keys that are not real must be 0 in LDS
-// for every pair below an even block count.
+// for every pair below an even block count.  V hi / lo are row-major (kVRow).
 template <int kT, int kWords>
 __device__ __forceinline__ void attend_split(float4 (&u)[kT], v8h qh, v8h ql, float qk_mul,
                                              const SlotBits<kWords> &real, int T,
-                                             const uint16_t *Ks, const uint16_t *Vth,
-                                             const uint16_t *Vtl, v4f &o, float &l) {
-    constexpr int kVt = vt_stride(kT);
+                                             const uint16_t *Ks, const uint16_t *Vh,
+                                             const uint16_t *Vl, v4f &o, float &l) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     // U of padded keys -> -inf, so that every score is an FMA result
 #pragma unroll
@@ -177,9 +191,8 @@ __device__ __forceinline__ void attend_split(float4 (&u)[kT], v8h qh, v8h ql, fl
             p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][r], kLog2e, -mb));
         }
         lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        const int off = c * kVt + kb * kTile + 8 * g;
-        const v8h vh = *(const v8h *)(Vth + off);
-        const v8h vl = *(const v8h *)(Vtl + off);
+        const v8h vh = v_operand(Vh, kb * kTile);
+        const v8h vl = v_operand(Vl, kb * kTile);
         v8h ph, pl;
         split_f16<8>(p, ph, pl);
         o = mfma32h(vh, pl, o);
