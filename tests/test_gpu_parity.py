@@ -286,6 +286,23 @@ def test_pair_embed_bf16_ragged(B, P, ns):
     assert_zero_bits(U.transpose(0, 2, 3, 1), ~pair_mask(mask), "U bf16 padding")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pair_embed_more_jets_than_threads(dtype):
+    # B > 512: each entry of the in-kernel cost scan covers a range of jets, the
+    # split points are walked from the range start, and the zero tiles read
+    # jet activity from the mask (empty jets and holes included)
+    B, P = 1300, 32
+    rng = np.random.default_rng(81)
+    ns = tuple(int(x) for x in rng.integers(0, P + 1, size=B))
+    p4, mask = ragged_jets(B, P, ns, seed=81)
+    params = mlp_for(81, biases=True)
+    mlp = pip.PairMLP(params)
+    U = host(pip.pair_embed(g(p4), g(mask), mlp, dtype=dtype))
+    ref = oracle.pair_embed(p4, mask, params)
+    assert_close(U, ref, TOL32 if dtype == "f32" else TOLBF_U, "U %s B=1300" % dtype)
+    assert_zero_bits(U.transpose(0, 2, 3, 1), ~pair_mask(mask), "U %s B=1300 padding" % dtype)
+
+
 def test_single_full_jet_at_max_p_every_entry():
     B, P = 1, 256
     p4, mask = ragged_jets(B, P, (256,), seed=60, hole=False)
