@@ -159,6 +159,56 @@ __device__ __forceinline__ void first_operands(const v8h *__restrict__ Ahi,
     }
 }
 
+// The W operands of every k-step (C <= 128: 64 registers), loaded together
+// with the rows, so that the product never waits on L2.
+template <int kKS, int kJ>
+__device__ __forceinline__ void all_operands(const v8h *__restrict__ Ahi,
+                                             const v8h *__restrict__ Alo, size_t op0, int tile0,
+                                             int ntiles, int KS, v8h (&ch)[kJ][kKS],
+                                             v8h (&cl)[kJ][kKS]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+        const int t = tile0 + kStackWaves * j;
+#pragma unroll
+        for (int s = 0; s < kKS; ++s) {
+            const size_t o =
+                (op0 + (size_t)(t < ntiles ? t : tile0) * KS + min(s, KS - 1)) * 64 + lane;
+            ch[j][s] = Ahi[o];
+            cl[j][s] = Alo[o];
+        }
+    }
+}
+
+// gemm_rows with every k-step's operands already in registers (all_operands).
+template <int kKS, int kRB, int kJ>
+__device__ __forceinline__ void gemm_rows_pre(int tile0, int ntiles, int KS, const float *Xs,
+                                              const float *rsc, const bool (&any)[kRB],
+                                              const v8h (&ch)[kJ][kKS],
+                                              const v8h (&cl)[kJ][kKS], v4f (&acc)[kJ][kRB]) {
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+        for (int i = 0; i < kRB; ++i) acc[j][i] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+        if (s >= KS) break;
+#pragma unroll
+        for (int i = 0; i < kRB; ++i) {
+            if (!any[i]) continue;
+            v8h bh, bl;
+            b_operand<kKS>(Xs, rsc, i, s, bh, bl);
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                if (tile0 + kStackWaves * j >= ntiles) continue;
+                acc[j][i] = mfma32h(ch[j][s], bl, acc[j][i]);
+                acc[j][i] = mfma32h(cl[j][s], bh, acc[j][i]);
+                acc[j][i] = mfma32h(ch[j][s], bh, acc[j][i]);
+            }
+        }
+    }
+}
+
 // ch / cl: the operands of step 0 (first_operands), consumed.
 template <int kKS, int kRB, int kJ>
 __device__ __forceinline__ void gemm_rows(const v8h *__restrict__ Ahi, const v8h *__restrict__ Alo,
@@ -252,7 +302,8 @@ struct RowLoad {
 
 // X += O Wo for the workgroup's 16 kRB rows (O head-major (B, H, P, 16)).
 template <int kKS, int kRB>
-__global__ __launch_bounds__(kStackThreads) void stack_out_kernel(
+__global__ __launch_bounds__(kStackThreads)
+__attribute__((amdgpu_waves_per_eu(kKS <= 4 ? 4 : 1))) void stack_out_kernel(
     float *__restrict__ X, const float *__restrict__ O, const v8h *__restrict__ Awhi,
     const v8h *__restrict__ Awlo, const float *__restrict__ ciw,
     const uint8_t *__restrict__ mask, int R, int P, int C, int H) {
@@ -270,8 +321,13 @@ __global__ __launch_bounds__(kStackThreads) void stack_out_kernel(
 
     // W operands of the first k-step, the mask bytes (address clamped: every
     // load issued before the first wait), the O and X rows
-    v8h wh[kJw], wl[kJw];
-    first_operands<kKS, kRB, kJw>(Awhi, Awlo, (size_t)3 * NT * KS, wave, NT, KS, wh, wl);
+    // (C <= 128: every k-step's operands at once; beyond, one step ahead)
+    constexpr bool kPre = kKS <= 4;
+    v8h wh[kJw], wl[kJw], ah[kJw][kKS], al[kJw][kKS];
+    if constexpr (kPre)
+        all_operands<kKS, kJw>(Awhi, Awlo, (size_t)3 * NT * KS, wave, NT, KS, ah, al);
+    else
+        first_operands<kKS, kRB, kJw>(Awhi, Awlo, (size_t)3 * NT * KS, wave, NT, KS, wh, wl);
     int row[kRB];
     uint8_t mb[kRB];
 #pragma unroll
@@ -294,8 +350,11 @@ __global__ __launch_bounds__(kStackThreads) void stack_out_kernel(
     row_scales<kKS, kRows>(Xs, part, rsc, rinv, C);
     __syncthreads();
     v4f acc[kJw][kRB];
-    gemm_rows<kKS, kRB, kJw>(Awhi, Awlo, (size_t)3 * NT * KS, wave, NT, KS, Xs, rsc, any, wh, wl,
-                             acc);
+    if constexpr (kPre)
+        gemm_rows_pre<kKS, kRB, kJw>(wave, NT, KS, Xs, rsc, any, ah, al, acc);
+    else
+        gemm_rows<kKS, kRB, kJw>(Awhi, Awlo, (size_t)3 * NT * KS, wave, NT, KS, Xs, rsc, any, wh,
+                                 wl, acc);
 #pragma unroll
     for (int j = 0; j < kJw; ++j) {
         const int nt = wave + kStackWaves * j;
