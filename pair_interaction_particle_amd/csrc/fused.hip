@@ -77,6 +77,55 @@ __device__ __forceinline__ v4f pv(const QkvT<kBf16> *Vh, int k0, const v4f &p,
     if constexpr (kBf16) return pv_bf16(Vh, k0, p, kreal, acc);
     else return pv_f32(Vh, k0, p, kreal, acc);
 }
+// The Q, K and V values one attention unit (query block q0 against key block
+// k0) needs in this lane, loaded ahead of the round's MLP so that their L2
+// latency overlaps it.  Every load is unconditional (rows < P); padded keys
+// are selected to 0 only when used.
+template <bool kBf16>
+struct UnitIn {
+    using Q4 = typename std::conditional<kBf16, v4s, float4>::type;
+    Q4 q, k;
+    QkvT<kBf16> v[4];
+
+    __device__ __forceinline__ void load(const QkvT<kBf16> *__restrict__ Qh,
+                                         const QkvT<kBf16> *__restrict__ Kh,
+                                         const QkvT<kBf16> *__restrict__ Vh, int q0, int k0) {
+        const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+        q = *(const Q4 *)(Qh + (size_t)(q0 + c) * 16 + 4 * g);
+        k = *(const Q4 *)(Kh + (size_t)(k0 + c) * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = Vh[(size_t)(k0 + 4 * g + r) * 16 + c];
+    }
+    // S^T tile, as scores_f32 / scores_bf16
+    __device__ __forceinline__ v4f scores() const {
+        if constexpr (kBf16) {
+            return mfma16bf(k, q, (v4f){0.f, 0.f, 0.f, 0.f});
+        } else {
+            v4f s = {0.f, 0.f, 0.f, 0.f};
+            s = mfma4(k.x, q.x, s);
+            s = mfma4(k.y, q.y, s);
+            s = mfma4(k.z, q.z, s);
+            return mfma4(k.w, q.w, s);
+        }
+    }
+    // acc += V^T P^T, as pv_f32 / pv_bf16
+    __device__ __forceinline__ v4f pv(const v4f &p, const int (&kreal)[4], v4f acc) const {
+        if constexpr (kBf16) {
+            v4s vv, pp;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                vv[r] = kreal[r] ? (short)v[r] : (short)0;
+                pp[r] = (short)f2bf(p[r]);
+            }
+            return mfma16bf(vv, pp, acc);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc = mfma4(kreal[r] ? v[r] : 0.f, p[r], acc);
+            return acc;
+        }
+    }
+};
+
 template <bool kBf16>
 __device__ __forceinline__ void store_o(QkvT<kBf16> *Orow, const v4f &o) {
     if constexpr (kBf16)
@@ -216,9 +265,10 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
 
     // one attention unit: query block qb against key block kb of head h, U
     // element (query q, key k) = Ut[q][k] (or Ut[k][q] when transposed)
-    auto unit = [&](const float (*Ut)[17], bool transposed, int qb, int kb) {
-        const int q0 = qb * kTile, k0 = kb * kTile;
-        v4f s = scores<kBf16>(Qh, Kh, q0, k0);
+    auto unit = [&](const float (*Ut)[17], bool transposed, int qb, int kb,
+                    const UnitIn<kBf16> &in) {
+        const int k0 = kb * kTile;
+        v4f s = in.scores();
         int kreal[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -230,7 +280,7 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
         const float corr = online_softmax(s, m, l);
         const float4 a4 = Ost[h][qb][lane];
         v4f acc = {a4.x * corr, a4.y * corr, a4.z * corr, a4.w * corr};
-        acc = pv<kBf16>(Vh, k0, s, kreal, acc);
+        acc = in.pv(s, kreal, acc);
         Ost[h][qb][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         if (g == 0) {
             mst[h][qb][c] = m;
@@ -248,6 +298,10 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
         const bool diag = (I == J);
         const int nblk = diag ? 9 : 16;
         const int r0 = I * kTile, c0 = J * kTile;
+        // this round's Q, K, V (both units), in flight during the MLP
+        UnitIn<kBf16> inIJ, inJI;
+        inIJ.load(Qh, Kh, Vh, r0, c0);
+        inJI.load(Qh, Kh, Vh, c0, r0);
         int iA, jA, iB, jB;
         const bool vA = block_pair_f(diag, 2 * wave, nblk, lane, iA, jA);
         const bool vB = block_pair_f(diag, 2 * wave + 1, nblk, lane, iB, jB);
@@ -275,8 +329,8 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
             }
         }
         __syncthreads();
-        unit(us[buf][h], false, I, J);
-        if (!diag) unit(us[buf][h], true, J, I);
+        unit(us[buf][h], false, I, J, inIJ);
+        if (!diag) unit(us[buf][h], true, J, I, inJI);
     }
 
     // ---- finalise this head: O = acc / l on real queries, exact 0 elsewhere
