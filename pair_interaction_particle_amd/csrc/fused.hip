@@ -65,18 +65,6 @@ __device__ __forceinline__ int nz_bytes(uint32_t w) {
 template <bool kBf16>
 using QkvT = typename std::conditional<kBf16, uint16_t, float>::type;
 
-template <bool kBf16>
-__device__ __forceinline__ v4f scores(const QkvT<kBf16> *Qh, const QkvT<kBf16> *Kh, int q0,
-                                      int k0) {
-    if constexpr (kBf16) return scores_bf16(Qh, Kh, q0, k0);
-    else return scores_f32(Qh, Kh, q0, k0);
-}
-template <bool kBf16>
-__device__ __forceinline__ v4f pv(const QkvT<kBf16> *Vh, int k0, const v4f &p,
-                                  const int (&kreal)[4], v4f acc) {
-    if constexpr (kBf16) return pv_bf16(Vh, k0, p, kreal, acc);
-    else return pv_f32(Vh, k0, p, kreal, acc);
-}
 // The Q, K and V values one attention unit (query block q0 against key block
 // k0) needs in this lane, loaded ahead of the round's MLP so that their L2
 // latency overlaps it.  Every load is unconditional (rows < P); padded keys
@@ -96,7 +84,9 @@ struct UnitIn {
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = Vh[(size_t)(k0 + 4 * g + r) * 16 + c];
     }
-    // S^T tile, as scores_f32 / scores_bf16
+    // S^T tile (keys x queries): lane l gets the scores of query q0 + l%16
+    // against keys k0 + 4(l/16) + r; the reduction over d pairs lane group g,
+    // step s with d = 4g + s
     __device__ __forceinline__ v4f scores() const {
         if constexpr (kBf16) {
             return mfma16bf(k, q, (v4f){0.f, 0.f, 0.f, 0.f});
@@ -108,7 +98,9 @@ struct UnitIn {
             return mfma4(k.w, q.w, s);
         }
     }
-    // acc += V^T P^T, as pv_f32 / pv_bf16
+    // acc (O^T: lane l holds O[q0 + l%16][4(l/16) + r]) += V^T P^T for key
+    // block k0, p[r] the probability of key k0 + 4(l/16) + r; V of padded keys
+    // is selected to 0 (a NaN there must not meet p = 0 inside the MFMA)
     __device__ __forceinline__ v4f pv(const v4f &p, const int (&kreal)[4], v4f acc) const {
         if constexpr (kBf16) {
             v4s vv, pp;
@@ -399,6 +391,13 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
     for (int J = 0; J < T; ++J) {
         if (!blkAny[J]) continue;
         const int c0 = J * kTile;
+        // this key block's Q, K, V for the wave's two heads, in flight during the MLP
+        UnitIn<kBf16> in[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const size_t hb = ((size_t)jet * kHeads + 2 * wave + hh) * P;
+            in[hh].load(Q + hb * 16, K + hb * 16, V + hb * 16, r0, c0);
+        }
         for (int pass = 0; pass < 2; ++pass) {  // rows 8 pass + 2 wave + {0, 1}
             const int iA = 8 * pass + 2 * wave, iB = iA + 1, j = lane & 15;
             const bool realA = L.real[r0 + iA] && L.real[c0 + j];
@@ -422,8 +421,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int h = 2 * wave + hh;
-            const size_t hb = ((size_t)jet * kHeads + h) * P;
-            v4f s = scores<kBf16>(Q + hb * 16, K + hb * 16, r0, c0);
+            v4f s = in[hh].scores();
             int kreal[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -433,7 +431,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
             }
             const float corr = online_softmax(s, m[hh], l[hh]);
             acc[hh] *= corr;
-            acc[hh] = pv<kBf16>(V + hb * 16, c0, s, kreal, acc[hh]);
+            acc[hh] = in[hh].pv(s, kreal, acc[hh]);
         }
         __syncthreads();
     }

@@ -64,51 +64,4 @@ __device__ __forceinline__ v4f mfma16bf(v4s a, v4s b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// S^T tile (keys x queries) of one head: lane l gets the scores of query
-// q0 + l%16 against keys k0 + 4(l/16) + r.  Qh / Kh point at the head's
-// (P, 16) rows.  The reduction over d pairs lane group g, step s with d = 4g+s.
-__device__ __forceinline__ v4f scores_f32(const float *__restrict__ Qh,
-                                          const float *__restrict__ Kh, int q0, int k0) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    const float4 qv = *(const float4 *)(Qh + (size_t)(q0 + c) * 16 + 4 * g);
-    const float4 kv = *(const float4 *)(Kh + (size_t)(k0 + c) * 16 + 4 * g);
-    v4f s = {0.f, 0.f, 0.f, 0.f};
-    s = mfma4(kv.x, qv.x, s);
-    s = mfma4(kv.y, qv.y, s);
-    s = mfma4(kv.z, qv.z, s);
-    return mfma4(kv.w, qv.w, s);
-}
-__device__ __forceinline__ v4f scores_bf16(const uint16_t *__restrict__ Qh,
-                                           const uint16_t *__restrict__ Kh, int q0, int k0) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    const v4s qv = *(const v4s *)(Qh + (size_t)(q0 + c) * 16 + 4 * g);
-    const v4s kv = *(const v4s *)(Kh + (size_t)(k0 + c) * 16 + 4 * g);
-    return mfma16bf(kv, qv, (v4f){0.f, 0.f, 0.f, 0.f});
-}
-
-// acc (O^T: lane l holds O[q0 + l%16][4(l/16) + r]) += V^T P^T for key block
-// k0; p[r] is the probability of key k0 + 4(l/16) + r.  V rows of padded keys
-// are selected to 0 (a NaN there must not meet p = 0 inside the MFMA).
-__device__ __forceinline__ v4f pv_f32(const float *__restrict__ Vh, int k0, const v4f &p,
-                                      const int (&kreal)[4], v4f acc) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float vv = kreal[r] ? Vh[(size_t)(k0 + 4 * g + r) * 16 + c] : 0.f;
-        acc = mfma4(vv, p[r], acc);
-    }
-    return acc;
-}
-__device__ __forceinline__ v4f pv_bf16(const uint16_t *__restrict__ Vh, int k0, const v4f &p,
-                                       const int (&kreal)[4], v4f acc) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    v4s vv, pv;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        vv[r] = kreal[r] ? (short)Vh[(size_t)(k0 + 4 * g + r) * 16 + c] : (short)0;
-        pv[r] = (short)f2bf(p[r]);
-    }
-    return mfma16bf(vv, pv, acc);
-}
-
 }  // namespace pip
