@@ -174,7 +174,7 @@ __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
         }
         lsum = fmaf(lsum, corr, ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
         o = o * corr;
-        const v8bf vt = __builtin_bit_cast(v8bf, v_operand(Vsh, kb * kTile));
+        const v8bf vt = __builtin_bit_cast(v8bf, v_operand<true>(Vsh, kb * kTile));
         o = mfma32bf(vt, __builtin_convertvector(p, v8bf), o);
     }
     const float inv = 1.0f / xsum16(lsum);
@@ -197,8 +197,9 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     constexpr int kWaves = kAttnQBlocks / kQ, kThreads = 64 * kWaves;
     constexpr int kWords = (kT * 16 + 63) / 64;
     // fp32: K rows as 32 fp16 [hi d0..15 | lo d0..15], V hi and lo;
-    // bf16: K rows of 16 bf16 and V.  K rows in key_row order, V row-major in
-    // plain key order (read transposed as the P V operand).
+    // bf16: K rows of 16 bf16 and V.  K rows in key order (fp32) or key_row
+    // order (bf16), V row-major in key order (read transposed as the P V
+    // operand).
     constexpr int kKRow = kBf16 ? 16 : 32;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kT * 16 * kKRow];
     __shared__ __attribute__((aligned(16))) uint16_t Vsh[kT * 16 * kVRow];
@@ -252,14 +253,16 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
             // (a pair past an odd block count is half outside the row:
             // clamped, and those keys are masked)
             const bool need = act && kb < T && real.pair(kb >> 1) != 0;
-            const int off = min(need ? u_col(kb, g) : u_col(kb, g) * zero, P - 8);
             if constexpr (kBf16) {
+                const int off = min(need ? u_col(kb, g) : u_col(kb, g) * zero, P - 8);
                 const uint4 v = *(const uint4 *)(urow + off);
                 u[j][kb] = make_uint2(v.x, v.y);
                 u[j][kb + 1] = make_uint2(v.z, v.w);
             } else {
-                u[j][kb] = *(const float4 *)(urow + off);
-                u[j][kb + 1] = *(const float4 *)(urow + off + 4);
+                // natural order: 4 keys 16 kb + 4g .. of each block
+                const int o0 = 16 * kb + 4 * g, o1 = o0 + 16;
+                u[j][kb] = *(const float4 *)(urow + min(need ? o0 : o0 * zero, P - 4));
+                u[j][kb + 1] = *(const float4 *)(urow + min(need ? o1 : o1 * zero, P - 4));
             }
         }
         if constexpr (kBf16) {
@@ -278,7 +281,7 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
         const int i = tid + it * kThreads, k = i >> 2, d0 = (i & 3) * 4;
         if (i >= nst * 4) continue;
         const bool rk = k < P && real.slot(k);
-        const int kr = key_row(k);
+        const int kr = kBf16 ? key_row(k) : k;
         if constexpr (kBf16) {
             const uint2 kz = rk ? kk[it] : make_uint2(0u, 0u);
             const uint2 vz = rk ? vv[it] : make_uint2(0u, 0u);

@@ -553,9 +553,10 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
         for (int kb = 0; kb < kT; kb += 2) {
             // (half a pair lies past an odd block count: clamped, masked)
             const bool need = qact && kb < T && real.pair(kb >> 1) != 0;
-            const int off = min(need ? u_col(kb, g) : u_col(kb, g) * zero, P - 8);
-            u[kb] = *(const float4 *)(urow + off);
-            u[kb + 1] = *(const float4 *)(urow + off + 4);
+            // natural key order: 4 keys 16 kb + 4g .. of each block
+            const int o0 = 16 * kb + 4 * g, o1 = o0 + 16;
+            u[kb] = *(const float4 *)(urow + min(need ? o0 : o0 * zero, P - 4));
+            u[kb + 1] = *(const float4 *)(urow + min(need ? o1 : o1 * zero, P - 4));
         }
     }
 
@@ -589,9 +590,8 @@ __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(
         v4h kh, kl, vh, vl;
         split4_f16(kk, kh, kl);
         split4_f16(vv, vh, vl);
-        const int kr = key_row(k);
-        *(v4h *)(Ks + kr * 32 + 4 * g) = kh;
-        *(v4h *)(Ks + kr * 32 + 16 + 4 * g) = kl;
+        *(v4h *)(Ks + k * 32 + 4 * g) = kh;
+        *(v4h *)(Ks + k * 32 + 16 + 4 * g) = kl;
         *(v4h *)(Vsh + k * kVRow + 4 * g) = vh;
         *(v4h *)(Vsl + k * kVRow + 4 * g) = vl;
     }

@@ -2,8 +2,8 @@
 // fp16 operands, shared by the attention kernel and the block stack.
 //
 // "Fusion 3" of the ml4sci_cms_e2e26 README ("How the Kernel Fusion Works"):
-// softmax(Q K^T / sqrt(d) + bias) V.  K (as [key_row(key)][hi d0..15 | lo
-// d0..15] fp16) and V (hi and lo, row-major in plain key order) sit in LDS; the bias rows
+// softmax(Q K^T / sqrt(d) + bias) V.  K (as [key][hi d0..15 | lo d0..15]
+// fp16) and V (hi and lo, row-major in key order) sit in LDS; the bias rows
 // of one query block (the "U strip") sit in registers.  Scores are computed
 // transposed, S^T = K Q^T, so that lane l holds query l%16 against keys
 // 4(l/16)+r; the softmax is exact (two passes over the strip); P V takes one
@@ -73,30 +73,39 @@ struct SlotBits {
 constexpr int kVRow = 16;
 
 // The P V A operand (V^T: row d = lane % 16, reduction slots 8 (lane / 16) ..
-// + 7 = keys k0 + 8 (lane / 16) .. + 7, k0 = 32 p for pair p) from row-major V
-// with two gfx950 LDS transpose reads.  Within a 16-lane group,
+// + 7, k0 = 32 p for pair p) from row-major V with two gfx950 LDS transpose
+// reads.  In the pair key order (kPairOrder) the slots of lane group g are the
+// keys k0 + 8g .. + 7; in the natural order they are k0 + 4g .. + 3 and
+// k0 + 16 + 4g .. + 3 (the keys that group's probabilities hold).  Within a 16-lane group,
 // ds_read_b64_tr_b16 gives lane 4c + d, slot e, element d of the 4-element
 // block addressed by lane 4e + c; so lane j addresses V[k + j / 4][4 (j % 4)]
 // and lane i receives V[k .. k + 3][i].
+template <bool kPairOrder>
 __device__ __forceinline__ v8h v_operand(const uint16_t *Vr, int k0) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     typedef __attribute__((address_space(3))) v4s *LdsV4s;
-    const uint16_t *p = Vr + (k0 + 8 * g + (c >> 2)) * kVRow + 4 * (c & 3);
+    const int row = kPairOrder ? k0 + 8 * g : k0 + 4 * g, step = kPairOrder ? 4 : 16;
+    const uint16_t *p = Vr + (row + (c >> 2)) * kVRow + 4 * (c & 3);
     const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4s)p);
-    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4s)(p + 4 * kVRow));
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsV4s)(p + step * kVRow));
     return __builtin_bit_cast(v8h, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Key order inside a pair of key blocks (keys 32p .. 32p+31): the score MFMA
-// of block t = 0, 1 of the pair puts key 32p + 8g + 4t + r in lane group g,
-// register r.  Lane group g's keys of both blocks are then the 8 consecutive
-// keys 32p + 8g .. +7: one contiguous U read per lane and pair, and V in
-// plain key order for P V.  key_row(k) is the K row (score A-operand row
-// 16 (2p + t) + 4g + r) that holds key k.
+// Key orders of the score MFMA (D row 4g + r of key block kb lands in lane
+// group g, register r).
+// * Natural (the float32 paths): K row = key, so block kb puts key
+//   16 kb + 4g + r in lane group g, register r.  A lane's U entries of a block
+//   are 4 consecutive floats: one 16-byte load per lane and block, and each
+//   load instruction reads 64 contiguous bytes of every row of the strip.
+// * Pair order (bfloat16): inside a pair of key blocks (keys 32p .. 32p+31)
+//   block t = 0, 1 puts key 32p + 8g + 4t + r in lane group g, register r.
+//   Lane group g's keys of both blocks are then the 8 consecutive keys
+//   32p + 8g .. +7: one 16-byte U read per lane and pair.  key_row(k) is the
+//   K row (score A-operand row 16 (2p + t) + 4g + r) that holds key k.
 __device__ __forceinline__ int key_row(int k) {
     return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
 }
-// Offset inside a U row of lane group g's 4 keys of key block kb.
+// Offset inside a U row of lane group g's 4 keys of key block kb (pair order).
 __device__ __forceinline__ int u_col(int kb, int g) {
     return 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
 }
@@ -122,7 +131,7 @@ __device__ __forceinline__ bool pair_real(const SlotBits<kWords> &real, int kb, 
 //   s = qk_mul (k . q) + u   (u = -inf for keys to exclude),
 //   p = exp(s - max s),  o = sum_k p v_k (lane layout of O^T), l = sum_k p.
 // qh / ql are this lane's split Q entries 8(g&1) .. +7 of query l%16; u is
-// the strip in the pair key order of key_row / u_col (U of padded keys inside
+// the strip in the natural key order (U of padded keys inside
 // a pair with a real key is replaced here; pairs without a real key must
 // already hold -inf).  K and V rows of keys that are not real must be 0 in LDS
 // for every pair below an even block count.  V hi / lo are row-major (kVRow).
@@ -137,10 +146,9 @@ __device__ __forceinline__ void attend_split(float4 (&u)[kT], v8h qh, v8h ql, fl
     for (int kb = 0; kb < kT; kb += 2) {
         const uint32_t bits = real.pair(kb >> 1);
         if (kb < T && bits != 0 && bits != 0xffffffffu) {
-            const uint32_t lb = bits >> (8 * g);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const uint32_t kbits = lb >> (4 * t);
+                const uint32_t kbits = bits >> (16 * t + 4 * g);
                 u[kb + t].x = (kbits & 1) ? u[kb + t].x : -INFINITY;
                 u[kb + t].y = (kbits & 2) ? u[kb + t].y : -INFINITY;
                 u[kb + t].z = (kbits & 4) ? u[kb + t].z : -INFINITY;
@@ -191,8 +199,8 @@ __device__ __forceinline__ void attend_split(float4 (&u)[kT], v8h qh, v8h ql, fl
             p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][r], kLog2e, -mb));
         }
         lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        const v8h vh = v_operand(Vh, kb * kTile);
-        const v8h vl = v_operand(Vl, kb * kTile);
+        const v8h vh = v_operand<false>(Vh, kb * kTile);
+        const v8h vl = v_operand<false>(Vl, kb * kTile);
         v8h ph, pl;
         split_f16<8>(p, ph, pl);
         o = mfma32h(vh, pl, o);
