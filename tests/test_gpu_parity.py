@@ -316,3 +316,65 @@ def test_single_full_jet_at_max_p_every_entry():
     assert_close(O, ref, TOL32, "O P=256")
     O2 = host(pip.pair_embed_attention(g(p4), g(mask), mlp, g(q), g(k), g(v)))
     assert_close(O2, ref, TOL32, "fused O P=256")
+
+
+# ---------------------------------------------------------------- masks that are not prefixes
+def scattered_mask(B, P, seed):
+    """Jet 0: a random half of the slots; jet 1: odd slots only; jet 2: the
+    last 40 slots; jet 3: two slots far apart (the rest of a jet is padding)."""
+    assert B == 4
+    m = np.zeros((B, P), dtype=np.uint8)
+    m[0, np.random.default_rng(seed).random(P) < 0.5] = 1
+    m[1, 1::2] = 1
+    m[2, P - 40:] = 1
+    m[3, [5, P - 8]] = 1
+    return m
+
+
+@pytest.mark.parametrize("P", [128, 160])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scattered_masks_every_entry(dtype, P):
+    # Work estimates and fast paths assume real slots first; any other layout
+    # may only move split points, never change a result.  Padded particles keep
+    # non-zero values, which every entry must ignore.
+    B = 4
+    mask = scattered_mask(B, P, seed=P)
+    p4, _ = ragged_jets(B, P, (P,) * B, seed=90 + P, hole=False)
+    params = mlp_for(90 + P, biases=True)
+    mlp = pip.PairMLP(params)
+    bf = dtype == "bf16"
+    tt = torch.bfloat16 if bf else None
+    real = pair_mask(mask)
+    what = "%s P=%d scattered" % (dtype, P)
+
+    U = host(pip.pair_embed(g(p4), g(mask), mlp, dtype=dtype))
+    Uref = oracle.pair_embed(p4, mask, params)
+    assert_close(U, Uref, TOLBF_U if bf else TOL32, "U " + what)
+    assert_zero_bits(U.transpose(0, 2, 3, 1), ~real, "U padding " + what)
+
+    q, k, v = rand_qkv(B, 8, P, mask, seed=91 + P, dtype=dtype)
+    Uin = Uref.astype(np.float32)
+    if bf:
+        Uin = synth.bf16_round(Uin)
+    O = host(pip.pair_bias_attention(g(q, tt), g(k, tt), g(v, tt), g(Uin, tt), g(mask)))
+    assert_close(O, oracle.attention(q, k, v, Uin, mask), TOLBF if bf else TOL32, "O " + what)
+    assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "O padded rows " + what)
+
+    O2 = host(pip.pair_embed_attention(g(p4), g(mask), mlp, g(q, tt), g(k, tt), g(v, tt)))
+    ref2 = oracle.pair_embed_attention(p4, mask, params, q, k, v)
+    assert_close(O2, ref2, TOLBF if bf else TOL32, "fused O " + what)
+    assert_zero_bits(O2.transpose(0, 2, 1, 3), mask == 0, "fused O padded rows " + what)
+
+    if not bf:
+        F = host(pip.pair_features(g(p4), g(mask)))
+        assert_close(F, oracle.pair_features(p4, mask), TOL32, "features " + what)
+        assert_zero_bits(F.transpose(0, 2, 3, 1), ~real, "features padding " + what)
+        x0, wq, wk, wv, wo = synth.make_block_stack(B, P, 128, 2, mask,
+                                                    rng=np.random.default_rng(92 + P))
+        X = g(x0)
+        pip.block_stack(X, g(wq), g(wk), g(wv), g(wo), g(Uin), g(mask))
+        got = host(X)
+        ref = oracle.block_stack(x0, wq, wk, wv, wo, Uin, mask)
+        sel = mask != 0
+        assert_close(got[sel], ref[sel], TOL32, "block stack X " + what)
+        np.testing.assert_array_equal(got[~sel].view(np.uint32), x0[~sel].view(np.uint32))
