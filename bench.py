@@ -246,8 +246,8 @@ def main():
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": 5}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the path shards over jets with no exchange, "
-              "and this build runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only (use --gpus 1): the path shards over jets with "
+              "no exchange, and only the single-MI355X kernel is implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
