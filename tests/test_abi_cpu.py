@@ -127,3 +127,16 @@ def test_fold_validation(L):
     with pytest.raises(binding.PipError) as e:
         binding.fold(q)
     assert e.value.status == NULL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # bench.py times one GPU; N > 1 must end with a message and status 2,
+    # before any GPU work
+    import os
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""
