@@ -62,7 +62,9 @@ typedef enum {
     PIP_ERR_DTYPE = 4,       /* unknown dtype code */
     PIP_ERR_UNSUPPORTED = 5, /* well-formed but outside what the kernels take
                                 (P % 16 != 0, P > 256, D != 16, H != 8 where fixed, ...) */
-    PIP_ERR_HIP = 6          /* a HIP runtime call (launch, alloc, copy) failed */
+    PIP_ERR_HIP = 6,         /* a HIP runtime call (launch, alloc, copy) failed */
+    PIP_ERR_VALUE = 7        /* a scalar argument is outside its domain (a scale that is
+                                not finite) */
 } pip_status;
 
 typedef enum { PIP_F32 = 0, PIP_BF16 = 1 } pip_dtype;
@@ -99,8 +101,10 @@ int pip_version(void);
  * Touches no GPU.  Errors: PIP_ERR_NULL, PIP_ERR_SHAPE (var + eps <= 0). */
 pip_status pip_pair_mlp_fold(const pip_pair_mlp_params *raw, float *w_out, float *b_out);
 
-/* Fold (as pip_pair_mlp_fold), repack into MFMA operand order (float32 and
- * bfloat16 copies) and upload to the CURRENT device.  *out receives a handle
+/* Fold (as pip_pair_mlp_fold), repack into MFMA operand order and upload to
+ * the CURRENT device.  The handle holds every operand form the kernels take
+ * (float32, fp16 hi / lo and bfloat16), so it has no dtype of its own: the
+ * compute entries choose the precision per call.  *out receives a handle
  * the caller frees with pip_pair_mlp_destroy.  Allocates device memory once
  * (about 60 KB); not meant for the hot loop.
  * Errors: PIP_ERR_NULL, PIP_ERR_SHAPE, PIP_ERR_HIP. */
@@ -130,28 +134,37 @@ pip_status pip_pair_embed(const float *p4, const uint8_t *mask, int64_t B, int64
                           const pip_pair_mlp *mlp, void *U, int u_dtype, void *stream);
 
 /* Masked biased attention ("Fusion 3"): for every head h and real query a,
- *   O[b,h,a,:] = sum_c softmax_c(Q[b,h,a,:] . K[b,h,c,:] / sqrt(D) + U[b,h,a,c]) V[b,h,c,:]
- * over real keys c only; padded query rows are 0.  Q, K, V, O are (B, H, P, D),
- * U is (B, H, P, P), all in `dtype` (PIP_BF16: bf16 storage, MFMA in bf16
- * with float32 accumulation, softmax in float32).
+ *   O[b,h,a,:] = sum_c softmax_c(scale * Q[b,h,a,:] . K[b,h,c,:] + U[b,h,a,c]) V[b,h,c,:]
+ * over real keys c only; padded query rows are 0.  "Fusion 3" writes the
+ * score scale as 1/sqrt(d); `scale` is that factor, passed by the caller
+ * (0.25 for D = 16), and must be finite (PIP_ERR_VALUE otherwise).  U is
+ * added after the scaling, unscaled.  Q, K, V, O are (B, H, P, D), U is
+ * (B, H, P, P), all in `dtype`.
+ * PIP_F32: float32-faithful; the products run on the fp16 matrix cores with
+ * split operands (hi + lo), K and V scaled per head and Q per row by exact
+ * powers of two first, so any finite magnitudes keep ~2^-22 relative product
+ * error.  Real Q, K or V entries that are not finite give non-finite outputs
+ * in the rows they reach.
+ * PIP_BF16: bf16 storage, MFMA in bf16 with float32 accumulation, softmax in
+ * float32.
  * Requires D == 16, P % 16 == 0, 16 <= P <= 256, H >= 1.  Errors: NULL,
- * SHAPE, ALIGN, DTYPE, UNSUPPORTED, HIP. */
+ * SHAPE, ALIGN, DTYPE, UNSUPPORTED, VALUE, HIP. */
 pip_status pip_pair_bias_attention(const void *Q, const void *K, const void *V, const void *U,
                                    const uint8_t *mask, int64_t B, int64_t H, int64_t P,
-                                   int64_t D, void *O, int dtype, void *stream);
+                                   int64_t D, float scale, void *O, int dtype, void *stream);
 
 /* Fused pair embedding + attention with H = 8: the same O as pip_pair_embed
- * followed by pip_pair_bias_attention, but U only ever lives on chip.
- * Q, K, V, O are (B, 8, P, D) in `dtype` (PIP_BF16: the MLP as in
+ * followed by pip_pair_bias_attention (same `scale`), but U only ever lives
+ * on chip.  Q, K, V, O are (B, 8, P, D) in `dtype` (PIP_BF16: the MLP as in
  * pip_pair_embed's bf16 mode, U kept in float32 on chip, attention as in
  * pip_pair_bias_attention's bf16 mode).  Unlike the other entries it also
  * requires `mask` to be 16-byte aligned (rows are read as 16-byte vectors).
  * Requires D == 16, P % 16 == 0, 16 <= P <= 256.  Errors: NULL, SHAPE,
- * ALIGN, DTYPE, UNSUPPORTED, HIP. */
+ * ALIGN, DTYPE, UNSUPPORTED, VALUE, HIP. */
 pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
                                     const pip_pair_mlp *mlp, const void *Q, const void *K,
-                                    const void *V, int64_t B, int64_t P, int64_t D, void *O,
-                                    int dtype, void *stream);
+                                    const void *V, int64_t B, int64_t P, int64_t D, float scale,
+                                    void *O, int dtype, void *stream);
 
 /* Bytes of device workspace pip_block_stack needs for L layers: the attention
  * output of a layer (B * P * C floats) plus every layer's weights packed as

@@ -54,9 +54,10 @@ def lib():
         L.oracle_pair_features.argtypes = [dp, u8p, i64, i64, C.c_double, dp]
         L.oracle_pair_mlp.argtypes = [dp, u8p, i64, i64, C.POINTER(_Mlp), dp]
         L.oracle_pair_embed.argtypes = [dp, u8p, i64, i64, C.c_double, C.POINTER(_Mlp), dp]
-        L.oracle_attention.argtypes = [dp, dp, dp, dp, u8p, i64, i64, i64, i64, dp]
+        L.oracle_attention.argtypes = [dp, dp, dp, dp, u8p, i64, i64, i64, i64, C.c_double, dp]
         L.oracle_pair_embed_attention.argtypes = [dp, u8p, i64, i64, C.c_double,
-                                                  C.POINTER(_Mlp), dp, dp, dp, i64, dp]
+                                                  C.POINTER(_Mlp), dp, dp, dp, i64, C.c_double,
+                                                  dp]
         L.oracle_block_stack.argtypes = [dp, dp, dp, dp, dp, dp, u8p, i64, i64, i64, i64,
                                          i64, dp]
         for f in ("oracle_pair_features", "oracle_pair_mlp", "oracle_pair_embed",
@@ -176,30 +177,34 @@ def pair_embed(p4, mask, params: dict, eps: float = EPS) -> np.ndarray:
     return U
 
 
-def attention(Q, K, V, U, mask) -> np.ndarray:
-    """O (B, H, P, D): masked softmax(Q K^T / sqrt(D) + U) V per head."""
+def attention(Q, K, V, U, mask, scale=None) -> np.ndarray:
+    """O (B, H, P, D): masked softmax(scale Q K^T + U) V per head; scale
+    defaults to 1 / sqrt(D)."""
     q, k, v, u = _f64(Q), _f64(K), _f64(V), _f64(U)
     B, H, P, D = q.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     assert k.shape == q.shape and v.shape == q.shape and u.shape == (B, H, P, P)
     m = _u8(mask)
     O = np.zeros((B, H, P, D))
     rc = lib().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(m), B, H, P, D,
-                                _ptr(O))
+                                scale, _ptr(O))
     assert rc == 0
     return O
 
 
-def pair_embed_attention(p4, mask, params: dict, Q, K, V, eps: float = EPS) -> np.ndarray:
+def pair_embed_attention(p4, mask, params: dict, Q, K, V, eps: float = EPS,
+                         scale=None) -> np.ndarray:
     p = _f64(p4)
     q, k, v = _f64(Q), _f64(K), _f64(V)
     B, H, P, D = q.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     assert H == 8 and p.shape == (B, P, 4)
     m = _u8(mask)
     a = _MlpArgs(params)
     O = np.zeros((B, H, P, D))
     rc = lib().oracle_pair_embed_attention(_ptr(p), _ptr(m), B, P, float(eps),
                                            C.byref(a.struct), _ptr(q), _ptr(k), _ptr(v), D,
-                                           _ptr(O))
+                                           scale, _ptr(O))
     assert rc == 0
     return O
 

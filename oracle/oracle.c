@@ -225,13 +225,13 @@ int oracle_pair_embed(const double *p4, const uint8_t *mask, int64_t B, int64_t 
 
 /* ------------------------------------------------------------ attention */
 /* One head of masked biased attention for one jet ([R] Fusion 3):
- * for each real query a, s_c = (q_a . k_c) / sqrt(D) + Ub[a, c] over real keys
- * c, p = softmax(s) (two passes: max, then exp and sum), O_a = sum_c p_c v_c.
+ * for each real query a, s_c = scale (q_a . k_c) + Ub[a, c] over real keys c
+ * (Fusion 3 writes the scale as 1/sqrt(d)), p = softmax(s) (two passes: max,
+ * then exp and sum), O_a = sum_c p_c v_c.
  * q, k, v, o are (P, ld) with the head's D columns starting at column 0. */
 static void attention_head(const double *q, const double *k, const double *v, int64_t ld,
                            const double *Ub, const uint8_t *mj, int64_t P, int64_t D,
-                           double *o, double *s) {
-    double scale = 1.0 / sqrt((double)D);
+                           double scale, double *o, double *s) {
     for (int64_t a = 0; a < P; ++a) {
         double *oa = o + a * ld;
         for (int64_t d = 0; d < D; ++d) oa[d] = 0.0;
@@ -262,10 +262,10 @@ static void attention_head(const double *q, const double *k, const double *v, in
 }
 
 /* O (B, H, P, D) = masked biased attention of Q, K, V (B, H, P, D) with bias
- * U (B, H, P, P). */
+ * U (B, H, P, P) and score scale `scale` (1/sqrt(D) in the pages' formula). */
 int oracle_attention(const double *Q, const double *K, const double *V, const double *U,
                      const uint8_t *mask, int64_t B, int64_t H, int64_t P, int64_t D,
-                     double *O) {
+                     double scale, double *O) {
     if (!Q || !K || !V || !U || !mask || !O || B < 0 || H < 1 || P < 0 || D < 1) return 1;
 #pragma omp parallel
     {
@@ -275,7 +275,7 @@ int oracle_attention(const double *Q, const double *K, const double *V, const do
             int64_t b = bh / H;
             size_t off = (size_t)bh * P * D;
             attention_head(Q + off, K + off, V + off, D, U + (size_t)bh * P * P, mask + b * P,
-                           P, D, O + off, s);
+                           P, D, scale, O + off, s);
         }
         free(s);
     }
@@ -286,12 +286,13 @@ int oracle_attention(const double *Q, const double *K, const double *V, const do
  * reproduce): O (B, 8, P, D). */
 int oracle_pair_embed_attention(const double *p4, const uint8_t *mask, int64_t B, int64_t P,
                                 double eps, const oracle_mlp *m, const double *Q,
-                                const double *K, const double *V, int64_t D, double *O) {
+                                const double *K, const double *V, int64_t D, double scale,
+                                double *O) {
     if (!p4 || !mask || !m || !Q || !K || !V || !O) return 1;
     double *U = (double *)malloc(sizeof(double) * (size_t)B * NOUT * P * P);
     if (!U) return 2;
     int rc = oracle_pair_embed(p4, mask, B, P, eps, m, U);
-    if (!rc) rc = oracle_attention(Q, K, V, U, mask, B, NOUT, P, D, O);
+    if (!rc) rc = oracle_attention(Q, K, V, U, mask, B, NOUT, P, D, scale, O);
     free(U);
     return rc;
 }
@@ -339,7 +340,7 @@ int oracle_block_stack(const double *X0, const double *Wq, const double *Wk, con
                 for (int64_t h = 0; h < H; ++h)
                     attention_head(q + h * D, k + h * D, v + h * D, C,
                                    U + ((size_t)b * H + h) * P * P, mask + b * P, P, D,
-                                   o + h * D, s);
+                                   1.0 / sqrt((double)D), o + h * D, s);
                 matmul(o, Wo + l * C * C, P, C, t);
                 for (int64_t i = 0; i < P * C; ++i) X[i] += t[i];
             }

@@ -9,6 +9,7 @@ has no fallback.
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 import re
 
@@ -20,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pip.h")
 
 PIP_F32, PIP_BF16 = 0, 1
 STATUS = {0: "PIP_OK", 1: "PIP_ERR_NULL", 2: "PIP_ERR_SHAPE", 3: "PIP_ERR_ALIGN",
-          4: "PIP_ERR_DTYPE", 5: "PIP_ERR_UNSUPPORTED", 6: "PIP_ERR_HIP"}
+          4: "PIP_ERR_DTYPE", 5: "PIP_ERR_UNSUPPORTED", 6: "PIP_ERR_HIP", 7: "PIP_ERR_VALUE"}
 W_FOLDED = 64 * 4 + 2 * 64 * 64 + 8 * 64
 B_FOLDED = 3 * 64 + 8
 
@@ -70,8 +71,11 @@ def lib():
         L.pip_pair_mlp_destroy.argtypes = [vp]
         L.pip_pair_features.argtypes = [vp, vp, i64, i64, vp, vp]
         L.pip_pair_embed.argtypes = [vp, vp, i64, i64, vp, vp, i, vp]
-        L.pip_pair_bias_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i, vp]
-        L.pip_pair_embed_attention.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, i, vp]
+        f32 = C.c_float
+        L.pip_pair_bias_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, vp,
+                                              i, vp]
+        L.pip_pair_embed_attention.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp,
+                                               i, vp]
         L.pip_block_stack_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.pip_block_stack_workspace_bytes.restype = C.c_size_t
         L.pip_block_stack.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
@@ -216,32 +220,37 @@ def pair_embed(p4, mask, mlp: PairMLP, dtype="f32", out=None):
     return out
 
 
-def pair_bias_attention(q, k, v, u, mask, out=None):
-    """O (B, H, P, D) = masked softmax(Q K^T / sqrt(D) + U) V, dtype of q."""
+def pair_bias_attention(q, k, v, u, mask, out=None, scale=None):
+    """O (B, H, P, D) = masked softmax(scale Q K^T + U) V, dtype of q;
+    scale defaults to 1 / sqrt(D)."""
     torch = _torch()
     code, tdt = _code(q.dtype)
     B, H, P, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
     st = lib().pip_pair_bias_attention(
         _dev(q, "Q", tdt), _dev(k, "K", tdt, q.shape), _dev(v, "V", tdt, q.shape),
         _dev(u, "U", tdt, (B, H, P, P)), _dev(mask, "mask", torch.uint8, (B, P)), B, H, P, D,
-        _dev(out, "O", tdt, q.shape), code, _stream())
+        scale, _dev(out, "O", tdt, q.shape), code, _stream())
     _check("pip_pair_bias_attention", st)
     return out
 
 
-def pair_embed_attention(p4, mask, mlp: PairMLP, q, k, v, out=None):
-    """Fused pair embedding + attention (H = 8): O (B, 8, P, D), dtype of q."""
+def pair_embed_attention(p4, mask, mlp: PairMLP, q, k, v, out=None, scale=None):
+    """Fused pair embedding + attention (H = 8): O (B, 8, P, D), dtype of q;
+    scale defaults to 1 / sqrt(D)."""
     torch = _torch()
     code, tdt = _code(q.dtype)
     B, H, P, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
     st = lib().pip_pair_embed_attention(
         _dev(p4, "p4", torch.float32, (B, P, 4)), _dev(mask, "mask", torch.uint8, (B, P)),
         mlp.handle, _dev(q, "Q", tdt, (B, 8, P, D)), _dev(k, "K", tdt, q.shape),
-        _dev(v, "V", tdt, q.shape), B, P, D, _dev(out, "O", tdt, q.shape), code, _stream())
+        _dev(v, "V", tdt, q.shape), B, P, D, scale, _dev(out, "O", tdt, q.shape), code,
+        _stream())
     _check("pip_pair_embed_attention", st)
     return out
 

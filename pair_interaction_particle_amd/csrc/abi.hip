@@ -54,6 +54,7 @@ const char *pip_status_string(int s) {
         case PIP_ERR_DTYPE: return "unknown dtype";
         case PIP_ERR_UNSUPPORTED: return "unsupported size or configuration";
         case PIP_ERR_HIP: return "HIP runtime error";
+        case PIP_ERR_VALUE: return "invalid argument value";
         default: return "unknown status";
     }
 }
@@ -259,11 +260,12 @@ pip_status pip_pair_embed(const float *p4, const uint8_t *mask, int64_t B, int64
 
 pip_status pip_pair_bias_attention(const void *Q, const void *K, const void *V, const void *U,
                                    const uint8_t *mask, int64_t B, int64_t H, int64_t P,
-                                   int64_t D, void *O, int dtype, void *stream) {
+                                   int64_t D, float scale, void *O, int dtype, void *stream) {
     if (dtype != PIP_F32 && dtype != PIP_BF16) return PIP_ERR_DTYPE;
     if (H < 0 || D < 0) return PIP_ERR_SHAPE;
     pip_status st = check_pair_grid(B, P);
     if (st != PIP_OK) return st;
+    if (!std::isfinite(scale)) return PIP_ERR_VALUE;
     if (B == 0 || P == 0 || H == 0) return PIP_OK;
     if (!Q || !K || !V || !U || !mask || !O) return PIP_ERR_NULL;
     if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
@@ -275,20 +277,24 @@ pip_status pip_pair_bias_attention(const void *Q, const void *K, const void *V, 
     if (dtype == PIP_F32)
         return hip_status(pip::launch_attention_f32((const float *)Q, (const float *)K,
                                                     (const float *)V, (const float *)U, mask,
-                                                    (int)B, (int)H, (int)P, (float *)O, s));
+                                                    (int)B, (int)H, (int)P, scale, (float *)O,
+                                                    s));
     return hip_status(pip::launch_attention_bf16((const uint16_t *)Q, (const uint16_t *)K,
                                                  (const uint16_t *)V, (const uint16_t *)U, mask,
-                                                 (int)B, (int)H, (int)P, (uint16_t *)O, s));
+                                                 (int)B, (int)H, (int)P, scale, (uint16_t *)O,
+                                                 s));
 }
 
 pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
                                     const pip_pair_mlp *mlp, const void *Q, const void *K,
-                                    const void *V, int64_t B, int64_t P, int64_t D, void *O,
-                                    int dtype, void *stream) {
+                                    const void *V, int64_t B, int64_t P, int64_t D, float scale,
+                                    void *O, int dtype, void *stream) {
     if (dtype != PIP_F32 && dtype != PIP_BF16) return PIP_ERR_DTYPE;
     if (D < 0) return PIP_ERR_SHAPE;
     pip_status st = check_pair_grid(B, P);
-    if (st != PIP_OK || B == 0 || P == 0) return st;
+    if (st != PIP_OK) return st;
+    if (!std::isfinite(scale)) return PIP_ERR_VALUE;
+    if (B == 0 || P == 0) return PIP_OK;
     if (!p4 || !mask || !mlp || !Q || !K || !V || !O) return PIP_ERR_NULL;
     if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
     if (!aligned16(p4) || !aligned16(mask) || !aligned16(Q) || !aligned16(K) ||
@@ -299,10 +305,11 @@ pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
     if (dtype == PIP_F32)
         return hip_status(pip::launch_embed_attention_f32(p4, mask, (int)B, (int)P, mlp,
                                                           (const float *)Q, (const float *)K,
-                                                          (const float *)V, (float *)O, s));
+                                                          (const float *)V, scale, (float *)O,
+                                                          s));
     return hip_status(pip::launch_embed_attention_bf16(
         p4, mask, (int)B, (int)P, mlp, (const uint16_t *)Q, (const uint16_t *)K,
-        (const uint16_t *)V, (uint16_t *)O, s));
+        (const uint16_t *)V, scale, (uint16_t *)O, s));
 }
 
 size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C, int64_t L) {

@@ -48,71 +48,30 @@ constexpr int kAttnQBlocks = 8;  // query blocks per workgroup
 // ------------------------------------------------------------ float32
 // One query block (rows q0 .. q0+15) of a float32 head.  u is the U strip
 // (-inf for key blocks without a real key), qa / qc are this lane's Q row
-// entries 8(g&1) .. +3 and +4 .. +7 (0 for padded queries).
+// entries 8(g&1) .. +3 and +4 .. +7 (0 for padded queries).  K and V sit in
+// LDS scaled by the head's powers of two (kinv, vinv undo them); each query
+// row is scaled here by its own power of two before the split, so a row of
+// any magnitude keeps 22 significand bits against K of any magnitude.
 template <int kT, int kWords>
 __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc, bool rq,
-                                           bool kvbad, const SlotBits<kWords> &real, int T,
+                                           float qk_mul, float vinv,
+                                           const SlotBits<kWords> &real, int T,
                                            const uint16_t *Ks, const uint16_t *Vsh,
-                                           const uint16_t *Vsl, const float *__restrict__ Qh,
-                                           const float *__restrict__ Kh,
-                                           const float *__restrict__ Vh,
-                                           const float *__restrict__ urow, int q0,
-                                           float *__restrict__ orow) {
-    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-    float m = -INFINITY, lsum = 0.f;
-    v4f o = {0.f, 0.f, 0.f, 0.f};
-    if (!(kvbad || __any(rq && !(f16_safe(qa) && f16_safe(qc))))) {
-        v8h qh, ql;
-        {
-            v4h h0, l0, h1, l1;
-            split4_f16(qa, h0, l0);
-            split4_f16(qc, h1, l1);
-            qh = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-            ql = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        attend_split<kT>(u, qh, ql, 0.25f, real, T, Ks, Vsh, Vsl, o, lsum);
-    } else {
-        // A real Q, K or V value beyond the fp16 range: float32 MFMA with an
-        // online softmax, everything re-read from global memory (rare path).
-        const float4 qv = rq ? *(const float4 *)(Qh + (size_t)(q0 + c) * 16 + 4 * g)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int kb = 0; kb < T; ++kb) {
-            const uint32_t bits = real.block_rt(kb);
-            if (!bits) continue;
-            const uint32_t kbits = bits >> (4 * g);
-            const int kr = kb * kTile + c;
-            const float4 kv = real.slot(kr) ? *(const float4 *)(Kh + (size_t)kr * 16 + 4 * g)
-                                            : make_float4(0.f, 0.f, 0.f, 0.f);
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma4(kv.x, qv.x, acc);
-            acc = mfma4(kv.y, qv.y, acc);
-            acc = mfma4(kv.z, qv.z, acc);
-            acc = mfma4(kv.w, qv.w, acc);
-            const float4 uv = *(const float4 *)(urow + kb * kTile);
-            const float uu[4] = {uv.x, uv.y, uv.z, uv.w};
-            float sb[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sb[r] = ((kbits >> r) & 1) ? fmaf(acc[r], 0.25f, uu[r]) : -INFINITY;
-            const float bm = xmax16(fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
-            const float mn = fmaxf(m, bm);
-            const float corr = __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-            m = mn;
-            lsum *= corr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] *= corr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = __builtin_amdgcn_exp2f((sb[r] - m) * kLog2e);
-                lsum += p;
-                const int kk = kb * kTile + 4 * g + r;
-                const float vv = ((kbits >> r) & 1) ? Vh[(size_t)kk * 16 + c] : 0.f;
-                o = mfma4(vv, p, o);
-            }
-        }
-        lsum = xsum16(lsum);
+                                           const uint16_t *Vsl, float *__restrict__ orow) {
+    float qsc, qinv;
+    pow2_scale(xmax16(fmaxf(absmax4(qa), absmax4(qc))), qsc, qinv);
+    v8h qh, ql;
+    {
+        v4h h0, l0, h1, l1;
+        split4_f16(make_float4(qa.x * qsc, qa.y * qsc, qa.z * qsc, qa.w * qsc), h0, l0);
+        split4_f16(make_float4(qc.x * qsc, qc.y * qsc, qc.z * qsc, qc.w * qsc), h1, l1);
+        qh = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+        ql = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    const float inv = 1.0f / lsum;
+    v4f o;
+    float lsum;
+    attend_split<kT>(u, qh, ql, qk_mul * qinv, real, T, Ks, Vsh, Vsl, o, lsum);
+    const float inv = vinv / lsum;
     *(float4 *)orow = rq ? make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
 }
@@ -121,7 +80,7 @@ __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc
 // One query block of a bf16 head.  u holds bf16 pairs (-inf for key blocks
 // without a real key), qv this lane's Q row entries 4g .. 4g+3.
 template <int kT, int kWords>
-__device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
+__device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq, float scale,
                                             const SlotBits<kWords> &real, int T,
                                             const uint16_t *Ks, const uint16_t *Vsh,
                                             uint16_t *__restrict__ orow) {
@@ -154,14 +113,14 @@ __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq,
         const v4f a0 = mfma16bf(k0, qv, (v4f){0.f, 0.f, 0.f, 0.f});
         const v4f a1 = mfma16bf(k1, qv, (v4f){0.f, 0.f, 0.f, 0.f});
         float s0[4], s1[4];
-        s0[0] = fmaf(a0[0], 0.25f, bf2f(u[kb].x & 0xffff));
-        s0[1] = fmaf(a0[1], 0.25f, bf2f(u[kb].x >> 16));
-        s0[2] = fmaf(a0[2], 0.25f, bf2f(u[kb].y & 0xffff));
-        s0[3] = fmaf(a0[3], 0.25f, bf2f(u[kb].y >> 16));
-        s1[0] = fmaf(a1[0], 0.25f, bf2f(u[kb + 1].x & 0xffff));
-        s1[1] = fmaf(a1[1], 0.25f, bf2f(u[kb + 1].x >> 16));
-        s1[2] = fmaf(a1[2], 0.25f, bf2f(u[kb + 1].y & 0xffff));
-        s1[3] = fmaf(a1[3], 0.25f, bf2f(u[kb + 1].y >> 16));
+        s0[0] = fmaf(a0[0], scale, bf2f(u[kb].x & 0xffff));
+        s0[1] = fmaf(a0[1], scale, bf2f(u[kb].x >> 16));
+        s0[2] = fmaf(a0[2], scale, bf2f(u[kb].y & 0xffff));
+        s0[3] = fmaf(a0[3], scale, bf2f(u[kb].y >> 16));
+        s1[0] = fmaf(a1[0], scale, bf2f(u[kb + 1].x & 0xffff));
+        s1[1] = fmaf(a1[1], scale, bf2f(u[kb + 1].x >> 16));
+        s1[2] = fmaf(a1[2], scale, bf2f(u[kb + 1].y & 0xffff));
+        s1[3] = fmaf(a1[3], scale, bf2f(u[kb + 1].y >> 16));
         const float mn = fmaxf(m, xmax16(max8(s0, s1)));
         const float corr = __builtin_amdgcn_exp2f((m - mn) * kLog2e);
         m = mn;
@@ -192,7 +151,8 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ)
 __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_kernel(
     const AttnElt<kBf16> *__restrict__ Q, const AttnElt<kBf16> *__restrict__ K,
     const AttnElt<kBf16> *__restrict__ V, const AttnElt<kBf16> *__restrict__ U,
-    const uint8_t *__restrict__ mask, int H, int P, int chunks, AttnElt<kBf16> *__restrict__ O) {
+    const uint8_t *__restrict__ mask, int H, int P, int chunks, float scale,
+    AttnElt<kBf16> *__restrict__ O) {
     using E = AttnElt<kBf16>;
     constexpr int kWaves = kAttnQBlocks / kQ, kThreads = 64 * kWaves;
     constexpr int kWords = (kT * 16 + 63) / 64;
@@ -204,7 +164,7 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kT * 16 * kKRow];
     __shared__ __attribute__((aligned(16))) uint16_t Vsh[kT * 16 * kVRow];
     __shared__ __attribute__((aligned(16))) uint16_t Vsl[kBf16 ? 1 : kT * 16 * kVRow];
-    __shared__ int badw[kWaves];
+    __shared__ float kvmax[2][kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -274,8 +234,35 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
         }
     }
 
-    // ---- 2. K and V into LDS
-    bool bad = false;  // a real K or V value outside the fp16-safe range
+    // ---- 2. K and V into LDS.  float32: the head's largest |K| and |V| over
+    // real keys first (one barrier), then K and V scaled by powers of two
+    // into [2^13, 2^14) and split into fp16 hi / lo.
+    float ksc = 1.f, kinv = 1.f, vsc = 1.f, vinv = 1.f;
+    if constexpr (!kBf16) {
+        float kmx = 0.f, vmx = 0.f;
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int i = tid + it * kThreads, k = i >> 2;
+            if (i >= nst * 4 || !(k < P && real.slot(k))) continue;
+            kmx = fmaxf(kmx, absmax4(kk[it]));
+            vmx = fmaxf(vmx, absmax4(vv[it]));
+        }
+        kmx = wave_max(kmx);
+        vmx = wave_max(vmx);
+        if (lane == 0) {
+            kvmax[0][wave] = kmx;
+            kvmax[1][wave] = vmx;
+        }
+        __syncthreads();
+        float km = 0.f, vm = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            km = fmaxf(km, kvmax[0][w]);
+            vm = fmaxf(vm, kvmax[1][w]);
+        }
+        pow2_scale(km, ksc, kinv);
+        pow2_scale(vm, vsc, vinv);
+    }
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
         const int i = tid + it * kThreads, k = i >> 2, d0 = (i & 3) * 4;
@@ -289,8 +276,9 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
             *(uint2 *)(Vsh + k * kVRow + d0) = vz;
         } else {
             const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-            const float4 kz = rk ? kk[it] : zero, vz = rk ? vv[it] : zero;
-            bad |= !(f16_safe(kz) && f16_safe(vz));
+            const float4 a = kk[it], b = vv[it];
+            const float4 kz = rk ? make_float4(a.x * ksc, a.y * ksc, a.z * ksc, a.w * ksc) : zero;
+            const float4 vz = rk ? make_float4(b.x * vsc, b.y * vsc, b.z * vsc, b.w * vsc) : zero;
             v4h kh, kl, vh, vl;
             split4_f16(kz, kh, kl);
             split4_f16(vz, vh, vl);
@@ -300,13 +288,7 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
             *(v4h *)(Vsl + k * kVRow + d0) = vl;
         }
     }
-    // one flag word per wave; __syncthreads() (not a workgroup-reduction
-    // primitive) is what orders the LDS stores above before the reads below
-    if (lane == 0) badw[wave] = __any(bad);
     __syncthreads();
-    bool kvbad = false;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) kvbad |= badw[w] != 0;
 
     // ---- 3. per query block
 #pragma unroll
@@ -331,11 +313,12 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
         }
         const bool rq = real.slot(q0 + c);
         if constexpr (kBf16) {
-            attend_bf16<kT>(u[j], rq ? qb16[j] : (v4s){0, 0, 0, 0}, rq, real, T, Ks, Vsh, orow);
+            attend_bf16<kT>(u[j], rq ? qb16[j] : (v4s){0, 0, 0, 0}, rq, scale, real, T, Ks, Vsh,
+                            orow);
         } else {
             const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-            attend_f32<kT>(u[j], rq ? qa[j] : zero, rq ? qc[j] : zero, rq, kvbad, real, T, Ks,
-                           Vsh, Vsl, Qh, Kh, Vh, U + (base + q0 + c) * P + 4 * g, q0, orow);
+            attend_f32<kT>(u[j], rq ? qa[j] : zero, rq ? qc[j] : zero, rq, scale * kinv, vinv,
+                           real, T, Ks, Vsh, Vsl, orow);
         }
     }
 }
@@ -345,29 +328,29 @@ int attention_chunks(int P) { return (P / kTile + kAttnQBlocks - 1) / kAttnQBloc
 template <bool kBf16>
 static hipError_t launch_attention(const AttnElt<kBf16> *Q, const AttnElt<kBf16> *K,
                                    const AttnElt<kBf16> *V, const AttnElt<kBf16> *U,
-                                   const uint8_t *mask, int B, int H, int P,
+                                   const uint8_t *mask, int B, int H, int P, float scale,
                                    AttnElt<kBf16> *O, hipStream_t s) {
     const int chunks = attention_chunks(P);
     const dim3 grid((unsigned)((size_t)B * H * chunks));
     if (P <= 128)
         hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1>), grid, dim3(64 * kAttnQBlocks), 0,
-                           s, Q, K, V, U, mask, H, P, chunks, O);
+                           s, Q, K, V, U, mask, H, P, chunks, scale, O);
     else
         hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1>), grid, dim3(64 * kAttnQBlocks), 0, s,
-                           Q, K, V, U, mask, H, P, chunks, O);
+                           Q, K, V, U, mask, H, P, chunks, scale, O);
     return hipGetLastError();
 }
 
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V,
                                 const float *U, const uint8_t *mask, int B, int H, int P,
-                                float *O, hipStream_t s) {
-    return launch_attention<false>(Q, K, V, U, mask, B, H, P, O, s);
+                                float scale, float *O, hipStream_t s) {
+    return launch_attention<false>(Q, K, V, U, mask, B, H, P, scale, O, s);
 }
 
 hipError_t launch_attention_bf16(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                  const uint16_t *U, const uint8_t *mask, int B, int H, int P,
-                                 uint16_t *O, hipStream_t s) {
-    return launch_attention<true>(Q, K, V, U, mask, B, H, P, O, s);
+                                 float scale, uint16_t *O, hipStream_t s) {
+    return launch_attention<true>(Q, K, V, U, mask, B, H, P, scale, O, s);
 }
 
 }  // namespace pip

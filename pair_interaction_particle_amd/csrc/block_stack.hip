@@ -29,20 +29,6 @@ namespace pip {
 constexpr int kStackWaves = 4;
 constexpr int kStackThreads = 64 * kStackWaves;
 
-// Power-of-two scale s (and 1/s) that puts amax into [2^13, 2^14); 1 for
-// zero, inf or NaN.
-__device__ __forceinline__ void pow2_scale(float amax, float &s, float &inv) {
-    const int eb = (int)((__float_as_uint(amax) >> 23) & 0xff);
-    if (!(amax > 0.f) || eb == 255) {
-        s = inv = 1.f;
-        return;
-    }
-    int e = 13 - (eb - 127);
-    e = min(max(e, -126), 126);
-    s = __uint_as_float((uint32_t)(e + 127) << 23);
-    inv = __uint_as_float((uint32_t)(127 - e) << 23);
-}
-
 // ------------------------------------------------------------ prep
 // One workgroup per (layer, matrix, column tile nt).  Packed operand index:
 // (((layer * 4 + m) * NT + nt) * KS + s) * 64 + lane, 8 halves each; slot j
@@ -396,13 +382,6 @@ __attribute__((amdgpu_waves_per_eu(kKS <= 4 ? 4 : 1))) void stack_out_kernel(
 //      head-major (B, H, P, 16) buffer the Wo step reads.
 constexpr int kSaWaves = 8;
 constexpr int kSaThreads = 64 * kSaWaves;
-
-__device__ __forceinline__ float wave_max(float x) {
-    x = xmax16(x);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-    return x;
-}
 
 template <int kT, int kKS>
 __global__ __launch_bounds__(kSaThreads) void stack_attention_kernel(

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
     const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B, int P, int sort,
     const float4 *__restrict__ w32, const v8bf *__restrict__ w16, const v8h *__restrict__ wx2,
     const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
-    const QkvT<kBf16> *__restrict__ K, const QkvT<kBf16> *__restrict__ V,
+    const QkvT<kBf16> *__restrict__ K, const QkvT<kBf16> *__restrict__ V, float qk2,
     QkvT<kBf16> *__restrict__ O) {
     MlpLds<kMode> M;
     __shared__ PartLds<kJetMaxP> L;
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
         for (int r = 0; r < 4; ++r) {
             kreal[r] = L.real[k0 + 4 * g + r];
             const float u = transposed ? Ut[4 * g + r][c] : Ut[c][4 * g + r];
-            s[r] = kreal[r] ? fmaf(s[r], kQkScale2, u * kLog2e) : -INFINITY;
+            s[r] = kreal[r] ? fmaf(s[r], qk2, u * kLog2e) : -INFINITY;
         }
         float m = mst[h][qb][c], l = lst[h][qb][c];
         const float corr = online_softmax(s, m, l);
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
     const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
     const float4 *__restrict__ w32, const v8bf *__restrict__ w16, const v8h *__restrict__ wx2,
     const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
-    const QkvT<kBf16> *__restrict__ K, const QkvT<kBf16> *__restrict__ V,
+    const QkvT<kBf16> *__restrict__ K, const QkvT<kBf16> *__restrict__ V, float qk2,
     QkvT<kBf16> *__restrict__ O) {
     MlpLds<kMode> M;
     __shared__ PartLds<kMaxP> L;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 kreal[r] = L.real[c0 + 4 * g + r];
-                s[r] = kreal[r] ? fmaf(s[r], kQkScale2, us[h][c][4 * g + r] * kLog2e)
+                s[r] = kreal[r] ? fmaf(s[r], qk2, us[h][c][4 * g + r] * kLog2e)
                                 : -INFINITY;
             }
             const float corr = online_softmax(s, m[hh], l[hh]);
@@ -450,34 +450,35 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
 template <int kMode, bool kBf16 = (kMode == kMlpBf16)>
 static hipError_t launch_fused(const float *p4, const uint8_t *mask, int B, int P,
                                const pip_pair_mlp *m, const QkvT<kBf16> *Q,
-                               const QkvT<kBf16> *K, const QkvT<kBf16> *V, QkvT<kBf16> *O,
-                               hipStream_t s) {
+                               const QkvT<kBf16> *K, const QkvT<kBf16> *V, float scale,
+                               QkvT<kBf16> *O, hipStream_t s) {
+    const float qk2 = scale * kLog2e;  // scores in base-2 units
     if (P <= kJetMaxP) {
         const int sort = B <= kSortMaxB ? 1 : 0;
         hipLaunchKernelGGL(embed_attention_jet_kernel<kMode>, dim3(B), dim3(kJetThreads), 0, s,
                            (const float4 *)p4, mask, B, P, sort, (const float4 *)m->w32,
-                           (const v8bf *)m->w16, (const v8h *)m->wx2, m->bias, Q, K, V, O);
+                           (const v8bf *)m->w16, (const v8h *)m->wx2, m->bias, Q, K, V, qk2, O);
     } else {
         hipLaunchKernelGGL(embed_attention_row_kernel<kMode>, dim3(B * (P / kTile)),
                            dim3(kRowThreads), 0, s, (const float4 *)p4, mask, P,
                            (const float4 *)m->w32, (const v8bf *)m->w16, (const v8h *)m->wx2,
-                           m->bias, Q, K, V, O);
+                           m->bias, Q, K, V, qk2, O);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_embed_attention_f32(const float *p4, const uint8_t *mask, int B, int P,
                                       const pip_pair_mlp *m, const float *Q, const float *K,
-                                      const float *V, float *O, hipStream_t s) {
-    return m->f16ok ? launch_fused<kMlpF16x2>(p4, mask, B, P, m, Q, K, V, O, s)
-                    : launch_fused<kMlpF32>(p4, mask, B, P, m, Q, K, V, O, s);
+                                      const float *V, float scale, float *O, hipStream_t s) {
+    return m->f16ok ? launch_fused<kMlpF16x2>(p4, mask, B, P, m, Q, K, V, scale, O, s)
+                    : launch_fused<kMlpF32>(p4, mask, B, P, m, Q, K, V, scale, O, s);
 }
 
 hipError_t launch_embed_attention_bf16(const float *p4, const uint8_t *mask, int B, int P,
                                        const pip_pair_mlp *m, const uint16_t *Q,
-                                       const uint16_t *K, const uint16_t *V, uint16_t *O,
-                                       hipStream_t s) {
-    return launch_fused<kMlpBf16>(p4, mask, B, P, m, Q, K, V, O, s);
+                                       const uint16_t *K, const uint16_t *V, float scale,
+                                       uint16_t *O, hipStream_t s) {
+    return launch_fused<kMlpBf16>(p4, mask, B, P, m, Q, K, V, scale, O, s);
 }
 
 }  // namespace pip

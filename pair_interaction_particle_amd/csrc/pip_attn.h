@@ -14,7 +14,6 @@
 namespace pip {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kQkScale2 = 1.4426950408889634f * 0.25f;  // log2(e) / sqrt(16)
 
 // Reductions over the four lanes l, l^16, l^32, l^48 with the gfx950 row
 // swaps: v_permlane16_swap of x with itself gives {x[l], x[l^16]} (in some

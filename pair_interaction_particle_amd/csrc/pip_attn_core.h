@@ -15,7 +15,6 @@
 
 namespace pip {
 
-constexpr float kF16Safe = 65504.0f;
 constexpr uint32_t kBf16NegInf = 0xff80ff80u;  // two bf16 -inf
 
 template <bool kBf16>
@@ -110,9 +109,35 @@ __device__ __forceinline__ int u_col(int kb, int g) {
     return 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
 }
 
-__device__ __forceinline__ bool f16_safe(float4 x) {
-    return fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))) <= kF16Safe &&
-           x.x == x.x && x.y == x.y && x.z == x.z && x.w == x.w;
+__device__ __forceinline__ float absmax4(float4 x) {
+    return fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+}
+
+// Power-of-two scale s (and 1/s) that puts amax into [2^13, 2^14); 1 for
+// zero, inf or NaN.  A float32 value scaled this way is split into fp16
+// hi + lo with 22 significand bits whatever its magnitude: the largest
+// element sits just below fp16's maximum, and an element 2^k times smaller
+// keeps relative error 2^-22 down to k = 16, below which its error is at
+// most 2^-25 of the largest element, absolute.  Scaling by a power of two
+// is exact and undone exactly.
+__device__ __forceinline__ void pow2_scale(float amax, float &s, float &inv) {
+    const int eb = (int)((__float_as_uint(amax) >> 23) & 0xff);
+    if (!(amax > 0.f) || eb == 255) {
+        s = inv = 1.f;
+        return;
+    }
+    int e = 13 - (eb - 127);
+    e = min(max(e, -126), 126);
+    s = __uint_as_float((uint32_t)(e + 127) << 23);
+    inv = __uint_as_float((uint32_t)(127 - e) << 23);
+}
+
+// Maximum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+    x = xmax16(x);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
 }
 
 __device__ __forceinline__ float max8(const float (&a)[4], const float (&b)[4]) {

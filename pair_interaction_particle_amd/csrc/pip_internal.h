@@ -37,17 +37,17 @@ hipError_t launch_pair_embed_bf16(const float *p4, const uint8_t *mask, int B, i
 int attention_chunks(int P);
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V,
                                 const float *U, const uint8_t *mask, int B, int H, int P,
-                                float *O, hipStream_t s);
+                                float scale, float *O, hipStream_t s);
 hipError_t launch_attention_bf16(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                  const uint16_t *U, const uint8_t *mask, int B, int H, int P,
-                                 uint16_t *O, hipStream_t s);
+                                 float scale, uint16_t *O, hipStream_t s);
 hipError_t launch_embed_attention_f32(const float *p4, const uint8_t *mask, int B, int P,
                                       const pip_pair_mlp *m, const float *Q, const float *K,
-                                      const float *V, float *O, hipStream_t s);
+                                      const float *V, float scale, float *O, hipStream_t s);
 hipError_t launch_embed_attention_bf16(const float *p4, const uint8_t *mask, int B, int P,
                                        const pip_pair_mlp *m, const uint16_t *Q,
-                                       const uint16_t *K, const uint16_t *V, uint16_t *O,
-                                       hipStream_t s);
+                                       const uint16_t *K, const uint16_t *V, float scale,
+                                       uint16_t *O, hipStream_t s);
 // bytes of workspace the block stack needs
 size_t block_stack_workspace(int B, int P, int C, int L);
 hipError_t launch_block_stack(float *X, const float *Wq, const float *Wk, const float *Wv,

@@ -13,7 +13,7 @@ import scipy.special as sp
 import oracle
 from pair_interaction_particle_amd import binding, synth
 
-OK, NULL, SHAPE, ALIGN, DTYPE, UNSUP = 0, 1, 2, 3, 4, 5
+OK, NULL, SHAPE, ALIGN, DTYPE, UNSUP, VALUE = 0, 1, 2, 3, 4, 5, 7
 # Fake device addresses: never dereferenced, because every call below fails
 # validation before it reaches the GPU.
 A16, A17 = 0x10000, 0x10001
@@ -66,17 +66,23 @@ def test_pair_embed_validation(L):
 def test_attention_validation(L):
     f = L.pip_pair_bias_attention
     args = [A16] * 4 + [A16]
-    assert f(None, A16, A16, A16, A16, 1, 8, 16, 16, A16, 0, None) == NULL
-    assert f(*args, 1, 8, 16, 32, A16, 0, None) == UNSUP  # D != 16
-    assert f(*args, 1, 8, 20, 16, A16, 0, None) == UNSUP  # P % 16
-    assert f(*args, 1, -1, 16, 16, A16, 0, None) == SHAPE
-    assert f(*args, 1, 8, 16, 16, A16, 2, None) == DTYPE
-    assert f(A16, A16, A17, A16, A16, 1, 8, 16, 16, A16, 0, None) == ALIGN
-    assert f(*args, 1, 0, 16, 16, A16, 0, None) == OK  # no heads
+    sc = 0.25
+    assert f(None, A16, A16, A16, A16, 1, 8, 16, 16, sc, A16, 0, None) == NULL
+    assert f(*args, 1, 8, 16, 32, sc, A16, 0, None) == UNSUP  # D != 16
+    assert f(*args, 1, 8, 20, 16, sc, A16, 0, None) == UNSUP  # P % 16
+    assert f(*args, 1, -1, 16, 16, sc, A16, 0, None) == SHAPE
+    assert f(*args, 1, 8, 16, 16, sc, A16, 2, None) == DTYPE
+    assert f(A16, A16, A17, A16, A16, 1, 8, 16, 16, sc, A16, 0, None) == ALIGN
+    assert f(*args, 1, 0, 16, 16, sc, A16, 0, None) == OK  # no heads
+    for bad in (math.inf, -math.inf, math.nan):
+        assert f(*args, 1, 8, 16, 16, bad, A16, 0, None) == VALUE  # scale not finite
+    assert f(*args, 1, 8, 16, 16, -3.0, A16, 7, None) == DTYPE  # dtype checked first
     g = L.pip_pair_embed_attention
-    assert g(A16, A16, None, A16, A16, A16, 1, 16, 16, A16, 0, None) == NULL
-    assert g(A16, A16, A16, A16, A16, A16, 1, 16, 8, A16, 0, None) == UNSUP
-    assert g(A16, A16, A16, A16, A16, A16, 1, 16, 16, A17, 0, None) == ALIGN
+    assert g(A16, A16, None, A16, A16, A16, 1, 16, 16, sc, A16, 0, None) == NULL
+    assert g(A16, A16, A16, A16, A16, A16, 1, 16, 8, sc, A16, 0, None) == UNSUP
+    assert g(A16, A16, A16, A16, A16, A16, 1, 16, 16, sc, A17, 0, None) == ALIGN
+    assert g(A16, A16, A16, A16, A16, A16, 1, 16, 16, math.nan, A16, 0, None) == VALUE
+    assert L.pip_status_string(VALUE) == b"invalid argument value"
 
 
 def test_block_stack_validation(L):

@@ -66,6 +66,28 @@ def test_matches_torch_sdpa_with_float_mask():
         assert np.all(O[b][:, ~real[b]] == 0)
 
 
+@pytest.mark.parametrize("scale", [0.0, 0.1, -0.7, 3.0])
+def test_explicit_scale_matches_torch_sdpa(scale):
+    # the score scale is an argument (Fusion 3 writes it as 1/sqrt(d)); any
+    # finite value, zero and negative included, against SDPA's own scale=
+    rng = np.random.default_rng(12)
+    B, H, P, D = 2, 3, 20, 16
+    Q, K, V, U = _rand(rng, B, H, P, D)
+    mask = (np.arange(P)[None] < np.array([20, 9])[:, None]).astype(np.uint8)
+    O = oracle.attention(Q, K, V, U, mask, scale=scale)
+    bias = torch.from_numpy(U).clone()
+    bias.masked_fill_(torch.from_numpy(mask[:, None, None, :] == 0).expand_as(bias), -math.inf)
+    ref = Fn.scaled_dot_product_attention(torch.from_numpy(Q), torch.from_numpy(K),
+                                          torch.from_numpy(V), attn_mask=bias,
+                                          scale=scale).numpy()
+    real = mask.astype(bool)
+    for b in range(B):
+        np.testing.assert_allclose(O[b][:, real[b]], ref[b][:, real[b]], rtol=1e-12, atol=1e-13)
+    # the default is 1 / sqrt(D), bit for bit
+    np.testing.assert_array_equal(oracle.attention(Q, K, V, U, mask),
+                                  oracle.attention(Q, K, V, U, mask, scale=0.25))
+
+
 def test_rows_of_p_sum_to_one():
     # With V rows the unit vectors e_c (D >= P), O row a is the probability row.
     rng = np.random.default_rng(3)

@@ -203,3 +203,55 @@ def test_padding_values_are_ignored():
     bad[0, -1] = [1e30, -1e30, 1e30, 0]
     F1 = oracle.pair_features(bad, mask, EPS)
     np.testing.assert_array_equal(F1, F0)
+
+
+# ---------------------------------------------------------------- beam-axis particles
+# A particle with pT = 0 sits on the beam axis.  Massless there, E = |pz| and
+# the rapidity 1/2 ln((E+pz)/(E-pz)) has a zero denominator (or numerator);
+# the oracle floors both arguments at 1e-300, so y = +-(1/2) ln(2E / 1e-300)
+# stays finite.  Its azimuth is atan2(0, 0) = 0.  With pT = 0, kT = 0 and
+# z = 0, so ln kT = ln z = ln eps.  When both particles have pT = 0 the
+# pT sum in z is clamped at eps too (0 / eps = 0, again ln eps).
+RAP_FLOOR = 1e-300
+
+
+def test_massless_beam_axis_particle_uses_the_rapidity_floor():
+    # a = (5,0,0,5): y_a = 1/2 ln(10 / 1e-300) = 1/2 (ln 10 + 300 ln 10),
+    # phi_a = 0.  b = (3,1,2,2): y_b = 1/2 ln 5, phi_b = atan 2.
+    # m2 = 8^2 - 1^2 - 2^2 - 7^2 = 10.
+    np.testing.assert_allclose(oracle.particle(np.array([5.0, 0, 0, 5])),
+                               [0.0, 150.5 * math.log(10.0), 0.0], rtol=1e-14, atol=0)
+    dy = 150.5 * math.log(10.0) - 0.5 * math.log(5.0)
+    dr = math.sqrt(dy * dy + math.atan(2.0) ** 2)
+    check(f([5, 0, 0, 5], [3, 1, 2, 2]), LN_EPS, LN_EPS, math.log(dr), math.log(10.0), 1e-12)
+    # the pair is symmetric
+    check(f([3, 1, 2, 2], [5, 0, 0, 5]), LN_EPS, LN_EPS, math.log(dr), math.log(10.0), 1e-12)
+
+
+def test_backward_and_spacelike_beam_axis_particles():
+    # (4,0,0,-4): E + pz = 0 -> y = 1/2 ln(1e-300 / 8).
+    # (1,0,0,2): E < |pz| (not a physical 4-vector): E - pz = -1 is floored,
+    # y = 1/2 ln(3 / 1e-300).
+    np.testing.assert_allclose(oracle.particle(np.array([4.0, 0, 0, -4]))[1],
+                               0.5 * (math.log(RAP_FLOOR) - math.log(8.0)), rtol=1e-14)
+    np.testing.assert_allclose(oracle.particle(np.array([1.0, 0, 0, 2]))[1],
+                               0.5 * (math.log(3.0) - math.log(RAP_FLOOR)), rtol=1e-14)
+    # pair of the two: dy = 1/2 (ln 3 + ln 8) - ln 1e-300, dphi = 0;
+    # m2 = 5^2 - (-2)^2 = 21
+    dy = 0.5 * (math.log(3.0) + math.log(8.0)) - math.log(RAP_FLOOR)
+    check(f([1, 0, 0, 2], [4, 0, 0, -4]), LN_EPS, LN_EPS, math.log(dy), math.log(21.0), 1e-12)
+    # (1,0,0,2) with (3,1,2,2): m2 = 4^2 - 1 - 4 - 16 = -5 < eps -> ln eps
+    dy2 = 0.5 * (math.log(3.0) - math.log(RAP_FLOOR)) - 0.5 * math.log(5.0)
+    dr2 = math.sqrt(dy2 * dy2 + math.atan(2.0) ** 2)
+    check(f([1, 0, 0, 2], [3, 1, 2, 2]), LN_EPS, LN_EPS, math.log(dr2), LN_EPS, 1e-12)
+
+
+def test_two_zero_pt_particles_clamp_the_pt_sum():
+    # a = (5,0,0,3): m = 4, y_a = 1/2 ln(8/2) = ln 2.  b = (5,0,0,-4): m = 3,
+    # y_b = 1/2 ln(1/9) = -ln 3.  Both pT = 0: the pT sum 0 is clamped at eps,
+    # z = 0 / eps = 0 -> ln eps; kT = 0 -> ln eps.  dR = |dy| = ln 6,
+    # m2 = 10^2 - (-1)^2 = 99.
+    check(f([5, 0, 0, 3], [5, 0, 0, -4]), LN_EPS, LN_EPS, math.log(math.log(6.0)),
+          math.log(99.0), 1e-13)
+    # self-pair of a zero-pT particle: every clamp at once except m2 = 4 m^2
+    check(f([5, 0, 0, 3], [5, 0, 0, 3]), LN_EPS, LN_EPS, LN_EPS, math.log(64.0), 1e-13)
