@@ -53,6 +53,8 @@ extern "C" {
 #define PIP_HEADS 8          /* pair-MLP outputs = attention heads */
 #define PIP_HEAD_DIM 16      /* the only head dimension the kernels take */
 #define PIP_MAX_P 256        /* largest particle count per jet */
+/* bytes of the fixed per-device scratch array behind pip_block_stack_noalloc */
+#define PIP_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef enum {
     PIP_OK = 0,
@@ -63,8 +65,10 @@ typedef enum {
     PIP_ERR_UNSUPPORTED = 5, /* well-formed but outside what the kernels take
                                 (P % 16 != 0, P > 256, D != 16, H != 8 where fixed, ...) */
     PIP_ERR_HIP = 6,         /* a HIP runtime call (launch, alloc, copy) failed */
-    PIP_ERR_VALUE = 7        /* a scalar argument is outside its domain (a scale that is
+    PIP_ERR_VALUE = 7,       /* a scalar argument is outside its domain (a scale that is
                                 not finite) */
+    PIP_ERR_TOO_LARGE = 8    /* the problem needs more scratch than the library's fixed
+                                device buffer holds (pip_block_stack_noalloc) */
 } pip_status;
 
 typedef enum { PIP_F32 = 0, PIP_BF16 = 1 } pip_dtype;
@@ -191,6 +195,24 @@ pip_status pip_block_stack(float *X, const float *Wq, const float *Wk, const flo
                            const float *Wo, const float *U, const uint8_t *mask, int64_t B,
                            int64_t P, int64_t C, int64_t H, int64_t L, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* pip_block_stack without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP stream or
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (minus the workspace), result and errors as pip_block_stack.
+ * The workspace lives in a fixed array of PIP_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * inside the library, one per GPU, held until the process ends; problems
+ * whose pip_block_stack_workspace_bytes exceed it return PIP_ERR_TOO_LARGE
+ * before any launch (B=128, P=128, C=128, L=8 needs about 10 MiB).  All calls
+ * on one GPU share that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * The first call on a device looks the array's address up (no allocation);
+ * nothing in the array needs to start at zero.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, TOO_LARGE, HIP. */
+pip_status pip_block_stack_noalloc(float *X, const float *Wq, const float *Wk, const float *Wv,
+                                   const float *Wo, const float *U, const uint8_t *mask,
+                                   int64_t B, int64_t P, int64_t C, int64_t H, int64_t L,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pip.h")
 
 PIP_F32, PIP_BF16 = 0, 1
 STATUS = {0: "PIP_OK", 1: "PIP_ERR_NULL", 2: "PIP_ERR_SHAPE", 3: "PIP_ERR_ALIGN",
-          4: "PIP_ERR_DTYPE", 5: "PIP_ERR_UNSUPPORTED", 6: "PIP_ERR_HIP", 7: "PIP_ERR_VALUE"}
+          4: "PIP_ERR_DTYPE", 5: "PIP_ERR_UNSUPPORTED", 6: "PIP_ERR_HIP", 7: "PIP_ERR_VALUE",
+          8: "PIP_ERR_TOO_LARGE"}
 W_FOLDED = 64 * 4 + 2 * 64 * 64 + 8 * 64
 B_FOLDED = 3 * 64 + 8
 
@@ -80,9 +81,11 @@ def lib():
         L.pip_block_stack_workspace_bytes.restype = C.c_size_t
         L.pip_block_stack.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
                                       C.c_size_t, vp]
+        L.pip_block_stack_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                              i64, vp]
         for f in ("pip_pair_mlp_fold", "pip_pair_mlp_create", "pip_pair_mlp_destroy",
                   "pip_pair_features", "pip_pair_embed", "pip_pair_bias_attention",
-                  "pip_pair_embed_attention", "pip_block_stack"):
+                  "pip_pair_embed_attention", "pip_block_stack", "pip_block_stack_noalloc"):
             getattr(L, f).restype = i
         _lib = L
     return _lib
@@ -275,4 +278,20 @@ def block_stack(x, wq, wk, wv, wo, u, mask, workspace=None):
         _dev(mask, "mask", torch.uint8, (B, P)), B, P, Cw, H, L,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream())
     _check("pip_block_stack", st)
+    return x
+
+
+def block_stack_noalloc(x, wq, wk, wv, wo, u, mask):
+    """pip_block_stack_noalloc: as block_stack, with the workspace in the
+    library's fixed per-GPU scratch array (no allocation).  Returns x."""
+    torch = _torch()
+    B, P, Cw = x.shape
+    L = wq.shape[0]
+    H = u.shape[1]
+    st = lib().pip_block_stack_noalloc(
+        _dev(x, "X", torch.float32, (B, P, Cw)), _dev(wq, "Wq", torch.float32, (L, Cw, Cw)),
+        _dev(wk, "Wk", torch.float32, (L, Cw, Cw)), _dev(wv, "Wv", torch.float32, (L, Cw, Cw)),
+        _dev(wo, "Wo", torch.float32, (L, Cw, Cw)), _dev(u, "U", torch.float32, (B, H, P, P)),
+        _dev(mask, "mask", torch.uint8, (B, P)), B, P, Cw, H, L, _stream())
+    _check("pip_block_stack_noalloc", st)
     return x

@@ -55,6 +55,7 @@ const char *pip_status_string(int s) {
         case PIP_ERR_UNSUPPORTED: return "unsupported size or configuration";
         case PIP_ERR_HIP: return "HIP runtime error";
         case PIP_ERR_VALUE: return "invalid argument value";
+        case PIP_ERR_TOO_LARGE: return "problem exceeds the fixed scratch buffer";
         default: return "unknown status";
     }
 }

@@ -102,6 +102,21 @@ def test_block_stack_validation(L):
     assert f(*w, 2, 16, 128, 8, 0, None, 0, None) == OK  # zero layers
 
 
+def test_block_stack_noalloc_validation(L):
+    f = L.pip_block_stack_noalloc
+    w = [A16] * 7
+    assert f(None, *w[1:], 2, 16, 128, 8, 1, None) == NULL
+    assert f(*w, 2, 16, 100, 8, 1, None) == SHAPE  # C != 16 H
+    assert f(*w, 2, 24, 128, 8, 1, None) == UNSUP  # P % 16
+    assert f(A17, *w[1:], 2, 16, 128, 8, 1, None) == ALIGN
+    assert f(*w, 2, 16, 128, 8, 0, None) == OK  # zero layers
+    assert f(None, None, None, None, None, None, None, 0, 16, 128, 8, 1, None) == OK
+    # beyond the fixed 16 MiB scratch: refused before any device call
+    assert L.pip_block_stack_workspace_bytes(512, 128, 128, 8) > 16 << 20
+    assert f(*w, 512, 128, 128, 8, 8, None) == 8  # PIP_ERR_TOO_LARGE
+    assert L.pip_status_string(8) == b"problem exceeds the fixed scratch buffer"
+
+
 def _params(seed, **kw):
     return synth.make_mlp_params(rng=np.random.default_rng(seed), **kw)
 
