@@ -7,21 +7,28 @@ Kernels": N=128 jets, P=128 slots, H=8, D=16): pair_embed (features + pair MLP
 -> U, float32) then pair_bias_attention (masked softmax(QK^T/sqrt(D) + U) V).
 Inputs are resident on the GPU before the timed region.  Prints ONE JSON line.
 
-  value            = B * P^2 slot pairs per second of the whole step
+  value            = B * P^2 slot pairs per second of the whole step (K steps
+                     bracketed by synchronize() and events at the two ends)
   roofline         = the pair-embed kernel (the dominant one) against the
                      float32 MFMA peak, algorithmic flops = unique real pairs
-                     n(n+1)/2 per jet x 17,920 flop
-  cpu_baseline     = the CPU oracle on the same workload (host threads)
-  workloads        = the other workloads (fused batch-512, bf16 large jets,
-                     8-layer block stack) timed the same way
+                     n(n+1)/2 per jet x 17,920 flop, over its warm median
+                     duration (HIP events on the launch stream)
+  attention_roofline, workloads.*.rooflines
+                   = every other kernel of every workload, each with warm and
+                     cold (L2 and MALL evicted by a 512 MiB write before each
+                     rep) medians and p10/p90, and the rocprofv3 counters
+                     committed under profiles/ for the same kernel source
+  cpu_baseline     = the CPU oracle on the same workload (host threads); each
+                     other workload carries its own oracle timing on a sample
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --profile WORKLOAD [--reps R]   (kernels only, for rocprofv3)
 """
 import argparse
 import hashlib
 import json
-import math
 import os
+import platform
 import sys
 import time
 
@@ -31,38 +38,63 @@ sys.path.insert(0, ROOT)
 METRIC = ("pairs/s fused PairEmbed+MLP and µs biased attn at B=128 P=128 H=8 D=16; "
           "%roofline")
 MLP_FLOP_PER_PAIR = 2 * (4 * 64 + 64 * 64 + 64 * 64 + 64 * 8)  # 17,920
+ATTN_FLOP_PER_PAIR_HEAD = 2 * 2 * 16                           # QK^T and PV at D=16
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pair_embed_f32_kernel_B128_P128_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "pair_interaction_particle_amd", "csrc", f)
-                  for f in ("pair_embed.hip", "pip_device.h", "pip_mlp.h")]
+# non-packed VALU issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s
+PEAK_VALU_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+COLD_BYTES = 512 << 20
+CSRC = os.path.join(ROOT, "pair_interaction_particle_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+# kernel -> (profile summary file, sources whose sha256 it was taken on)
+KERNELS = {
+    "pair_embed_f32": ("pair_embed_f32_kernel_B128_P128.md",
+                       ["pair_embed.hip", "pip_device.h", "pip_mlp.h"]),
+    "attention_f32": ("attention_f32_kernel_B128_P128.md",
+                      ["attention.hip", "pip_attn_core.h", "pip_attn.h", "pip_device.h"]),
+    "pair_embed_bf16": ("pair_embed_bf16_large_B64_P256.md",
+                        ["pair_embed.hip", "pip_device.h", "pip_mlp.h"]),
+    "attention_bf16": ("attention_bf16_large_B64_P256.md",
+                       ["attention.hip", "pip_attn_core.h", "pip_attn.h", "pip_device.h"]),
+    "fused_f32": ("pair_embed_attention_f32_fused512_B512_P128.md",
+                  ["fused.hip", "pip_mlp.h", "pip_attn.h", "pip_device.h"]),
+    "block_stack_f32": ("block_stack_f32_stack8_B128_P128_C128_L8.md",
+                        ["block_stack.hip", "pip_attn_core.h", "pip_attn.h", "pip_device.h"]),
+}
 
 
-def kernel_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per pair-embed launch from the committed rocprofv3 --pmc
-    summary, or None when absent or taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_profile(kernel):
+    """Figures from the committed rocprofv3 summary of `kernel` (the
+    'key: value' lines at its end), or None when the summary is absent or was
+    taken on different kernel sources."""
+    fname, srcs = KERNELS[kernel]
+    path = os.path.join(PROFILES, fname)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
-        if ":" in line:
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ", "\t")):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != kernel_source_hash():
+    if vals.get("source_sha256") != source_hash(srcs):
         return None
-    try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    out = {"file": "profiles/" + fname}
+    for k, v in vals.items():
+        try:
+            out[k] = float(v)
+        except ValueError:
+            pass
+    return out
 
 
 def pair_counts(mask):
@@ -80,11 +112,17 @@ def attention_bytes(mask, H, P, D, elt):
     return int(H * (3 * n.sum() * D + (n * n).sum()) * elt + B * H * P * D * elt)
 
 
+def stats(ts_ms):
+    import numpy as np
+    a = np.asarray(ts_ms, np.float64) * 1e3
+    return {"median_us": float(np.median(a)), "p10_us": float(np.percentile(a, 10)),
+            "p90_us": float(np.percentile(a, 90)), "mean_us": float(a.mean()), "reps": len(a)}
+
+
 def time_steps(step, reps, warmup):
     """Wall and device time (ms) per step of `reps` back-to-back steps, after
     `warmup` untimed ones, bracketed by synchronize() on both sides and events
-    at the two ends only (an event between kernels adds a barrier and a
-    timestamp write to the queue, which idles the GPU between them)."""
+    at the two ends only."""
     import torch
     for _ in range(warmup):
         step()
@@ -99,27 +137,84 @@ def time_steps(step, reps, warmup):
     return (time.perf_counter() - t0) * 1e3 / reps, s.elapsed_time(e) / reps
 
 
-def time_events(fns, reps, warmup):
-    """Average device time (ms) of each callable in fns, measured with events
-    recorded on the current stream around each launch."""
+def time_kernel(fn, reps, warmup, cold=None):
+    """Per-launch device duration (ms) of fn() from HIP events recorded on the
+    current stream (the stream the binding launches on) right around each
+    launch.  A spin kernel before each rep keeps the GPU busy while the host
+    enqueues the events and the launch, so the events bracket the kernel and
+    not the host (they still add the event packets' own few microseconds).
+    cold: a buffer of COLD_BYTES written before each rep, which evicts L2 and
+    the MALL (the write itself is outside the events)."""
     import torch
     for _ in range(warmup):
-        for f in fns:
-            f()
+        fn()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
-          for _ in range(reps)]
-    t0 = time.perf_counter()
+    evs = []
     for r in range(reps):
-        ev[r][0].record()
-        for i, f in enumerate(fns):
-            f()
-            ev[r][i + 1].record()
+        if cold is not None:
+            cold.fill_(float(r & 7))
+        torch.cuda._sleep(100000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / reps
-    per = [sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
-           for i in range(len(fns))]
-    return per, wall_ms
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def time_bursts(fn, bursts, per_burst, warmup):
+    """Mean device duration (ms) per launch of `per_burst` back-to-back
+    launches between two events, one figure per burst.  A spin kernel long
+    enough for the host to enqueue the whole burst runs first, so the launches
+    reach the GPU queued and the figure is the kernel's own back-to-back time
+    (launch gaps included, no host time)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(bursts):
+        torch.cuda._sleep(per_burst * 120000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(per_burst):
+            fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) / per_burst for a, b in evs]
+
+
+def roofline(kind, work, warm, cold, prof, peak, extra=None):
+    """One roofline block: work (flop or bytes per launch) over the warm
+    median duration, with the cold figures and the counters beside it."""
+    def rate(us):
+        return work / (us * 1e-6) / (1e12 if kind == "mfma" else 1e9)
+    achieved = rate(warm["median_us"])
+    out = {"bound": kind, "achieved": achieved, "peak": peak,
+           "unit": "TFLOP/s" if kind == "mfma" else "GB/s", "frac": achieved / peak,
+           "traffic": prof.get("hbm_bytes_per_launch") if prof else None,
+           "warm": warm, "cold": cold,
+           "cold_frac": rate(cold["single_launch"]["median_us"]) / peak,
+           "warm_single_frac": rate(cold["warm_single_launch"]["median_us"]) / peak}
+    if prof:
+        out["counters"] = {k: prof[k] for k in (
+            "rocprof_avg_us", "mfma_busy_pct", "valu_busy_pct", "valu_issue_pct",
+            "valu_lane_ops_per_launch", "mfma_mops_f16", "mfma_mops_bf16", "mfma_mops_f32",
+            "hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch") if k in prof}
+        # which unit the counters say is busiest: MFMA pipes, VALU issue, or
+        # HBM (counted bytes over the profiled duration)
+        util = {"mfma": prof.get("mfma_busy_pct", 0.0), "valu": prof.get("valu_issue_pct", 0.0)}
+        if prof.get("hbm_bytes_per_launch") and prof.get("rocprof_avg_us"):
+            util["hbm"] = 100.0 * prof["hbm_bytes_per_launch"] / (
+                prof["rocprof_avg_us"] * 1e-6) / (PEAK_HBM_GBS * 1e9)
+        out["counters"]["hbm_pct_of_peak"] = util.get("hbm")
+        out["counter_bound"] = max(util, key=util.get)
+        out["profile"] = prof["file"]
+    if extra:
+        out.update(extra)
+    return out
 
 
 def to_dev(x, dtype=None):
@@ -129,9 +224,106 @@ def to_dev(x, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
+# ---------------------------------------------------------------- workloads
+def setup(pip, synth, name):
+    """Device inputs of a workload and its kernels as callables, in step order."""
+    import torch
+    d = synth.make_workload(name)
+    B, P = d["mask"].shape
+    mask = to_dev(d["mask"])
+    mlp = pip.PairMLP(d["mlp"])
+    k = {"d": d, "mlp": mlp}
+    if name in ("kernel", "large_bf16"):
+        bf = name == "large_bf16"
+        tdt = torch.bfloat16 if bf else torch.float32
+        p4 = to_dev(d["p4"])
+        q, kk, v = (to_dev(d[x], tdt) for x in ("q", "k", "v"))
+        U = torch.empty((B, 8, P, P), device="cuda", dtype=tdt)
+        O = torch.empty_like(q)
+        dt = "bf16" if bf else "f32"
+        k["fns"] = [("pair_embed_" + dt, lambda: pip.pair_embed(p4, mask, mlp, dt, out=U)),
+                    ("attention_" + dt, lambda: pip.pair_bias_attention(q, kk, v, U, mask,
+                                                                        out=O))]
+    elif name == "fused512":
+        p4 = to_dev(d["p4"])
+        q, kk, v = (to_dev(d[x]) for x in ("q", "k", "v"))
+        O = torch.empty_like(q)
+        k["fns"] = [("fused_f32", lambda: pip.pair_embed_attention(p4, mask, mlp, q, kk, v,
+                                                                   out=O))]
+    elif name == "stack8":
+        U = pip.pair_embed(to_dev(d["p4"]), mask, mlp)
+        X = to_dev(d["x0"])
+        w = [to_dev(d[x]) for x in ("wq", "wk", "wv", "wo")]
+        ws = torch.empty(pip.block_stack_workspace_bytes(B, P, 128, 8) // 4, device="cuda")
+        # X is updated in place; re-applying the stack to the running X does
+        # the same work every time (the stack has no data-dependent work)
+        k["fns"] = [("block_stack_f32", lambda: pip.block_stack(X, *w, U, mask, workspace=ws))]
+    return k
+
+
+def work_of(kernel, d):
+    """(roofline kind, algorithmic work per launch, peak) of one kernel."""
+    mask = d["mask"]
+    B, P = mask.shape
+    uniq, ordered, n = pair_counts(mask)
+    if kernel == "pair_embed_f32":
+        return "mfma", uniq * MLP_FLOP_PER_PAIR, PEAK_FP32_MFMA_TFLOPS
+    if kernel == "pair_embed_bf16":
+        return "mfma", uniq * MLP_FLOP_PER_PAIR, PEAK_BF16_MFMA_TFLOPS
+    if kernel == "attention_f32":
+        return "hbm", attention_bytes(mask, 8, P, 16, 4), PEAK_HBM_GBS
+    if kernel == "attention_bf16":
+        return "hbm", attention_bytes(mask, 8, P, 16, 2), PEAK_HBM_GBS
+    if kernel == "fused_f32":
+        return ("mfma", uniq * MLP_FLOP_PER_PAIR + ordered * 8 * ATTN_FLOP_PER_PAIR_HEAD,
+                PEAK_FP32_MFMA_TFLOPS)
+    if kernel == "block_stack_f32":
+        nr = int((mask != 0).sum())
+        return ("mfma", 8 * (nr * 128 * 128 * 2 * 4 + ordered * 8 * ATTN_FLOP_PER_PAIR_HEAD),
+                PEAK_FP32_MFMA_TFLOPS)
+    raise KeyError(kernel)
+
+
+def measure(k, reps, warmup, cold):
+    """Warm and cold duration statistics and roofline blocks of each kernel."""
+    out = {}
+    for name, fn in k["fns"]:
+        # warm: back-to-back bursts (the roofline figure); cold: single
+        # launches after a 512 MiB write, next to warm single launches timed
+        # the same way (both carry the events' own overhead)
+        warm = stats(time_bursts(fn, max(5, reps // 10), 20, warmup))
+        cld = {"single_launch": stats(time_kernel(fn, max(10, reps // 2), 2, cold=cold)),
+               "warm_single_launch": stats(time_kernel(fn, max(10, reps // 2), 2))}
+        kind, work, peak = work_of(name, k["d"])
+        prof = read_profile(name)
+        extra = {"algorithmic_%s_per_launch" % ("flop" if kind == "mfma" else "bytes"): work}
+        if name == "pair_embed_bf16" and prof and "valu_lane_ops_per_launch" in prof:
+            # the bf16 embed is bound by VALU issue (GELU), not by its bf16
+            # matrix cores: report the issued VALU lane-ops against the
+            # non-packed VALU peak beside the bf16 MFMA fraction
+            lane_ops = prof["valu_lane_ops_per_launch"]
+            extra["valu"] = {"bound": "alu", "achieved": lane_ops / (warm["median_us"] * 1e-6)
+                             / 1e12, "peak": PEAK_VALU_TLANEOPS, "unit": "T lane-ops/s (issued)",
+                             "frac": lane_ops / (warm["median_us"] * 1e-6) / 1e12
+                             / PEAK_VALU_TLANEOPS}
+        out[name] = roofline(kind, work, warm, cld, prof, peak, extra)
+    return out
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(d, budget_s):
-    """The oracle (fp64, OpenMP over jets) on the same workload, repeated
-    until about budget_s seconds of wall time have passed."""
+    """The oracle (fp64, OpenMP over jets) on the whole kernel workload,
+    repeated until about budget_s seconds of wall time have passed."""
     import oracle
     B, P = d["mask"].shape
     reps, t_total = 0, 0.0
@@ -142,82 +334,43 @@ def cpu_baseline(d, budget_s):
         t_total += time.perf_counter() - t
         reps += 1
     return {"value": B * P * P * reps / t_total, "unit": "slot-pairs/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "whole kernel workload (B=128 jets, P=128) run %d time(s): float64 pair "
                       "embed + attention, %.1f s wall" % (reps, t_total)}
 
 
-def bench_extra(pip, synth, reps, warmup):
-    """Time the other workloads' entries (parity for them is in tests/)."""
-    import torch
-    out = {}
-    # bf16 large jets: pair_embed (bf16 MLP) + attention (bf16)
-    d = synth.make_workload("large_bf16")
+def cpu_sample(name, d, jets):
+    """The oracle on the first `jets` jets of another workload, once; the
+    rate is scaled to the whole workload."""
+    import oracle
     B, P = d["mask"].shape
-    p4, mask = to_dev(d["p4"]), to_dev(d["mask"])
-    bf = torch.bfloat16
-    q, k, v = (to_dev(d[x], bf) for x in ("q", "k", "v"))
-    mlp = pip.PairMLP(d["mlp"])
-    U = torch.empty((B, 8, P, P), device="cuda", dtype=bf)
-    O = torch.empty_like(q)
-    (te, ta), _ = time_events([lambda: pip.pair_embed(p4, mask, mlp, "bf16", out=U),
-                               lambda: pip.pair_bias_attention(q, k, v, U, mask, out=O)],
-                              reps, warmup)
-    uniq, ordered, _ = pair_counts(d["mask"])
-    ab = attention_bytes(d["mask"], 8, P, 16, 2)
-    out["large_bf16"] = {
-        "shape": "B=64 P=256 n~U{60..256} H=8 D=16 bf16",
-        "pair_embed_us": te * 1e3, "attention_us": ta * 1e3,
-        "pair_embed_slot_pairs_per_s": B * P * P / (te * 1e-3),
-        "pair_embed_mfma_tflops": uniq * MLP_FLOP_PER_PAIR / (te * 1e-3) / 1e12,
-        "attention_gbs": ab / (ta * 1e-3) / 1e9,
-        "attention_hbm_frac": ab / (ta * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    del U, O, q, k, v
-    # fused batch-512
-    d = synth.make_workload("fused512")
-    B, P = d["mask"].shape
-    p4, mask = to_dev(d["p4"]), to_dev(d["mask"])
-    q, k, v = (to_dev(d[x]) for x in ("q", "k", "v"))
-    mlp = pip.PairMLP(d["mlp"])
-    O = torch.empty_like(q)
-    try:
-        (tf,), _ = time_events([lambda: pip.pair_embed_attention(p4, mask, mlp, q, k, v, out=O)],
-                               reps, warmup)
-        uniq, ordered, _ = pair_counts(d["mask"])
-        flops = uniq * MLP_FLOP_PER_PAIR + ordered * 8 * 64
-        out["fused512"] = {"shape": "B=512 P=128 n~U{20..128} H=8 D=16 fp32, 5% massive",
-                           "pair_embed_attention_us": tf * 1e3,
-                           "slot_pairs_per_s": B * P * P / (tf * 1e-3),
-                           "mfma_tflops": flops / (tf * 1e-3) / 1e12,
-                           "mfma_frac": flops / (tf * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
-    except pip.PipError as e:
-        out["fused512"] = {"error": str(e)}
-    del O, q, k, v
-    # block stack: 8 layers reusing U
-    d = synth.make_workload("stack8")
-    B, P = d["mask"].shape
-    mask = to_dev(d["mask"])
-    mlp = pip.PairMLP(d["mlp"])
-    U = pip.pair_embed(to_dev(d["p4"]), mask, mlp)
-    x0 = to_dev(d["x0"])
-    X = x0.clone()
-    w = [to_dev(d[x]) for x in ("wq", "wk", "wv", "wo")]
-    ws = torch.empty(pip.block_stack_workspace_bytes(B, P, 128, 8) // 4, device="cuda")
-    try:
-        # X is updated in place; re-applying the stack to the running X does
-        # the same work every time (the path has no data-dependent work).
-        (tb,), _ = time_events([lambda: pip.block_stack(X, *w, U, mask, workspace=ws)],
-                               reps, warmup)
-        nr = int((d["mask"] != 0).sum())
-        _, ordered, _ = pair_counts(d["mask"])
-        flops = 8 * (nr * 128 * 128 * 2 * 4 + ordered * 8 * 64)
-        out["stack8"] = {"shape": "B=128 P=128 C=128 H=8 D=16 L=8 fp32",
-                         "block_stack_us": tb * 1e3,
-                         "mfma_tflops": flops / (tb * 1e-3) / 1e12,
-                         "mfma_frac": flops / (tb * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS}
-    except pip.PipError as e:
-        out["stack8"] = {"error": str(e)}
-    return out
+    s = slice(0, jets)
+    t = time.perf_counter()
+    if name == "fused512":
+        oracle.pair_embed_attention(d["p4"][s], d["mask"][s], d["mlp"], d["q"][s], d["k"][s],
+                                    d["v"][s])
+        what = "pair embed + attention"
+    elif name == "large_bf16":
+        U = oracle.pair_embed(d["p4"][s], d["mask"][s], d["mlp"])
+        oracle.attention(d["q"][s], d["k"][s], d["v"][s], U, d["mask"][s])
+        what = "pair embed + attention (bf16-rounded inputs, float64 arithmetic)"
+    else:
+        U = oracle.pair_embed(d["p4"][s], d["mask"][s], d["mlp"]).astype("float32")
+        oracle.block_stack(d["x0"][s], d["wq"], d["wk"], d["wv"], d["wo"], U, d["mask"][s])
+        what = "8-layer block stack (U precomputed)"
+    dt = time.perf_counter() - t
+    return {"value": jets * P * P / dt, "unit": "slot-pairs/s",
+            "us_per_workload_call": dt * 1e6 * B / jets, "cores": oracle.num_threads(),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": "first %d of %d jets, float64 %s, %.2f s wall" % (jets, B, what, dt)}
+
+
+SHAPES = {
+    "large_bf16": "B=64 P=256 n~U{60..256} H=8 D=16 bf16",
+    "fused512": "B=512 P=128 n~U{20..128} H=8 D=16 fp32, 5% massive",
+    "stack8": "B=128 P=128 C=128 H=8 D=16 L=8 fp32",
+}
+CPU_JETS = {"large_bf16": 16, "fused512": 128, "stack8": 32}
 
 
 def main():
@@ -228,9 +381,14 @@ def main():
     # after); 500 warmup steps are ~45 ms.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--reps", type=int, default=100,
+                    help="per-kernel timed reps (warm; cold takes half)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--profile", default=None, metavar="WORKLOAD",
+                    help="only run WORKLOAD's kernels (--warmup untimed, then --reps) and "
+                         "exit: the command rocprofv3 wraps for profiles/")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -250,40 +408,39 @@ def main():
               "no exchange, and only the single-MI355X kernel is implemented.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from pair_interaction_particle_amd import binding as pip
     from pair_interaction_particle_amd import synth
 
     torch.cuda.set_device(0)
-    d = synth.make_workload("kernel")
+    if args.profile:
+        k = setup(pip, synth, args.profile)
+        for _ in range(args.warmup):
+            for _, fn in k["fns"]:
+                fn()
+        torch.cuda.synchronize()
+        for _ in range(args.reps):
+            for _, fn in k["fns"]:
+                fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": args.profile, "reps": args.reps,
+                          "kernels": [n for n, _ in k["fns"]]}))
+        return
+
+    k = setup(pip, synth, "kernel")
+    d = k["d"]
     B, P = d["mask"].shape
     H, D = 8, 16
-    p4, mask = to_dev(d["p4"]), to_dev(d["mask"])
-    q, k, v = (to_dev(d[x]) for x in ("q", "k", "v"))
-    mlp = pip.PairMLP(d["mlp"])
-    U = torch.empty((B, H, P, P), device="cuda", dtype=torch.float32)
-    O = torch.empty_like(q)
-
-    def embed():
-        pip.pair_embed(p4, mask, mlp, out=U)
-
-    def attn():
-        pip.pair_bias_attention(q, k, v, U, mask, out=O)
-
+    (_, embed), (_, attn) = k["fns"]
     # the timed region: K steps bracketed only at the ends
-    ms_per_step, gpu_ms_per_step = time_steps(lambda: (embed(), attn()), args.steps, args.warmup)
-    # per-kernel durations (roofline): a second pass of K steps with events
-    # around each launch (these events lengthen the step, so it is not the
-    # headline pass)
-    (t_embed, t_attn), ms_instrumented = time_events([embed, attn], args.steps, 0)
+    ms_per_step, gpu_ms_per_step = time_steps(lambda: (embed(), attn()), args.steps,
+                                              args.warmup)
+    cold = torch.empty(COLD_BYTES // 4, device="cuda")
+    per = measure(k, args.reps, 20, cold)
     slot_pairs = B * P * P
     uniq, ordered, n = pair_counts(d["mask"])
-    flops = uniq * MLP_FLOP_PER_PAIR
-    achieved = flops / (t_embed * 1e-3) / 1e12
-    traffic = measured_traffic()
-    ab = attention_bytes(d["mask"], H, P, D, 4)
+    pe, at = per["pair_embed_f32"], per["attention_f32"]
     res = {
         "metric": METRIC,
         "value": slot_pairs / (ms_per_step * 1e-3),
@@ -291,34 +448,31 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "gpu_ms_per_step": gpu_ms_per_step,
-        "ms_per_step_with_kernel_events": ms_instrumented,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "kernel: B=128 jets, P=128 slots, real n~U{20..128}, H=8, "
                                "D=16, fp32; step = pair_embed + pair_bias_attention",
                    "B": B, "P": P, "H": H, "D": D, "global_batch": B, "seq_len": P,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-                     "traffic": traffic, "kernel": "pair_embed_kernel<kMlpF16x2> (fp32 path)",
-                     "algorithmic_flop_per_launch": flops,
-                     "unique_real_pairs": uniq},
-        "pair_embed_us": t_embed * 1e3,
-        "pair_embed_slot_pairs_per_s": slot_pairs / (t_embed * 1e-3),
-        "attention_us": t_attn * 1e3,
-        "attention_roofline": {"bound": "hbm", "achieved": ab / (t_attn * 1e-3) / 1e9,
-                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": ab / (t_attn * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                               "algorithmic_bytes_per_launch": ab},
+        "roofline": dict(pe, kernel="pair_embed_kernel<kMlpF16x2> (fp32 path)",
+                         unique_real_pairs=uniq),
+        "pair_embed_us": pe["warm"]["median_us"],
+        "pair_embed_slot_pairs_per_s": slot_pairs / (pe["warm"]["median_us"] * 1e-6),
+        "attention_us": at["warm"]["median_us"],
+        "attention_roofline": dict(at, kernel="attention_kernel<f32>"),
         "real_ordered_pairs": ordered,
     }
     if not args.no_extra:
-        res["workloads"] = bench_extra(pip, synth, max(10, args.steps // 2),
-                                       max(3, args.warmup // 2))
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
-    else:
-        res["cpu_baseline"] = None
+        res["workloads"] = {}
+        for name in ("fused512", "large_bf16", "stack8"):
+            kw = setup(pip, synth, name)
+            res["workloads"][name] = {"shape": SHAPES[name],
+                                      "rooflines": measure(kw, args.reps, 20, cold)}
+            if not args.no_cpu_baseline:
+                res["workloads"][name]["cpu_oracle"] = cpu_sample(name, kw["d"],
+                                                                  CPU_JETS[name])
+            del kw
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(d, args.cpu_seconds)
     print(json.dumps(res))
 
 
