@@ -62,6 +62,11 @@ KERNELS = {
                   ["fused.hip", "pip_mlp.h", "pip_attn.h", "pip_device.h"]),
     "block_stack_f32": ("block_stack_f32_stack8_B128_P128_C128_L8.md",
                         ["block_stack.hip", "pip_attn_core.h", "pip_attn.h", "pip_device.h"]),
+    "pair_embed_packed_f32": ("pair_embed_packed_f32_kernel_B128_n20-128.md",
+                              ["packed_embed.hip", "pip_device.h", "pip_mlp.h"]),
+    "attention_packed_f32": ("attention_packed_f32_kernel_B128_n20-128.md",
+                             ["attention.hip", "pip_attn_core.h", "pip_attn.h",
+                              "pip_device.h"]),
 }
 
 
@@ -228,7 +233,7 @@ def to_dev(x, dtype=None):
 def setup(pip, synth, name):
     """Device inputs of a workload and its kernels as callables, in step order."""
     import torch
-    d = synth.make_workload(name)
+    d = synth.make_workload("kernel" if name == "packed" else name)
     B, P = d["mask"].shape
     mask = to_dev(d["mask"])
     mlp = pip.PairMLP(d["mlp"])
@@ -250,6 +255,20 @@ def setup(pip, synth, name):
         O = torch.empty_like(q)
         k["fns"] = [("fused_f32", lambda: pip.pair_embed_attention(p4, mask, mlp, q, kk, v,
                                                                    out=O))]
+    elif name == "packed":
+        # the kernel workload's jets packed back to back (no padding)
+        m = d["mask"]
+        cu = to_dev(synth.cu_seqlens(m))
+        p4 = to_dev(synth.pack_rows(d["p4"], m))
+        q, kk, v = (to_dev(synth.pack_heads(d[x], m)) for x in ("q", "k", "v"))
+        U, uoff = pip.pair_embed_packed(p4, cu, mlp)
+        O = torch.empty_like(q)
+        mx = int(d["n"].max())
+        k["fns"] = [("pair_embed_packed_f32",
+                     lambda: pip.pair_embed_packed(p4, cu, mlp, u_offsets=uoff, max_n=mx, out=U)),
+                    ("attention_packed_f32",
+                     lambda: pip.pair_bias_attention_packed(q, kk, v, U, cu, uoff, max_n=mx,
+                                                            out=O))]
     elif name == "stack8":
         U = pip.pair_embed(to_dev(d["p4"]), mask, mlp)
         X = to_dev(d["x0"])
@@ -274,6 +293,11 @@ def work_of(kernel, d):
         return "hbm", attention_bytes(mask, 8, P, 16, 4), PEAK_HBM_GBS
     if kernel == "attention_bf16":
         return "hbm", attention_bytes(mask, 8, P, 16, 2), PEAK_HBM_GBS
+    if kernel == "pair_embed_packed_f32":
+        return "mfma", uniq * MLP_FLOP_PER_PAIR, PEAK_FP32_MFMA_TFLOPS
+    if kernel == "attention_packed_f32":
+        # real Q, K, V rows and real U pairs read, real O rows written
+        return "hbm", int(8 * (4 * n.sum() * 16 + (n * n).sum()) * 4), PEAK_HBM_GBS
     if kernel == "fused_f32":
         return ("mfma", uniq * MLP_FLOP_PER_PAIR + ordered * 8 * ATTN_FLOP_PER_PAIR_HEAD,
                 PEAK_FP32_MFMA_TFLOPS)
@@ -366,6 +390,8 @@ def cpu_sample(name, d, jets):
 
 
 SHAPES = {
+    "packed": "kernel workload packed: B=128 jets back to back, n~U{20..128} (N=%d), H=8, "
+              "D=16, fp32",
     "large_bf16": "B=64 P=256 n~U{60..256} H=8 D=16 bf16",
     "fused512": "B=512 P=128 n~U{20..128} H=8 D=16 fp32, 5% massive",
     "stack8": "B=128 P=128 C=128 H=8 D=16 L=8 fp32",
@@ -464,11 +490,12 @@ def main():
     }
     if not args.no_extra:
         res["workloads"] = {}
-        for name in ("fused512", "large_bf16", "stack8"):
+        for name in ("packed", "fused512", "large_bf16", "stack8"):
             kw = setup(pip, synth, name)
-            res["workloads"][name] = {"shape": SHAPES[name],
+            shape = SHAPES[name] % int(kw["d"]["n"].sum()) if name == "packed" else SHAPES[name]
+            res["workloads"][name] = {"shape": shape,
                                       "rooflines": measure(kw, args.reps, 20, cold)}
-            if not args.no_cpu_baseline:
+            if not args.no_cpu_baseline and name in CPU_JETS:
                 res["workloads"][name]["cpu_oracle"] = cpu_sample(name, kw["d"],
                                                                   CPU_JETS[name])
             del kw

@@ -170,6 +170,58 @@ pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
                                     const void *V, int64_t B, int64_t P, int64_t D, float scale,
                                     void *O, int dtype, void *stream);
 
+/* ---- Packed variable-length layout.  Jets are stored back to back instead
+ * of zero-padded to P slots: jet b owns particle rows cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1, n_b = cu_seqlens[b+1] - cu_seqlens[b] (the `ptr` of the
+ * lloca transformer_v2.Transformer.forward documentation; the gist.science
+ * summary of "Virtues and Vices of Equivariant Transformers", Methodologie,
+ * names sparse representations as the way to skip padding).  Every row is a
+ * real particle; there is no mask.
+ *   p4      (N, 4) float32, energy-first
+ *   Q, K, V, O  (H, N, D), head-major: head h of jet b is rows
+ *           h*N + cu_seqlens[b] .. h*N + cu_seqlens[b+1]-1
+ *   U       jet b: (H, n_b, ld_b) with ld_b = n_b rounded up to a multiple of 8
+ *           (rows start 16-byte aligned; pip_pair_embed_packed writes the <= 7
+ *           columns past n_b as 0 and attention never reads them into a
+ *           result), starting at element H * u_offsets[b], where
+ *           u_offsets[0] = 0 and u_offsets[b+1] = u_offsets[b] + n_b * ld_b.
+ *           u_elems is the U buffer's length in elements (>= H * u_offsets[B]).
+ * cu_seqlens is int32 (B + 1), u_offsets int64 (B + 1), both DEVICE arrays
+ * (4- and 8-byte aligned).  max_n (<= 256) bounds every n_b; the kernels read
+ * cu_seqlens / u_offsets on the device and skip any jet whose entries are
+ * inconsistent (n_b < 0 or > max_n, rows past N, a U block of the wrong size
+ * or past u_elems): nothing of such a jet is written.
+ * Results equal those of the padded entries on the same jets (mask = the
+ * first n_b slots), row for row. */
+
+/* u_offsets (B + 1, device int64) from cu_seqlens (B + 1, device int32), on
+ * the stream (one workgroup scans the batch).  Errors: NULL, SHAPE, ALIGN,
+ * UNSUPPORTED (B > 2^24), HIP. */
+pip_status pip_packed_u_offsets(const int32_t *cu_seqlens, int64_t B, int64_t *u_offsets,
+                                void *stream);
+
+/* pip_pair_embed on the packed layout ("Fusion 2"): U blocks as above, in
+ * u_dtype (PIP_F32 or PIP_BF16, the same arithmetic as pip_pair_embed).  No
+ * padded tile is computed or written.  Errors: NULL, SHAPE, ALIGN, DTYPE,
+ * UNSUPPORTED (max_n > 256, N > 2^30, B > 2^24), HIP. */
+pip_status pip_pair_embed_packed(const float *p4, const int32_t *cu_seqlens,
+                                 const int64_t *u_offsets, int64_t B, int64_t N, int64_t max_n,
+                                 const pip_pair_mlp *mlp, void *U, int64_t u_elems, int u_dtype,
+                                 void *stream);
+
+/* pip_pair_bias_attention on the packed layout ("Fusion 3"): for every jet b,
+ * head h and row a < n_b,
+ *   O[h, cu[b]+a, :] = sum_{c < n_b} softmax_c(scale Q[h,cu[b]+a,:] . K[h,cu[b]+c,:]
+ *                                              + U_b[h, a, c]) V[h, cu[b]+c, :].
+ * Rows of skipped jets are not written.  dtype as in pip_pair_bias_attention.
+ * Requires D == 16.  Errors: NULL, SHAPE, ALIGN, DTYPE, UNSUPPORTED, VALUE,
+ * HIP. */
+pip_status pip_pair_bias_attention_packed(const void *Q, const void *K, const void *V,
+                                          const void *U, const int32_t *cu_seqlens,
+                                          const int64_t *u_offsets, int64_t B, int64_t H,
+                                          int64_t N, int64_t max_n, int64_t D, float scale,
+                                          int64_t u_elems, void *O, int dtype, void *stream);
+
 /* Bytes of device workspace pip_block_stack needs for L layers: the attention
  * output of a layer (B * P * C floats) plus every layer's weights packed as
  * split fp16 matrix-core operands (L * 4 * C^2 * 2 * 2 bytes for C a multiple

@@ -77,6 +77,10 @@ def lib():
                                               i, vp]
         L.pip_pair_embed_attention.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp,
                                                i, vp]
+        L.pip_packed_u_offsets.argtypes = [vp, i64, vp, vp]
+        L.pip_pair_embed_packed.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i, vp]
+        L.pip_pair_bias_attention_packed.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                     i64, f32, i64, vp, i, vp]
         L.pip_block_stack_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.pip_block_stack_workspace_bytes.restype = C.c_size_t
         L.pip_block_stack.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
@@ -85,7 +89,9 @@ def lib():
                                               i64, vp]
         for f in ("pip_pair_mlp_fold", "pip_pair_mlp_create", "pip_pair_mlp_destroy",
                   "pip_pair_features", "pip_pair_embed", "pip_pair_bias_attention",
-                  "pip_pair_embed_attention", "pip_block_stack", "pip_block_stack_noalloc"):
+                  "pip_pair_embed_attention", "pip_block_stack", "pip_block_stack_noalloc",
+                  "pip_packed_u_offsets", "pip_pair_embed_packed",
+                  "pip_pair_bias_attention_packed"):
             getattr(L, f).restype = i
         _lib = L
     return _lib
@@ -295,3 +301,74 @@ def block_stack_noalloc(x, wq, wk, wv, wo, u, mask):
         _dev(mask, "mask", torch.uint8, (B, P)), B, P, Cw, H, L, _stream())
     _check("pip_block_stack_noalloc", st)
     return x
+
+
+# ---------------------------------------------------------------- packed layout
+def packed_ld(n):
+    """Row stride of a packed jet's U block: n rounded up to a multiple of 8."""
+    return (int(n) + 7) // 8 * 8
+
+
+def packed_u_offsets(cu):
+    """u_offsets (B + 1, int64, device) of the packed U blocks, computed on the
+    GPU from cu_seqlens (B + 1, int32, device)."""
+    torch = _torch()
+    B = cu.numel() - 1
+    out = torch.empty(B + 1, device=cu.device, dtype=torch.int64)
+    _check("pip_packed_u_offsets",
+           lib().pip_packed_u_offsets(_dev(cu, "cu_seqlens", torch.int32), B,
+                                      _dev(out, "u_offsets", torch.int64), _stream()))
+    return out
+
+
+def _packed_sizes(cu):
+    """(B, max_n, total U pairs) from a host copy of cu_seqlens, for sizing
+    outputs (the kernels read cu_seqlens on the device)."""
+    c = cu.cpu().numpy().astype(np.int64)
+    n = np.diff(c)
+    ld = (n + 7) // 8 * 8
+    return len(n), int(n.max()) if len(n) else 0, int((n * ld).sum())
+
+
+def pair_embed_packed(p4, cu, mlp: PairMLP, dtype="f32", u_offsets=None, max_n=None,
+                      out=None):
+    """Packed U (one (8, n_b, ld_b) block per jet, concatenated) from p4 (N, 4)
+    and cu_seqlens (B + 1).  Returns (U, u_offsets)."""
+    torch = _torch()
+    code, tdt = _code(dtype)
+    N = p4.shape[0]
+    B = cu.numel() - 1
+    if max_n is None or out is None:
+        _, mx, pairs = _packed_sizes(cu)  # host copy of cu: only to size outputs
+        max_n = mx if max_n is None else int(max_n)
+        if out is None:
+            out = torch.empty(8 * pairs, device=p4.device, dtype=tdt)
+    if u_offsets is None:
+        u_offsets = packed_u_offsets(cu)
+    st = lib().pip_pair_embed_packed(
+        _dev(p4, "p4", torch.float32, (N, 4)), _dev(cu, "cu_seqlens", torch.int32, (B + 1,)),
+        _dev(u_offsets, "u_offsets", torch.int64, (B + 1,)), B, N, max_n, mlp.handle,
+        _dev(out, "U", tdt), out.numel(), code, _stream())
+    _check("pip_pair_embed_packed", st)
+    return out, u_offsets
+
+
+def pair_bias_attention_packed(q, k, v, u, cu, u_offsets, max_n=None, out=None, scale=None):
+    """O (H, N, D) on the packed layout: per jet and head, masked-free
+    softmax(scale Q K^T + U_b) V over the jet's rows; dtype of q."""
+    torch = _torch()
+    code, tdt = _code(q.dtype)
+    H, N, D = q.shape
+    B = cu.numel() - 1
+    if max_n is None:
+        max_n = _packed_sizes(cu)[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib().pip_pair_bias_attention_packed(
+        _dev(q, "Q", tdt), _dev(k, "K", tdt, q.shape), _dev(v, "V", tdt, q.shape),
+        _dev(u, "U", tdt), _dev(cu, "cu_seqlens", torch.int32, (B + 1,)),
+        _dev(u_offsets, "u_offsets", torch.int64, (B + 1,)), B, H, N, int(max_n), D, scale,
+        u.numel(), _dev(out, "O", tdt, q.shape), code, _stream())
+    _check("pip_pair_bias_attention_packed", st)
+    return out

@@ -313,6 +313,77 @@ pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
         (const uint16_t *)V, scale, (uint16_t *)O, s));
 }
 
+pip_status pip_packed_u_offsets(const int32_t *cu_seqlens, int64_t B, int64_t *u_offsets,
+                                void *stream) {
+    if (B < 0) return PIP_ERR_SHAPE;
+    if (B > ((int64_t)1 << 24)) return PIP_ERR_UNSUPPORTED;
+    if (!cu_seqlens || !u_offsets) return PIP_ERR_NULL;
+    if (((uintptr_t)cu_seqlens & 3u) || ((uintptr_t)u_offsets & 7u)) return PIP_ERR_ALIGN;
+    return hip_status(pip::launch_packed_offsets(cu_seqlens, (int)B, u_offsets,
+                                                 (hipStream_t)stream));
+}
+
+// Sizes the packed kernels take: B jets, N particles, max_n <= 256.
+static pip_status check_packed(int64_t B, int64_t N, int64_t max_n, int64_t u_elems) {
+    if (B < 0 || N < 0 || max_n < 0 || u_elems < 0) return PIP_ERR_SHAPE;
+    if (max_n > PIP_MAX_P || B > ((int64_t)1 << 24) || N > ((int64_t)1 << 30))
+        return PIP_ERR_UNSUPPORTED;
+    return PIP_OK;
+}
+
+pip_status pip_pair_embed_packed(const float *p4, const int32_t *cu_seqlens,
+                                 const int64_t *u_offsets, int64_t B, int64_t N, int64_t max_n,
+                                 const pip_pair_mlp *mlp, void *U, int64_t u_elems, int u_dtype,
+                                 void *stream) {
+    if (u_dtype != PIP_F32 && u_dtype != PIP_BF16) return PIP_ERR_DTYPE;
+    pip_status st = check_packed(B, N, max_n, u_elems);
+    if (st != PIP_OK) return st;
+    if (B == 0 || max_n == 0) return PIP_OK;
+    if (!p4 || !cu_seqlens || !u_offsets || !mlp || !U) return PIP_ERR_NULL;
+    if (!aligned16(p4) || !aligned16(U) || ((uintptr_t)cu_seqlens & 3u) ||
+        ((uintptr_t)u_offsets & 7u))
+        return PIP_ERR_ALIGN;
+    if ((st = check_device(mlp)) != PIP_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (u_dtype == PIP_F32)
+        return hip_status(pip::launch_pair_embed_packed_f32(p4, cu_seqlens, u_offsets, (int)B,
+                                                            (int)N, (int)max_n, mlp, (float *)U,
+                                                            u_elems, s));
+    return hip_status(pip::launch_pair_embed_packed_bf16(p4, cu_seqlens, u_offsets, (int)B,
+                                                         (int)N, (int)max_n, mlp, (uint16_t *)U,
+                                                         u_elems, s));
+}
+
+pip_status pip_pair_bias_attention_packed(const void *Q, const void *K, const void *V,
+                                          const void *U, const int32_t *cu_seqlens,
+                                          const int64_t *u_offsets, int64_t B, int64_t H,
+                                          int64_t N, int64_t max_n, int64_t D, float scale,
+                                          int64_t u_elems, void *O, int dtype, void *stream) {
+    if (dtype != PIP_F32 && dtype != PIP_BF16) return PIP_ERR_DTYPE;
+    if (H < 0 || D < 0) return PIP_ERR_SHAPE;
+    pip_status st = check_packed(B, N, max_n, u_elems);
+    if (st != PIP_OK) return st;
+    if (!std::isfinite(scale)) return PIP_ERR_VALUE;
+    if (B == 0 || H == 0 || max_n == 0) return PIP_OK;
+    if (!Q || !K || !V || !U || !cu_seqlens || !u_offsets || !O) return PIP_ERR_NULL;
+    if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
+    if (B * H * pip::attention_chunks((int)((max_n + 15) & ~15)) > ((int64_t)1 << 31) - 1 ||
+        H * N > ((int64_t)1 << 31))
+        return PIP_ERR_UNSUPPORTED;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(O) ||
+        ((uintptr_t)cu_seqlens & 3u) || ((uintptr_t)u_offsets & 7u))
+        return PIP_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == PIP_F32)
+        return hip_status(pip::launch_attention_packed_f32(
+            (const float *)Q, (const float *)K, (const float *)V, (const float *)U, cu_seqlens,
+            u_offsets, (int)B, (int)H, (int)N, (int)max_n, u_elems, scale, (float *)O, s));
+    return hip_status(pip::launch_attention_packed_bf16(
+        (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)U,
+        cu_seqlens, u_offsets, (int)B, (int)H, (int)N, (int)max_n, u_elems, scale,
+        (uint16_t *)O, s));
+}
+
 size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C, int64_t L) {
     if (B <= 0 || P <= 0 || C <= 0 || L <= 0) return 0;
     if (check_pair_grid(B, P) != PIP_OK || C % 16 != 0 || C > 16 * 16 || L > (1 << 20))

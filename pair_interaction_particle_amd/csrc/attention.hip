@@ -54,7 +54,7 @@ constexpr int kAttnQBlocks = 8;  // query blocks per workgroup
 // any magnitude keeps 22 significand bits against K of any magnitude.
 template <int kT, int kWords>
 __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc, bool rq,
-                                           float qk_mul, float vinv,
+                                           bool wr, float qk_mul, float vinv,
                                            const SlotBits<kWords> &real, int T,
                                            const uint16_t *Ks, const uint16_t *Vsh,
                                            const uint16_t *Vsl, float *__restrict__ orow) {
@@ -72,15 +72,16 @@ __device__ __forceinline__ void attend_f32(float4 (&u)[kT], float4 qa, float4 qc
     float lsum;
     attend_split<kT>(u, qh, ql, qk_mul * qinv, real, T, Ks, Vsh, Vsl, o, lsum);
     const float inv = vinv / lsum;
-    *(float4 *)orow = rq ? make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (wr)
+        *(float4 *)orow = rq ? make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ------------------------------------------------------------ bfloat16
 // One query block of a bf16 head.  u holds bf16 pairs (-inf for key blocks
 // without a real key), qv this lane's Q row entries 4g .. 4g+3.
 template <int kT, int kWords>
-__device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq, float scale,
+__device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq, bool wr, float scale,
                                             const SlotBits<kWords> &real, int T,
                                             const uint16_t *Ks, const uint16_t *Vsh,
                                             uint16_t *__restrict__ orow) {
@@ -137,22 +138,30 @@ __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq, flo
         o = mfma32bf(vt, __builtin_convertvector(p, v8bf), o);
     }
     const float inv = 1.0f / xsum16(lsum);
-    *(uint2 *)orow =
-        rq ? make_uint2((uint32_t)f2bf(o[0] * inv) | ((uint32_t)f2bf(o[1] * inv) << 16),
-                        (uint32_t)f2bf(o[2] * inv) | ((uint32_t)f2bf(o[3] * inv) << 16))
-           : make_uint2(0u, 0u);
+    if (wr)
+        *(uint2 *)orow =
+            rq ? make_uint2((uint32_t)f2bf(o[0] * inv) | ((uint32_t)f2bf(o[1] * inv) << 16),
+                            (uint32_t)f2bf(o[2] * inv) | ((uint32_t)f2bf(o[3] * inv) << 16))
+               : make_uint2(0u, 0u);
 }
 
 // ------------------------------------------------------------ kernel
+// Padded layout (kPacked false): Q, K, V, O (B, H, P, 16), U (B, H, P, P),
+// mask (B, P).  Packed layout (kPacked true): jet b owns rows cu[b] ..
+// cu[b+1]-1 of Q, K, V, O (H, N, 16); its bias is (H, n_b, ld_b) at element
+// H u_off[b], ld_b = n_b rounded up to 8; every row < n_b is real and rows
+// of other jets are never read or written.  A packed jet with inconsistent
+// cu / u_off entries is skipped (its O rows are not written).
 // (float32 at P <= 128: held to 6 waves per SIMD, i.e. at most 80 VGPRs, so
 // that three workgroups stay resident per CU)
-template <bool kBf16, int kT, int kQ>
+template <bool kBf16, int kT, int kQ, bool kPacked>
 __global__ __launch_bounds__(64 * kAttnQBlocks / kQ)
 __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_kernel(
     const AttnElt<kBf16> *__restrict__ Q, const AttnElt<kBf16> *__restrict__ K,
     const AttnElt<kBf16> *__restrict__ V, const AttnElt<kBf16> *__restrict__ U,
     const uint8_t *__restrict__ mask, int H, int P, int chunks, float scale,
-    AttnElt<kBf16> *__restrict__ O) {
+    AttnElt<kBf16> *__restrict__ O, const int *__restrict__ cu,
+    const int64_t *__restrict__ uoff, int N, int64_t u_elems) {
     using E = AttnElt<kBf16>;
     constexpr int kWaves = kAttnQBlocks / kQ, kThreads = 64 * kWaves;
     constexpr int kWords = (kT * 16 + 63) / 64;
@@ -170,9 +179,42 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
     const int chunk = blockIdx.x % chunks, bh = blockIdx.x / chunks, jet = bh / H;
-    const int T = P / kTile;
-    const size_t base = (size_t)bh * P;
-    const E *Qh = Q + base * 16, *Kh = K + base * 16, *Vh = V + base * 16;
+    // rows: rows of this (jet, head) that exist (P, or n in the packed
+    // layout); ld: U row stride; T: blocks of 16 rows
+    int rows, ld, T;
+    const E *Qh, *Kh, *Vh, *Ub;
+    E *Oh;
+    SlotBits<kWords> real;
+    if constexpr (!kPacked) {
+        rows = ld = P;
+        T = P / kTile;
+        const size_t base = (size_t)bh * P;
+        Qh = Q + base * 16;
+        Kh = K + base * 16;
+        Vh = V + base * 16;
+        Oh = O + base * 16;
+        Ub = U + base * P;
+    } else {
+        const int h = bh - jet * H;
+        const int start = __builtin_amdgcn_readfirstlane(cu[jet]);
+        const int end = __builtin_amdgcn_readfirstlane(cu[jet + 1]);
+        const int64_t a0 = uoff[jet], a1 = uoff[jet + 1];
+        int n = end - start;
+        const int lp = (n + 7) & ~7;
+        const bool ok = start >= 0 && n >= 0 && n <= P && end <= N && a0 >= 0 &&
+                        a1 - a0 == (int64_t)n * lp && a1 <= u_elems / H;
+        n = ok ? n : 0;
+        rows = n;
+        ld = lp;
+        T = (n + kTile - 1) / kTile;
+        if (chunk * kAttnQBlocks >= T) return;  // uniform: nothing of this jet here
+        const size_t base = (size_t)h * N + start;
+        Qh = Q + base * 16;
+        Kh = K + base * 16;
+        Vh = V + base * 16;
+        Oh = O + base * 16;
+        Ub = U + (size_t)H * a0 + (size_t)h * n * lp;
+    }
 
     // ---- 1. K and V rows this thread stages, issued before the mask is known
     // (blocks below an even block count; the mask only decides what is kept),
@@ -186,13 +228,13 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
         const int i = tid + it * kThreads, k = i >> 2, d0 = (i & 3) * 4;
-        const size_t off = (i < nst * 4 && k < P) ? (size_t)k * 16 + d0 : 0;
+        const size_t off = (i < nst * 4 && k < rows) ? (size_t)k * 16 + d0 : 0;
         kk[it] = *(const KVec *)(Kh + off);
         vv[it] = *(const KVec *)(Vh + off);
     }
 
-    SlotBits<kWords> real;
-    real.load(mask + (size_t)jet * P, P);
+    if constexpr (!kPacked) real.load(mask + (size_t)jet * P, P);
+    else real.first(rows);
 
     using UVec = typename std::conditional<kBf16, uint2, float4>::type;
     UVec u[kQ][kT];
@@ -205,8 +247,8 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     for (int j = 0; j < kQ; ++j) {
         const int qb = chunk * kAttnQBlocks + wave + j * kWaves;
         const bool act = qb < T && real.block_rt(qb) != 0;
-        const int qr = act ? qb * kTile + c : 0;  // query row read
-        const E *urow = U + (base + qr) * P;
+        const int qr = act && qb * kTile + c < rows ? qb * kTile + c : 0;  // query row read
+        const E *urow = Ub + (size_t)qr * ld;
 #pragma unroll
         for (int kb = 0; kb < kT; kb += 2) {
             // lane group g's 8 keys of the pair: one contiguous run
@@ -214,15 +256,15 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
             // clamped, and those keys are masked)
             const bool need = act && kb < T && real.pair(kb >> 1) != 0;
             if constexpr (kBf16) {
-                const int off = min(need ? u_col(kb, g) : u_col(kb, g) * zero, P - 8);
+                const int off = min(need ? u_col(kb, g) : u_col(kb, g) * zero, ld - 8);
                 const uint4 v = *(const uint4 *)(urow + off);
                 u[j][kb] = make_uint2(v.x, v.y);
                 u[j][kb + 1] = make_uint2(v.z, v.w);
             } else {
                 // natural order: 4 keys 16 kb + 4g .. of each block
                 const int o0 = 16 * kb + 4 * g, o1 = o0 + 16;
-                u[j][kb] = *(const float4 *)(urow + min(need ? o0 : o0 * zero, P - 4));
-                u[j][kb + 1] = *(const float4 *)(urow + min(need ? o1 : o1 * zero, P - 4));
+                u[j][kb] = *(const float4 *)(urow + min(need ? o0 : o0 * zero, ld - 4));
+                u[j][kb + 1] = *(const float4 *)(urow + min(need ? o1 : o1 * zero, ld - 4));
             }
         }
         if constexpr (kBf16) {
@@ -267,7 +309,7 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     for (int it = 0; it < kItems; ++it) {
         const int i = tid + it * kThreads, k = i >> 2, d0 = (i & 3) * 4;
         if (i >= nst * 4) continue;
-        const bool rk = k < P && real.slot(k);
+        const bool rk = k < rows && real.slot(k);
         const int kr = kBf16 ? key_row(k) : k;
         if constexpr (kBf16) {
             const uint2 kz = rk ? kk[it] : make_uint2(0u, 0u);
@@ -296,7 +338,8 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
         const int qb = chunk * kAttnQBlocks + wave + j * kWaves;
         const int q0 = qb * kTile;
         if (qb >= T) continue;
-        E *orow = O + (base + q0 + c) * 16 + 4 * g;
+        E *orow = Oh + (size_t)(q0 + c) * 16 + 4 * g;
+        const bool wr = !kPacked || q0 + c < rows;  // packed: rows past n are another jet's
         if (real.block_rt(qb) == 0) {
             if constexpr (kBf16) *(uint2 *)orow = make_uint2(0u, 0u);
             else *(float4 *)orow = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -313,12 +356,12 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
         }
         const bool rq = real.slot(q0 + c);
         if constexpr (kBf16) {
-            attend_bf16<kT>(u[j], rq ? qb16[j] : (v4s){0, 0, 0, 0}, rq, scale, real, T, Ks, Vsh,
-                            orow);
+            attend_bf16<kT>(u[j], rq ? qb16[j] : (v4s){0, 0, 0, 0}, rq, wr, scale, real, T, Ks,
+                            Vsh, orow);
         } else {
             const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-            attend_f32<kT>(u[j], rq ? qa[j] : zero, rq ? qc[j] : zero, rq, scale * kinv, vinv,
-                           real, T, Ks, Vsh, Vsl, orow);
+            attend_f32<kT>(u[j], rq ? qa[j] : zero, rq ? qc[j] : zero, rq, wr, scale * kinv,
+                           vinv, real, T, Ks, Vsh, Vsl, orow);
         }
     }
 }
@@ -333,11 +376,13 @@ static hipError_t launch_attention(const AttnElt<kBf16> *Q, const AttnElt<kBf16>
     const int chunks = attention_chunks(P);
     const dim3 grid((unsigned)((size_t)B * H * chunks));
     if (P <= 128)
-        hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1>), grid, dim3(64 * kAttnQBlocks), 0,
-                           s, Q, K, V, U, mask, H, P, chunks, scale, O);
+        hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1, false>), grid, dim3(64 * kAttnQBlocks),
+                           0, s, Q, K, V, U, mask, H, P, chunks, scale, O, nullptr, nullptr, 0,
+                           (int64_t)0);
     else
-        hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1>), grid, dim3(64 * kAttnQBlocks), 0, s,
-                           Q, K, V, U, mask, H, P, chunks, scale, O);
+        hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1, false>), grid,
+                           dim3(64 * kAttnQBlocks), 0, s, Q, K, V, U, mask, H, P, chunks, scale,
+                           O, nullptr, nullptr, 0, (int64_t)0);
     return hipGetLastError();
 }
 
@@ -351,6 +396,45 @@ hipError_t launch_attention_bf16(const uint16_t *Q, const uint16_t *K, const uin
                                  const uint16_t *U, const uint8_t *mask, int B, int H, int P,
                                  float scale, uint16_t *O, hipStream_t s) {
     return launch_attention<true>(Q, K, V, U, mask, B, H, P, scale, O, s);
+}
+
+// Packed layout: max_n plays the part of P (the largest jet; jets beyond it
+// are skipped).
+template <bool kBf16>
+static hipError_t launch_attention_packed(const AttnElt<kBf16> *Q, const AttnElt<kBf16> *K,
+                                          const AttnElt<kBf16> *V, const AttnElt<kBf16> *U,
+                                          const int *cu, const int64_t *uoff, int B, int H,
+                                          int N, int max_n, int64_t u_elems, float scale,
+                                          AttnElt<kBf16> *O, hipStream_t s) {
+    const int chunks = attention_chunks((max_n + 15) & ~15);
+    if (chunks == 0) return hipSuccess;
+    const dim3 grid((unsigned)((size_t)B * H * chunks));
+    if (max_n <= 128)
+        hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1, true>), grid, dim3(64 * kAttnQBlocks),
+                           0, s, Q, K, V, U, nullptr, H, max_n, chunks, scale, O, cu, uoff, N,
+                           u_elems);
+    else
+        hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1, true>), grid,
+                           dim3(64 * kAttnQBlocks), 0, s, Q, K, V, U, nullptr, H, max_n, chunks,
+                           scale, O, cu, uoff, N, u_elems);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_packed_f32(const float *Q, const float *K, const float *V,
+                                       const float *U, const int *cu, const int64_t *uoff, int B,
+                                       int H, int N, int max_n, int64_t u_elems, float scale,
+                                       float *O, hipStream_t s) {
+    return launch_attention_packed<false>(Q, K, V, U, cu, uoff, B, H, N, max_n, u_elems, scale,
+                                          O, s);
+}
+
+hipError_t launch_attention_packed_bf16(const uint16_t *Q, const uint16_t *K,
+                                        const uint16_t *V, const uint16_t *U, const int *cu,
+                                        const int64_t *uoff, int B, int H, int N, int max_n,
+                                        int64_t u_elems, float scale, uint16_t *O,
+                                        hipStream_t s) {
+    return launch_attention_packed<true>(Q, K, V, U, cu, uoff, B, H, N, max_n, u_elems, scale,
+                                         O, s);
 }
 
 }  // namespace pip

@@ -35,6 +35,12 @@ struct SlotBits {
 #pragma unroll
         for (int i = 0; i < kWords; ++i) w[i] = __ballot(64 * i + lane < P && b[i] != 0);
     }
+    // the first n slots real, the rest not (n wave-uniform)
+    __device__ __forceinline__ void first(int n) {
+#pragma unroll
+        for (int i = 0; i < kWords; ++i)
+            w[i] = n >= 64 * (i + 1) ? ~0ull : (n > 64 * i ? (1ull << (n - 64 * i)) - 1 : 0ull);
+    }
     // word i for a run-time i.  The words pass through readfirstlane (free:
     // they are wave-uniform) so that the selects act on values; a select
     // between two fields would otherwise be folded into an indexed load,

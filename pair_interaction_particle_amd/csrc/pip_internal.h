@@ -48,6 +48,23 @@ hipError_t launch_embed_attention_bf16(const float *p4, const uint8_t *mask, int
                                        const pip_pair_mlp *m, const uint16_t *Q,
                                        const uint16_t *K, const uint16_t *V, float scale,
                                        uint16_t *O, hipStream_t s);
+// packed (variable-length) layout
+hipError_t launch_packed_offsets(const int *cu, int B, int64_t *uoff, hipStream_t s);
+hipError_t launch_pair_embed_packed_f32(const float *p4, const int *cu, const int64_t *uoff,
+                                        int B, int N, int max_n, const pip_pair_mlp *m,
+                                        float *U, int64_t u_elems, hipStream_t s);
+hipError_t launch_pair_embed_packed_bf16(const float *p4, const int *cu, const int64_t *uoff,
+                                         int B, int N, int max_n, const pip_pair_mlp *m,
+                                         uint16_t *U, int64_t u_elems, hipStream_t s);
+hipError_t launch_attention_packed_f32(const float *Q, const float *K, const float *V,
+                                       const float *U, const int *cu, const int64_t *uoff, int B,
+                                       int H, int N, int max_n, int64_t u_elems, float scale,
+                                       float *O, hipStream_t s);
+hipError_t launch_attention_packed_bf16(const uint16_t *Q, const uint16_t *K,
+                                        const uint16_t *V, const uint16_t *U, const int *cu,
+                                        const int64_t *uoff, int B, int H, int N, int max_n,
+                                        int64_t u_elems, float scale, uint16_t *O,
+                                        hipStream_t s);
 // bytes of workspace the block stack needs
 size_t block_stack_workspace(int B, int P, int C, int L);
 hipError_t launch_block_stack(float *X, const float *Wq, const float *Wk, const float *Wv,

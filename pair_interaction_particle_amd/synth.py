@@ -43,6 +43,9 @@ __all__ = [
     "bf16_round",
     "bf16_bits",
     "bf16_bits_to_f32",
+    "pack_rows",
+    "pack_heads",
+    "cu_seqlens",
 ]
 
 
@@ -240,3 +243,26 @@ def make_workload(name: str, seed: int = 0) -> dict:
         x0, wq, wk, wv, wo = make_block_stack(w.B, w.P, w.C, w.L, mask, rng=stack_rng)
         out.update(x0=x0, wq=wq, wk=wk, wv=wv, wo=wo)
     return out
+
+
+# ---------------------------------------------------------------- packed layout
+def cu_seqlens(mask) -> np.ndarray:
+    """int32 (B + 1) offsets of jets packed back to back, from a mask whose
+    real slots are a prefix of each row."""
+    n = (np.asarray(mask) != 0).sum(axis=1).astype(np.int64)
+    return np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+
+
+def pack_rows(x, mask) -> np.ndarray:
+    """(B, P, ...) -> (N, ...): the real rows of every jet, back to back
+    (prefix masks)."""
+    m = np.asarray(mask) != 0
+    return np.ascontiguousarray(np.asarray(x)[m])
+
+
+def pack_heads(x, mask) -> np.ndarray:
+    """(B, H, P, D) -> (H, N, D): per head, the real rows of every jet back to
+    back (prefix masks)."""
+    x = np.asarray(x)
+    m = np.asarray(mask) != 0
+    return np.ascontiguousarray(np.stack([x[:, h][m] for h in range(x.shape[1])]))

@@ -161,3 +161,28 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_packed_validation(L):
+    f = L.pip_pair_embed_packed
+    A8 = 0x10008  # 8-byte aligned, not 16
+    assert f(A16, A16, A16, 2, 40, 30, A16, A16, 1000, 9, None) == DTYPE
+    assert f(A16, A16, A16, -1, 40, 30, A16, A16, 1000, 0, None) == SHAPE
+    assert f(A16, A16, A16, 2, 40, 257, A16, A16, 1000, 0, None) == UNSUP  # max_n > 256
+    assert f(A16, A16, A16, 2, 40, 30, None, A16, 1000, 0, None) == NULL
+    assert f(A8, A16, A16, 2, 40, 30, A16, A16, 1000, 0, None) == ALIGN  # p4 16-byte
+    assert f(A16, A16 + 2, A16, 2, 40, 30, A16, A16, 1000, 0, None) == ALIGN  # cu 4-byte
+    assert f(A16, A16, A16 + 4, 2, 40, 30, A16, A16, 1000, 0, None) == ALIGN  # offsets 8-byte
+    assert f(None, None, None, 0, 0, 0, None, None, 0, 0, None) == OK  # empty
+    a = L.pip_pair_bias_attention_packed
+    args = [A16] * 6
+    assert a(*args, 2, 8, 40, 30, 16, 0.25, 1000, A16, 2, None) == DTYPE
+    assert a(*args, 2, 8, 40, 30, 32, 0.25, 1000, A16, 0, None) == UNSUP  # D != 16
+    assert a(*args, 2, 8, 40, 30, 16, math.nan, 1000, A16, 0, None) == VALUE
+    assert a(*args, 2, 8, 40, 300, 16, 0.25, 1000, A16, 0, None) == UNSUP
+    assert a(*args, 2, 8, 40, 30, 16, 0.25, 1000, None, 0, None) == NULL
+    assert a(*args, 2, 0, 40, 30, 16, 0.25, 1000, A16, 0, None) == OK  # no heads
+    o = L.pip_packed_u_offsets
+    assert o(None, 3, A16, None) == NULL
+    assert o(A16, -1, A16, None) == SHAPE
+    assert o(A16, 3, A16 + 4, None) == ALIGN
