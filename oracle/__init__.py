@@ -60,7 +60,12 @@ def lib():
                                                   dp]
         L.oracle_block_stack.argtypes = [dp, dp, dp, dp, dp, dp, u8p, i64, i64, i64, i64,
                                          i64, dp]
-        for f in ("oracle_pair_features", "oracle_pair_mlp", "oracle_pair_embed",
+        L.oracle_attention_backward.argtypes = [dp, dp, dp, dp, u8p, i64, i64, i64, i64,
+                                                C.c_double, dp, dp, dp, dp, dp]
+        L.oracle_pair_mlp_backward.argtypes = [dp, u8p, i64, i64, C.POINTER(_Mlp), dp, dp]
+        L.oracle_pair_mlp_grad_count.restype = C.c_int
+        for f in ("oracle_attention_backward", "oracle_pair_mlp_backward",
+                  "oracle_pair_features", "oracle_pair_mlp", "oracle_pair_embed",
                   "oracle_attention", "oracle_pair_embed_attention", "oracle_block_stack"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -223,3 +228,53 @@ def block_stack(X0, Wq, Wk, Wv, Wo, U, mask) -> np.ndarray:
                                   _ptr(m), B, P, Cw, H, L, _ptr(X))
     assert rc == 0
     return X
+
+
+# ---------------------------------------------------------------- backward
+GRAD_LAYOUT = (("w1", (64, 4)), ("b1", (64,)), ("bn1_gamma", (64,)), ("bn1_beta", (64,)),
+               ("w2", (64, 64)), ("b2", (64,)), ("bn2_gamma", (64,)), ("bn2_beta", (64,)),
+               ("w3", (64, 64)), ("b3", (64,)), ("bn3_gamma", (64,)), ("bn3_beta", (64,)),
+               ("w4", (8, 64)), ("b4", (8,)), ("in_gamma", (4,)), ("in_beta", (4,)))
+
+
+def attention_backward(Q, K, V, U, mask, dO, scale=None):
+    """(dQ, dK, dV, dU) of the masked biased attention for dL/dO = dO."""
+    q, k, v, u, g = _f64(Q), _f64(K), _f64(V), _f64(U), _f64(dO)
+    B, H, P, D = q.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    m = _u8(mask)
+    dQ, dK, dV = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
+    dU = np.zeros_like(u)
+    rc = lib().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _ptr(m), B, H, P,
+                                         D, scale, _ptr(g), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                         _ptr(dU))
+    assert rc == 0
+    return dQ, dK, dV, dU
+
+
+def pair_mlp_backward(F, mask, params: dict, dU) -> dict:
+    """Gradients of sum(U * dU) with respect to the raw MLP parameters (conv
+    weights and biases, BatchNorm gamma and beta, input BatchNorm gamma and
+    beta), U = pair_mlp(F, mask, params).  Returns {name: float64 array}."""
+    f, g = _f64(F), _f64(dU)
+    B, _, P, _ = f.shape
+    m = _u8(mask)
+    a = _MlpArgs(params)
+    n = lib().oracle_pair_mlp_grad_count()
+    out = np.zeros(n)
+    rc = lib().oracle_pair_mlp_backward(_ptr(f), _ptr(m), B, P, C.byref(a.struct), _ptr(g),
+                                        _ptr(out))
+    assert rc == 0
+    res, o = {}, 0
+    for name, shape in GRAD_LAYOUT:
+        size = int(np.prod(shape))
+        res[name] = out[o:o + size].reshape(shape)
+        o += size
+    assert o == n
+    return res
+
+
+def pair_embed_backward(p4, mask, params: dict, dU, eps: float = EPS) -> dict:
+    """pair_mlp_backward on the features of p4 (the features have no
+    parameters)."""
+    return pair_mlp_backward(pair_features(p4, mask, eps), mask, params, dU)

@@ -349,3 +349,197 @@ int oracle_block_stack(const double *X0, const double *Wq, const double *Wk, con
     }
     return err;
 }
+
+/* ------------------------------------------------------------ backward */
+/* Gradients of the masked biased attention ([R] Fusion 3 names forward and
+ * backward kernels) for a loss L with dL/dO = dO, by the chain rule through
+ * s_c = scale (q_a . k_c) + U[a, c], p = softmax over real c, O_a = sum p_c v_c:
+ *   dp_c = dO_a . v_c,   dS_c = p_c (dp_c - dO_a . O_a),   dU[a, c] = dS_c,
+ *   dQ_a = scale sum_c dS_c k_c,  dK_c += scale dS_c q_a,  dV_c += p_c dO_a.
+ * Everything that involves a padded slot is 0.  All arrays (B, H, P, D) or
+ * (B, H, P, P) like the forward's. */
+int oracle_attention_backward(const double *Q, const double *K, const double *V,
+                              const double *U, const uint8_t *mask, int64_t B, int64_t H,
+                              int64_t P, int64_t D, double scale, const double *dO, double *dQ,
+                              double *dK, double *dV, double *dU) {
+    if (!Q || !K || !V || !U || !mask || !dO || !dQ || !dK || !dV || !dU) return 1;
+    if (B < 0 || H < 1 || P < 0 || D < 1) return 1;
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(P > 0 ? P : 1));
+        double *o = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * H; ++bh) {
+            const int64_t b = bh / H;
+            const size_t off = (size_t)bh * P * D;
+            const double *q = Q + off, *k = K + off, *v = V + off, *g = dO + off;
+            const double *Ub = U + (size_t)bh * P * P;
+            double *dq = dQ + off, *dk = dK + off, *dv = dV + off, *du = dU + (size_t)bh * P * P;
+            const uint8_t *mj = mask + b * P;
+            for (int64_t i = 0; i < P * D; ++i) dq[i] = dk[i] = dv[i] = 0.0;
+            for (int64_t i = 0; i < P * P; ++i) du[i] = 0.0;
+            for (int64_t a = 0; a < P; ++a) {
+                if (!mj[a]) continue;
+                /* forward of row a: two-pass softmax, then O_a */
+                double mx = -INFINITY;
+                int any = 0;
+                for (int64_t c = 0; c < P; ++c) {
+                    if (!mj[c]) continue;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += q[a * D + d] * k[c * D + d];
+                    p[c] = dot * scale + Ub[a * P + c];
+                    if (!any || p[c] > mx) mx = p[c];
+                    any = 1;
+                }
+                if (!any) continue;
+                double Z = 0.0;
+                for (int64_t c = 0; c < P; ++c)
+                    if (mj[c]) {
+                        p[c] = exp(p[c] - mx);
+                        Z += p[c];
+                    }
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                for (int64_t c = 0; c < P; ++c)
+                    if (mj[c]) {
+                        p[c] /= Z;
+                        for (int64_t d = 0; d < D; ++d) o[d] += p[c] * v[c * D + d];
+                    }
+                double Da = 0.0; /* dO_a . O_a */
+                for (int64_t d = 0; d < D; ++d) Da += g[a * D + d] * o[d];
+                for (int64_t c = 0; c < P; ++c) {
+                    if (!mj[c]) continue;
+                    double dp = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dp += g[a * D + d] * v[c * D + d];
+                    const double ds = p[c] * (dp - Da);
+                    du[a * P + c] = ds;
+                    for (int64_t d = 0; d < D; ++d) {
+                        dq[a * D + d] += scale * ds * k[c * D + d];
+                        dk[c * D + d] += scale * ds * q[a * D + d];
+                        dv[c * D + d] += p[c] * g[a * D + d];
+                    }
+                }
+            }
+        }
+        free(p);
+        free(o);
+    }
+    return 0;
+}
+
+/* d GELU(x) / dx = Phi(x) + x phi(x) (exact erf form) */
+static double gelu_grad(double x) {
+    return 0.5 * erfc(-x / sqrt(2.0)) + x * exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+}
+
+/* Layout of the raw-parameter gradient array of the pair MLP (the
+ * parameters of pip_pair_mlp_params that a training step updates; BatchNorm
+ * running statistics are not trained):
+ *   w1 (64*4) b1 (64) g1 (64) be1 (64) | w2 (64*64) b2 g2 be2 | w3 (64*64) b3 g3 be3 |
+ *   w4 (8*64) b4 (8) | in_g (4) in_be (4)      (input BN entries 0 when absent) */
+#define GR_W1 0
+#define GR_L1 (GR_W1 + HID * NIN)
+#define GR_W2 (GR_L1 + 3 * HID)
+#define GR_L2 (GR_W2 + HID * HID)
+#define GR_W3 (GR_L2 + 3 * HID)
+#define GR_L3 (GR_W3 + HID * HID)
+#define GR_W4 (GR_L3 + 3 * HID)
+#define GR_B4 (GR_W4 + NOUT * HID)
+#define GR_IN (GR_B4 + NOUT)
+#define GR_TOTAL (GR_IN + 2 * NIN)
+
+int oracle_pair_mlp_grad_count(void) { return GR_TOTAL; }
+
+/* Adds to grad (GR_TOTAL) the gradient of u . gu for one feature vector f,
+ * where u = MLP(f) as in oracle_mlp_pair: forward keeping every
+ * intermediate, then the chain rule layer by layer. */
+static void mlp_pair_backward(const oracle_mlp *m, const double *f_in, const double *gu,
+                              double *grad) {
+    double x[NIN], xh[NIN]; /* BN'd input, normalised input (input BN) */
+    double z[3][HID], y[3][HID], h[3][HID], zn[3][HID];
+    for (int k = 0; k < NIN; ++k) {
+        if (m->in_gamma) {
+            xh[k] = (f_in[k] - m->in_mean[k]) / sqrt(m->in_var[k] + m->bn_eps);
+            x[k] = m->in_gamma[k] * xh[k] + m->in_beta[k];
+        } else {
+            xh[k] = 0.0;
+            x[k] = f_in[k];
+        }
+    }
+    const double *W[3] = {m->w1, m->w2, m->w3}, *bb[3] = {m->b1, m->b2, m->b3};
+    for (int l = 0; l < 3; ++l) {
+        const double *in = l == 0 ? x : h[l - 1];
+        linear(W[l], bb[l], in, l == 0 ? NIN : HID, HID, z[l]);
+        for (int o = 0; o < HID; ++o) {
+            zn[l][o] = (z[l][o] - m->bn_mean[l][o]) / sqrt(m->bn_var[l][o] + m->bn_eps);
+            y[l][o] = m->bn_gamma[l][o] * zn[l][o] + m->bn_beta[l][o];
+            h[l][o] = oracle_gelu(y[l][o]);
+        }
+    }
+    /* output layer */
+    double dh[HID], dz[HID];
+    for (int o = 0; o < NOUT; ++o) {
+        grad[GR_B4 + o] += gu[o];
+        for (int i = 0; i < HID; ++i) grad[GR_W4 + o * HID + i] += gu[o] * h[2][i];
+    }
+    for (int i = 0; i < HID; ++i) {
+        double s = 0.0;
+        for (int o = 0; o < NOUT; ++o) s += m->w4[o * HID + i] * gu[o];
+        dh[i] = s;
+    }
+    const int wbase[3] = {GR_W1, GR_W2, GR_W3}, lbase[3] = {GR_L1, GR_L2, GR_L3};
+    for (int l = 2; l >= 0; --l) {
+        const int nin = l == 0 ? NIN : HID;
+        const double *in = l == 0 ? x : h[l - 1];
+        for (int o = 0; o < HID; ++o) {
+            const double dy = dh[o] * gelu_grad(y[l][o]);
+            grad[lbase[l] + 2 * HID + o] += dy;               /* beta */
+            grad[lbase[l] + HID + o] += dy * zn[l][o];        /* gamma */
+            dz[o] = dy * m->bn_gamma[l][o] / sqrt(m->bn_var[l][o] + m->bn_eps);
+            grad[lbase[l] + o] += dz[o];                      /* conv bias */
+            for (int i = 0; i < nin; ++i) grad[wbase[l] + o * nin + i] += dz[o] * in[i];
+        }
+        if (l > 0) {
+            for (int i = 0; i < HID; ++i) {
+                double s = 0.0;
+                for (int o = 0; o < HID; ++o) s += W[l][o * HID + i] * dz[o];
+                dh[i] = s;
+            }
+        } else if (m->in_gamma) {
+            for (int i = 0; i < NIN; ++i) {
+                double dx = 0.0;
+                for (int o = 0; o < HID; ++o) dx += m->w1[o * NIN + i] * dz[o];
+                grad[GR_IN + i] += dx * xh[i];       /* input BN gamma */
+                grad[GR_IN + NIN + i] += dx;         /* input BN beta */
+            }
+        }
+    }
+}
+
+/* Gradient of L = sum_{b,h,a,c} U[b,h,a,c] dU[b,h,a,c] with respect to the
+ * raw MLP parameters, U = oracle_pair_mlp(F, mask): every ordered real pair
+ * contributes the backward of its own MLP evaluation.  grad: GR_TOTAL. */
+int oracle_pair_mlp_backward(const double *F, const uint8_t *mask, int64_t B, int64_t P,
+                             const oracle_mlp *m, const double *dU, double *grad) {
+    if (!F || !mask || !m || !dU || !grad || B < 0 || P < 0) return 1;
+    for (int i = 0; i < GR_TOTAL; ++i) grad[i] = 0.0;
+#pragma omp parallel
+    {
+        double *gl = (double *)calloc(GR_TOTAL, sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t b = 0; b < B; ++b) {
+            const uint8_t *mj = mask + b * P;
+            for (int64_t a = 0; a < P; ++a)
+                for (int64_t c = 0; c < P; ++c) {
+                    if (!(mj[a] && mj[c])) continue;
+                    double f[NIN], gu[NOUT];
+                    for (int k = 0; k < NIN; ++k) f[k] = F[((b * NIN + k) * P + a) * P + c];
+                    for (int h = 0; h < NOUT; ++h) gu[h] = dU[((b * NOUT + h) * P + a) * P + c];
+                    mlp_pair_backward(m, f, gu, gl);
+                }
+        }
+#pragma omp critical
+        for (int i = 0; i < GR_TOTAL; ++i) grad[i] += gl[i];
+        free(gl);
+    }
+    return 0;
+}
