@@ -62,6 +62,10 @@ KERNELS = {
                   ["fused.hip", "pip_mlp.h", "pip_attn.h", "pip_device.h"]),
     "block_stack_f32": ("block_stack_f32_stack8_B128_P128_C128_L8.md",
                         ["block_stack.hip", "pip_attn_core.h", "pip_attn.h", "pip_device.h"]),
+    "attention_bwd_f32": ("attention_backward_f32_kernel_B128_P128.md",
+                          ["attention_bwd.hip", "pip_attn.h", "pip_device.h"]),
+    "pair_mlp_bwd_f32": ("pair_mlp_backward_f32_kernel_B128_P128.md",
+                         ["mlp_bwd.hip", "pip_device.h", "pip_mlp.h"]),
     "pair_embed_packed_f32": ("pair_embed_packed_f32_kernel_B128_n20-128.md",
                               ["packed_embed.hip", "pip_device.h", "pip_mlp.h"]),
     "attention_packed_f32": ("attention_packed_f32_kernel_B128_n20-128.md",
@@ -232,8 +236,9 @@ def to_dev(x, dtype=None):
 # ---------------------------------------------------------------- workloads
 def setup(pip, synth, name):
     """Device inputs of a workload and its kernels as callables, in step order."""
+    import numpy as np
     import torch
-    d = synth.make_workload("kernel" if name == "packed" else name)
+    d = synth.make_workload("kernel" if name in ("packed", "backward") else name)
     B, P = d["mask"].shape
     mask = to_dev(d["mask"])
     mlp = pip.PairMLP(d["mlp"])
@@ -269,6 +274,19 @@ def setup(pip, synth, name):
                     ("attention_packed_f32",
                      lambda: pip.pair_bias_attention_packed(q, kk, v, U, cu, uoff, max_n=mx,
                                                             out=O))]
+    elif name == "backward":
+        # the kernel workload's backward: dO -> dQ, dK, dV, dU -> MLP gradient
+        p4 = to_dev(d["p4"])
+        q, kk, v = (to_dev(d[x]) for x in ("q", "k", "v"))
+        U = pip.pair_embed(p4, mask, mlp)
+        dO = to_dev(np.random.default_rng(7).normal(0, 1, size=d["q"].shape).astype("float32"))
+        dq, dk, dv, du = pip.pair_bias_attention_backward(q, kk, v, U, mask, dO)
+        ws = torch.empty(pip.lib().pip_pair_mlp_backward_workspace_bytes(B, P) // 4,
+                         device="cuda")
+        k["fns"] = [("attention_bwd_f32",
+                     lambda: pip.pair_bias_attention_backward(q, kk, v, U, mask, dO)),
+                    ("pair_mlp_bwd_f32",
+                     lambda: pip.pair_mlp_backward(p4, mask, mlp, du, workspace=ws))]
     elif name == "stack8":
         U = pip.pair_embed(to_dev(d["p4"]), mask, mlp)
         X = to_dev(d["x0"])
@@ -293,6 +311,16 @@ def work_of(kernel, d):
         return "hbm", attention_bytes(mask, 8, P, 16, 4), PEAK_HBM_GBS
     if kernel == "attention_bf16":
         return "hbm", attention_bytes(mask, 8, P, 16, 2), PEAK_HBM_GBS
+    if kernel == "attention_bwd_f32":
+        # reads: real Q, K, V, dO rows and real U pairs; writes: dQ, dK, dV
+        # and dU in full (padding zeros are part of the result)
+        return ("hbm", int(8 * (4 * n.sum() * 16 + (n * n).sum()) * 4
+                           + B * 8 * P * (3 * 16 + P) * 4), PEAK_HBM_GBS)
+    if kernel == "pair_mlp_bwd_f32":
+        # per unique real pair: the forward (17,920 flop), the backward chain
+        # 2 (8*64 + 2*64*64) and the weight gradients 2 (64*4 + 2*64*64 + 8*64)
+        per = MLP_FLOP_PER_PAIR + 2 * (8 * 64 + 2 * 64 * 64) + 2 * (64 * 4 + 2 * 64 * 64 + 8 * 64)
+        return "mfma", uniq * per, PEAK_FP32_MFMA_TFLOPS
     if kernel == "pair_embed_packed_f32":
         return "mfma", uniq * MLP_FLOP_PER_PAIR, PEAK_FP32_MFMA_TFLOPS
     if kernel == "attention_packed_f32":
@@ -390,6 +418,8 @@ def cpu_sample(name, d, jets):
 
 
 SHAPES = {
+    "backward": "kernel workload backward: B=128 P=128 n~U{20..128} H=8 D=16 fp32; "
+                "attention dO -> dQ, dK, dV, dU, then pair-MLP parameter gradient",
     "packed": "kernel workload packed: B=128 jets back to back, n~U{20..128} (N=%d), H=8, "
               "D=16, fp32",
     "large_bf16": "B=64 P=256 n~U{60..256} H=8 D=16 bf16",
@@ -490,7 +520,7 @@ def main():
     }
     if not args.no_extra:
         res["workloads"] = {}
-        for name in ("packed", "fused512", "large_bf16", "stack8"):
+        for name in ("packed", "backward", "fused512", "large_bf16", "stack8"):
             kw = setup(pip, synth, name)
             shape = SHAPES[name] % int(kw["d"]["n"].sum()) if name == "packed" else SHAPES[name]
             res["workloads"][name] = {"shape": shape,

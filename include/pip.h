@@ -55,6 +55,9 @@ extern "C" {
 #define PIP_MAX_P 256        /* largest particle count per jet */
 /* bytes of the fixed per-device scratch array behind pip_block_stack_noalloc */
 #define PIP_NOALLOC_SCRATCH_BYTES (16u << 20)
+/* gradient arrays of the pair MLP (pip_pair_mlp_backward, pip_pair_mlp_unfold_grads) */
+#define PIP_PAIR_MLP_FOLDED_GRADS 9160
+#define PIP_PAIR_MLP_RAW_GRADS 9552
 
 typedef enum {
     PIP_OK = 0,
@@ -169,6 +172,66 @@ pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
                                     const pip_pair_mlp *mlp, const void *Q, const void *K,
                                     const void *V, int64_t B, int64_t P, int64_t D, float scale,
                                     void *O, int dtype, void *stream);
+
+/* ---- Backward pass (float32).  Fusion 3 of the ml4sci_cms_e2e26 README names
+ * a forward and a backward kernel for the biased attention; the README's
+ * end-to-end benchmarks have a "Train" column.  A training step runs
+ * pip_pair_bias_attention_backward (dL/dO -> dQ, dK, dV and dU = dL/dU) and
+ * then pip_pair_mlp_backward (dU -> the gradient of the pair MLP's
+ * parameters; the features have none).  BatchNorm is in eval mode (running
+ * statistics fixed), as in the forward. */
+
+/* Gradients of pip_pair_bias_attention for dL/dO = dO (B, H, P, D): with
+ * p = softmax over real keys of s_c = scale q.k_c + U[a, c],
+ *   dS = p o (dO v^T - dO . O),  dU = dS,  dQ = scale dS K,  dK = scale dS^T Q,
+ *   dV = P^T dO.
+ * dQ, dK, dV are (B, H, P, D) and dU (B, H, P, P), all written in full:
+ * every entry that involves a padded slot is +0.0 (values in padded slots of
+ * the inputs, dO included, are never read into a result).  The forward is
+ * recomputed from Q, K, V, U (no saved statistics).  Only PIP_F32 (float32
+ * matrix cores, float32 results); PIP_BF16 returns PIP_ERR_UNSUPPORTED.
+ * dK and dV add the query blocks' contributions with LDS float atomics, so
+ * their last bits can differ from run to run.
+ * Requires D == 16, P % 16 == 0, P <= 256.  Errors: NULL, SHAPE, ALIGN,
+ * DTYPE, UNSUPPORTED, VALUE, HIP. */
+pip_status pip_pair_bias_attention_backward(const void *Q, const void *K, const void *V,
+                                            const void *U, const uint8_t *mask,
+                                            const void *dO, int64_t B, int64_t H, int64_t P,
+                                            int64_t D, float scale, void *dQ, void *dK,
+                                            void *dV, void *dU, int dtype, void *stream);
+
+/* Bytes of workspace pip_pair_mlp_backward needs (one slot of
+ * PIP_PAIR_MLP_FOLDED_GRADS floats per workgroup: B * P/16 slots). */
+size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
+
+/* Gradient of L with respect to the folded pair-MLP parameters, for dL/dU =
+ * dU (B, 8, P, P) float32 and U = pip_pair_embed(p4, mask, mlp): every
+ * unique real pair contributes the backward of its MLP evaluation with
+ * g = dU[a, c] + dU[c, a] (dU[a, a] on the diagonal; U is symmetric), so
+ * dU's padded entries are never read into the result.  grad (device,
+ * PIP_PAIR_MLP_FOLDED_GRADS floats) has pip_pair_mlp_fold's layout:
+ *   dW1' (64*4) dW2' (64*64) dW3' (64*64) dW4 (8*64) | db1' db2' db3' (64) db4 (8)
+ * The MLP runs in exact float32 on the matrix cores (GELU in its erf form).
+ * workspace: pip_pair_mlp_backward_workspace_bytes(B, P) bytes, scratch
+ * (overwritten; calls sharing one on different streams race).  Per-
+ * workgroup sums use LDS float atomics, so the last bits of a result can
+ * differ from run to run; the workgroup sums are then added in a fixed
+ * order.  Requires P % 16 == 0, P <= 256.  Errors: NULL, SHAPE, ALIGN,
+ * UNSUPPORTED, HIP. */
+pip_status pip_pair_mlp_backward(const float *p4, const uint8_t *mask, int64_t B, int64_t P,
+                                 const pip_pair_mlp *mlp, const float *dU, float *grad,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Chain rule from the folded gradient (HOST, PIP_PAIR_MLP_FOLDED_GRADS) to
+ * the raw parameters of `raw` (HOST, PIP_PAIR_MLP_RAW_GRADS floats), in
+ * float64, through W' = diag(s) W diag(si), b' = s (W ti + b - mean) + beta,
+ * s = gamma / sqrt(var + eps) (si, ti: the optional input BatchNorm):
+ *   w1 (64*4) b1 g1 be1 (64 each) | w2 (64*64) b2 g2 be2 | w3 (64*64) b3 g3 be3 |
+ *   w4 (8*64) b4 (8) | in_gamma (4) in_beta (4)   (0 without input BatchNorm)
+ * (g = BatchNorm gamma, be = beta; running statistics are not trained).
+ * Touches no GPU.  Errors: NULL, SHAPE (var + eps <= 0). */
+pip_status pip_pair_mlp_unfold_grads(const pip_pair_mlp_params *raw, const float *grad_folded,
+                                     float *grad_raw);
 
 /* ---- Packed variable-length layout.  Jets are stored back to back instead
  * of zero-padded to P slots: jet b owns particle rows cu_seqlens[b] ..

@@ -81,6 +81,12 @@ def lib():
         L.pip_pair_embed_packed.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i, vp]
         L.pip_pair_bias_attention_packed.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                      i64, f32, i64, vp, i, vp]
+        L.pip_pair_bias_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                                       i64, f32, vp, vp, vp, vp, i, vp]
+        L.pip_pair_mlp_backward_workspace_bytes.argtypes = [i64, i64]
+        L.pip_pair_mlp_backward_workspace_bytes.restype = C.c_size_t
+        L.pip_pair_mlp_backward.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, C.c_size_t, vp]
+        L.pip_pair_mlp_unfold_grads.argtypes = [C.POINTER(_Params), vp, vp]
         L.pip_block_stack_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.pip_block_stack_workspace_bytes.restype = C.c_size_t
         L.pip_block_stack.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
@@ -91,7 +97,8 @@ def lib():
                   "pip_pair_features", "pip_pair_embed", "pip_pair_bias_attention",
                   "pip_pair_embed_attention", "pip_block_stack", "pip_block_stack_noalloc",
                   "pip_packed_u_offsets", "pip_pair_embed_packed",
-                  "pip_pair_bias_attention_packed"):
+                  "pip_pair_bias_attention_packed", "pip_pair_bias_attention_backward",
+                  "pip_pair_mlp_backward", "pip_pair_mlp_unfold_grads"):
             getattr(L, f).restype = i
         _lib = L
     return _lib
@@ -371,4 +378,62 @@ def pair_bias_attention_packed(q, k, v, u, cu, u_offsets, max_n=None, out=None, 
         _dev(u_offsets, "u_offsets", torch.int64, (B + 1,)), B, H, N, int(max_n), D, scale,
         u.numel(), _dev(out, "O", tdt, q.shape), code, _stream())
     _check("pip_pair_bias_attention_packed", st)
+    return out
+
+
+# ---------------------------------------------------------------- backward
+FOLDED_GRADS, RAW_GRADS = 9160, 9552
+RAW_GRAD_LAYOUT = (("w1", (64, 4)), ("b1", (64,)), ("bn1_gamma", (64,)), ("bn1_beta", (64,)),
+                   ("w2", (64, 64)), ("b2", (64,)), ("bn2_gamma", (64,)), ("bn2_beta", (64,)),
+                   ("w3", (64, 64)), ("b3", (64,)), ("bn3_gamma", (64,)), ("bn3_beta", (64,)),
+                   ("w4", (8, 64)), ("b4", (8,)), ("in_gamma", (4,)), ("in_beta", (4,)))
+
+
+def pair_bias_attention_backward(q, k, v, u, mask, dO, scale=None):
+    """(dQ, dK, dV, dU) of pair_bias_attention for dL/dO = dO (float32)."""
+    torch = _torch()
+    code, tdt = _code(q.dtype)
+    B, H, P, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dQ, dK, dV = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dU = torch.empty_like(u)
+    st = lib().pip_pair_bias_attention_backward(
+        _dev(q, "Q", tdt), _dev(k, "K", tdt, q.shape), _dev(v, "V", tdt, q.shape),
+        _dev(u, "U", tdt, (B, H, P, P)), _dev(mask, "mask", torch.uint8, (B, P)),
+        _dev(dO, "dO", tdt, q.shape), B, H, P, D, scale, _dev(dQ, "dQ", tdt),
+        _dev(dK, "dK", tdt), _dev(dV, "dV", tdt), _dev(dU, "dU", tdt), code, _stream())
+    _check("pip_pair_bias_attention_backward", st)
+    return dQ, dK, dV, dU
+
+
+def pair_mlp_backward(p4, mask, mlp: PairMLP, dU, workspace=None):
+    """Folded-parameter gradient (device, FOLDED_GRADS floats) of sum(U * dU)."""
+    torch = _torch()
+    B, P = p4.shape[:2]
+    nbytes = int(lib().pip_pair_mlp_backward_workspace_bytes(B, P))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes // 4, 1), device=p4.device, dtype=torch.float32)
+    grad = torch.empty(FOLDED_GRADS, device=p4.device, dtype=torch.float32)
+    st = lib().pip_pair_mlp_backward(
+        _dev(p4, "p4", torch.float32, (B, P, 4)), _dev(mask, "mask", torch.uint8, (B, P)), B, P,
+        mlp.handle, _dev(dU, "dU", torch.float32, (B, 8, P, P)), _dev(grad, "grad"),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream())
+    _check("pip_pair_mlp_backward", st)
+    return grad
+
+
+def unfold_grads(params: dict, grad_folded) -> dict:
+    """pip_pair_mlp_unfold_grads: raw-parameter gradients {name: float32
+    array} from the folded gradient (host array or tensor)."""
+    hp = _HostParams(params)
+    gf = np.ascontiguousarray(np.asarray(grad_folded, dtype=np.float32)).reshape(-1)
+    assert gf.size == FOLDED_GRADS
+    gr = np.zeros(RAW_GRADS, np.float32)
+    _check("pip_pair_mlp_unfold_grads",
+           lib().pip_pair_mlp_unfold_grads(C.byref(hp.struct), gf.ctypes.data, gr.ctypes.data))
+    out, o = {}, 0
+    for name, shape in RAW_GRAD_LAYOUT:
+        size = int(np.prod(shape))
+        out[name] = gr[o:o + size].reshape(shape)
+        o += size
     return out

@@ -204,11 +204,15 @@ pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **ou
     m->w16 = nullptr;
     m->wx2 = nullptr;
     m->bias = nullptr;
+    m->wplain = nullptr;
     hipError_t e = hipGetDevice(&m->device);
     if (e == hipSuccess) e = hipMalloc((void **)&m->w32, p32.size() * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void **)&m->w16, p16.size() * sizeof(uint16_t));
     if (e == hipSuccess) e = hipMalloc((void **)&m->wx2, px2.size() * sizeof(uint16_t));
     if (e == hipSuccess) e = hipMalloc((void **)&m->bias, b.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void **)&m->wplain, w.size() * sizeof(float));
+    if (e == hipSuccess)
+        e = hipMemcpy(m->wplain, w.data(), w.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(m->w32, p32.data(), p32.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess)
@@ -232,6 +236,7 @@ pip_status pip_pair_mlp_destroy(pip_pair_mlp *m) {
     if (m->w16 && (e2 = hipFree(m->w16)) != hipSuccess) e = e2;
     if (m->wx2 && (e2 = hipFree(m->wx2)) != hipSuccess) e = e2;
     if (m->bias && (e2 = hipFree(m->bias)) != hipSuccess) e = e2;
+    if (m->wplain && (e2 = hipFree(m->wplain)) != hipSuccess) e = e2;
     delete m;
     return hip_status(e);
 }
@@ -382,6 +387,122 @@ pip_status pip_pair_bias_attention_packed(const void *Q, const void *K, const vo
         (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, (const uint16_t *)U,
         cu_seqlens, u_offsets, (int)B, (int)H, (int)N, (int)max_n, u_elems, scale,
         (uint16_t *)O, s));
+}
+
+pip_status pip_pair_bias_attention_backward(const void *Q, const void *K, const void *V,
+                                            const void *U, const uint8_t *mask,
+                                            const void *dO, int64_t B, int64_t H, int64_t P,
+                                            int64_t D, float scale, void *dQ, void *dK,
+                                            void *dV, void *dU, int dtype, void *stream) {
+    if (dtype != PIP_F32 && dtype != PIP_BF16) return PIP_ERR_DTYPE;
+    if (H < 0 || D < 0) return PIP_ERR_SHAPE;
+    pip_status st = check_pair_grid(B, P);
+    if (st != PIP_OK) return st;
+    if (!std::isfinite(scale)) return PIP_ERR_VALUE;
+    if (B == 0 || P == 0 || H == 0) return PIP_OK;
+    if (!Q || !K || !V || !U || !mask || !dO || !dQ || !dK || !dV || !dU) return PIP_ERR_NULL;
+    if (D != PIP_HEAD_DIM || dtype != PIP_F32) return PIP_ERR_UNSUPPORTED;
+    if (B * H > ((int64_t)1 << 31) - 1) return PIP_ERR_UNSUPPORTED;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(dO) ||
+        !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(dU))
+        return PIP_ERR_ALIGN;
+    return hip_status(pip::launch_attention_bwd_f32(
+        (const float *)Q, (const float *)K, (const float *)V, (const float *)U, mask,
+        (const float *)dO, (int)B, (int)H, (int)P, scale, (float *)dQ, (float *)dK,
+        (float *)dV, (float *)dU, (hipStream_t)stream));
+}
+
+size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P) {
+    if (B <= 0 || P <= 0 || check_pair_grid(B, P) != PIP_OK) return 0;
+    return pip::mlp_bwd_workspace((int)B, (int)P);
+}
+
+pip_status pip_pair_mlp_backward(const float *p4, const uint8_t *mask, int64_t B, int64_t P,
+                                 const pip_pair_mlp *mlp, const float *dU, float *grad,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    pip_status st = check_pair_grid(B, P);
+    if (st != PIP_OK) return st;
+    if (!grad || !mlp) return PIP_ERR_NULL;
+    if (((uintptr_t)grad & 3u)) return PIP_ERR_ALIGN;
+    if ((st = check_device(mlp)) != PIP_OK) return st;
+    if (B == 0 || P == 0)  // no pair: the gradient is 0 (a fill kernel, no memset node)
+        return hip_status(pip::launch_mlp_bwd_f32(nullptr, nullptr, 0, 16, mlp, nullptr, grad,
+                                                  nullptr, (hipStream_t)stream));
+    if (!p4 || !mask || !dU || !workspace) return PIP_ERR_NULL;
+    if (workspace_bytes < pip_pair_mlp_backward_workspace_bytes(B, P)) return PIP_ERR_SHAPE;
+    if (!aligned16(p4) || !aligned16(dU) || !aligned16(workspace)) return PIP_ERR_ALIGN;
+    return hip_status(pip::launch_mlp_bwd_f32(p4, mask, (int)B, (int)P, mlp, dU, grad,
+                                              workspace, (hipStream_t)stream));
+}
+
+pip_status pip_pair_mlp_unfold_grads(const pip_pair_mlp_params *raw, const float *gf,
+                                     float *gr) {
+    if (!raw || !gf || !gr) return PIP_ERR_NULL;
+    if (!raw->w1 || !raw->w2 || !raw->w3 || !raw->w4) return PIP_ERR_NULL;
+    for (int k = 0; k < 3; ++k)
+        if (!raw->bn_gamma[k] || !raw->bn_beta[k] || !raw->bn_mean[k] || !raw->bn_var[k])
+            return PIP_ERR_NULL;
+    const int nin = (raw->in_gamma != 0) + (raw->in_beta != 0) + (raw->in_mean != 0) +
+                    (raw->in_var != 0);
+    if (nin != 0 && nin != 4) return PIP_ERR_NULL;
+    const double eps = raw->bn_eps;
+    // input BatchNorm as x' = si x + ti (identity when absent)
+    double si[4], ti[4], sdin[4];
+    for (int i = 0; i < 4; ++i) {
+        if (nin) {
+            const double v = (double)raw->in_var[i] + eps;
+            if (!(v > 0.0)) return PIP_ERR_SHAPE;
+            sdin[i] = sqrt(v);
+            si[i] = (double)raw->in_gamma[i] / sdin[i];
+            ti[i] = (double)raw->in_beta[i] - si[i] * (double)raw->in_mean[i];
+        } else {
+            sdin[i] = si[i] = 1.0;
+            ti[i] = 0.0;
+        }
+    }
+    // folded (gf): W1' (64x4) W2' W3' (64x64) W4 (8x64) | b1' b2' b3' (64) b4 (8)
+    // raw (gr): w1 b1 g1 be1 | w2 b2 g2 be2 | w3 b3 g3 be3 | w4 b4 | in_g in_be
+    const int nins[3] = {4, 64, 64}, wof[3] = {0, 256, 4352}, bof[3] = {8960, 9024, 9088};
+    const float *W[3] = {raw->w1, raw->w2, raw->w3};
+    const float *bias[3] = {raw->b1, raw->b2, raw->b3};
+    int ro = 0;
+    double dsi[4] = {0, 0, 0, 0}, dti[4] = {0, 0, 0, 0};
+    for (int l = 0; l < 3; ++l) {
+        const int ni = nins[l];
+        float *gw = gr + ro, *gb = gw + 64 * ni, *gg = gb + 64, *gbe = gg + 64;
+        for (int o = 0; o < 64; ++o) {
+            const double v = (double)raw->bn_var[l][o] + eps;
+            if (!(v > 0.0)) return PIP_ERR_SHAPE;
+            const double sd = sqrt(v), s = (double)raw->bn_gamma[l][o] / sd;
+            const double db = gf[bof[l] + o];
+            double z = bias[l] ? (double)bias[l][o] : 0.0, dg = 0.0;
+            for (int i = 0; i < ni; ++i) {
+                const double w = W[l][o * ni + i], dw = gf[wof[l] + o * ni + i];
+                if (l == 0) {
+                    gw[o * ni + i] = (float)(s * (dw * si[i] + db * ti[i]));
+                    dg += dw * w * si[i];
+                    z += w * ti[i];
+                    dsi[i] += s * w * dw;
+                    dti[i] += s * w * db;
+                } else {
+                    gw[o * ni + i] = (float)(s * dw);
+                    dg += dw * w;
+                }
+            }
+            gb[o] = (float)(s * db);
+            gg[o] = (float)((dg + db * (z - (double)raw->bn_mean[l][o])) / sd);
+            gbe[o] = (float)db;
+        }
+        ro += 64 * ni + 3 * 64;
+    }
+    for (int e = 0; e < 8 * 64 + 8; ++e) gr[ro + e] = gf[8448 + (e < 512 ? e : 704 + e - 512)];
+    ro += 8 * 64 + 8;
+    for (int i = 0; i < 4; ++i) {
+        gr[ro + i] = nin ? (float)(dsi[i] / sdin[i] - dti[i] * (double)raw->in_mean[i] / sdin[i])
+                         : 0.0f;
+        gr[ro + 4 + i] = nin ? (float)dti[i] : 0.0f;
+    }
+    return PIP_OK;
 }
 
 size_t pip_block_stack_workspace_bytes(int64_t B, int64_t P, int64_t C, int64_t L) {

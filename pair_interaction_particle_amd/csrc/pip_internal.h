@@ -22,6 +22,7 @@ struct pip_pair_mlp {
     uint16_t *w16;
     uint16_t *wx2;
     float *bias;
+    float *wplain;  // the folded weights in pip_pair_mlp_fold's plain layout (backward)
 };
 
 namespace pip {
@@ -65,6 +66,15 @@ hipError_t launch_attention_packed_bf16(const uint16_t *Q, const uint16_t *K,
                                         const int64_t *uoff, int B, int H, int N, int max_n,
                                         int64_t u_elems, float scale, uint16_t *O,
                                         hipStream_t s);
+// backward pass
+hipError_t launch_attention_bwd_f32(const float *Q, const float *K, const float *V,
+                                    const float *U, const uint8_t *mask, const float *dO, int B,
+                                    int H, int P, float scale, float *dQ, float *dK, float *dV,
+                                    float *dU, hipStream_t s);
+size_t mlp_bwd_workspace(int B, int P);
+hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P,
+                              const pip_pair_mlp *m, const float *dU, float *grad, void *ws,
+                              hipStream_t s);
 // bytes of workspace the block stack needs
 size_t block_stack_workspace(int B, int P, int C, int L);
 hipError_t launch_block_stack(float *X, const float *Wq, const float *Wk, const float *Wv,
