@@ -64,7 +64,11 @@ def lib():
                                                 C.c_double, dp, dp, dp, dp, dp]
         L.oracle_pair_mlp_backward.argtypes = [dp, u8p, i64, i64, C.POINTER(_Mlp), dp, dp]
         L.oracle_pair_mlp_grad_count.restype = C.c_int
+        L.oracle_pair_embed_int8.argtypes = [dp, u8p, i64, i64, C.c_double, C.POINTER(_Mlp), dp,
+                                             dp, C.c_double, dp, u8p]
+        L.oracle_pair_mlp_ranges.argtypes = [dp, u8p, i64, i64, C.c_double, C.POINTER(_Mlp), dp]
         for f in ("oracle_attention_backward", "oracle_pair_mlp_backward",
+                  "oracle_pair_embed_int8", "oracle_pair_mlp_ranges",
                   "oracle_pair_features", "oracle_pair_mlp", "oracle_pair_embed",
                   "oracle_attention", "oracle_pair_embed_attention", "oracle_block_stack"):
             getattr(L, f).restype = C.c_int
@@ -278,3 +282,48 @@ def pair_embed_backward(p4, mask, params: dict, dU, eps: float = EPS) -> dict:
     """pair_mlp_backward on the features of p4 (the features have no
     parameters)."""
     return pair_mlp_backward(pair_features(p4, mask, eps), mask, params, dU)
+
+
+# ---------------------------------------------------------------- int8 variant
+def pair_embed_int8(p4, mask, params: dict, act_scale, act_zero, tie_delta=3e-4,
+                    eps: float = EPS):
+    """(U, tie): the pair MLP with int8 inputs to layers 2, 3, 4 (per-tensor
+    scale / zero point) and per-channel int8 weights, float64 otherwise;
+    tie (B, P, P) marks pairs with a quantisation decision within tie_delta
+    of a rounding boundary."""
+    p = _f64(p4)
+    B, P = p.shape[:2]
+    m = _u8(mask)
+    a = _MlpArgs(params)
+    s = np.ascontiguousarray(act_scale, dtype=np.float64)
+    z = np.ascontiguousarray(act_zero, dtype=np.float64)
+    assert s.shape == (3,) and z.shape == (3,)
+    U = np.zeros((B, 8, P, P))
+    tie = np.zeros((B, P, P), np.uint8)
+    rc = lib().oracle_pair_embed_int8(_ptr(p), _ptr(m), B, P, float(eps), C.byref(a.struct),
+                                      _ptr(s), _ptr(z), float(tie_delta), _ptr(U), _ptr(tie))
+    assert rc == 0
+    return U, tie.astype(bool)
+
+
+def pair_mlp_ranges(p4, mask, params: dict, eps: float = EPS) -> np.ndarray:
+    """[[min, max] of h1], [.. h2], [.. h3] of the float MLP over real pairs."""
+    p = _f64(p4)
+    B, P = p.shape[:2]
+    m = _u8(mask)
+    a = _MlpArgs(params)
+    out = np.zeros(6)
+    rc = lib().oracle_pair_mlp_ranges(_ptr(p), _ptr(m), B, P, float(eps), C.byref(a.struct),
+                                      _ptr(out))
+    assert rc == 0
+    return out.reshape(3, 2)
+
+
+def int8_calibration(ranges) -> tuple:
+    """Per-tensor (scale, zero point) of each hidden input from its range:
+    S = (max - min) / 255, Z = -128 - rint(min / S), so that [min, max]
+    maps onto [-128, 127]."""
+    r = np.asarray(ranges, np.float64)
+    S = (r[:, 1] - r[:, 0]) / 255.0
+    Z = -128.0 - np.rint(r[:, 0] / S)
+    return S, Z

@@ -543,3 +543,165 @@ int oracle_pair_mlp_backward(const double *F, const uint8_t *mask, int64_t B, in
     }
     return 0;
 }
+
+/* ------------------------------------------------------------ int8 variant */
+/* The pair MLP with int8 inputs to its hidden linears, after the "Economical
+ * Jet Taggers" summary (gist.science, Technische Samenvatting, Methodologie,
+ * "Datatype Kwantisering": inputs of linear layers quantised to int8 with a
+ * zero point).  Readings: BatchNorm is folded first (the deployed linear is
+ * W' = diag(s) W, b' = s (b - mean) + beta, input BatchNorm folded into layer
+ * 1); layer 1 and every GELU stay in high precision; the inputs h of layers
+ * 2, 3, 4 are quantised per tensor with a given scale S and zero point Z,
+ *     q = clamp(rint(h / S) + Z, -128, 127),   h^ = S (q - Z);
+ * the weights of layers 2, 3, 4 per output channel o, symmetrically,
+ *     sw_o = max_i |W'[o][i]| / 127,  Wq = clamp(rint(W' / sw_o), -127, 127),
+ * and the layer output is sum_i sw_o Wq[o][i] h^_i + b'_o.  rint rounds half
+ * to even.  Everything here is float64.
+ * tie (B, P, P) flags the pairs where some h / S + Z lies within tie_delta of
+ * a rounding boundary (a half-integer): there a float32 implementation may
+ * legitimately take the other code. */
+static void fold_layers(const oracle_mlp *m, double *W1, double *b1, double *W2, double *b2,
+                        double *W3, double *b3) {
+    double si[NIN], ti[NIN];
+    for (int k = 0; k < NIN; ++k) {
+        if (m->in_gamma) {
+            si[k] = m->in_gamma[k] / sqrt(m->in_var[k] + m->bn_eps);
+            ti[k] = m->in_beta[k] - si[k] * m->in_mean[k];
+        } else {
+            si[k] = 1.0;
+            ti[k] = 0.0;
+        }
+    }
+    const double *W[3] = {m->w1, m->w2, m->w3}, *bb[3] = {m->b1, m->b2, m->b3};
+    double *Wo[3] = {W1, W2, W3}, *bo[3] = {b1, b2, b3};
+    for (int l = 0; l < 3; ++l) {
+        const int nin = l == 0 ? NIN : HID;
+        for (int o = 0; o < HID; ++o) {
+            const double s = m->bn_gamma[l][o] / sqrt(m->bn_var[l][o] + m->bn_eps);
+            double z = bb[l] ? bb[l][o] : 0.0;
+            for (int i = 0; i < nin; ++i) {
+                const double w = W[l][o * nin + i];
+                if (l == 0) {
+                    Wo[l][o * nin + i] = s * w * si[i];
+                    z += w * ti[i];
+                } else {
+                    Wo[l][o * nin + i] = s * w;
+                }
+            }
+            bo[l][o] = s * (z - m->bn_mean[l][o]) + m->bn_beta[l][o];
+        }
+    }
+}
+
+/* per-channel symmetric int8 weights: Wq (as doubles) and sw */
+static void quant_weights(const double *W, int nout, int nin, double *Wq, double *sw) {
+    for (int o = 0; o < nout; ++o) {
+        double mx = 0.0;
+        for (int i = 0; i < nin; ++i) mx = fmax(mx, fabs(W[o * nin + i]));
+        sw[o] = mx > 0.0 ? mx / 127.0 : 1.0;
+        for (int i = 0; i < nin; ++i) {
+            double q = rint(W[o * nin + i] / sw[o]);
+            Wq[o * nin + i] = q < -127.0 ? -127.0 : (q > 127.0 ? 127.0 : q);
+        }
+    }
+}
+
+/* fake-quantise h (n values) with scale S and zero point Z; returns whether
+ * some value was within delta of a rounding boundary */
+static int quant_act(double *h, int n, double S, double Z, double delta) {
+    int tie = 0;
+    for (int i = 0; i < n; ++i) {
+        const double d = h[i] / S + Z;
+        if (fabs(d - floor(d) - 0.5) < delta) tie = 1;
+        double q = rint(h[i] / S) + Z;
+        q = q < -128.0 ? -128.0 : (q > 127.0 ? 127.0 : q);
+        h[i] = S * (q - Z);
+    }
+    return tie;
+}
+
+int oracle_pair_embed_int8(const double *p4, const uint8_t *mask, int64_t B, int64_t P,
+                           double eps, const oracle_mlp *m, const double *act_scale,
+                           const double *act_zero, double tie_delta, double *U, uint8_t *tie) {
+    if (!p4 || !mask || !m || !act_scale || !act_zero || !U || !tie || B < 0 || P < 0) return 1;
+    static const int kW = HID * NIN + 2 * HID * HID;
+    double *W = (double *)malloc(sizeof(double) * (kW + 3 * HID + 2 * HID * HID + NOUT * HID +
+                                                   2 * HID + NOUT));
+    if (!W) return 2;
+    double *W1 = W, *W2 = W1 + HID * NIN, *W3 = W2 + HID * HID;
+    double *b1 = W3 + HID * HID, *b2 = b1 + HID, *b3 = b2 + HID;
+    double *Q2 = b3 + HID, *Q3 = Q2 + HID * HID, *Q4 = Q3 + HID * HID;
+    double *s2 = Q4 + NOUT * HID, *s3 = s2 + HID, *s4 = s3 + HID;
+    fold_layers(m, W1, b1, W2, b2, W3, b3);
+    quant_weights(W2, HID, HID, Q2, s2);
+    quant_weights(W3, HID, HID, Q3, s3);
+    quant_weights(m->w4, NOUT, HID, Q4, s4);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        const double *pj = p4 + b * P * 4;
+        const uint8_t *mj = mask + b * P;
+        for (int64_t a = 0; a < P; ++a)
+            for (int64_t c = 0; c < P; ++c) {
+                double f[NIN], h[HID], y[HID], u[NOUT] = {0};
+                int t = 0;
+                if (mj[a] && mj[c]) {
+                    oracle_pair_feature(pj + 4 * a, pj + 4 * c, eps, f);
+                    linear(W1, b1, f, NIN, HID, y);
+                    for (int o = 0; o < HID; ++o) h[o] = oracle_gelu(y[o]);
+                    const double *Qs[2] = {Q2, Q3}, *ss[2] = {s2, s3}, *bs[2] = {b2, b3};
+                    for (int l = 0; l < 2; ++l) {
+                        t |= quant_act(h, HID, act_scale[l], act_zero[l], tie_delta);
+                        for (int o = 0; o < HID; ++o) {
+                            double acc = 0.0;
+                            for (int i = 0; i < HID; ++i) acc += Qs[l][o * HID + i] * h[i];
+                            y[o] = ss[l][o] * acc + bs[l][o];
+                        }
+                        for (int o = 0; o < HID; ++o) h[o] = oracle_gelu(y[o]);
+                    }
+                    t |= quant_act(h, HID, act_scale[2], act_zero[2], tie_delta);
+                    for (int o = 0; o < NOUT; ++o) {
+                        double acc = 0.0;
+                        for (int i = 0; i < HID; ++i) acc += Q4[o * HID + i] * h[i];
+                        u[o] = s4[o] * acc + (m->b4 ? m->b4[o] : 0.0);
+                    }
+                }
+                for (int hh = 0; hh < NOUT; ++hh) U[((b * NOUT + hh) * P + a) * P + c] = u[hh];
+                tie[(b * P + a) * P + c] = (uint8_t)t;
+            }
+    }
+    free(W);
+    return 0;
+}
+
+/* Smallest and largest input of each hidden linear (h1, h2, h3) of the
+ * float pair MLP over the real pairs: a calibration of the int8 variant's
+ * activation ranges.  out6 = {min1, max1, min2, max2, min3, max3}. */
+int oracle_pair_mlp_ranges(const double *p4, const uint8_t *mask, int64_t B, int64_t P,
+                           double eps, const oracle_mlp *m, double *out6) {
+    if (!p4 || !mask || !m || !out6) return 1;
+    double W1[HID * NIN], W2[HID * HID], W3[HID * HID], b1[HID], b2[HID], b3[HID];
+    fold_layers(m, W1, b1, W2, b2, W3, b3);
+    for (int l = 0; l < 3; ++l) {
+        out6[2 * l] = INFINITY;
+        out6[2 * l + 1] = -INFINITY;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t a = 0; a < P; ++a)
+            for (int64_t c = 0; c <= a; ++c) {
+                if (!(mask[b * P + a] && mask[b * P + c])) continue;
+                double f[NIN], y[HID], h[HID];
+                oracle_pair_feature(p4 + (b * P + a) * 4, p4 + (b * P + c) * 4, eps, f);
+                const double *Ws[3] = {W1, W2, W3}, *bs[3] = {b1, b2, b3};
+                const double *in = f;
+                for (int l = 0; l < 3; ++l) {
+                    linear(Ws[l], bs[l], in, l == 0 ? NIN : HID, HID, y);
+                    for (int o = 0; o < HID; ++o) {
+                        h[o] = oracle_gelu(y[o]);
+                        out6[2 * l] = fmin(out6[2 * l], h[o]);
+                        out6[2 * l + 1] = fmax(out6[2 * l + 1], h[o]);
+                    }
+                    in = h;
+                }
+            }
+    return 0;
+}
