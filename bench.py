@@ -41,6 +41,8 @@ MLP_FLOP_PER_PAIR = 2 * (4 * 64 + 64 * 64 + 64 * 64 + 64 * 8)  # 17,920
 ATTN_FLOP_PER_PAIR_HEAD = 2 * 2 * 16                           # QK^T and PV at D=16
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_BF16_MFMA_TFLOPS = 2500.0
+PEAK_INT8_MFMA_TOPS = 5000.0
+INT8_CALIB = os.path.join(ROOT, "tests", "golden", "int8_calibration.json")
 PEAK_HBM_GBS = 8000.0
 # non-packed VALU issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s
 PEAK_VALU_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -66,6 +68,11 @@ KERNELS = {
                           ["attention_bwd.hip", "pip_attn.h", "pip_device.h"]),
     "pair_mlp_bwd_f32": ("pair_mlp_backward_f32_kernel_B128_P128.md",
                          ["mlp_bwd.hip", "pip_device.h", "pip_mlp.h"]),
+    "pair_embed_int8": ("pair_embed_int8_kernel_B128_P128.md",
+                        ["pair_embed.hip", "pip_device.h", "pip_mlp.h"]),
+    "attention_bf16_kernel": ("attention_bf16_kernel_B128_P128.md",
+                              ["attention.hip", "pip_attn_core.h", "pip_attn.h",
+                               "pip_device.h"]),
     "pair_embed_packed_f32": ("pair_embed_packed_f32_kernel_B128_n20-128.md",
                               ["packed_embed.hip", "pip_device.h", "pip_mlp.h"]),
     "attention_packed_f32": ("attention_packed_f32_kernel_B128_n20-128.md",
@@ -238,7 +245,7 @@ def setup(pip, synth, name):
     """Device inputs of a workload and its kernels as callables, in step order."""
     import numpy as np
     import torch
-    d = synth.make_workload("kernel" if name in ("packed", "backward") else name)
+    d = synth.make_workload("kernel" if name in ("packed", "backward", "int8") else name)
     B, P = d["mask"].shape
     mask = to_dev(d["mask"])
     mlp = pip.PairMLP(d["mlp"])
@@ -274,6 +281,18 @@ def setup(pip, synth, name):
                     ("attention_packed_f32",
                      lambda: pip.pair_bias_attention_packed(q, kk, v, U, cu, uoff, max_n=mx,
                                                             out=O))]
+    elif name == "int8":
+        # the kernel workload through the int8 MLP (U bf16) and the bf16
+        # attention; activation quantisation from the committed calibration
+        c = json.load(open(INT8_CALIB))["kernel"]
+        p4 = to_dev(d["p4"])
+        q, kk, v = (to_dev(synth.bf16_round(d[x]), torch.bfloat16) for x in ("q", "k", "v"))
+        U = torch.empty((B, 8, P, P), device="cuda", dtype=torch.bfloat16)
+        O = torch.empty_like(q)
+        S, Z = c["act_scale"], c["act_zero"]
+        k["fns"] = [("pair_embed_int8", lambda: pip.pair_embed_int8(p4, mask, mlp, S, Z, out=U)),
+                    ("attention_bf16_kernel",
+                     lambda: pip.pair_bias_attention(q, kk, v, U, mask, out=O))]
     elif name == "backward":
         # the kernel workload's backward: dO -> dQ, dK, dV, dU -> MLP gradient
         p4 = to_dev(d["p4"])
@@ -310,6 +329,11 @@ def work_of(kernel, d):
     if kernel == "attention_f32":
         return "hbm", attention_bytes(mask, 8, P, 16, 4), PEAK_HBM_GBS
     if kernel == "attention_bf16":
+        return "hbm", attention_bytes(mask, 8, P, 16, 2), PEAK_HBM_GBS
+    if kernel == "pair_embed_int8":
+        # int8 MFMA operations of layers 2, 3, 4 per unique real pair
+        return "mfma", uniq * 2 * (64 * 64 * 2 + 64 * 8), PEAK_INT8_MFMA_TOPS
+    if kernel == "attention_bf16_kernel":
         return "hbm", attention_bytes(mask, 8, P, 16, 2), PEAK_HBM_GBS
     if kernel == "attention_bwd_f32":
         # reads: real Q, K, V, dO rows and real U pairs; writes: dQ, dK, dV
@@ -349,7 +373,8 @@ def measure(k, reps, warmup, cold):
         kind, work, peak = work_of(name, k["d"])
         prof = read_profile(name)
         extra = {"algorithmic_%s_per_launch" % ("flop" if kind == "mfma" else "bytes"): work}
-        if name == "pair_embed_bf16" and prof and "valu_lane_ops_per_launch" in prof:
+        if name in ("pair_embed_bf16", "pair_embed_int8") and prof and \
+                "valu_lane_ops_per_launch" in prof:
             # the bf16 embed is bound by VALU issue (GELU), not by its bf16
             # matrix cores: report the issued VALU lane-ops against the
             # non-packed VALU peak beside the bf16 MFMA fraction
@@ -359,6 +384,8 @@ def measure(k, reps, warmup, cold):
                              "frac": lane_ops / (warm["median_us"] * 1e-6) / 1e12
                              / PEAK_VALU_TLANEOPS}
         out[name] = roofline(kind, work, warm, cld, prof, peak, extra)
+        if name == "pair_embed_int8":
+            out[name]["unit"] = "TOP/s"
     return out
 
 
@@ -418,6 +445,8 @@ def cpu_sample(name, d, jets):
 
 
 SHAPES = {
+    "int8": "kernel workload, int8 MLP: B=128 P=128 n~U{20..128} H=8 D=16; int8 inputs to "
+            "layers 2-4 (calibrated zero points), U bf16, bf16 attention",
     "backward": "kernel workload backward: B=128 P=128 n~U{20..128} H=8 D=16 fp32; "
                 "attention dO -> dQ, dK, dV, dU, then pair-MLP parameter gradient",
     "packed": "kernel workload packed: B=128 jets back to back, n~U{20..128} (N=%d), H=8, "
@@ -520,7 +549,7 @@ def main():
     }
     if not args.no_extra:
         res["workloads"] = {}
-        for name in ("packed", "backward", "fused512", "large_bf16", "stack8"):
+        for name in ("packed", "int8", "backward", "fused512", "large_bf16", "stack8"):
             kw = setup(pip, synth, name)
             shape = SHAPES[name] % int(kw["d"]["n"].sum()) if name == "packed" else SHAPES[name]
             res["workloads"][name] = {"shape": shape,

@@ -140,6 +140,25 @@ pip_status pip_pair_features(const float *p4, const uint8_t *mask, int64_t B, in
 pip_status pip_pair_embed(const float *p4, const uint8_t *mask, int64_t B, int64_t P,
                           const pip_pair_mlp *mlp, void *U, int u_dtype, void *stream);
 
+/* Pair embedding with int8 inputs to the hidden linears: the "Economical Jet
+ * Taggers" summary (gist.science, Technische Samenvatting, Methodologie,
+ * "Datatype Kwantisering") quantises the inputs of linear layers to int8
+ * with a zero point and keeps bfloat16 for the rest.  Here: features and
+ * layer 1 float32, GELU float32; the inputs h of layers 2, 3, 4 quantised
+ * per tensor, q = clamp(rint(h / S) + Z, -128, 127) with the caller's
+ * act_scale[l] = S > 0 and act_zero[l] = Z in [-128, 127] (HOST arrays of 3,
+ * a calibration of the model); the folded weights of layers 2, 3, 4
+ * quantised per output channel when the handle is created, sw = max |W'| /
+ * 127, Wq = clamp(rint(W' / sw), -127, 127); each product on the int8 matrix
+ * cores with exact int32 sums, y = S sw (sum Wq q - Z sum Wq) + b'.  U
+ * (B, 8, P, P) is stored as bfloat16; pairs touching a padded slot are +0.0.
+ * Requires P % 16 == 0, 16 <= P <= 256.  Errors: NULL, SHAPE, ALIGN,
+ * UNSUPPORTED, VALUE (a scale not finite and positive, a zero point out of
+ * range), HIP. */
+pip_status pip_pair_embed_int8(const float *p4, const uint8_t *mask, int64_t B, int64_t P,
+                               const pip_pair_mlp *mlp, const float *act_scale,
+                               const int32_t *act_zero, void *U, void *stream);
+
 /* Masked biased attention ("Fusion 3"): for every head h and real query a,
  *   O[b,h,a,:] = sum_c softmax_c(scale * Q[b,h,a,:] . K[b,h,c,:] + U[b,h,a,c]) V[b,h,c,:]
  * over real keys c only; padded query rows are 0.  "Fusion 3" writes the

@@ -81,6 +81,7 @@ def lib():
         L.pip_pair_embed_packed.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i64, i, vp]
         L.pip_pair_bias_attention_packed.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                      i64, f32, i64, vp, i, vp]
+        L.pip_pair_embed_int8.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp]
         L.pip_pair_bias_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                                        i64, f32, vp, vp, vp, vp, i, vp]
         L.pip_pair_mlp_backward_workspace_bytes.argtypes = [i64, i64]
@@ -98,7 +99,7 @@ def lib():
                   "pip_pair_embed_attention", "pip_block_stack", "pip_block_stack_noalloc",
                   "pip_packed_u_offsets", "pip_pair_embed_packed",
                   "pip_pair_bias_attention_packed", "pip_pair_bias_attention_backward",
-                  "pip_pair_mlp_backward", "pip_pair_mlp_unfold_grads"):
+                  "pip_pair_mlp_backward", "pip_pair_mlp_unfold_grads", "pip_pair_embed_int8"):
             getattr(L, f).restype = i
         _lib = L
     return _lib
@@ -436,4 +437,22 @@ def unfold_grads(params: dict, grad_folded) -> dict:
         size = int(np.prod(shape))
         out[name] = gr[o:o + size].reshape(shape)
         o += size
+    return out
+
+
+# ---------------------------------------------------------------- int8 variant
+def pair_embed_int8(p4, mask, mlp: PairMLP, act_scale, act_zero, out=None):
+    """U (B, 8, P, P) bfloat16 with int8 inputs to the hidden linears:
+    act_scale / act_zero (3 each) quantise the inputs of layers 2, 3, 4."""
+    torch = _torch()
+    B, P = p4.shape[:2]
+    s = np.ascontiguousarray(np.asarray(act_scale, dtype=np.float32).reshape(3))
+    z = np.ascontiguousarray(np.asarray(act_zero, dtype=np.int32).reshape(3))
+    if out is None:
+        out = torch.empty((B, 8, P, P), device=p4.device, dtype=torch.bfloat16)
+    st = lib().pip_pair_embed_int8(_dev(p4, "p4", torch.float32, (B, P, 4)),
+                                   _dev(mask, "mask", torch.uint8, (B, P)), B, P, mlp.handle,
+                                   s.ctypes.data, z.ctypes.data,
+                                   _dev(out, "U", torch.bfloat16, (B, 8, P, P)), _stream())
+    _check("pip_pair_embed_int8", st)
     return out

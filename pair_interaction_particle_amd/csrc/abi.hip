@@ -62,7 +62,11 @@ const char *pip_status_string(int s) {
 
 int pip_version(void) { return PIP_VERSION; }
 
-pip_status pip_pair_mlp_fold(const pip_pair_mlp_params *raw, float *w_out, float *b_out) {
+}  // extern "C"
+
+// The BatchNorm fold in float64 (pip_pair_mlp_fold rounds it to float32; the
+// int8 weights are quantised from it directly).
+static pip_status fold_double(const pip_pair_mlp_params *raw, double *w_out, double *b_out) {
     if (!raw || !w_out || !b_out) return PIP_ERR_NULL;
     if (!raw->w1 || !raw->w2 || !raw->w3 || !raw->w4) return PIP_ERR_NULL;
     for (int k = 0; k < 3; ++k)
@@ -89,7 +93,7 @@ pip_status pip_pair_mlp_fold(const pip_pair_mlp_params *raw, float *w_out, float
     const float *W[3] = {raw->w1, raw->w2, raw->w3};
     const float *bias[3] = {raw->b1, raw->b2, raw->b3};
     const int nins[3] = {4, 64, 64};
-    float *wo = w_out;
+    double *wo = w_out;
     for (int l = 0; l < 3; ++l) {
         const int ni = nins[l];
         for (int o = 0; o < 64; ++o) {
@@ -100,21 +104,33 @@ pip_status pip_pair_mlp_fold(const pip_pair_mlp_params *raw, float *w_out, float
             for (int i = 0; i < ni; ++i) {
                 const double w = (double)W[l][o * ni + i];
                 if (l == 0) {
-                    wo[o * ni + i] = (float)(s * w * si[i]);
+                    wo[o * ni + i] = s * w * si[i];
                     z += w * ti[i];
                 } else {
-                    wo[o * ni + i] = (float)(s * w);
+                    wo[o * ni + i] = s * w;
                 }
             }
-            b_out[64 * l + o] =
-                (float)(s * (z - (double)raw->bn_mean[l][o]) + (double)raw->bn_beta[l][o]);
+            b_out[64 * l + o] = s * (z - (double)raw->bn_mean[l][o]) + (double)raw->bn_beta[l][o];
         }
         wo += 64 * ni;
     }
     for (int i = 0; i < 8 * 64; ++i) wo[i] = raw->w4[i];
-    for (int o = 0; o < 8; ++o) b_out[192 + o] = raw->b4 ? raw->b4[o] : 0.0f;
+    for (int o = 0; o < 8; ++o) b_out[192 + o] = raw->b4 ? raw->b4[o] : 0.0;
     return PIP_OK;
 }
+
+extern "C" {
+
+pip_status pip_pair_mlp_fold(const pip_pair_mlp_params *raw, float *w_out, float *b_out) {
+    if (!raw || !w_out || !b_out) return PIP_ERR_NULL;
+    double w[8960], b[200];
+    const pip_status st = fold_double(raw, w, b);
+    if (st != PIP_OK) return st;
+    for (int i = 0; i < 8960; ++i) w_out[i] = (float)w[i];
+    for (int i = 0; i < 200; ++i) b_out[i] = (float)b[i];
+    return PIP_OK;
+}
+
 
 pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **out) {
     if (!out) return PIP_ERR_NULL;
@@ -198,8 +214,44 @@ pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **ou
                 put_x2(pip::kW16L4 + (s * 64 + l) * 8 + j,
                        (l % 16 < 8) ? W4[(l % 16) * 64 + chan(s, l / 16, j)] : 0.0f);
 
+    // int8 weights of layers 2, 3, 4 from the float64 fold: per output channel
+    // sw = max |W'| / 127 (1 for an all-zero row), Wq = clamp(rint(W' / sw),
+    // -127, 127).  Operand (layer, co) of lane l holds, in byte 4c + r of
+    // dword c, Wq[16co + l%16][16c + 4(l/16) + r] (the order the int8 chain
+    // keeps its inputs in); layer 4 rows >= 8 are 0.  q8: sw (channels 0..63
+    // layer 2, 64..127 layer 3, 128..135 layer 4, padded to 144) then the
+    // per-channel sums of Wq, as floats.
+    std::vector<int8_t> p8(pip::kW8Ops * 64 * 16, 0);
+    std::vector<float> q8(pip::kQ8Floats, 0.0f);
+    {
+        double wd[8960], bd[200];
+        fold_double(raw, wd, bd);  // cannot fail: pip_pair_mlp_fold above succeeded
+        const double *Wq3[3] = {wd + 256, wd + 4352, wd + 8448};
+        const int nout[3] = {64, 64, 8};
+        for (int l = 0; l < 3; ++l)
+            for (int o = 0; o < nout[l]; ++o) {
+                double mx = 0.0;
+                for (int i = 0; i < 64; ++i) mx = fmax(mx, fabs(Wq3[l][o * 64 + i]));
+                const double sw = mx > 0.0 ? mx / 127.0 : 1.0;
+                int sum = 0;
+                for (int i = 0; i < 64; ++i) {
+                    double q = rint(Wq3[l][o * 64 + i] / sw);
+                    q = q < -127.0 ? -127.0 : (q > 127.0 ? 127.0 : q);
+                    const int qi = (int)q;
+                    sum += qi;
+                    const int co = o / 16, row = o % 16, c = i / 16, g = (i % 16) / 4, r = i % 4;
+                    const int lane = 16 * g + row;
+                    p8[(((l * 4 + co) * 64 + lane) * 4 + c) * 4 + r] = (int8_t)qi;
+                }
+                q8[64 * l + o] = (float)sw;
+                q8[pip::kQ8Floats / 2 + 64 * l + o] = (float)sum;
+            }
+    }
+
     pip_pair_mlp *m = new pip_pair_mlp();
     m->f16ok = f16ok ? 1 : 0;
+    m->w8 = nullptr;
+    m->q8 = nullptr;
     m->w32 = nullptr;
     m->w16 = nullptr;
     m->wx2 = nullptr;
@@ -211,6 +263,11 @@ pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **ou
     if (e == hipSuccess) e = hipMalloc((void **)&m->wx2, px2.size() * sizeof(uint16_t));
     if (e == hipSuccess) e = hipMalloc((void **)&m->bias, b.size() * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void **)&m->wplain, w.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void **)&m->w8, p8.size());
+    if (e == hipSuccess) e = hipMalloc((void **)&m->q8, q8.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMemcpy(m->w8, p8.data(), p8.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(m->q8, q8.data(), q8.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(m->wplain, w.data(), w.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess)
@@ -237,6 +294,8 @@ pip_status pip_pair_mlp_destroy(pip_pair_mlp *m) {
     if (m->wx2 && (e2 = hipFree(m->wx2)) != hipSuccess) e = e2;
     if (m->bias && (e2 = hipFree(m->bias)) != hipSuccess) e = e2;
     if (m->wplain && (e2 = hipFree(m->wplain)) != hipSuccess) e = e2;
+    if (m->w8 && (e2 = hipFree(m->w8)) != hipSuccess) e = e2;
+    if (m->q8 && (e2 = hipFree(m->q8)) != hipSuccess) e = e2;
     delete m;
     return hip_status(e);
 }
@@ -262,6 +321,27 @@ pip_status pip_pair_embed(const float *p4, const uint8_t *mask, int64_t B, int64
     if (u_dtype == PIP_F32)
         return hip_status(pip::launch_pair_embed_f32(p4, mask, (int)B, (int)P, mlp, (float *)U, s));
     return hip_status(pip::launch_pair_embed_bf16(p4, mask, (int)B, (int)P, mlp, (uint16_t *)U, s));
+}
+
+pip_status pip_pair_embed_int8(const float *p4, const uint8_t *mask, int64_t B, int64_t P,
+                               const pip_pair_mlp *mlp, const float *act_scale,
+                               const int32_t *act_zero, void *U, void *stream) {
+    pip_status st = check_pair_grid(B, P);
+    if (st != PIP_OK) return st;
+    if (!act_scale || !act_zero) return PIP_ERR_NULL;
+    for (int l = 0; l < 3; ++l) {
+        if (!std::isfinite(act_scale[l]) || !(act_scale[l] > 0.0f) ||
+            !std::isfinite(1.0f / act_scale[l]))
+            return PIP_ERR_VALUE;
+        if (act_zero[l] < -128 || act_zero[l] > 127) return PIP_ERR_VALUE;
+    }
+    if (B == 0 || P == 0) return PIP_OK;
+    if (!p4 || !mask || !mlp || !U) return PIP_ERR_NULL;
+    if (!aligned16(p4) || !aligned16(mask) || !aligned16(U)) return PIP_ERR_ALIGN;
+    if ((st = check_device(mlp)) != PIP_OK) return st;
+    return hip_status(pip::launch_pair_embed_int8(p4, mask, (int)B, (int)P, mlp, act_scale,
+                                                  act_zero, (uint16_t *)U,
+                                                  (hipStream_t)stream));
 }
 
 pip_status pip_pair_bias_attention(const void *Q, const void *K, const void *V, const void *U,

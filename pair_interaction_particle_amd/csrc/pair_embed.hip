@@ -260,8 +260,8 @@ __device__ __forceinline__ void write_row_pair(const PL &L, OutT *U, int P, int 
 // only moves the split points; every iteration is still done exactly once.
 template <int kMode>
 struct WorkCost {  // relative cost of a real and an all-padding iteration, and of a jet
-    static constexpr int kReal = kMode == kMlpBf16 ? 4 : 5, kPad = 1,
-                         kJet = kMode == kMlpBf16 ? 4 : 15;
+    static constexpr bool kLow = kMode == kMlpBf16 || kMode == kMlpInt8;
+    static constexpr int kReal = kLow ? 4 : 5, kPad = 1, kJet = kLow ? 4 : 15;
 };
 
 struct JetInfo {
@@ -399,8 +399,9 @@ __global__ __launch_bounds__(kEmbedThreads) __attribute__((amdgpu_waves_per_eu(4
 void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B,
                        int P, const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
                        const v8h *__restrict__ wx2, const float *__restrict__ bias,
-                       void *__restrict__ Uout, int wz) {
+                       void *__restrict__ Uout, int wz, Int8Args ia) {
     MlpLds<kMode> M;
+    if constexpr (kMode == kMlpInt8) M.set_act(ia);
     __shared__ PartLds<kMaxP> Ls[2];  // the particles of two jets
     __shared__ int scan[kEmbedThreads];
     __shared__ JetInfo jinfo[kEmbedThreads];
@@ -414,7 +415,7 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // which no valid entry can equal since j <= i
     __shared__ uint8_t diagPair[160];
 
-    typedef typename std::conditional<kMode == kMlpBf16, uint16_t, float>::type OutT;
+    typedef MlpOut<kMode> OutT;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (tid < 160) {
@@ -465,7 +466,7 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         uint4 v[kJ];
         round_loads(0, v);
         __asm__ volatile("" ::: "memory");  // (issue order: mask rows, then weights)
-        wst.load(w32, w16, wx2, bias);
+        wst.load(w32, w16, wx2, bias, &ia);
         round_info(0, v);
         for (int r0 = kGroups * kJ; r0 < B; r0 += kGroups * kJ) {
             round_loads(r0, v);
@@ -754,8 +755,9 @@ static int persistent_grid(int B, int P) {
 // stay far inside int range.
 template <int kMode>
 static hipError_t launch_embed(const float *p4, const uint8_t *mask, int B, int P,
-                               const pip_pair_mlp *m, void *U, hipStream_t s) {
-    typedef typename std::conditional<kMode == kMlpBf16, uint16_t, float>::type OutT;
+                               const pip_pair_mlp *m, void *U, hipStream_t s,
+                               const Int8Args &ia = Int8Args{}) {
+    typedef MlpOut<kMode> OutT;
     constexpr int kSeg = 65536;
     for (int b0 = 0; b0 < B; b0 += kSeg) {
         const int nb = std::min(kSeg, B - b0);
@@ -765,7 +767,7 @@ static hipError_t launch_embed(const float *p4, const uint8_t *mask, int B, int 
         hipLaunchKernelGGL(pair_embed_kernel<kMode>, dim3(grid), dim3(kEmbedThreads), 0, s,
                            (const float4 *)p4 + (size_t)b0 * P, mask + (size_t)b0 * P, nb, P,
                            (const float4 *)m->w32, (const v8bf *)m->w16, (const v8h *)m->wx2,
-                           m->bias, (void *)((OutT *)U + (size_t)b0 * kHeads * P * P), wz);
+                           m->bias, (void *)((OutT *)U + (size_t)b0 * kHeads * P * P), wz, ia);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -781,6 +783,20 @@ hipError_t launch_pair_embed_f32(const float *p4, const uint8_t *mask, int B, in
 hipError_t launch_pair_embed_bf16(const float *p4, const uint8_t *mask, int B, int P,
                                   const pip_pair_mlp *m, uint16_t *U, hipStream_t s) {
     return launch_embed<kMlpBf16>(p4, mask, B, P, m, U, s);
+}
+
+hipError_t launch_pair_embed_int8(const float *p4, const uint8_t *mask, int B, int P,
+                                  const pip_pair_mlp *m, const float *act_scale,
+                                  const int *act_zero, uint16_t *U, hipStream_t s) {
+    Int8Args ia;
+    ia.w8 = (const v4i *)m->w8;
+    ia.q8 = m->q8;
+    for (int l = 0; l < 3; ++l) {
+        ia.s[l] = act_scale[l];
+        ia.inv_s[l] = 1.0f / act_scale[l];
+        ia.zp[l] = (float)act_zero[l];
+    }
+    return launch_embed<kMlpInt8>(p4, mask, B, P, m, U, s, ia);
 }
 
 }  // namespace pip

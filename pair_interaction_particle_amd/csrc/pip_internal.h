@@ -23,6 +23,8 @@ struct pip_pair_mlp {
     uint16_t *wx2;
     float *bias;
     float *wplain;  // the folded weights in pip_pair_mlp_fold's plain layout (backward)
+    int8_t *w8;     // int8 operands of layers 2..4 (int8 mode, layout in abi.hip)
+    float *q8;      // their per-channel scales and sums (int8 mode)
 };
 
 namespace pip {
@@ -34,6 +36,10 @@ hipError_t launch_pair_embed_f32(const float *p4, const uint8_t *mask, int B, in
                                  const pip_pair_mlp *m, float *U, hipStream_t s);
 hipError_t launch_pair_embed_bf16(const float *p4, const uint8_t *mask, int B, int P,
                                   const pip_pair_mlp *m, uint16_t *U, hipStream_t s);
+// act_scale / act_zero: quantisation of the inputs of layers 2, 3, 4 (host)
+hipError_t launch_pair_embed_int8(const float *p4, const uint8_t *mask, int B, int P,
+                                  const pip_pair_mlp *m, const float *act_scale,
+                                  const int *act_zero, uint16_t *U, hipStream_t s);
 // workgroups per (jet, head) of the attention kernel
 int attention_chunks(int P);
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V,

@@ -8,6 +8,8 @@
 // read from LDS feeds two MFMAs and the two chains interleave.
 #pragma once
 
+#include <type_traits>
+
 #include "pip_device.h"
 
 namespace pip {
@@ -383,23 +385,141 @@ __device__ __forceinline__ bool all_finite(const v4f &a, const v4f &b) {
 }
 
 
+// ------------------------------------------------------------ int8 chain
+// Inputs of layers 2, 3, 4 quantised to int8 with a per-tensor zero point
+// ("Economical Jet Taggers" summary, Methodologie, "Datatype Kwantisering"):
+// q = clamp(rint(h / S) + Z, -128, 127); per-channel symmetric int8 weights
+// Wq with scale sw; y = S sw (sum Wq q - Z sum Wq) + b' on
+// v_mfma_i32_16x16x64_i8 with exact int32 sums.  Layer 1 and the GELUs are
+// float32.  One K = 64 product per 16 output channels: lane group g's 16
+// bytes hold the inputs 16c + 4g + r (byte 4c + r), which is where the
+// float32 result registers of the previous layer already sit; the host packs
+// the weight operands in the same order.
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr int kW8Ops = 9;              // 4 + 4 output tiles of layers 2, 3 and 1 of layer 4
+constexpr int kQ8Floats = 2 * 144;     // sw (136, padded to 144) | sum Wq (as floats)
+
+__device__ __forceinline__ v4i mfma64i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// 16 activations (h[c][r] = input 16c + 4g + r) -> int8 codes, byte 4c + r
+__device__ __forceinline__ v4i quant16(const v4f (&h)[4], float inv_s, float zp) {
+    v4i out;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float q = fminf(fmaxf(__builtin_rintf(fmaf(h[c][r], inv_s, zp)), -128.0f), 127.0f);
+            w |= ((uint32_t)(int)q & 0xffu) << (8 * r);
+        }
+        out[c] = (int)w;
+    }
+    return out;
+}
+
+// Two pair blocks through the int8 chain.  wl: the float32 layer-1 group;
+// w8: the int8 operands [op][lane]; deq / zs: per-channel S sw and Z sum Wq
+// of layers 2 (0..63), 3 (64..127), 4 (128..143, rows >= 8 zero).
+__device__ __forceinline__ void mlp2_int8(const float4 *__restrict__ wl,
+                                          const v4i *__restrict__ w8,
+                                          const float *__restrict__ deq,
+                                          const float *__restrict__ zs,
+                                          const float *__restrict__ bl, const float (&inv_s)[3],
+                                          const float (&zp)[3], float vA, float vB, v4f &uA,
+                                          v4f &uB) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    v4f hA[4], hB[4];
+    {
+        const float4 w = wl[lane];
+        const float w1[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const v4f b = bias4(bl, 16 * c + 4 * g);
+            hA[c] = mfma4(w1[c], vA, b);
+            hB[c] = mfma4(w1[c], vB, b);
+        }
+    }
+#pragma unroll
+    for (int layer = 0; layer < 3; ++layer) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hA[c][r] = gelu_f32(hA[c][r]);
+                hB[c][r] = gelu_f32(hB[c][r]);
+            }
+        const v4i xA = quant16(hA, inv_s[layer], zp[layer]);
+        const v4i xB = quant16(hB, inv_s[layer], zp[layer]);
+        const int nco = layer < 2 ? 4 : 1;
+#pragma unroll
+        for (int co = 0; co < nco; ++co) {
+            const v4i w = w8[(layer * 4 + co) * 64 + lane];
+            const v4i aA = mfma64i8(w, xA, (v4i){0, 0, 0, 0});
+            const v4i aB = mfma64i8(w, xB, (v4i){0, 0, 0, 0});
+            const int ch = 64 * layer + 16 * co + 4 * g;
+            const v4f d = bias4(deq, ch), z = bias4(zs, ch);
+            v4f b;
+            if (layer < 2) {
+                b = bias4(bl, 64 * (layer + 1) + 16 * co + 4 * g);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) b[r] = (4 * g + r < kHeads) ? bl[192 + 4 * g + r] : 0.0f;
+            }
+            v4f yA, yB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                yA[r] = fmaf(d[r], (float)aA[r] - z[r], b[r]);
+                yB[r] = fmaf(d[r], (float)aB[r] - z[r], b[r]);
+            }
+            if (layer < 2) {
+                hA[co] = yA;
+                hB[co] = yB;
+            } else {
+                uA = yA;
+                uB = yB;
+            }
+        }
+    }
+}
+
+// Everything the int8 mode needs besides the float32 operands: the packed
+// int8 weights, their scales and column sums (device), and the activation
+// quantisation of the inputs of layers 2, 3, 4 (scale S, zero point Z).
+struct Int8Args {
+    const v4i *w8;
+    const float *q8;
+    float s[3], inv_s[3], zp[3];
+};
+
 // ------------------------------------------------------------ mode dispatch
 // kMlpF32: every layer on the float32 MFMA (weights 37 KB in LDS).
 // kMlpF16x2: layer 1 float32, layers 2..4 fp16 x 2 (float32-faithful), with
 //   a per-block-pair fall back to the float32 chain (weights from global
 //   memory) when an activation left the fp16 range.
 // kMlpBf16: layer 1 float32, layers 2..4 bf16 operands, GELU degree 3.
-constexpr int kMlpF32 = 0, kMlpF16x2 = 1, kMlpBf16 = 2;
+// kMlpInt8: layer 1 float32, layers 2..4 int8 inputs and weights (above).
+constexpr int kMlpF32 = 0, kMlpF16x2 = 1, kMlpBf16 = 2, kMlpInt8 = 3;
+
+// U is stored as bfloat16 by the bf16 and int8 modes, as float32 otherwise.
+template <int kMode>
+using MlpOut = typename std::conditional<kMode == kMlpBf16 || kMode == kMlpInt8, uint16_t,
+                                         float>::type;
 
 template <int kMode>
 struct MlpLds {
     static constexpr int kW4 = kMode == kMlpF32 ? kW32Groups * 64 : 64;
     static constexpr int kOps16 = kMode == kMlpF32 ? 1 : kW16Ops * 64;
+    static constexpr bool kI8 = kMode == kMlpInt8;
     float4 *wl;
     v8h *wh;
     v8h *wlo;
     v8bf *wb;
     float *bl;
+    v4i *w8;
+    float *deq, *zs;
+    float inv_s[3], zp[3];  // activation quantisation (int8 mode)
 
     __device__ MlpLds() {
         __shared__ float4 s_wl[kW4];
@@ -407,11 +527,25 @@ struct MlpLds {
         __shared__ v8h s_wlo[kMode == kMlpF16x2 ? kOps16 : 1];
         __shared__ v8bf s_wb[kMode == kMlpBf16 ? kOps16 : 1];
         __shared__ float s_bl[kBiasFloats];
+        __shared__ v4i s_w8[kI8 ? kW8Ops * 64 : 1];
+        __shared__ float s_dz[kI8 ? kQ8Floats : 1];
         wl = s_wl;
         wh = s_wh;
         wlo = s_wlo;
         wb = s_wb;
         bl = s_bl;
+        w8 = s_w8;
+        deq = s_dz;
+        zs = s_dz + kQ8Floats / 2;
+#pragma unroll
+        for (int l = 0; l < 3; ++l) inv_s[l] = zp[l] = 0.f;
+    }
+    __device__ void set_act(const Int8Args &ia) {
+#pragma unroll
+        for (int l = 0; l < 3; ++l) {
+            inv_s[l] = ia.inv_s[l];
+            zp[l] = ia.zp[l];
+        }
     }
 
     // Copy this mode's operands and the biases into LDS (all threads; the
@@ -424,10 +558,14 @@ struct MlpLds {
         LdsCopy<kThreads, kBiasFloats, float> cb;
         LdsCopy<kThreads, kMode == kMlpF16x2 ? kOps16 : 1, v8h> chi, clo;
         LdsCopy<kThreads, kMode == kMlpBf16 ? kOps16 : 1, v8bf> c16;
+        LdsCopy<kThreads, kI8 ? kW8Ops * 64 : 1, v4i> c8;
+        LdsCopy<kThreads, kI8 ? kQ8Floats : 1, float> cq;
+        float qs[3], qz[3];
         __device__ __forceinline__ void load(const float4 *__restrict__ w32,
                                              const v8bf *__restrict__ w16,
                                              const v8h *__restrict__ wx2,
-                                             const float *__restrict__ bias) {
+                                             const float *__restrict__ bias,
+                                             const Int8Args *ia = nullptr) {
             c32.load(w32);
             cb.load(bias);
             if constexpr (kMode == kMlpF16x2) {
@@ -435,6 +573,15 @@ struct MlpLds {
                 clo.load(wx2 + kOps16);
             }
             if constexpr (kMode == kMlpBf16) c16.load(w16);
+            if constexpr (kI8) {
+                c8.load(ia->w8);
+                cq.load(ia->q8);
+#pragma unroll
+                for (int l = 0; l < 3; ++l) {
+                    qs[l] = ia->s[l];
+                    qz[l] = ia->zp[l];
+                }
+            }
         }
         __device__ __forceinline__ void store(const MlpLds &M) const {
             c32.store(M.wl);
@@ -444,13 +591,26 @@ struct MlpLds {
                 clo.store(M.wlo);
             }
             if constexpr (kMode == kMlpBf16) c16.store(M.wb);
+            if constexpr (kI8) {
+                c8.store(M.w8);
+                // deq = S sw and zs = Z sum Wq per output channel (layer by
+                // channel range: 0..63 layer 2, 64..127 layer 3, 128.. layer 4)
+#pragma unroll
+                for (int it = 0; it < decltype(cq)::kIt; ++it) {
+                    const int i = threadIdx.x + it * kThreads;
+                    if (i >= kQ8Floats) continue;
+                    const int ch = i % (kQ8Floats / 2), l = ch < 64 ? 0 : (ch < 128 ? 1 : 2);
+                    M.deq[i] = cq.v[it] * (i < kQ8Floats / 2 ? qs[l] : qz[l]);
+                }
+            }
         }
     };
     template <int kThreads>
     __device__ void stage(const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
-                          const v8h *__restrict__ wx2, const float *__restrict__ bias) {
+                          const v8h *__restrict__ wx2, const float *__restrict__ bias,
+                          const Int8Args *ia = nullptr) {
         Staging<kThreads> st;
-        st.load(w32, w16, wx2, bias);
+        st.load(w32, w16, wx2, bias, ia);
         st.store(*this);
     }
 
@@ -465,8 +625,11 @@ struct MlpLds {
         } else if constexpr (kMode == kMlpF16x2) {
             mlp2_f16x2(wl, wh, wlo, bl, fA, fB, uA, uB);
             return __ballot(!all_finite(uA, uB)) == 0;
-        } else {
+        } else if constexpr (kMode == kMlpBf16) {
             mlp2_bf16(wl, wb, bl, fA, fB, uA, uB);
+            return true;
+        } else {
+            mlp2_int8(wl, w8, deq, zs, bl, inv_s, zp, fA, fB, uA, uB);
             return true;
         }
     }
