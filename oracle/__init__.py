@@ -67,8 +67,13 @@ def lib():
         L.oracle_pair_embed_int8.argtypes = [dp, u8p, i64, i64, C.c_double, C.POINTER(_Mlp), dp,
                                              dp, C.c_double, dp, u8p]
         L.oracle_pair_mlp_ranges.argtypes = [dp, u8p, i64, i64, C.c_double, C.POINTER(_Mlp), dp]
+        L.oracle_geometric_product.argtypes = [dp, dp, i64, dp]
+        L.oracle_blade_grade.argtypes = [C.c_int]
+        L.oracle_blade_grade.restype = C.c_int
+        L.oracle_equilinear.argtypes = [dp, dp, i64, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp,
+                                         dp, dp]
         for f in ("oracle_attention_backward", "oracle_pair_mlp_backward",
-                  "oracle_pair_embed_int8", "oracle_pair_mlp_ranges",
+                  "oracle_pair_embed_int8", "oracle_pair_mlp_ranges", "oracle_equilinear",
                   "oracle_pair_features", "oracle_pair_mlp", "oracle_pair_embed",
                   "oracle_attention", "oracle_pair_embed_attention", "oracle_block_stack"):
             getattr(L, f).restype = C.c_int
@@ -327,3 +332,42 @@ def int8_calibration(ranges) -> tuple:
     S = (r[:, 1] - r[:, 0]) / 255.0
     Z = -128.0 - np.rint(r[:, 0] / S)
     return S, Z
+
+
+# ---------------------------------------------------------------- L-GATr
+def geometric_product(x, y) -> np.ndarray:
+    """z = x y in Cl(1,3) for multivectors (..., 16) in grade order."""
+    a, b = _f64(x), _f64(y)
+    shape = np.broadcast_shapes(a.shape, b.shape)
+    a = np.ascontiguousarray(np.broadcast_to(a, shape)).reshape(-1, 16)
+    b = np.ascontiguousarray(np.broadcast_to(b, shape)).reshape(-1, 16)
+    z = np.zeros_like(a)
+    lib().oracle_geometric_product(_ptr(a), _ptr(b), a.shape[0], _ptr(z))
+    return z.reshape(shape)
+
+
+def blade_grades() -> np.ndarray:
+    return np.array([lib().oracle_blade_grade(i) for i in range(16)])
+
+
+def equilinear(x_mv, x_s, w, s2mv=None, mv2s=None, ss=None, b_mv=None, b_s=None):
+    """(y_mv, y_s) of the equivariant linear layer: x_mv (n, in_mv, 16),
+    x_s (n, in_s), w (out_mv, in_mv, 10), s2mv (out_mv, in_s), mv2s
+    (out_s, in_mv), ss (out_s, in_s), b_mv (out_mv), b_s (out_s)."""
+    xm = _f64(x_mv)
+    n, in_mv, _ = xm.shape
+    xs = _f64(x_s) if x_s is not None else np.zeros((n, 0))
+    in_s = xs.shape[1]
+    wm = _f64(w)
+    out_mv = wm.shape[0]
+    out_s = 0
+    for a, ax in ((mv2s, 0), (ss, 0), (b_s, 0)):
+        if a is not None:
+            out_s = np.asarray(a).shape[ax]
+    arrs = [None if a is None else _f64(a) for a in (s2mv, mv2s, ss, b_mv, b_s)]
+    y_mv = np.zeros((n, out_mv, 16))
+    y_s = np.zeros((n, out_s))
+    rc = lib().oracle_equilinear(_ptr(xm), _ptr(xs), n, in_mv, in_s, out_mv, out_s, _ptr(wm),
+                                 *[_ptr(a) for a in arrs], _ptr(y_mv), _ptr(y_s))
+    assert rc == 0
+    return y_mv, y_s

@@ -21,6 +21,10 @@
  *      - "Fusion 3": attention is softmax(Q K^T / sqrt(d) + bias) V.
  *      - "Architecture Comparison": ParT uses 8 heads and PairEmbed
  *        4->64->64->64->8, i.e. one bias plane per head.
+ *      - "Fusion 1" and "Results" table "L-GATr Kernels": the L-GATr
+ *        equivariant linear layer on [multivectors, scalars] (its weights
+ *        span the 10 Lorentz-equivariant maps of a 16-component multivector)
+ *        and the geometric product of two multivector tensors.
  *  [S] gist.science summary of "Virtues and Vices of Equivariant
  *      Transformers", "Methodologie": ParT pair features are invariant under
  *      SO(2) x SO+(1,1) (azimuthal rotation x longitudinal boost).
@@ -39,6 +43,12 @@
  *    after the last linear.  GELU is the exact erf form.
  *  - output channel h of the MLP is the bias of head h.
  *  - a padded query row gives O = 0; padded keys get weight exactly 0.
+ *  - L-GATr: the spacetime algebra Cl(1,3), metric (+,-,-,-), blades of
+ *    sorted generator indices in grade order; the 10 equivariant maps are the
+ *    5 grade projections and the pseudoscalar (left) times each of them;
+ *    scalar channels enter only the scalar component of the multivector
+ *    outputs, and the scalar outputs read only the scalar component of the
+ *    multivector inputs.
  *
  * Parity pins live in tests/test_oracle_*.py; parity is pinned for every
  * function here (closed forms, symmetries, brute force, library routines).
@@ -703,5 +713,116 @@ int oracle_pair_mlp_ranges(const double *p4, const uint8_t *mask, int64_t B, int
                     in = h;
                 }
             }
+    return 0;
+}
+
+/* ------------------------------------------------------------ L-GATr */
+/* The spacetime algebra Cl(1,3) of L-GATr ([R] "How the Kernel Fusion Works",
+ * Fusion 1; "Results", table "L-GATr Kernels"): metric diag(+1, -1, -1, -1)
+ * on e0..e3, 16 basis blades in grade order
+ *   1, e0, e1, e2, e3, e01, e02, e03, e12, e13, e23, e012, e013, e023, e123, e0123.
+ * A blade is a set of generators (bit g = e_g); the product of two blades is
+ * the symmetric difference, with sign (-1)^(number of generator pairs that
+ * must be swapped to sort) times the metric of every repeated generator. */
+static const int BLADE_BITS[16] = {0, 1, 2, 4, 8, 3, 5, 9, 6, 10, 12, 7, 11, 13, 14, 15};
+
+static int blade_index(int bits) {
+    for (int i = 0; i < 16; ++i)
+        if (BLADE_BITS[i] == bits) return i;
+    return -1;
+}
+
+static int popcount4(int x) { return (x & 1) + ((x >> 1) & 1) + ((x >> 2) & 1) + ((x >> 3) & 1); }
+
+/* e_A e_B = sign * e_{A xor B} for blade index a, b */
+static int blade_product(int a, int b, int *sign) {
+    const int A = BLADE_BITS[a], B = BLADE_BITS[b];
+    int swaps = 0;
+    for (int i = 0; i < 4; ++i)        /* generator i of A ... */
+        if (A >> i & 1)
+            for (int j = 0; j < i; ++j) /* ... passes every smaller generator j of B */
+                if (B >> j & 1) ++swaps;
+    int s = (swaps & 1) ? -1 : 1;
+    const int common = A & B;
+    for (int g = 1; g < 4; ++g)
+        if (common >> g & 1) s = -s; /* e1^2 = e2^2 = e3^2 = -1; e0^2 = +1 */
+    *sign = s;
+    return blade_index(A ^ B);
+}
+
+int oracle_blade_grade(int i) { return popcount4(BLADE_BITS[i]); }
+
+/* z = x y for n multivectors (n, 16) */
+void oracle_geometric_product(const double *x, const double *y, int64_t n, double *z) {
+    for (int64_t m = 0; m < n; ++m) {
+        const double *a = x + 16 * m, *b = y + 16 * m;
+        double *c = z + 16 * m;
+        for (int k = 0; k < 16; ++k) c[k] = 0.0;
+        for (int i = 0; i < 16; ++i)
+            for (int j = 0; j < 16; ++j) {
+                int s;
+                const int k = blade_product(i, j, &s);
+                c[k] += s * a[i] * b[j];
+            }
+    }
+}
+
+/* The Lorentz-equivariant linear maps of one multivector, basis map q:
+ * q = 0..4: the grade-q part of x; q = 5..9: e0123 times the grade-(q-5)
+ * part (left multiplication by the pseudoscalar, which every proper
+ * orthochronous Lorentz transformation leaves invariant). */
+static void equi_basis(const double *x, int q, double *y) {
+    double part[16];
+    const int grade = q < 5 ? q : q - 5;
+    for (int i = 0; i < 16; ++i) part[i] = popcount4(BLADE_BITS[i]) == grade ? x[i] : 0.0;
+    if (q < 5) {
+        for (int i = 0; i < 16; ++i) y[i] = part[i];
+        return;
+    }
+    double ps[16] = {0};
+    ps[15] = 1.0;
+    oracle_geometric_product(ps, part, 1, y);
+}
+
+/* EquiLinear on n items (the structure of L-GATr's equivariant linear layer):
+ *   y_mv[o] = sum_i sum_q w[o][i][q] basis_q(x_mv[i])
+ *             + (sum_j s2mv[o][j] x_s[j] + b_mv[o]) e_scalar
+ *   y_s[o]  = sum_j ss[o][j] x_s[j] + sum_i mv2s[o][i] x_mv[i][scalar] + b_s[o]
+ * x_mv (n, in_mv, 16), x_s (n, in_s), w (out_mv, in_mv, 10), s2mv (out_mv,
+ * in_s), mv2s (out_s, in_mv), ss (out_s, in_s); NULL matrices and biases are
+ * zero.  y_mv (n, out_mv, 16), y_s (n, out_s). */
+int oracle_equilinear(const double *x_mv, const double *x_s, int64_t n, int64_t in_mv,
+                      int64_t in_s, int64_t out_mv, int64_t out_s, const double *w,
+                      const double *s2mv, const double *mv2s, const double *ss,
+                      const double *b_mv, const double *b_s, double *y_mv, double *y_s) {
+    if (!x_mv || !w || !y_mv || n < 0 || in_mv < 0 || out_mv < 0 || in_s < 0 || out_s < 0)
+        return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < n; ++m) {
+        double t[16];
+        for (int64_t o = 0; o < out_mv; ++o) {
+            double *y = y_mv + (m * out_mv + o) * 16;
+            for (int k = 0; k < 16; ++k) y[k] = 0.0;
+            for (int64_t i = 0; i < in_mv; ++i)
+                for (int q = 0; q < 10; ++q) {
+                    const double wq = w[(o * in_mv + i) * 10 + q];
+                    equi_basis(x_mv + (m * in_mv + i) * 16, q, t);
+                    for (int k = 0; k < 16; ++k) y[k] += wq * t[k];
+                }
+            double sc = b_mv ? b_mv[o] : 0.0;
+            if (s2mv)
+                for (int64_t j = 0; j < in_s; ++j) sc += s2mv[o * in_s + j] * x_s[m * in_s + j];
+            y[0] += sc;
+        }
+        for (int64_t o = 0; o < out_s; ++o) {
+            double v = b_s ? b_s[o] : 0.0;
+            if (ss)
+                for (int64_t j = 0; j < in_s; ++j) v += ss[o * in_s + j] * x_s[m * in_s + j];
+            if (mv2s)
+                for (int64_t i = 0; i < in_mv; ++i)
+                    v += mv2s[o * in_mv + i] * x_mv[(m * in_mv + i) * 16];
+            y_s[m * out_s + o] = v;
+        }
+    }
     return 0;
 }
