@@ -78,7 +78,14 @@ KERNELS = {
     "attention_packed_f32": ("attention_packed_f32_kernel_B128_n20-128.md",
                              ["attention.hip", "pip_attn_core.h", "pip_attn.h",
                               "pip_device.h"]),
+    "equilinear_f32": ("lgatr_equilinear_f32_B128_items128_mv8_s16.md",
+                       ["lgatr.hip", "pip_device.h"]),
+    "geometric_product_f32": ("lgatr_geometric_product_f32_B128_items128_mv8.md",
+                              ["lgatr.hip", "pip_device.h"]),
 }
+# L-GATr kernel shape ("Results", table "L-GATr Kernels"): B=128 jets x 128
+# items, 8 multivector channels (16 components) and 16 scalar channels
+LGATR_B, LGATR_ITEMS, LGATR_MV, LGATR_S = 128, 128, 8, 16
 
 
 def source_hash(files):
@@ -245,6 +252,8 @@ def setup(pip, synth, name):
     """Device inputs of a workload and its kernels as callables, in step order."""
     import numpy as np
     import torch
+    if name == "lgatr":
+        return setup_lgatr(pip, synth)
     d = synth.make_workload("kernel" if name in ("packed", "backward", "int8") else name)
     B, P = d["mask"].shape
     mask = to_dev(d["mask"])
@@ -317,8 +326,41 @@ def setup(pip, synth, name):
     return k
 
 
+def setup_lgatr(pip, synth):
+    """The L-GATr kernels at their table shape: the equivariant linear layer
+    (8 -> 8 multivector, 16 -> 16 scalar channels) on B x items tokens and
+    the geometric product of two (B, items, 8) multivector tensors."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(2024)
+    n = LGATR_B * LGATR_ITEMS
+    p = synth.equilinear_params(LGATR_MV, LGATR_MV, LGATR_S, LGATR_S, rng)
+    x_mv = synth.multivectors((n, LGATR_MV), rng)
+    x_s = rng.normal(size=(n, LGATR_S)).astype(np.float32)
+    y = synth.multivectors((n, LGATR_MV), rng)
+    layer = pip.EquiLinear(in_s=LGATR_S, out_s=LGATR_S, **p)
+    gx, gs, gy = to_dev(x_mv), to_dev(x_s), to_dev(y)
+    o_mv = torch.empty_like(gx)
+    o_s = torch.empty_like(gs)
+    z = torch.empty_like(gx)
+    d = {"lgatr": True, "n": n, "params": p, "x_mv": x_mv, "x_s": x_s, "y": y}
+    return {"d": d, "layer": layer,
+            "fns": [("equilinear_f32", lambda: layer(gx, gs, y_mv=o_mv, y_s=o_s)),
+                    ("geometric_product_f32", lambda: pip.geometric_product(gx, gy, out=z))]}
+
+
 def work_of(kernel, d):
     """(roofline kind, algorithmic work per launch, peak) of one kernel."""
+    if kernel == "equilinear_f32":
+        # x_mv, x_s read and y_mv, y_s written once; W_eff's nonzero blocks
+        # (8 blocks of 16 x 16, plus the scalar rows and columns) read once
+        n = d["n"]
+        io = n * 2 * (LGATR_MV * 16 + LGATR_S) * 4
+        w = (8 * (2 * LGATR_MV) ** 2 + 2 * LGATR_MV * LGATR_S + LGATR_S * (2 * LGATR_MV + LGATR_S)
+             + LGATR_MV + LGATR_S) * 4
+        return "hbm", io + w, PEAK_HBM_GBS
+    if kernel == "geometric_product_f32":
+        return "hbm", d["n"] * LGATR_MV * 3 * 16 * 4, PEAK_HBM_GBS
     mask = d["mask"]
     B, P = mask.shape
     uniq, ordered, n = pair_counts(mask)
@@ -433,6 +475,19 @@ def cpu_sample(name, d, jets):
         U = oracle.pair_embed(d["p4"][s], d["mask"][s], d["mlp"])
         oracle.attention(d["q"][s], d["k"][s], d["v"][s], U, d["mask"][s])
         what = "pair embed + attention (bf16-rounded inputs, float64 arithmetic)"
+    elif name == "lgatr":
+        p = d["params"]
+        items = jets * LGATR_ITEMS
+        t = time.perf_counter()
+        oracle.equilinear(d["x_mv"][:items], d["x_s"][:items], **p)
+        oracle.geometric_product(d["x_mv"][:items], d["y"][:items])
+        dt = time.perf_counter() - t
+        return {"value": items / dt, "unit": "items/s (equilinear + geometric product)",
+                "us_per_workload_call": dt * 1e6 * LGATR_B / jets,
+                "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
+                "sample": "first %d of %d jets (%d items): float64 equivariant linear layer "
+                          "8->8 mv, 16->16 s, then the geometric product of 8 channel pairs, "
+                          "%.2f s wall" % (jets, LGATR_B, items, dt)}
     else:
         U = oracle.pair_embed(d["p4"][s], d["mask"][s], d["mlp"]).astype("float32")
         oracle.block_stack(d["x0"][s], d["wq"], d["wk"], d["wv"], d["wo"], U, d["mask"][s])
@@ -454,8 +509,10 @@ SHAPES = {
     "large_bf16": "B=64 P=256 n~U{60..256} H=8 D=16 bf16",
     "fused512": "B=512 P=128 n~U{20..128} H=8 D=16 fp32, 5% massive",
     "stack8": "B=128 P=128 C=128 H=8 D=16 L=8 fp32",
+    "lgatr": "L-GATr kernels: B=128 x items=128, equivariant linear 8->8 multivectors + "
+             "16->16 scalars, geometric product of (128, 128, 8) multivector pairs, fp32",
 }
-CPU_JETS = {"large_bf16": 16, "fused512": 128, "stack8": 32}
+CPU_JETS = {"large_bf16": 16, "fused512": 128, "stack8": 32, "lgatr": 32}
 
 
 def main():
@@ -549,7 +606,7 @@ def main():
     }
     if not args.no_extra:
         res["workloads"] = {}
-        for name in ("packed", "int8", "backward", "fused512", "large_bf16", "stack8"):
+        for name in ("packed", "int8", "backward", "lgatr", "fused512", "large_bf16", "stack8"):
             kw = setup(pip, synth, name)
             shape = SHAPES[name] % int(kw["d"]["n"].sum()) if name == "packed" else SHAPES[name]
             res["workloads"][name] = {"shape": shape,

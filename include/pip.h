@@ -58,6 +58,9 @@ extern "C" {
 /* gradient arrays of the pair MLP (pip_pair_mlp_backward, pip_pair_mlp_unfold_grads) */
 #define PIP_PAIR_MLP_FOLDED_GRADS 9160
 #define PIP_PAIR_MLP_RAW_GRADS 9552
+/* L-GATr: components of one multivector; largest scalar channel count */
+#define PIP_LGATR_MV 16
+#define PIP_LGATR_MAX_S 256
 
 typedef enum {
     PIP_OK = 0,
@@ -347,6 +350,64 @@ pip_status pip_block_stack_noalloc(float *X, const float *Wq, const float *Wk, c
                                    const float *Wo, const float *U, const uint8_t *mask,
                                    int64_t B, int64_t P, int64_t C, int64_t H, int64_t L,
                                    void *stream);
+
+/* ---- L-GATr: spacetime-algebra multivectors ----------------------------
+ * Source: README "How the Kernel Fusion Works", "Fusion 1" (the equivariant
+ * linear layer of L-GATr: its weights span the 10 linear maps of a
+ * multivector that commute with Lorentz transformations; the fused form
+ * expands them once into W_eff over the concatenated [multivector
+ * components, scalars] and applies one contraction) and "Results", table
+ * "L-GATr Kernels" (the equivariant linear layer and the geometric product
+ * at B=128, items=128, 8 multivector and 16 scalar channels).
+ * A multivector of Cl(1,3) (generators e0..e3, e0^2 = +1, e1^2 = e2^2 =
+ * e3^2 = -1) is PIP_LGATR_MV = 16 float32 components in blade order
+ *   1, e0, e1, e2, e3, e01, e02, e03, e12, e13, e23, e012, e013, e023, e123, e0123
+ * (generator indices ascending within a blade). */
+
+/* z = x y, the geometric product of n multivector pairs; x, y, z are
+ * (n, 16) float32 device arrays.  z may be x or y (each thread reads its
+ * pair before it writes).  n == 0 is a no-op.
+ * Errors: NULL, SHAPE (n < 0), ALIGN, UNSUPPORTED (n > 2^40), HIP. */
+pip_status pip_lgatr_geometric_product(const float *x, const float *y, int64_t n, float *z,
+                                       void *stream);
+
+/* Host only: the expanded weight W_eff of the equivariant linear layer,
+ * rows out_mv*16 + out_s, columns in_mv*16 + in_s (row-major float32, caller's
+ * HOST buffer), row/column (c*16 + k) = channel c component k, then the
+ * scalar channels.  Basis weights w (out_mv, in_mv, 10): w[o][i][q] for
+ * q = 0..4 multiplies the grade-q part of input channel i, q = 5..9 the
+ * pseudoscalar e0123 times its grade-(q-5) part (left product).  s2mv
+ * (out_mv, in_s) feeds the scalars into the scalar component of the
+ * multivector outputs, mv2s (out_s, in_mv) the scalar component of the
+ * multivector inputs into the scalar outputs, ss (out_s, in_s) scalars to
+ * scalars; a NULL matrix is zero.  Any sizes >= 0.
+ * Errors: NULL (w_eff, or w with in_mv, out_mv > 0), SHAPE. */
+pip_status pip_lgatr_equilinear_expand(const float *w, const float *s2mv, const float *mv2s,
+                                       const float *ss, int in_mv, int out_mv, int in_s,
+                                       int out_s, float *w_eff);
+
+/* Device-resident equivariant linear layer: W_eff (pip_lgatr_equilinear_expand)
+ * and the biases b_mv (out_mv; added to the scalar component of each
+ * multivector output) and b_s (out_s), packed once as the layer's MFMA
+ * operands on the current device.  Arguments are HOST arrays (NULL = zero,
+ * except w).  Requires in_mv, out_mv in {8, 16}; in_s, out_s multiples of
+ * 16 in [0, PIP_LGATR_MAX_S].  Errors: NULL, SHAPE, UNSUPPORTED, HIP. */
+typedef struct pip_equilinear pip_equilinear;
+pip_status pip_lgatr_equilinear_create(const float *w, const float *s2mv, const float *mv2s,
+                                       const float *ss, const float *b_mv, const float *b_s,
+                                       int in_mv, int out_mv, int in_s, int out_s,
+                                       pip_equilinear **out);
+pip_status pip_lgatr_equilinear_destroy(pip_equilinear *layer);
+
+/* y = the equivariant linear layer on n items: x_mv (n, in_mv, 16), x_s
+ * (n, in_s) -> y_mv (n, out_mv, 16), y_s (n, out_s), float32 device arrays
+ * (x_s / y_s unused and may be NULL when in_s / out_s is 0).  Equal to
+ * [y_mv_flat, y_s] = W_eff [x_mv_flat, x_s] + bias, computed in float32 on
+ * the matrix cores.  Outputs must not overlap inputs.  The current device
+ * must be the layer's.  n == 0 is a no-op.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (other device, n > 2^36), HIP. */
+pip_status pip_lgatr_equilinear(const pip_equilinear *layer, const float *x_mv, const float *x_s,
+                                int64_t n, float *y_mv, float *y_s, void *stream);
 
 #ifdef __cplusplus
 }

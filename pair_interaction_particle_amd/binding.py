@@ -94,7 +94,16 @@ def lib():
                                       C.c_size_t, vp]
         L.pip_block_stack_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                               i64, vp]
-        for f in ("pip_pair_mlp_fold", "pip_pair_mlp_create", "pip_pair_mlp_destroy",
+        L.pip_lgatr_geometric_product.argtypes = [vp, vp, i64, vp, vp]
+        L.pip_lgatr_equilinear_expand.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+        L.pip_lgatr_equilinear_create.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                                  C.POINTER(vp)]
+        L.pip_lgatr_equilinear_destroy.argtypes = [vp]
+        L.pip_lgatr_equilinear.argtypes = [vp, vp, vp, i64, vp, vp, vp]
+        for f in ("pip_lgatr_geometric_product", "pip_lgatr_equilinear_expand",
+                  "pip_lgatr_equilinear_create", "pip_lgatr_equilinear_destroy",
+                  "pip_lgatr_equilinear",
+                  "pip_pair_mlp_fold", "pip_pair_mlp_create", "pip_pair_mlp_destroy",
                   "pip_pair_features", "pip_pair_embed", "pip_pair_bias_attention",
                   "pip_pair_embed_attention", "pip_block_stack", "pip_block_stack_noalloc",
                   "pip_packed_u_offsets", "pip_pair_embed_packed",
@@ -455,4 +464,97 @@ def pair_embed_int8(p4, mask, mlp: PairMLP, act_scale, act_zero, out=None):
                                    s.ctypes.data, z.ctypes.data,
                                    _dev(out, "U", torch.bfloat16, (B, 8, P, P)), _stream())
     _check("pip_pair_embed_int8", st)
+    return out
+
+
+# ---------------------------------------------------------------- L-GATr
+LGATR_MV = 16
+
+
+def _host_f32(a, shape=None, name="array"):
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), arr.shape))
+    return arr
+
+
+def _equi_weights(w, s2mv, mv2s, ss, in_s, out_s):
+    w = _host_f32(w)
+    if w is None or w.ndim != 3 or w.shape[2] != 10:
+        raise ValueError("w must have shape (out_mv, in_mv, 10)")
+    out_mv, in_mv = w.shape[:2]
+    return (w, _host_f32(s2mv, (out_mv, in_s), "s2mv"), _host_f32(mv2s, (out_s, in_mv), "mv2s"),
+            _host_f32(ss, (out_s, in_s), "ss"), in_mv, out_mv)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def equilinear_expand(w, s2mv=None, mv2s=None, ss=None, in_s=0, out_s=0):
+    """W_eff (out_mv*16 + out_s, in_mv*16 + in_s) float32 of the equivariant
+    linear layer (host only; pip_lgatr_equilinear_expand)."""
+    w, s2mv, mv2s, ss, in_mv, out_mv = _equi_weights(w, s2mv, mv2s, ss, in_s, out_s)
+    out = np.zeros((out_mv * 16 + out_s, in_mv * 16 + in_s), np.float32)
+    _check("pip_lgatr_equilinear_expand",
+           lib().pip_lgatr_equilinear_expand(_p(w), _p(s2mv), _p(mv2s), _p(ss), in_mv, out_mv,
+                                             in_s, out_s, out.ctypes.data))
+    return out
+
+
+class EquiLinear:
+    """L-GATr equivariant linear layer, W_eff packed on the current GPU."""
+
+    def __init__(self, w, s2mv=None, mv2s=None, ss=None, b_mv=None, b_s=None, in_s=0, out_s=0):
+        w, s2mv, mv2s, ss, in_mv, out_mv = _equi_weights(w, s2mv, mv2s, ss, in_s, out_s)
+        self._keep = (w, s2mv, mv2s, ss, _host_f32(b_mv, (out_mv,), "b_mv"),
+                      _host_f32(b_s, (out_s,), "b_s"))
+        self.in_mv, self.out_mv, self.in_s, self.out_s = in_mv, out_mv, in_s, out_s
+        h = C.c_void_p()
+        _check("pip_lgatr_equilinear_create",
+               lib().pip_lgatr_equilinear_create(*[_p(a) for a in self._keep], in_mv, out_mv,
+                                                 in_s, out_s, C.byref(h)))
+        self._h = h
+
+    def __call__(self, x_mv, x_s=None, y_mv=None, y_s=None):
+        torch = _torch()
+        n = x_mv.shape[0]
+        px = _dev(x_mv, "x_mv", torch.float32, (n, self.in_mv, 16))
+        ps = _dev(x_s, "x_s", torch.float32, (n, self.in_s)) if self.in_s else None
+        if y_mv is None:
+            y_mv = torch.empty((n, self.out_mv, 16), device=x_mv.device, dtype=torch.float32)
+        if y_s is None and self.out_s:
+            y_s = torch.empty((n, self.out_s), device=x_mv.device, dtype=torch.float32)
+        py = _dev(y_mv, "y_mv", torch.float32, (n, self.out_mv, 16))
+        pys = _dev(y_s, "y_s", torch.float32, (n, self.out_s)) if self.out_s else None
+        _check("pip_lgatr_equilinear",
+               lib().pip_lgatr_equilinear(self._h, px, ps, n, py, pys, _stream()))
+        return y_mv, y_s
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            _check("pip_lgatr_equilinear_destroy", lib().pip_lgatr_equilinear_destroy(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def geometric_product(x, y, out=None):
+    """z = x y (Cl(1,3) geometric product) of float32 multivectors (..., 16)."""
+    torch = _torch()
+    if x.shape != y.shape or x.shape[-1] != 16:
+        raise ValueError("x and y must have the same shape (..., 16)")
+    px = _dev(x, "x", torch.float32)
+    py = _dev(y, "y", torch.float32)
+    if out is None:
+        out = torch.empty_like(x)
+    pz = _dev(out, "out", torch.float32, x.shape)
+    _check("pip_lgatr_geometric_product",
+           lib().pip_lgatr_geometric_product(px, py, x.numel() // 16, pz, _stream()))
     return out

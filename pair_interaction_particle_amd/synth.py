@@ -266,3 +266,24 @@ def pack_heads(x, mask) -> np.ndarray:
     x = np.asarray(x)
     m = np.asarray(mask) != 0
     return np.ascontiguousarray(np.stack([x[:, h][m] for h in range(x.shape[1])]))
+
+
+# ---------------------------------------------------------------- L-GATr
+def multivectors(shape, rng, scale=1.0) -> np.ndarray:
+    """float32 multivectors (*shape, 16), every component N(0, scale^2)
+    (hidden-layer activations: all grades populated)."""
+    return (rng.normal(0.0, scale, size=tuple(shape) + (16,))).astype(np.float32)
+
+
+def equilinear_params(in_mv, out_mv, in_s, out_s, rng, biases=True) -> dict:
+    """Random float32 weights of an equivariant linear layer, each block
+    N(0, 1/fan_in) (fan_in = in_mv + in_s), as keyword arguments of the
+    layer's constructors."""
+    sd = 1.0 / np.sqrt(max(in_mv + in_s, 1))
+    f = lambda *s: rng.normal(0.0, sd, size=s).astype(np.float32)  # noqa: E731
+    p = dict(w=f(out_mv, in_mv, 10), s2mv=f(out_mv, in_s), mv2s=f(out_s, in_mv),
+             ss=f(out_s, in_s))
+    if biases:
+        p["b_mv"] = rng.normal(0.0, 0.1, size=out_mv).astype(np.float32)
+        p["b_s"] = rng.normal(0.0, 0.1, size=out_s).astype(np.float32)
+    return p
