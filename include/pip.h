@@ -367,7 +367,7 @@ pip_status pip_block_stack_noalloc(float *X, const float *Wq, const float *Wk, c
 /* z = x y, the geometric product of n multivector pairs; x, y, z are
  * (n, 16) float32 device arrays.  z may be x or y (each thread reads its
  * pair before it writes).  n == 0 is a no-op.
- * Errors: NULL, SHAPE (n < 0), ALIGN, UNSUPPORTED (n > 2^40), HIP. */
+ * Errors: NULL, SHAPE (n < 0), ALIGN, UNSUPPORTED (n > 2^38), HIP. */
 pip_status pip_lgatr_geometric_product(const float *x, const float *y, int64_t n, float *z,
                                        void *stream);
 
@@ -405,7 +405,7 @@ pip_status pip_lgatr_equilinear_destroy(pip_equilinear *layer);
  * [y_mv_flat, y_s] = W_eff [x_mv_flat, x_s] + bias, computed in float32 on
  * the matrix cores.  Outputs must not overlap inputs.  The current device
  * must be the layer's.  n == 0 is a no-op.
- * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (other device, n > 2^36), HIP. */
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED (other device, n > 2^34), HIP. */
 pip_status pip_lgatr_equilinear(const pip_equilinear *layer, const float *x_mv, const float *x_s,
                                 int64_t n, float *y_mv, float *y_s, void *stream);
 

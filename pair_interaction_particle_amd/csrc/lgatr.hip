@@ -25,6 +25,7 @@
 // so no LDS is used and nothing is read twice.
 #include <string.h>
 
+#include <type_traits>
 #include <vector>
 
 #include "pip_device.h"
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void geometric_product_kernel(const float4 *__
 
 // ---- equivariant linear layer ------------------------------------------------
 // Operand order (host packing and kernel agree).  Lane l, column m = l % 16,
-// k-group kq = l / 16; a 16-item tile per wave.
+// k-group kq = l / 16; a 16-item tile per workgroup.
 //  * multivector features of pair block p (components c = p, d = 15 - p):
 //    k-step s in [0, in_mv/2): h = s / (in_mv/4), g = s % (in_mv/4); lane
 //    group kq supplies channel i = (in_mv/4) kq + g, component (h ? d : c).
@@ -125,29 +126,37 @@ struct EquiShape {
     int bias_groups() const { return ti() + ts(); }
 };
 
+// One workgroup of 4 waves per 16-item tile (the MFMA column count): the
+// tile is read with coalesced 16-byte loads into LDS (rows padded by 4
+// floats), the 8 pair blocks and the scalar rows are split over the 4 waves
+// (about 12 MFMAs each at 8 -> 8 channels, so a wave's dependent chain is a
+// quarter of the whole), the multivector outputs meet in a second LDS tile
+// and leave with coalesced stores.
 template <int IM, int OM>
 __global__ __launch_bounds__(256) void equilinear_kernel(
     const float4 *__restrict__ xmv, const float4 *__restrict__ xs, int64_t n, int IS, int OS,
     const float4 *__restrict__ wpk, const float4 *__restrict__ bias, float4 *__restrict__ ymv,
     float4 *__restrict__ ys) {
-    constexpr int CI = IM / 4, CO = OM / 4, TI = OM / 8, QI = IM / 8;
-    const int lane = threadIdx.x & 63, m = lane & 15, kq = lane >> 4;
-    const int64_t item = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 + m;
+    constexpr int CI = IM / 4, TI = OM / 8, QI = IM / 8;
+    constexpr int XROW = IM * 16 + 4, YROW = OM * 16 + 4;
+    __shared__ float4 xt4[16 * XROW / 4], yt4[16 * YROW / 4];
+    float *xt = (float *)xt4, *yt = (float *)yt4;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, m = lane & 15, kq = lane >> 4;
+    const int64_t item0 = (int64_t)blockIdx.x * 16, item = item0 + m;
     const bool live = item < n;
     const int US = IS >> 4, TS = OS >> 4;
     constexpr int nA = 8 * TI * QI;
     const int nB = TI * US;
 
-    float xr[CI][16];
 #pragma unroll
-    for (int g = 0; g < CI; ++g)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 v = live ? xmv[(item * IM + CI * kq + g) * 4 + q]
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-            xr[g][4 * q] = v.x, xr[g][4 * q + 1] = v.y, xr[g][4 * q + 2] = v.z,
-                      xr[g][4 * q + 3] = v.w;
-        }
+    for (int j = 0; j < IM / 4; ++j) {
+        const int e = threadIdx.x + 256 * j, it = e / (4 * IM), c4 = e % (4 * IM);
+        const float4 v = item0 + it < n ? xmv[(item0 + it) * (4 * IM) + c4]
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        *(float4 *)(xt + it * XROW + 4 * c4) = v;
+    }
+    __syncthreads();
+
     auto xs_chunk = [&](int u) -> float4 {
         return live ? xs[(item * IS + 16 * u + 4 * kq) >> 2] : make_float4(0.f, 0.f, 0.f, 0.f);
     };
@@ -157,21 +166,27 @@ __global__ __launch_bounds__(256) void equilinear_kernel(
         acc = pip::mfma4(w.z, b2, acc);
         return pip::mfma4(w.w, b3, acc);
     };
-    // the multivector features of pair block (c, d), steps 4q .. 4q+3
-    auto mv_steps = [&](v4f acc, const float4 w, int q, int c, int d) {
+    // this lane's inputs of pair block (c, d): channel CI kq + g, component c / d
+    auto inputs = [&](float (&xb)[CI][2], int c, int d) {
+#pragma unroll
+        for (int g = 0; g < CI; ++g) {
+            xb[g][0] = xt[m * XROW + (CI * kq + g) * 16 + c];
+            xb[g][1] = xt[m * XROW + (CI * kq + g) * 16 + d];
+        }
+    };
+    auto mv_steps = [&](v4f acc, const float4 w, int q, const float (&xb)[CI][2]) {
         float b[4];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-            const int s = 4 * q + s4, h = s / CI, g = s % CI;
-            b[s4] = xr[g][h ? d : c];
+            const int s = 4 * q + s4;
+            b[s4] = xb[s % CI][s / CI];
         }
         return step4(acc, w, b[0], b[1], b[2], b[3]);
     };
-
-    float yr[CO][16];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int c = p, d = 15 - p;
+    auto block = [&](auto P_) {
+        constexpr int p = decltype(P_)::value, c = p, d = 15 - p;
+        float xb[CI][2];
+        inputs(xb, c, d);
 #pragma unroll
         for (int t = 0; t < TI; ++t) {
             v4f acc = {0.f, 0.f, 0.f, 0.f};
@@ -181,38 +196,55 @@ __global__ __launch_bounds__(256) void equilinear_kernel(
             }
 #pragma unroll
             for (int q = 0; q < QI; ++q)
-                acc = mv_steps(acc, wpk[((p * TI + t) * QI + q) * 64 + lane], q, c, d);
+                acc = mv_steps(acc, wpk[((p * TI + t) * QI + q) * 64 + lane], q, xb);
             if (p == 0)
                 for (int u = 0; u < US; ++u) {
                     const float4 sv = xs_chunk(u);
                     acc = step4(acc, wpk[(nA + t * US + u) * 64 + lane], sv.x, sv.y, sv.z, sv.w);
                 }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) yr[2 * t + (r & 1)][(r >> 1) ? d : c] = acc[r];
+            for (int r = 0; r < 4; ++r)
+                yt[m * YROW + (2 * (4 * t + kq) + (r & 1)) * 16 + ((r >> 1) ? d : c)] = acc[r];
         }
+    };
+    auto scalar_rows = [&]() {
+        float xb[CI][2];
+        inputs(xb, 0, 15);
+        for (int t = 0; t < TS; ++t) {
+            const float4 bv = bias[(TI + t) * 64 + lane];
+            v4f acc = {bv.x, bv.y, bv.z, bv.w};
+            const int g0 = nA + nB + t * (QI + US);
+#pragma unroll
+            for (int q = 0; q < QI; ++q) acc = mv_steps(acc, wpk[(g0 + q) * 64 + lane], q, xb);
+            for (int u = 0; u < US; ++u) {
+                const float4 sv = xs_chunk(u);
+                acc = step4(acc, wpk[(g0 + QI + u) * 64 + lane], sv.x, sv.y, sv.z, sv.w);
+            }
+            if (live)
+                ys[(item * OS + 16 * t + 4 * kq) >> 2] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+    };
+    using I = int;
+    if (wv == 0) {
+        block(std::integral_constant<I, 0>{});
+        block(std::integral_constant<I, 4>{});
+    } else if (wv == 1) {
+        block(std::integral_constant<I, 1>{});
+        block(std::integral_constant<I, 5>{});
+        block(std::integral_constant<I, 7>{});
+    } else if (wv == 2) {
+        block(std::integral_constant<I, 2>{});
+        block(std::integral_constant<I, 6>{});
+    } else {
+        block(std::integral_constant<I, 3>{});
+        scalar_rows();
     }
-    if (live)
+    __syncthreads();
 #pragma unroll
-        for (int lo = 0; lo < CO; ++lo) {
-            const int o = 8 * (lo >> 1) + 2 * kq + (lo & 1);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                ymv[(item * OM + o) * 4 + q] =
-                    make_float4(yr[lo][4 * q], yr[lo][4 * q + 1], yr[lo][4 * q + 2],
-                                yr[lo][4 * q + 3]);
-        }
-
-    for (int t = 0; t < TS; ++t) {
-        const float4 bv = bias[(TI + t) * 64 + lane];
-        v4f acc = {bv.x, bv.y, bv.z, bv.w};
-        const int g0 = nA + nB + t * (QI + US);
-#pragma unroll
-        for (int q = 0; q < QI; ++q) acc = mv_steps(acc, wpk[(g0 + q) * 64 + lane], q, 0, 15);
-        for (int u = 0; u < US; ++u) {
-            const float4 sv = xs_chunk(u);
-            acc = step4(acc, wpk[(g0 + QI + u) * 64 + lane], sv.x, sv.y, sv.z, sv.w);
-        }
-        if (live) ys[(item * OS + 16 * t + 4 * kq) >> 2] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    for (int j = 0; j < OM / 4; ++j) {
+        const int e = threadIdx.x + 256 * j, it = e / (4 * OM), c4 = e % (4 * OM);
+        if (item0 + it < n)
+            ymv[(item0 + it) * (4 * OM) + c4] = *(const float4 *)(yt + it * YROW + 4 * c4);
     }
 }
 
@@ -273,7 +305,7 @@ pip_status pip_lgatr_geometric_product(const float *x, const float *y, int64_t n
     if (n == 0) return PIP_OK;
     if (!x || !y || !z) return PIP_ERR_NULL;
     if (!aligned16(x) || !aligned16(y) || !aligned16(z)) return PIP_ERR_ALIGN;
-    if (n > ((int64_t)1 << 40)) return PIP_ERR_UNSUPPORTED;
+    if (n > ((int64_t)1 << 38)) return PIP_ERR_UNSUPPORTED;  // grid of n / 256 workgroups
     const int64_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(geometric_product_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const float4 *)x, (const float4 *)y, n, (float4 *)z);
@@ -392,11 +424,11 @@ pip_status pip_lgatr_equilinear(const pip_equilinear *h, const float *x_mv, cons
     if (!aligned16(x_mv) || !aligned16(y_mv) || (sh.is > 0 && !aligned16(x_s)) ||
         (sh.os > 0 && !aligned16(y_s)))
         return PIP_ERR_ALIGN;
-    if (n > ((int64_t)1 << 36)) return PIP_ERR_UNSUPPORTED;
+    if (n > ((int64_t)1 << 34)) return PIP_ERR_UNSUPPORTED;  // grid of n / 16 workgroups
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return PIP_ERR_HIP;
     if (dev != h->device) return PIP_ERR_UNSUPPORTED;
-    const int64_t blocks = (n + 63) / 64;
+    const int64_t blocks = (n + 15) / 16;
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, stream,
                            (const float4 *)x_mv, (const float4 *)x_s, n, sh.is, sh.os,
