@@ -464,18 +464,7 @@ def cpu_sample(name, d, jets):
     """The oracle on the first `jets` jets of another workload, once; the
     rate is scaled to the whole workload."""
     import oracle
-    B, P = d["mask"].shape
-    s = slice(0, jets)
-    t = time.perf_counter()
-    if name == "fused512":
-        oracle.pair_embed_attention(d["p4"][s], d["mask"][s], d["mlp"], d["q"][s], d["k"][s],
-                                    d["v"][s])
-        what = "pair embed + attention"
-    elif name == "large_bf16":
-        U = oracle.pair_embed(d["p4"][s], d["mask"][s], d["mlp"])
-        oracle.attention(d["q"][s], d["k"][s], d["v"][s], U, d["mask"][s])
-        what = "pair embed + attention (bf16-rounded inputs, float64 arithmetic)"
-    elif name == "lgatr":
+    if name == "lgatr":
         p = d["params"]
         items = jets * LGATR_ITEMS
         t = time.perf_counter()
@@ -488,6 +477,17 @@ def cpu_sample(name, d, jets):
                 "sample": "first %d of %d jets (%d items): float64 equivariant linear layer "
                           "8->8 mv, 16->16 s, then the geometric product of 8 channel pairs, "
                           "%.2f s wall" % (jets, LGATR_B, items, dt)}
+    B, P = d["mask"].shape
+    s = slice(0, jets)
+    t = time.perf_counter()
+    if name == "fused512":
+        oracle.pair_embed_attention(d["p4"][s], d["mask"][s], d["mlp"], d["q"][s], d["k"][s],
+                                    d["v"][s])
+        what = "pair embed + attention"
+    elif name == "large_bf16":
+        U = oracle.pair_embed(d["p4"][s], d["mask"][s], d["mlp"])
+        oracle.attention(d["q"][s], d["k"][s], d["v"][s], U, d["mask"][s])
+        what = "pair embed + attention (bf16-rounded inputs, float64 arithmetic)"
     else:
         U = oracle.pair_embed(d["p4"][s], d["mask"][s], d["mlp"]).astype("float32")
         oracle.block_stack(d["x0"][s], d["wq"], d["wk"], d["wv"], d["wo"], U, d["mask"][s])
@@ -512,7 +512,7 @@ SHAPES = {
     "lgatr": "L-GATr kernels: B=128 x items=128, equivariant linear 8->8 multivectors + "
              "16->16 scalars, geometric product of (128, 128, 8) multivector pairs, fp32",
 }
-CPU_JETS = {"large_bf16": 16, "fused512": 128, "stack8": 32, "lgatr": 32}
+CPU_JETS = {"large_bf16": 16, "fused512": 128, "stack8": 32, "lgatr": 128}
 
 
 def main():

@@ -69,3 +69,17 @@ def test_lgatr_validation():
     assert cr(w.ctypes.data, None, None, None, None, None, 8, 8, 16, 16, None) == NULL
     assert L.pip_lgatr_equilinear(None, A16, A16, 4, A16, A16, None) == NULL
     assert L.pip_lgatr_equilinear_destroy(None) == OK
+
+
+def test_bench_cpu_sample_of_the_lgatr_workload():
+    # the oracle leg of the benchmark's L-GATr workload runs on host arrays only
+    import bench
+    from pair_interaction_particle_amd import synth
+    rng = np.random.default_rng(9)
+    n = 2 * bench.LGATR_ITEMS
+    d = {"params": synth.equilinear_params(8, 8, 16, 16, rng),
+         "x_mv": synth.multivectors((n, 8), rng),
+         "x_s": rng.normal(size=(n, 16)).astype(np.float32),
+         "y": synth.multivectors((n, 8), rng)}
+    r = bench.cpu_sample("lgatr", d, 1)
+    assert r["value"] > 0 and r["kind"] == "oracle" and "128 items" in r["sample"]
