@@ -222,8 +222,9 @@ pip_status pip_pair_bias_attention_backward(const void *Q, const void *K, const 
                                             int64_t D, float scale, void *dQ, void *dK,
                                             void *dV, void *dU, int dtype, void *stream);
 
-/* Bytes of workspace pip_pair_mlp_backward needs (one slot of
- * PIP_PAIR_MLP_FOLDED_GRADS floats per workgroup: B * P/16 slots). */
+/* Bytes of workspace pip_pair_mlp_backward needs: one slot of
+ * PIP_PAIR_MLP_FOLDED_GRADS floats per workgroup (B * P/16 slots), then one
+ * per 32 slots for the partial sums of the fixed-order reduction. */
 size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
 
 /* Gradient of L with respect to the folded pair-MLP parameters, for dL/dU =
@@ -233,7 +234,8 @@ size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
  * dU's padded entries are never read into the result.  grad (device,
  * PIP_PAIR_MLP_FOLDED_GRADS floats) has pip_pair_mlp_fold's layout:
  *   dW1' (64*4) dW2' (64*64) dW3' (64*64) dW4 (8*64) | db1' db2' db3' (64) db4 (8)
- * The MLP runs in exact float32 on the matrix cores (GELU in its erf form).
+ * The MLP runs in float32 on the matrix cores (GELU in its erf form, Phi
+ * evaluated to 7.5e-8).
  * workspace: pip_pair_mlp_backward_workspace_bytes(B, P) bytes, scratch
  * (overwritten; calls sharing one on different streams race).  Per-
  * workgroup sums use LDS float atomics, so the last bits of a result can

@@ -10,7 +10,13 @@ to 0 for large |x| and no clamp is needed (checked below on [-40, 40]).  The
 device then needs n FMAs, one v_exp_f32, one integer max (for max(x, 0), on
 the bit pattern) and one FMA per element, with no branch.
 
-Run:  python gen_gelu_coeffs.py   (prints the tables pasted into pip_mlp.h)
+The backward of the MLP also needs Phi itself (GELU'(x) = Phi(x) + x phi(x)),
+so a third table fits Phi(-a) = 2^(-R(a)) towards the minimax of the absolute
+error of Phi (degree 8, the lowest degree whose fit keeps growing beyond A
+with an error below 1e-7).
+
+Run:  python gen_gelu_coeffs.py   (prints the tables pasted into pip_mlp.h
+                                    and mlp_bwd.hip)
 """
 import numpy as np
 from scipy.special import log_ndtr, ndtr
@@ -18,11 +24,12 @@ from scipy.special import log_ndtr, ndtr
 A = 7.0
 
 
-def fit(deg, A=A, nodes=6000, iters=40):
+def fit(deg, A=A, nodes=6000, iters=40, phi=False):
     k = np.arange(nodes)
     a = (A / 2) * (1 - np.cos(np.pi * (k + 0.5) / nodes))
     Q = -log_ndtr(-a) / np.log(2)
-    w = np.maximum(a, 0.02) * ndtr(-a) * np.log(2)
+    # GELU error |x| ln2 Phi(-a) dQ, or (phi) the error of Phi, ln2 Phi(-a) dQ
+    w = (1.0 if phi else np.maximum(a, 0.02)) * ndtr(-a) * np.log(2)
     V = np.vander(a, deg + 1, increasing=True)
     ww = w.copy()
     for _ in range(iters):
@@ -51,6 +58,22 @@ def max_error(c):
     return float(err.max())
 
 
+def max_phi_error(c):
+    """Largest |Phi error| on [-40, 40] of the float32 evaluation
+    Phi(x) = x > 0 ? 1 - t : t, t = 2^-R(|x|)."""
+    xs = np.linspace(-40, 40, 800001).astype(np.float32)
+    ax = np.abs(xs)
+    c32 = c.astype(np.float32)
+    p = np.full_like(ax, c32[-1])
+    for cc in c32[-2::-1]:
+        p = (p * ax + cc).astype(np.float32)
+    assert np.all(np.diff(p[xs > A]) >= 0), "R must keep growing beyond the fit range"
+    with np.errstate(over="ignore", under="ignore"):
+        t = np.exp2(-p.astype(np.float64)).astype(np.float32)
+    ph = np.where(xs > 0, (1 - t).astype(np.float32), t)
+    return float(np.abs(ph.astype(np.float64) - ndtr(xs.astype(np.float64))).max())
+
+
 if __name__ == "__main__":
     for deg, name in ((5, "kGeluQ"), (3, "kGeluQ3")):
         c = fit(deg)
@@ -58,3 +81,7 @@ if __name__ == "__main__":
               "(float32 evaluation, no clamp)" % (deg, A, max_error(c)))
         print("constexpr float %s[%d] = {%s};" % (
             name, deg + 1, ", ".join("%.9ef" % v for v in c.astype(np.float32))))
+    c = fit(8, phi=True)
+    print("// degree 8 fitted on [0, %.1f]: max |Phi error| on [-40, 40] %.2e "
+          "(float32 evaluation, no clamp)" % (A, max_phi_error(c)))
+    print("constexpr float kPhiR[9] = {%s};" % ", ".join("%.9ef" % v for v in c.astype(np.float32)))

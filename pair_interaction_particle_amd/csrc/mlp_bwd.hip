@@ -11,7 +11,8 @@
 // (g = dU[a, a] on the diagonal):
 //   dW4 += g h3^T, db4 += g;  dy3 = (W4^T g) o GELU'(y3);
 //   dW'_l += dy_l h_{l-1}^T, db'_l += dy_l;  dy_{l-1} = (W'_l^T dy_l) o GELU'(y_{l-1}).
-// GELU is the exact erf form here, GELU'(x) = Phi(x) + x phi(x).
+// GELU is the erf form x Phi(x), GELU'(x) = Phi(x) + x phi(x), with Phi from a
+// fitted exponent (absolute error <= 7.5e-8).
 //
 // One 512-thread workgroup per (jet, row tile I) of 16 particles; its pair
 // blocks (row i of tile (I, J < I): 16 pairs; the diagonal tile: 136 pairs
@@ -31,18 +32,32 @@
 
 namespace pip {
 
-constexpr int kMbWaves = 8;
+constexpr int kMbWaves = 4;
 constexpr int kMbThreads = 64 * kMbWaves;
 constexpr int kGradFloats = 64 * 4 + 2 * 64 * 64 + 8 * 64 + 3 * 64 + 8;  // 9,160
 constexpr int kGW1 = 0, kGW2 = 256, kGW3 = 4352, kGW4 = 8448;
 constexpr int kGB1 = 8960, kGB2 = 9024, kGB3 = 9088, kGB4 = 9152;
 
+// Phi(x) = x > 0 ? 1 - t : t with t = Phi(-|x|) = 2^-R(|x|), R a degree-8
+// polynomial fitted by gen_gelu_coeffs.py (kPhiR): |Phi error| <= 7.5e-8 on
+// [-40, 40], no clamp (R keeps growing, so t underflows to 0).  GELU(x) =
+// x Phi(x) and GELU'(x) = Phi(x) + x phi(x), phi(x) = exp(-x^2/2) / sqrt(2 pi).
+constexpr float kPhiR[9] = {1.000000000e+00f, 1.151105046e+00f, 4.592107534e-01f,
+                            5.248672515e-02f, -7.048579864e-03f, 1.256083196e-04f,
+                            1.904473174e-04f, -4.009847908e-05f, 2.873645371e-06f};
 __device__ __forceinline__ float normal_cdf(float x) {
-    return 0.5f * erfcf(-x * 0.70710678118654752f);
+    const float a = fabsf(x);
+    float p = kPhiR[8];
+#pragma unroll
+    for (int k = 7; k >= 0; --k) p = fmaf(p, a, kPhiR[k]);
+    const float t = __builtin_amdgcn_exp2f(-p);
+    return x > 0.f ? 1.f - t : t;
 }
 __device__ __forceinline__ float gelu_exact(float x) { return x * normal_cdf(x); }
 __device__ __forceinline__ float gelu_grad(float x) {
-    return normal_cdf(x) + x * 0.39894228040143268f * __expf(-0.5f * x * x);
+    // 1 / (2 ln 2) = 0.72134752..., 1 / sqrt(2 pi) = 0.39894228...
+    return fmaf(x * 0.39894228040143268f, __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x),
+                normal_cdf(x));
 }
 
 // Pair (i, j), i >= j, of lane `lane` in block k of a diagonal tile.
@@ -68,51 +83,69 @@ __device__ __forceinline__ void to_tile(float (*Tb)[17], const v4f (&X)[4]) {
         for (int r = 0; r < 4; ++r) Tb[16 * t + 4 * g + r][c] = X[t][r];
 }
 
-// acc[o][i] (row stride ld) += sum over the 16 pairs of A[o][pair] B[i][pair]
-// for the 16-row output tiles ot < no and 16-column tiles it < ni, from the
-// tiles TA and TB; rows >= rmax and columns >= cmax are not accumulated.
+// A[ot kNi + it] += sum over the 16 pairs of TA[o][pair] TB[i][pair]: the
+// weight-gradient product of one block of pairs, accumulated in registers
+// across a wave's blocks.  Output tile (ot, it): lane (g, c) holds rows
+// 16 ot + 4g + r, column 16 it + c.  Tile rows >= rmax and columns >= cmax
+// read as 0 (tile rows the block did not write).
 template <int kNo, int kNi>
-__device__ __forceinline__ void outer_acc(float *acc, int ld, const float (*TA)[17],
+__device__ __forceinline__ void outer_reg(v4f (&A)[kNo * kNi], const float (*TA)[17],
                                           const float (*TB)[17], int rmax, int cmax) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     float a[kNo][4], b[kNi][4];
 #pragma unroll
+    for (int t = 0; t < kNo; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a[t][s] = 16 * t + c < rmax ? TA[16 * t + c][4 * s + g] : 0.f;
+#pragma unroll
+    for (int t = 0; t < kNi; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b[t][s] = 16 * t + c < cmax ? TB[16 * t + c][4 * s + g] : 0.f;
+#pragma unroll
     for (int ot = 0; ot < kNo; ++ot)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a[ot][s] = 16 * ot + c < rmax ? TA[16 * ot + c][4 * s + g] : 0.f;
+        for (int it = 0; it < kNi; ++it)
 #pragma unroll
-    for (int it = 0; it < kNi; ++it)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) b[it][s] = 16 * it + c < cmax ? TB[16 * it + c][4 * s + g] : 0.f;
+            for (int s = 0; s < 4; ++s)
+                A[kNi * ot + it] = mfma4(a[ot][s], b[it][s], A[kNi * ot + it]);
+}
+
+// acc (row stride ld) += the register tiles of outer_reg, rows < rmax and
+// columns < cmax (once per wave, at the end)
+template <int kNo, int kNi>
+__device__ __forceinline__ void flush_reg(float *acc, int ld, const v4f (&A)[kNo * kNi], int rmax,
+                                          int cmax) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int ot = 0; ot < kNo; ++ot)
 #pragma unroll
-        for (int it = 0; it < kNi; ++it) {
-            v4f d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) d = mfma4(a[ot][s], b[it][s], d);
-            const int col = 16 * it + c;
+        for (int it = 0; it < kNi; ++it)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * ot + 4 * g + r;
-                if (row < rmax && col < cmax) atomicAdd(acc + row * ld + col, d[r]);
+                const int row = 16 * ot + 4 * g + r, col = 16 * it + c;
+                if (row < rmax && col < cmax)
+                    atomicAdd(acc + row * ld + col, A[kNi * ot + it][r]);
             }
+}
+
+// acc[16 t + 4g + r] += sum over the 16 lanes c of S[t][r] (lane (g, c)):
+// per-lane bias-gradient partial sums, reduced once per wave at the end.
+template <int kN>
+__device__ __forceinline__ void flush_rows(float *acc, const float (&S)[kN][4]) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int t = 0; t < kN; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = S[t][r];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+            if (c == 0) atomicAdd(acc + 16 * t + 4 * g + r, v);
         }
 }
 
-// acc[f] += sum over the 16 pairs of tile row f, f < rows (one lane per row)
-__device__ __forceinline__ void row_sums(float *acc, const float (*Tb)[17], int rows) {
-    const int lane = threadIdx.x & 63;
-    if (lane < rows) {
-        float s = 0.f;
-#pragma unroll
-        for (int p = 0; p < 16; ++p) s += Tb[lane][p];
-        atomicAdd(acc + lane, s);
-    }
-}
-
 template <int kPP>
-__global__ __launch_bounds__(kMbThreads) __attribute__((amdgpu_waves_per_eu(2))) void
+__global__ __launch_bounds__(kMbThreads) __attribute__((amdgpu_waves_per_eu(1))) void
 mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
                const float *__restrict__ wplain, const float *__restrict__ bias,
                const float *__restrict__ dU, float *__restrict__ partial) {
@@ -152,6 +185,19 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
     float (*T0)[17] = tr[wave][0];
     float (*T1)[17] = tr[wave][1];
     const int nb = 16 * I + 9;
+    // the gradients summed over this wave's blocks, in registers: weight
+    // tiles of every layer, per-lane partial sums of the bias gradients
+    v4f gw1[4], gw2[16], gw3[16], gw4[4];
+    float sb1[4][4], sb2[4][4], sb3[4][4], sb4[2];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) gw2[t] = gw3[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        gw1[t] = gw4[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sb1[t][r] = sb2[t][r] = sb3[t][r] = 0.f;
+    }
+    sb4[0] = sb4[1] = 0.f;
     for (int blk = wave; blk < nb; blk += kMbWaves) {
         int i, j;
         bool valid;
@@ -225,8 +271,9 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
 #pragma unroll
         for (int t = 0; t < 2; ++t) T0[4 * t + g][c] = gv[t];
         __builtin_amdgcn_wave_barrier();
-        outer_acc<1, 4>(acc + kGW4, 64, T0, T1, 8, 64);
-        row_sums(acc + kGB4, T0, 8);
+        outer_reg<1, 4>(gw4, T0, T1, 8, 64);
+        sb4[0] += gv[0];
+        sb4[1] += gv[1];
         v4f dy[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -248,8 +295,15 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
             to_tile(T0, dy);
             to_tile(T1, hh);
             __builtin_amdgcn_wave_barrier();
-            outer_acc<4, 4>(acc + (l == 1 ? kGW3 : kGW2), 64, T0, T1, 64, 64);
-            row_sums(acc + (l == 1 ? kGB3 : kGB2), T0, 64);
+            if (l == 1) outer_reg<4, 4>(gw3, T0, T1, 64, 64);
+            else outer_reg<4, 4>(gw2, T0, T1, 64, 64);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (l == 1) sb3[t][r] += dy[t][r];
+                    else sb2[t][r] += dy[t][r];
+                }
             v4f nd[4];
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
@@ -270,28 +324,68 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
         to_tile(T0, dy);
         T1[g][c] = f;
         __builtin_amdgcn_wave_barrier();
-        outer_acc<4, 1>(acc + kGW1, 4, T0, T1, 64, 4);
-        row_sums(acc + kGB1, T0, 64);
+        outer_reg<4, 1>(gw1, T0, T1, 64, 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sb1[t][r] += dy[t][r];
         __builtin_amdgcn_wave_barrier();
+    }
+    flush_reg<4, 1>(acc + kGW1, 4, gw1, 64, 4);
+    flush_reg<4, 4>(acc + kGW2, 64, gw2, 64, 64);
+    flush_reg<4, 4>(acc + kGW3, 64, gw3, 64, 64);
+    flush_reg<1, 4>(acc + kGW4, 64, gw4, 8, 64);
+    flush_rows<4>(acc + kGB1, sb1);
+    flush_rows<4>(acc + kGB2, sb2);
+    flush_rows<4>(acc + kGB3, sb3);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {  // db4[4t + g] (lane group g holds head 4t + g)
+        float v = sb4[t];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+        if (c == 0) atomicAdd(acc + kGB4 + 4 * t + g, v);
     }
     __syncthreads();
     float *out = partial + (size_t)blockIdx.x * kGradFloats;
     for (int e = tid; e < kGradFloats; e += kMbThreads) out[e] = acc[e];
 }
 
-// grad[e] = sum over the workgroup slots w = 0 .. nslots-1 of partial[w][e]
+// grad[e] = sum over the workgroup slots w = 0 .. nslots-1 of partial[w][e],
+// in a fixed order: chunk k = blockIdx.y of kRedChunk consecutive slots is
+// summed in slot order (its loads issued together) into chunk[k][e], then the
+// chunk sums are added in chunk order.  The chunk sums have their own region
+// after the slots.
+constexpr int kRedChunk = 32;
 __global__ __launch_bounds__(256) void mlp_bwd_reduce_kernel(const float *__restrict__ partial,
                                                              int nslots,
-                                                             float *__restrict__ grad) {
+                                                             float *__restrict__ chunk) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int w0 = blockIdx.y * kRedChunk;
+    if (e >= kGradFloats) return;
+    float v[kRedChunk];
+#pragma unroll
+    for (int w = 0; w < kRedChunk; ++w)
+        v[w] = w0 + w < nslots ? partial[(size_t)(w0 + w) * kGradFloats + e] : 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRedChunk; ++w) s += v[w];
+    chunk[(size_t)blockIdx.y * kGradFloats + e] = s;
+}
+
+__global__ __launch_bounds__(256) void mlp_bwd_final_kernel(const float *__restrict__ partial,
+                                                            int nchunks,
+                                                            float *__restrict__ grad) {
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= kGradFloats) return;
     float s = 0.f;
-    for (int w = 0; w < nslots; ++w) s += partial[(size_t)w * kGradFloats + e];
+    for (int k = 0; k < nchunks; ++k) s += partial[(size_t)k * kGradFloats + e];
     grad[e] = s;
 }
 
+// one slot per (jet, row tile) workgroup, then one chunk sum per kRedChunk slots
 size_t mlp_bwd_workspace(int B, int P) {
-    return (size_t)B * (P / kTile) * kGradFloats * sizeof(float);
+    const size_t nslots = (size_t)B * (P / kTile);
+    return (nslots + (nslots + kRedChunk - 1) / kRedChunk) * kGradFloats * sizeof(float);
 }
 
 hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P,
@@ -299,9 +393,9 @@ hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P
                               hipStream_t s) {
     const int T = P / kTile;
     float *partial = (float *)ws;
-    if (B == 0) {  // no pair: the reduction over no slot writes zeros
-        hipLaunchKernelGGL(mlp_bwd_reduce_kernel, dim3((kGradFloats + 255) / 256), dim3(256), 0,
-                           s, partial, 0, grad);
+    const dim3 rg((kGradFloats + 255) / 256);
+    if (B == 0) {  // no pair: the sum over no chunk writes zeros
+        hipLaunchKernelGGL(mlp_bwd_final_kernel, rg, dim3(256), 0, s, partial, 0, grad);
         return hipGetLastError();
     }
     if (P <= 128)
@@ -310,8 +404,12 @@ hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P
     else
         hipLaunchKernelGGL(mlp_bwd_kernel<256>, dim3((unsigned)(B * T)), dim3(kMbThreads), 0, s,
                            (const float4 *)p4, mask, P, m->wplain, m->bias, dU, partial);
-    hipLaunchKernelGGL(mlp_bwd_reduce_kernel, dim3((kGradFloats + 255) / 256), dim3(256), 0, s,
-                       partial, B * T, grad);
+    const int nslots = B * T, nchunks = (nslots + kRedChunk - 1) / kRedChunk;
+    float *chunk = partial + (size_t)nslots * kGradFloats;
+    hipLaunchKernelGGL(mlp_bwd_reduce_kernel, dim3(rg.x, (unsigned)nchunks), dim3(256), 0, s,
+                       (const float *)partial, nslots, chunk);
+    hipLaunchKernelGGL(mlp_bwd_final_kernel, rg, dim3(256), 0, s, (const float *)chunk, nchunks,
+                       grad);
     return hipGetLastError();
 }
 
