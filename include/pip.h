@@ -212,8 +212,8 @@ pip_status pip_pair_embed_attention(const float *p4, const uint8_t *mask,
  * the inputs, dO included, are never read into a result).  The forward is
  * recomputed from Q, K, V, U (no saved statistics).  Only PIP_F32 (float32
  * matrix cores, float32 results); PIP_BF16 returns PIP_ERR_UNSUPPORTED.
- * dK and dV add the query blocks' contributions with LDS float atomics, so
- * their last bits can differ from run to run.
+ * The query blocks' contributions to dK and dV are added in a fixed order:
+ * every output is the same bit for bit on every run.
  * Requires D == 16, P % 16 == 0, P <= 256.  Errors: NULL, SHAPE, ALIGN,
  * DTYPE, UNSUPPORTED, VALUE, HIP. */
 pip_status pip_pair_bias_attention_backward(const void *Q, const void *K, const void *V,
@@ -237,10 +237,9 @@ size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
  * The MLP runs in float32 on the matrix cores (GELU in its erf form, Phi
  * evaluated to 7.5e-8).
  * workspace: pip_pair_mlp_backward_workspace_bytes(B, P) bytes, scratch
- * (overwritten; calls sharing one on different streams race).  Per-
- * workgroup sums use LDS float atomics, so the last bits of a result can
- * differ from run to run; the workgroup sums are then added in a fixed
- * order.  Requires P % 16 == 0, P <= 256.  Errors: NULL, SHAPE, ALIGN,
+ * (overwritten; calls sharing one on different streams race).  Every sum
+ * is taken in a fixed order: the result is the same bit for bit on every
+ * run.  Requires P % 16 == 0, P <= 256.  Errors: NULL, SHAPE, ALIGN,
  * UNSUPPORTED, HIP. */
 pip_status pip_pair_mlp_backward(const float *p4, const uint8_t *mask, int64_t B, int64_t P,
                                  const pip_pair_mlp *mlp, const float *dU, float *grad,

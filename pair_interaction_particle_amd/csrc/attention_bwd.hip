@@ -10,18 +10,21 @@
 // Everything that involves a padded slot is exactly 0.
 //
 // One 512-thread workgroup per (jet, head).  K and V are staged in LDS
-// (float32, padded rows 0); dK and dV accumulate in LDS with float atomics
-// (beyond two query blocks the order of the additions, and so the last bits,
-// can differ from run to run).  Each wave owns
+// (float32, padded rows 0).  Each wave owns
 // query blocks of 16 queries and recomputes the forward of its rows from
 // the U strip: scores S^T = K Q^T (lane l: query l%16 against keys
 // 4(l/16)+r), an exact two-pass softmax, O^T = V^T P^T and D = dO . O; then
 // per key block dP^T = V dO^T, dS, the dU strip (one 16-byte store per lane
 // and block, the forward's U read layout), dQ^T += K^T dS^T in registers, and
 // P and dS transposed through a wave-private LDS tile into the operand layout
-// of dV = P^T dO and dK = dS^T Q, whose 16x16 results are added to the LDS
-// accumulators.  All products are float32 MFMA (v_mfma_f32_16x16x4_f32), so
-// the gradients are float32 results of the same definition.
+// of dV = P^T dO and dK = dS^T Q, whose 16x16 tiles stay in registers.  The
+// waves then merge their tiles into the LDS accumulators in 8 barrier-
+// separated phases (wave w adds key block (j + w) mod 8 in phase j): plain
+// read-add-write, no atomics (LDS float atomics cost several cycles per
+// lane here), and a fixed order of additions, so dK and dV are the same bit
+// for bit on every run.  All products are float32 MFMA
+// (v_mfma_f32_16x16x4_f32), so the gradients are float32 results of the
+// same definition.
 #include "pip_attn.h"
 #include "pip_internal.h"
 
@@ -63,15 +66,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const float *Ub = U + base * P;
     float *dUb = dU + base * P;
 
-    // ---- K, V, the mask into LDS; accumulators to 0
-    for (int i = tid; i < P; i += kBwdThreads) rs[i] = mask[(size_t)jet * P + i] != 0;
-    __syncthreads();
+    // ---- K, V, the mask into LDS (one pass: each thread reads its row's
+    // mask byte with its K and V pieces); accumulators to 0
     for (int i = tid; i < P * 4; i += kBwdThreads) {
         const int k = i >> 2, d0 = (i & 3) * 4;
-        const bool rk = rs[k];
+        const bool rk = mask[(size_t)jet * P + k] != 0;
         const float4 kv = *(const float4 *)(Kh + (size_t)k * 16 + d0);
         const float4 vv = *(const float4 *)(Vh + (size_t)k * 16 + d0);
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (d0 == 0) rs[k] = rk;
         *(float4 *)&Ks[k][d0] = keep4(rk, kv);
         *(float4 *)&Vs[k][d0] = keep4(rk, vv);
         *(float4 *)&dKs[k][d0] = z;
@@ -79,128 +82,161 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     }
     __syncthreads();
 
-    for (int qb = wave; qb < T; qb += kBwdWaves) {
-        const int q0 = qb * kTile;
-        const bool rq = rs[q0 + c];
-        bool anyq = false;
-        for (int i = 0; i < kTile; ++i) anyq |= rs[q0 + i] != 0;
-        if (!anyq) {
-            // no real query: zero dU strip, dQ rows
-            for (int kb = 0; kb < T; ++kb)
-                *(float4 *)(dUb + (size_t)(q0 + c) * P + kb * kTile + 4 * g) =
-                    make_float4(0.f, 0.f, 0.f, 0.f);
-            *(float4 *)(dQ + (base + q0 + c) * 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
-            continue;
+    // Rounds of up to 8 query blocks, one per wave; every wave runs every
+    // round (the dK / dV merge below has barriers).
+    for (int q8 = 0; q8 < T; q8 += kBwdWaves) {
+        const int qb = q8 + wave, q0 = qb * kTile;
+        bool act = qb < T;
+        const bool rq = act && rs[q0 + c];
+        if (act) {
+            bool anyq = false;
+            for (int i = 0; i < kTile; ++i) anyq |= rs[q0 + i] != 0;
+            if (!anyq) {
+                // no real query: zero dU strip, dQ rows
+                for (int kb = 0; kb < T; ++kb)
+                    *(float4 *)(dUb + (size_t)(q0 + c) * P + kb * kTile + 4 * g) =
+                        make_float4(0.f, 0.f, 0.f, 0.f);
+                *(float4 *)(dQ + (base + q0 + c) * 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+                act = false;
+            }
         }
         // operands of this query block: Q[q0+c][4s+g] and dO[q0+c][4s+g]
         // (B operands of the K = 4 slices), Q[q0+4s+g][c] and dO[q0+4s+g][c]
         // (B operands of dK and dV), dO[q0+c][4g..] for D; padded queries 0
         float qB[4], gB[4], qT[4], gT[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const float a = Qh[(size_t)(q0 + c) * 16 + 4 * s + g];
-            const float b = dOh[(size_t)(q0 + c) * 16 + 4 * s + g];
-            qB[s] = rq ? a : 0.f;
-            gB[s] = rq ? b : 0.f;
-            const int qr = q0 + 4 * s + g;
-            const bool rr = rs[qr];
-            const float a2 = Qh[(size_t)qr * 16 + c];
-            const float b2 = dOh[(size_t)qr * 16 + c];
-            qT[s] = rr ? a2 : 0.f;
-            gT[s] = rr ? b2 : 0.f;
-        }
-        const float4 gr4 = *(const float4 *)(dOh + (size_t)(q0 + c) * 16 + 4 * g);
-        // ---- pass 1: scores and the row max
         float s[kT][4];
-        float m = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < kT; ++kb) {
-            if (kb >= T) continue;
-            const float4 uv = *(const float4 *)(Ub + (size_t)(q0 + c) * P + kb * kTile + 4 * g);
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc = mfma4(Ks[kb * kTile + c][4 * t + g], qB[t], acc);
-            const float uu[4] = {uv.x, uv.y, uv.z, uv.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool rk = rs[kb * kTile + 4 * g + r];
-                s[kb][r] = rk ? fmaf(acc[r], scale, uu[r]) : -INFINITY;
-                m = fmaxf(m, s[kb][r]);
-            }
-        }
-        m = xmax16(m);
-        // ---- probabilities (0 for padded queries and keys)
-        float l = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < kT; ++kb) {
-            if (kb >= T) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = __expf(s[kb][r] - m);
-                s[kb][r] = e;
-                l += e;
-            }
-        }
-        l = xsum16(l);
-        const float il = 1.0f / l;
-#pragma unroll
-        for (int kb = 0; kb < kT; ++kb) {
-            if (kb >= T) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[kb][r] = rq ? s[kb][r] * il : 0.f;
-        }
-        // ---- pass 2: O^T = V^T P^T, then D = dO . O per query
-        v4f o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < kT; ++kb) {
-            if (kb >= T) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o = mfma4(Vs[kb * kTile + 4 * g + r][c], s[kb][r], o);
-        }
-        // lane (g, c) holds O[query c][4g + r]
-        const float Dq = xsum16(o[0] * gr4.x + o[1] * gr4.y + o[2] * gr4.z + o[3] * gr4.w);
-        // ---- pass 3: dP, dS, dU, dQ, and the dK / dV contributions
-        v4f dq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < kT; ++kb) {
-            if (kb >= T) continue;
-            const int k0 = kb * kTile;
-            v4f dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) dp = mfma4(Vs[k0 + c][4 * t + g], gB[t], dp);
-            // (a select, not the product: a padded pair is +0.0 bit for bit)
-            float ds[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                ds[r] = rq && rs[k0 + 4 * g + r] ? s[kb][r] * (dp[r] - Dq) : 0.f;
-            *(float4 *)(dUb + (size_t)(q0 + c) * P + k0 + 4 * g) =
-                make_float4(ds[0], ds[1], ds[2], ds[3]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dq = mfma4(Ks[k0 + 4 * g + r][c], ds[r], dq);
-            // P and dS of the tile, transposed through LDS: [query c][key 4g+r]
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                Tp[wave][c][4 * g + r] = s[kb][r];
-                Tds[wave][c][4 * g + r] = ds[r];
-            }
-            __builtin_amdgcn_wave_barrier();
-            // dV[key c'][d] += sum_q P[q][key] dO[q][d]: lane (g, c) supplies
-            // A = P[q0+4t+g][k0+c], B = dO[q0+4t+g][c]; D row = key 4g+r
-            v4f av = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+        float Dq = 0.f;
+        if (act) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                av = mfma4(Tp[wave][4 * t + g][c], gT[t], av);
-                ak = mfma4(Tds[wave][4 * t + g][c], qT[t], ak);
+                const float a = Qh[(size_t)(q0 + c) * 16 + 4 * t + g];
+                const float b = dOh[(size_t)(q0 + c) * 16 + 4 * t + g];
+                qB[t] = rq ? a : 0.f;
+                gB[t] = rq ? b : 0.f;
+                const int qr = q0 + 4 * t + g;
+                const bool rr = rs[qr];
+                const float a2 = Qh[(size_t)qr * 16 + c];
+                const float b2 = dOh[(size_t)qr * 16 + c];
+                qT[t] = rr ? a2 : 0.f;
+                gT[t] = rr ? b2 : 0.f;
             }
-            __builtin_amdgcn_wave_barrier();
+            const float4 gr4 = *(const float4 *)(dOh + (size_t)(q0 + c) * 16 + 4 * g);
+            // ---- pass 1: scores and the row max.  The whole U strip is
+            // loaded first, every load issued before any is waited for (key
+            // blocks past T re-read block 0, unused), into the registers the
+            // scores take.
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                atomicAdd(&dVs[k0 + 4 * g + r][c], av[r]);
-                atomicAdd(&dKs[k0 + 4 * g + r][c], ak[r]);
+            for (int kb = 0; kb < kT; ++kb) {
+                const int col = (kb < T ? kb * kTile : 0) + 4 * g;
+                const float4 uv = *(const float4 *)(Ub + (size_t)(q0 + c) * P + col);
+                s[kb][0] = uv.x, s[kb][1] = uv.y, s[kb][2] = uv.z, s[kb][3] = uv.w;
+            }
+            float m = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < kT; ++kb) {
+                if (kb >= T) continue;
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc = mfma4(Ks[kb * kTile + c][4 * t + g], qB[t], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool rk = rs[kb * kTile + 4 * g + r];
+                    s[kb][r] = rk ? fmaf(acc[r], scale, s[kb][r]) : -INFINITY;
+                    m = fmaxf(m, s[kb][r]);
+                }
+            }
+            m = xmax16(m);
+            // ---- probabilities (0 for padded queries and keys)
+            float l = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < kT; ++kb) {
+                if (kb >= T) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = __expf(s[kb][r] - m);
+                    s[kb][r] = e;
+                    l += e;
+                }
+            }
+            l = xsum16(l);
+            const float il = 1.0f / l;
+#pragma unroll
+            for (int kb = 0; kb < kT; ++kb) {
+                if (kb >= T) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s[kb][r] = rq ? s[kb][r] * il : 0.f;
+            }
+            // ---- pass 2: O^T = V^T P^T, then D = dO . O per query
+            v4f o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < kT; ++kb) {
+                if (kb >= T) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o = mfma4(Vs[kb * kTile + 4 * g + r][c], s[kb][r], o);
+            }
+            // lane (g, c) holds O[query c][4g + r]
+            Dq = xsum16(o[0] * gr4.x + o[1] * gr4.y + o[2] * gr4.z + o[3] * gr4.w);
+        }
+        // ---- pass 3, 8 key blocks at a time: dP, dS, dU, dQ, and this
+        // query block's dK / dV tiles, kept in registers, then merged into
+        // LDS without atomics: in merge phase j wave w adds its tile of key
+        // block (j + w) mod 8, so the 8 waves touch 8 different tiles.
+        v4f dq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h0 = 0; h0 < kT; h0 += 8) {
+            v4f avs[8], aks[8];
+#pragma unroll
+            for (int kl = 0; kl < 8; ++kl) {
+                const int kb = h0 + kl, k0 = kb * kTile;
+                avs[kl] = aks[kl] = (v4f){0.f, 0.f, 0.f, 0.f};
+                if (!act || kb >= T) continue;
+                v4f dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) dp = mfma4(Vs[k0 + c][4 * t + g], gB[t], dp);
+                // (a select, not the product: a padded pair is +0.0 bit for bit)
+                float ds[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ds[r] = rq && rs[k0 + 4 * g + r] ? s[kb][r] * (dp[r] - Dq) : 0.f;
+                *(float4 *)(dUb + (size_t)(q0 + c) * P + k0 + 4 * g) =
+                    make_float4(ds[0], ds[1], ds[2], ds[3]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dq = mfma4(Ks[k0 + 4 * g + r][c], ds[r], dq);
+                // P and dS of the tile, transposed through LDS: [query c][key 4g+r]
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    Tp[wave][c][4 * g + r] = s[kb][r];
+                    Tds[wave][c][4 * g + r] = ds[r];
+                }
+                __builtin_amdgcn_wave_barrier();
+                // dV[key c'][d] += sum_q P[q][key] dO[q][d]: lane (g, c) supplies
+                // A = P[q0+4t+g][k0+c], B = dO[q0+4t+g][c]; D row = key 4g+r
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    avs[kl] = mfma4(Tp[wave][4 * t + g][c], gT[t], avs[kl]);
+                    aks[kl] = mfma4(Tds[wave][4 * t + g][c], qT[t], aks[kl]);
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int kl_w = (j + wave) & 7;
+#pragma unroll
+                for (int kl = 0; kl < 8; ++kl) {
+                    const int kb = h0 + kl, k0 = kb * kTile;
+                    if (kl != kl_w || !act || kb >= T) continue;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        dVs[k0 + 4 * g + r][c] += avs[kl][r];
+                        dKs[k0 + 4 * g + r][c] += aks[kl][r];
+                    }
+                }
+                __syncthreads();
             }
         }
-        *(float4 *)(dQ + (base + q0 + c) * 16 + 4 * g) =
-            keep4(rq, make_float4(dq[0] * scale, dq[1] * scale, dq[2] * scale, dq[3] * scale));
+        if (act)
+            *(float4 *)(dQ + (base + q0 + c) * 16 + 4 * g) =
+                keep4(rq, make_float4(dq[0] * scale, dq[1] * scale, dq[2] * scale, dq[3] * scale));
     }
     __syncthreads();
     for (int i = tid; i < P * 4; i += kBwdThreads) {

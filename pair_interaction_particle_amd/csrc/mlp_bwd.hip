@@ -14,19 +14,19 @@
 // GELU is the erf form x Phi(x), GELU'(x) = Phi(x) + x phi(x), with Phi from a
 // fitted exponent (absolute error <= 7.5e-8).
 //
-// One 512-thread workgroup per (jet, row tile I) of 16 particles; its pair
+// One 256-thread workgroup per (jet, row tile I) of 16 particles; its pair
 // blocks (row i of tile (I, J < I): 16 pairs; the diagonal tile: 136 pairs
-// in 9 blocks) go round-robin to the 8 waves.  Per block a wave recomputes
+// in 9 blocks) go round-robin to the 4 waves.  Per block a wave recomputes
 // the forward on the float32 matrix cores (v_mfma_f32_16x16x4_f32, hidden
 // states in registers, feature-major: lane l holds features 4(l/16)+r of
 // pair l%16), runs the backward chain with W'^T operands read from a
 // row-major LDS copy of the weights, then forms the weight gradients as
 // products over the 16 pairs: both factors are transposed through a
 // wave-private LDS tile into the pair-major operand layout, and the 16x16
-// results are added to the workgroup's LDS accumulators (float atomics, so
-// the last bits depend on the order in which the waves add).  Each workgroup
-// writes its accumulators to one slot of the workspace; a second kernel adds
-// the slots in a fixed order.
+// results accumulate in registers across all of the wave's blocks.  At the
+// end the 4 waves merge their sums into LDS in a fixed order (no atomics),
+// each workgroup writes one slot of the workspace, and two more kernels add
+// the slots in a fixed order: the result is the same bit for bit on every run.
 #include "pip_internal.h"
 #include "pip_mlp.h"
 
@@ -111,7 +111,8 @@ __device__ __forceinline__ void outer_reg(v4f (&A)[kNo * kNi], const float (*TA)
 }
 
 // acc (row stride ld) += the register tiles of outer_reg, rows < rmax and
-// columns < cmax (once per wave, at the end)
+// columns < cmax: a plain read-add-write, so the caller makes sure no other
+// wave writes the same region meanwhile.
 template <int kNo, int kNi>
 __device__ __forceinline__ void flush_reg(float *acc, int ld, const v4f (&A)[kNo * kNi], int rmax,
                                           int cmax) {
@@ -123,13 +124,13 @@ __device__ __forceinline__ void flush_reg(float *acc, int ld, const v4f (&A)[kNo
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * ot + 4 * g + r, col = 16 * it + c;
-                if (row < rmax && col < cmax)
-                    atomicAdd(acc + row * ld + col, A[kNi * ot + it][r]);
+                if (row < rmax && col < cmax) acc[row * ld + col] += A[kNi * ot + it][r];
             }
 }
 
 // acc[16 t + 4g + r] += sum over the 16 lanes c of S[t][r] (lane (g, c)):
-// per-lane bias-gradient partial sums, reduced once per wave at the end.
+// per-lane bias-gradient partial sums, reduced once per wave at the end
+// (read-add-write, as flush_reg).
 template <int kN>
 __device__ __forceinline__ void flush_rows(float *acc, const float (&S)[kN][4]) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
@@ -140,7 +141,7 @@ __device__ __forceinline__ void flush_rows(float *acc, const float (&S)[kN][4]) 
             float v = S[t][r];
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-            if (c == 0) atomicAdd(acc + 16 * t + 4 * g + r, v);
+            if (c == 0) acc[16 * t + 4 * g + r] += v;
         }
 }
 
@@ -331,21 +332,35 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
             for (int r = 0; r < 4; ++r) sb1[t][r] += dy[t][r];
         __builtin_amdgcn_wave_barrier();
     }
-    flush_reg<4, 1>(acc + kGW1, 4, gw1, 64, 4);
-    flush_reg<4, 4>(acc + kGW2, 64, gw2, 64, 64);
-    flush_reg<4, 4>(acc + kGW3, 64, gw3, 64, 64);
-    flush_reg<1, 4>(acc + kGW4, 64, gw4, 8, 64);
-    flush_rows<4>(acc + kGB1, sb1);
-    flush_rows<4>(acc + kGB2, sb2);
-    flush_rows<4>(acc + kGB3, sb3);
+    // Merge the waves' register sums into acc without atomics: the gradient
+    // is cut into kMbWaves disjoint parts, and in phase j wave w adds part
+    // (j + w) mod kMbWaves, so no two waves touch the same floats at once and
+    // every float receives the waves' sums in a fixed order.
+    static_assert(kMbWaves == 4, "four gradient parts, one per wave and phase");
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {  // db4[4t + g] (lane group g holds head 4t + g)
-        float v = sb4[t];
+    for (int j = 0; j < kMbWaves; ++j) {
+        const int part = (j + wave) & 3;
+        if (part == 0) {
+            flush_reg<4, 4>(acc + kGW2, 64, gw2, 64, 64);
+        } else if (part == 1) {
+            flush_reg<4, 4>(acc + kGW3, 64, gw3, 64, 64);
+        } else if (part == 2) {
+            flush_reg<4, 1>(acc + kGW1, 4, gw1, 64, 4);
+            flush_reg<1, 4>(acc + kGW4, 64, gw4, 8, 64);
+        } else {
+            flush_rows<4>(acc + kGB1, sb1);
+            flush_rows<4>(acc + kGB2, sb2);
+            flush_rows<4>(acc + kGB3, sb3);
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-        if (c == 0) atomicAdd(acc + kGB4 + 4 * t + g, v);
+            for (int t = 0; t < 2; ++t) {  // db4[4t + g] (lane group g: head 4t + g)
+                float v = sb4[t];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+                if (c == 0) acc[kGB4 + 4 * t + g] += v;
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
     float *out = partial + (size_t)blockIdx.x * kGradFloats;
     for (int e = tid; e < kGradFloats; e += kMbThreads) out[e] = acc[e];
 }
