@@ -730,7 +730,7 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
 }
 
 // Compute units of the current device (cached per device).
-static int cu_count() {
+int cu_count() {
     static int cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;

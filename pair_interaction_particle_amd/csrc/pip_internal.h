@@ -28,6 +28,8 @@ struct pip_pair_mlp {
 };
 
 namespace pip {
+// compute units of the current device (cached per device)
+int cu_count();
 constexpr int kW16L2 = 0, kW16L3 = 8 * 512, kW16L4 = 16 * 512;  // bf16 element offsets
 
 hipError_t launch_pair_features(const float *p4, const uint8_t *mask, int B, int P, float *F,
