@@ -153,3 +153,21 @@ def test_inconsistent_jets_are_skipped():
             assert np.isnan(rows).all(), "skipped jet %d: O written" % b
         else:
             assert np.isfinite(rows).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_packed_embed_beyond_the_tile_prefix(dtype):
+    # more jets than the persistent kernel's LDS prefix holds (4096): the
+    # one-workgroup-per-row kernel takes the batch, same results
+    rng = np.random.default_rng(131)
+    ns = tuple(int(x) for x in rng.integers(0, 41, size=4100))
+    P = 48
+    p4, mask = jets(ns, P, seed=131)
+    params = mlp_for(131, biases=True)
+    mlp = pip.PairMLP(params)
+    cu = synth.cu_seqlens(mask)
+    U, _ = pip.pair_embed_packed(g(synth.pack_rows(p4, mask)), g(cu), mlp, dtype=dtype)
+    Uref = oracle.pair_embed(p4, mask, params)
+    bf = dtype == "bf16"
+    check_u(host(U), Uref, ns, TOLBF if bf else TOL32, TOLBF_U if bf else TOL32,
+            "packed U %s (B=4100)" % dtype)
