@@ -150,7 +150,10 @@ __global__ __launch_bounds__(kMbThreads) __attribute__((amdgpu_waves_per_eu(1)))
 mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
                const float *__restrict__ wplain, const float *__restrict__ bias,
                const float *__restrict__ dU, float *__restrict__ partial) {
-    __shared__ float Wl[2][64][65];  // W2', W3' row-major
+    // W2', W3' row-major and transposed (rows padded to 68 floats: 16-byte
+    // aligned, so each lane reads its four k-steps of an operand at once)
+    __shared__ float4 Wl4[2][64][17];
+    __shared__ float4 WlT4[2][64][17];
     __shared__ float W4s[8][65];
     __shared__ float W1s[64][4];
     __shared__ float bs[200];
@@ -165,8 +168,13 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
     const int g = lane >> 4, c = lane & 15;
 
     for (int e = tid; e < 64 * 64; e += kMbThreads) {
-        Wl[0][e >> 6][e & 63] = wplain[256 + e];
-        Wl[1][e >> 6][e & 63] = wplain[4352 + e];
+        float *w0 = (float *)Wl4[0][e >> 6], *w1 = (float *)Wl4[1][e >> 6];
+        float *t0 = (float *)WlT4[0][e & 63], *t1 = (float *)WlT4[1][e & 63];
+        const float a = wplain[256 + e], b = wplain[4352 + e];
+        w0[e & 63] = a;
+        w1[e & 63] = b;
+        t0[e >> 6] = a;
+        t1[e >> 6] = b;
     }
     for (int e = tid; e < 8 * 64; e += kMbThreads) W4s[e >> 6][e & 63] = wplain[8448 + e];
     if (tid < 256) W1s[tid >> 2][tid & 3] = wplain[tid];
@@ -244,10 +252,13 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
 #pragma unroll
             for (int r = 0; r < 4; ++r) y2[co][r] = bs[64 + 16 * co + 4 * g + r];
 #pragma unroll
-            for (int ci = 0; ci < 4; ++ci)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    y2[co] = mfma4(Wl[0][16 * co + c][16 * ci + 4 * g + r], hh[ci][r], y2[co]);
+            for (int ci = 0; ci < 4; ++ci) {
+                const float4 w = Wl4[0][16 * co + c][4 * ci + g];
+                y2[co] = mfma4(w.x, hh[ci][0], y2[co]);
+                y2[co] = mfma4(w.y, hh[ci][1], y2[co]);
+                y2[co] = mfma4(w.z, hh[ci][2], y2[co]);
+                y2[co] = mfma4(w.w, hh[ci][3], y2[co]);
+            }
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -258,10 +269,13 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
 #pragma unroll
             for (int r = 0; r < 4; ++r) y3[co][r] = bs[128 + 16 * co + 4 * g + r];
 #pragma unroll
-            for (int ci = 0; ci < 4; ++ci)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    y3[co] = mfma4(Wl[1][16 * co + c][16 * ci + 4 * g + r], hh[ci][r], y3[co]);
+            for (int ci = 0; ci < 4; ++ci) {
+                const float4 w = Wl4[1][16 * co + c][4 * ci + g];
+                y3[co] = mfma4(w.x, hh[ci][0], y3[co]);
+                y3[co] = mfma4(w.y, hh[ci][1], y3[co]);
+                y3[co] = mfma4(w.z, hh[ci][2], y3[co]);
+                y3[co] = mfma4(w.w, hh[ci][3], y3[co]);
+            }
         }
         // ---- layer 4: dW4 += g h3^T, db4 += g; dy3 = (W4^T g) o GELU'(y3)
 #pragma unroll
@@ -310,10 +324,14 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
             for (int it = 0; it < 4; ++it) {
                 v4f d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ot = 0; ot < 4; ++ot)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        d = mfma4(Wl[l][16 * ot + 4 * g + r][16 * it + c], dy[ot][r], d);
+                for (int ot = 0; ot < 4; ++ot) {
+                    // W'^T[16 it + c][16 ot + 4g + r] = W'[16 ot + 4g + r][16 it + c]
+                    const float4 w = WlT4[l][16 * it + c][4 * ot + g];
+                    d = mfma4(w.x, dy[ot][0], d);
+                    d = mfma4(w.y, dy[ot][1], d);
+                    d = mfma4(w.z, dy[ot][2], d);
+                    d = mfma4(w.w, dy[ot][3], d);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) nd[it][r] = d[r] * gelu_grad(yp[it][r]);
             }
