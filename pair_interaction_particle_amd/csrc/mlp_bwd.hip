@@ -162,7 +162,9 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
     __shared__ float tr[kMbWaves][2][64][17];
 
     const int T = P / kTile;
-    const int jet = blockIdx.x / T, I = T - 1 - (int)(blockIdx.x % T);
+    // the largest row tiles of every jet first (longest workgroups start early)
+    const int nj = (int)(gridDim.x / T);
+    const int jet = (int)(blockIdx.x % nj), I = T - 1 - (int)(blockIdx.x / nj);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
