@@ -89,8 +89,9 @@ __device__ __forceinline__ void to_tile(float (*Tb)[17], const v4f (&X)[4]) {
 // 16 ot + 4g + r, column 16 it + c.  Tile rows >= rmax and columns >= cmax
 // read as 0 (tile rows the block did not write).
 template <int kNo, int kNi>
-__device__ __forceinline__ void outer_reg(v4f (&A)[kNo * kNi], const float (*TA)[17],
-                                          const float (*TB)[17], int rmax, int cmax) {
+__device__ __forceinline__ void outer_reg(v4f (&A)[kNo * kNi], v4f (&R)[kNo],
+                                          const float (*TA)[17], const float (*TB)[17], int rmax,
+                                          int cmax) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
     float a[kNo][4], b[kNi][4];
 #pragma unroll
@@ -102,12 +103,17 @@ __device__ __forceinline__ void outer_reg(v4f (&A)[kNo * kNi], const float (*TA)
 #pragma unroll
         for (int s = 0; s < 4; ++s) b[t][s] = 16 * t + c < cmax ? TB[16 * t + c][4 * s + g] : 0.f;
 #pragma unroll
-    for (int ot = 0; ot < kNo; ++ot)
+    for (int ot = 0; ot < kNo; ++ot) {
 #pragma unroll
         for (int it = 0; it < kNi; ++it)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 A[kNi * ot + it] = mfma4(a[ot][s], b[it][s], A[kNi * ot + it]);
+        // the row sums over the pairs (the bias gradient): the same A
+        // operands against a column of ones; every column of R holds them
+#pragma unroll
+        for (int s = 0; s < 4; ++s) R[ot] = mfma4(a[ot][s], 1.0f, R[ot]);
+    }
 }
 
 // acc (row stride ld) += the register tiles of outer_reg, rows < rmax and
@@ -128,21 +134,17 @@ __device__ __forceinline__ void flush_reg(float *acc, int ld, const v4f (&A)[kNo
             }
 }
 
-// acc[16 t + 4g + r] += sum over the 16 lanes c of S[t][r] (lane (g, c)):
-// per-lane bias-gradient partial sums, reduced once per wave at the end
-// (read-add-write, as flush_reg).
+// acc[16 t + 4g + r] += R[t][r] for rows < rmax, from the lanes of column 0
+// (every column of the row-sum tiles of outer_reg holds the same sums)
 template <int kN>
-__device__ __forceinline__ void flush_rows(float *acc, const float (&S)[kN][4]) {
+__device__ __forceinline__ void flush_rows(float *acc, const v4f (&R)[kN], int rmax) {
     const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+    if (c != 0) return;
 #pragma unroll
     for (int t = 0; t < kN; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float v = S[t][r];
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-            if (c == 0) acc[16 * t + 4 * g + r] += v;
-        }
+        for (int r = 0; r < 4; ++r)
+            if (16 * t + 4 * g + r < rmax) acc[16 * t + 4 * g + r] += R[t][r];
 }
 
 template <int kPP>
@@ -198,17 +200,13 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
     const int nb = 16 * I + 9;
     // the gradients summed over this wave's blocks, in registers: weight
     // tiles of every layer, per-lane partial sums of the bias gradients
-    v4f gw1[4], gw2[16], gw3[16], gw4[4];
-    float sb1[4][4], sb2[4][4], sb3[4][4], sb4[2];
+    v4f gw1[4], gw2[16], gw3[16], gw4[4], gb1[4], gb2[4], gb3[4], gb4[1];
 #pragma unroll
     for (int t = 0; t < 16; ++t) gw2[t] = gw3[t] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        gw1[t] = gw4[t] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sb1[t][r] = sb2[t][r] = sb3[t][r] = 0.f;
-    }
-    sb4[0] = sb4[1] = 0.f;
+    for (int t = 0; t < 4; ++t)
+        gw1[t] = gw4[t] = gb1[t] = gb2[t] = gb3[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+    gb4[0] = (v4f){0.f, 0.f, 0.f, 0.f};
     for (int blk = wave; blk < nb; blk += kMbWaves) {
         int i, j;
         bool valid;
@@ -288,9 +286,7 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
 #pragma unroll
         for (int t = 0; t < 2; ++t) T0[4 * t + g][c] = gv[t];
         __builtin_amdgcn_wave_barrier();
-        outer_reg<1, 4>(gw4, T0, T1, 8, 64);
-        sb4[0] += gv[0];
-        sb4[1] += gv[1];
+        outer_reg<1, 4>(gw4, gb4, T0, T1, 8, 64);
         v4f dy[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -312,15 +308,8 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
             to_tile(T0, dy);
             to_tile(T1, hh);
             __builtin_amdgcn_wave_barrier();
-            if (l == 1) outer_reg<4, 4>(gw3, T0, T1, 64, 64);
-            else outer_reg<4, 4>(gw2, T0, T1, 64, 64);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (l == 1) sb3[t][r] += dy[t][r];
-                    else sb2[t][r] += dy[t][r];
-                }
+            if (l == 1) outer_reg<4, 4>(gw3, gb3, T0, T1, 64, 64);
+            else outer_reg<4, 4>(gw2, gb2, T0, T1, 64, 64);
             v4f nd[4];
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
@@ -345,11 +334,7 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
         to_tile(T0, dy);
         T1[g][c] = f;
         __builtin_amdgcn_wave_barrier();
-        outer_reg<4, 1>(gw1, T0, T1, 64, 4);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sb1[t][r] += dy[t][r];
+        outer_reg<4, 1>(gw1, gb1, T0, T1, 64, 4);
         __builtin_amdgcn_wave_barrier();
     }
     // Merge the waves' register sums into acc without atomics: the gradient
@@ -368,16 +353,10 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
             flush_reg<4, 1>(acc + kGW1, 4, gw1, 64, 4);
             flush_reg<1, 4>(acc + kGW4, 64, gw4, 8, 64);
         } else {
-            flush_rows<4>(acc + kGB1, sb1);
-            flush_rows<4>(acc + kGB2, sb2);
-            flush_rows<4>(acc + kGB3, sb3);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {  // db4[4t + g] (lane group g: head 4t + g)
-                float v = sb4[t];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
-                if (c == 0) acc[kGB4 + 4 * t + g] += v;
-            }
+            flush_rows<4>(acc + kGB1, gb1, 64);
+            flush_rows<4>(acc + kGB2, gb2, 64);
+            flush_rows<4>(acc + kGB3, gb3, 64);
+            flush_rows<1>(acc + kGB4, gb4, 8);
         }
         __syncthreads();
     }
