@@ -403,25 +403,35 @@ __device__ __forceinline__ v4i mfma64i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// 16 activations (h[c][r] = input 16c + 4g + r) -> int8 codes, byte 4c + r
+// 16 activations (h[c][r] = input 16c + 4g + r) -> int8 codes, byte 4c + r:
+// q = clamp(rint(h / S) + Z, -128, 127).  The clamp is one v_med3 (clamping
+// before the rounding gives the same code: the bounds are integers); adding
+// 1.5 * 2^23 rounds to the nearest integer, ties to even (the float32 sum
+// has a unit ulp there), and leaves the code's two's complement in the low
+// byte of the bit pattern; three byte permutes pack four codes.
 __device__ __forceinline__ v4i quant16(const v4f (&h)[4], float inv_s, float zp) {
     v4i out;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        uint32_t w = 0;
+        uint32_t b[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float q = fminf(fmaxf(__builtin_rintf(fmaf(h[c][r], inv_s, zp)), -128.0f), 127.0f);
-            w |= ((uint32_t)(int)q & 0xffu) << (8 * r);
+            const float x = __builtin_amdgcn_fmed3f(fmaf(h[c][r], inv_s, zp), -128.0f, 127.0f);
+            b[r] = __builtin_bit_cast(uint32_t, x + 12582912.0f);
         }
-        out[c] = (int)w;
+        // perm(hi, lo, sel): byte k of the result is byte sel_k of {hi:lo}
+        // (0..3 lo, 4..7 hi, 0x0c zero)
+        const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+        out[c] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
     return out;
 }
 
 // Two pair blocks through the int8 chain.  wl: the float32 layer-1 group;
-// w8: the int8 operands [op][lane]; deq / zs: per-channel S sw and Z sum Wq
-// of layers 2 (0..63), 3 (64..127), 4 (128..143, rows >= 8 zero).
+// w8: the int8 operands [op][lane]; deq / off: per channel S sw and
+// b' - S sw Z sum Wq of layers 2 (0..63), 3 (64..127), 4 (128..143, rows >= 8
+// zero), so that y = deq * sum + off.
 __device__ __forceinline__ void mlp2_int8(const float4 *__restrict__ wl,
                                           const v4i *__restrict__ w8,
                                           const float *__restrict__ deq,
@@ -460,18 +470,11 @@ __device__ __forceinline__ void mlp2_int8(const float4 *__restrict__ wl,
             const v4i aB = mfma64i8(w, xB, (v4i){0, 0, 0, 0});
             const int ch = 64 * layer + 16 * co + 4 * g;
             const v4f d = bias4(deq, ch), z = bias4(zs, ch);
-            v4f b;
-            if (layer < 2) {
-                b = bias4(bl, 64 * (layer + 1) + 16 * co + 4 * g);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) b[r] = (4 * g + r < kHeads) ? bl[192 + 4 * g + r] : 0.0f;
-            }
             v4f yA, yB;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                yA[r] = fmaf(d[r], (float)aA[r] - z[r], b[r]);
-                yB[r] = fmaf(d[r], (float)aB[r] - z[r], b[r]);
+                yA[r] = fmaf(d[r], (float)aA[r], z[r]);
+                yB[r] = fmaf(d[r], (float)aB[r], z[r]);
             }
             if (layer < 2) {
                 hA[co] = yA;
@@ -561,6 +564,8 @@ struct MlpLds {
         LdsCopy<kThreads, kI8 ? kW8Ops * 64 : 1, v4i> c8;
         LdsCopy<kThreads, kI8 ? kQ8Floats : 1, float> cq;
         float qs[3], qz[3];
+        // for the offset entries (second half of q8): the channel's sw and bias
+        float qw[decltype(cq)::kIt], qb[decltype(cq)::kIt];
         __device__ __forceinline__ void load(const float4 *__restrict__ w32,
                                              const v8bf *__restrict__ w16,
                                              const v8h *__restrict__ wx2,
@@ -581,6 +586,14 @@ struct MlpLds {
                     qs[l] = ia->s[l];
                     qz[l] = ia->zp[l];
                 }
+                // channel ch's folded bias is b' at 64 + ch (b2' | b3' | b4
+                // sit at 64..199), 0 for the unused layer-4 rows >= 8
+#pragma unroll
+                for (int it = 0; it < decltype(cq)::kIt; ++it) {
+                    const int ch = (threadIdx.x + it * kThreads) % (kQ8Floats / 2);
+                    qw[it] = ia->q8[ch];
+                    qb[it] = ch < 136 ? bias[64 + ch] : 0.0f;
+                }
             }
         }
         __device__ __forceinline__ void store(const MlpLds &M) const {
@@ -593,14 +606,16 @@ struct MlpLds {
             if constexpr (kMode == kMlpBf16) c16.store(M.wb);
             if constexpr (kI8) {
                 c8.store(M.w8);
-                // deq = S sw and zs = Z sum Wq per output channel (layer by
-                // channel range: 0..63 layer 2, 64..127 layer 3, 128.. layer 4)
+                // deq = S sw and off = b' - S sw Z sum Wq per output channel
+                // (channels 0..63 layer 2, 64..127 layer 3, 128.. layer 4)
 #pragma unroll
                 for (int it = 0; it < decltype(cq)::kIt; ++it) {
                     const int i = threadIdx.x + it * kThreads;
                     if (i >= kQ8Floats) continue;
                     const int ch = i % (kQ8Floats / 2), l = ch < 64 ? 0 : (ch < 128 ? 1 : 2);
-                    M.deq[i] = cq.v[it] * (i < kQ8Floats / 2 ? qs[l] : qz[l]);
+                    M.deq[i] = i < kQ8Floats / 2
+                                   ? cq.v[it] * qs[l]
+                                   : fmaf(-(qw[it] * qs[l]), cq.v[it] * qz[l], qb[it]);
                 }
             }
         }
