@@ -17,9 +17,10 @@
 // per key block dP^T = V dO^T, dS, the dU strip (one 16-byte store per lane
 // and block, the forward's U read layout), dQ^T += K^T dS^T in registers, and
 // P and dS transposed through a wave-private LDS tile into the operand layout
-// of dV = P^T dO and dK = dS^T Q, whose 16x16 tiles stay in registers.  The
-// waves then merge their tiles into the LDS accumulators in 8 barrier-
-// separated phases (wave w adds key block (j + w) mod 8 in phase j): plain
+// of dV = P^T dO and dK = dS^T Q, whose 16x16 tiles stay in registers for
+// two key blocks at a time.  The waves then merge their tiles into the LDS
+// accumulators in 8 barrier-separated phases (wave w adds key block
+// (j + w) mod 8 in phase j when it holds that block's tile): plain
 // read-add-write, no atomics (LDS float atomics cost several cycles per
 // lane here), and a fixed order of additions, so dK and dV are the same bit
 // for bit on every run.  All products are float32 MFMA
@@ -39,9 +40,14 @@ __device__ __forceinline__ float4 keep4(bool keep, float4 x) {
 }
 
 constexpr int kBwdThreads = 64 * kBwdWaves;
+// key blocks whose dK / dV tiles a wave holds between two merges (2: 16
+// registers, so that the P <= 128 kernel fits in 128 VGPRs without a spill
+// and two workgroups share a CU; 4 spilled 32 bytes, 8 held one per CU)
+constexpr int kMg = 2;
+static_assert(kBwdWaves == 8 && kMg <= 8, "merge phases map 8 waves onto key blocks mod 8");
 
 template <int kT>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_bwd_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kT <= 8 ? 4 : 2))) void attention_bwd_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     const float *__restrict__ U, const uint8_t *__restrict__ mask,
     const float *__restrict__ dO, int H, int P, float scale, float *__restrict__ dQ,
@@ -177,16 +183,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             // lane (g, c) holds O[query c][4g + r]
             Dq = xsum16(o[0] * gr4.x + o[1] * gr4.y + o[2] * gr4.z + o[3] * gr4.w);
         }
-        // ---- pass 3, 8 key blocks at a time: dP, dS, dU, dQ, and this
+        // ---- pass 3, kMg key blocks at a time: dP, dS, dU, dQ, and this
         // query block's dK / dV tiles, kept in registers, then merged into
-        // LDS without atomics: in merge phase j wave w adds its tile of key
-        // block (j + w) mod 8, so the 8 waves touch 8 different tiles.
+        // LDS without atomics: in merge phase j (of 8) wave w adds its tile
+        // of key block (j + w) mod 8 when that is below kMg, so no two waves
+        // touch one tile in a phase and each wave visits each tile once.
         v4f dq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h0 = 0; h0 < kT; h0 += 8) {
-            v4f avs[8], aks[8];
+        for (int h0 = 0; h0 < kT; h0 += kMg) {
+            v4f avs[kMg], aks[kMg];
 #pragma unroll
-            for (int kl = 0; kl < 8; ++kl) {
+            for (int kl = 0; kl < kMg; ++kl) {
                 const int kb = h0 + kl, k0 = kb * kTile;
                 avs[kl] = aks[kl] = (v4f){0.f, 0.f, 0.f, 0.f};
                 if (!act || kb >= T) continue;
@@ -222,7 +229,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             for (int j = 0; j < 8; ++j) {
                 const int kl_w = (j + wave) & 7;
 #pragma unroll
-                for (int kl = 0; kl < 8; ++kl) {
+                for (int kl = 0; kl < kMg; ++kl) {
                     const int kb = h0 + kl, k0 = kb * kTile;
                     if (kl != kl_w || !act || kb >= T) continue;
 #pragma unroll
