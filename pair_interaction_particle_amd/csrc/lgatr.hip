@@ -396,9 +396,9 @@ pip_status pip_lgatr_equilinear_create(const float *w, const float *s2mv, const 
         e = hipMemcpy(h->wpk, pk.data(), pk.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(h->bias, bk.data(), bk.size() * sizeof(float), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        hipFree(h->wpk);
-        hipFree(h->bias);
+    if (e != hipSuccess) {  // (the first error is the one reported)
+        if (h->wpk) (void)hipFree(h->wpk);
+        if (h->bias) (void)hipFree(h->bias);
         delete h;
         return PIP_ERR_HIP;
     }
