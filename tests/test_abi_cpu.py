@@ -186,3 +186,12 @@ def test_packed_validation(L):
     assert o(None, 3, A16, None) == NULL
     assert o(A16, -1, A16, None) == SHAPE
     assert o(A16, 3, A16 + 4, None) == ALIGN
+
+
+def test_pair_mlp_backward_workspace_bytes(L):
+    # one slot of PIP_PAIR_MLP_FOLDED_GRADS floats per (jet, row tile)
+    # workgroup, then one per 32 slots for the fixed-order reduction
+    f = L.pip_pair_mlp_backward_workspace_bytes
+    for B, P in ((1, 16), (128, 128), (3, 256), (33, 48)):
+        slots = B * (P // 16)
+        assert f(B, P) == (slots + (slots + 31) // 32) * 9160 * 4
