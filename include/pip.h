@@ -223,8 +223,9 @@ pip_status pip_pair_bias_attention_backward(const void *Q, const void *K, const 
                                             void *dV, void *dU, int dtype, void *stream);
 
 /* Bytes of workspace pip_pair_mlp_backward needs: one slot of
- * PIP_PAIR_MLP_FOLDED_GRADS floats per workgroup (B * P/16 slots), then one
- * per 32 slots for the partial sums of the fixed-order reduction. */
+ * PIP_PAIR_MLP_FOLDED_GRADS floats per (jet, row tile of 16) (B * P/16
+ * slots), then one per 32 slots for the partial sums of the fixed-order
+ * reduction, then one int per slot (the slots to recompute in float32). */
 size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
 
 /* Gradient of L with respect to the folded pair-MLP parameters, for dL/dU =
@@ -234,8 +235,12 @@ size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
  * dU's padded entries are never read into the result.  grad (device,
  * PIP_PAIR_MLP_FOLDED_GRADS floats) has pip_pair_mlp_fold's layout:
  *   dW1' (64*4) dW2' (64*64) dW3' (64*64) dW4 (8*64) | db1' db2' db3' (64) db4 (8)
- * The MLP runs in float32 on the matrix cores (GELU in its erf form, Phi
- * evaluated to 7.5e-8).
+ * GELU in its erf form, Phi evaluated to 7.5e-8.  When the handle's weights
+ * fit fp16 (as for the fp16 x 2 forward), the products run on the fp16
+ * matrix cores with every float32 factor split into two fp16 halves
+ * (relative error ~2^-22 per product) and g scaled by a power of two per
+ * round of 128 pairs; a slot whose sums leave the fp16 range is recomputed
+ * with float32 products, as are all slots otherwise.
  * workspace: pip_pair_mlp_backward_workspace_bytes(B, P) bytes, scratch
  * (overwritten; calls sharing one on different streams race).  Every sum
  * is taken in a fixed order: the result is the same bit for bit on every

@@ -213,6 +213,22 @@ pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **ou
             for (int j = 0; j < 8; ++j)
                 put_x2(pip::kW16L4 + (s * 64 + l) * 8 + j,
                        (l % 16 < 8) ? W4[(l % 16) * 64 + chan(s, l / 16, j)] : 0.0f);
+    // the transposed operands of layers 2 and 3 for the backward chain:
+    // operand (t, it, s) of lane l, slot j: W'[chan(s, l/16, j)][16 it + l%16]
+    constexpr size_t kWt = 16 * 64 * 8;
+    std::vector<uint16_t> ptx2(2 * kWt);
+    for (int t = 0; t < 2; ++t)
+        for (int it = 0; it < 4; ++it)
+            for (int s = 0; s < 2; ++s)
+                for (int l = 0; l < 64; ++l)
+                    for (int j = 0; j < 8; ++j) {
+                        const float wv = Wh[t][chan(s, l / 16, j) * 64 + 16 * it + l % 16];
+                        const _Float16 hi = (_Float16)wv;
+                        const _Float16 lo = (_Float16)(wv - (float)hi);
+                        const size_t at = (((size_t)t * 8 + it * 2 + s) * 64 + l) * 8 + j;
+                        ptx2[at] = __builtin_bit_cast(uint16_t, hi);
+                        ptx2[kWt + at] = __builtin_bit_cast(uint16_t, lo);
+                    }
 
     // int8 weights of layers 2, 3, 4 from the float64 fold: per output channel
     // sw = max |W'| / 127 (1 for an all-zero row), Wq = clamp(rint(W' / sw),
@@ -255,12 +271,14 @@ pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **ou
     m->w32 = nullptr;
     m->w16 = nullptr;
     m->wx2 = nullptr;
+    m->wtx2 = nullptr;
     m->bias = nullptr;
     m->wplain = nullptr;
     hipError_t e = hipGetDevice(&m->device);
     if (e == hipSuccess) e = hipMalloc((void **)&m->w32, p32.size() * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void **)&m->w16, p16.size() * sizeof(uint16_t));
     if (e == hipSuccess) e = hipMalloc((void **)&m->wx2, px2.size() * sizeof(uint16_t));
+    if (e == hipSuccess) e = hipMalloc((void **)&m->wtx2, ptx2.size() * sizeof(uint16_t));
     if (e == hipSuccess) e = hipMalloc((void **)&m->bias, b.size() * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void **)&m->wplain, w.size() * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void **)&m->w8, p8.size());
@@ -277,6 +295,9 @@ pip_status pip_pair_mlp_create(const pip_pair_mlp_params *raw, pip_pair_mlp **ou
     if (e == hipSuccess)
         e = hipMemcpy(m->wx2, px2.data(), px2.size() * sizeof(uint16_t), hipMemcpyHostToDevice);
     if (e == hipSuccess)
+        e = hipMemcpy(m->wtx2, ptx2.data(), ptx2.size() * sizeof(uint16_t),
+                      hipMemcpyHostToDevice);
+    if (e == hipSuccess)
         e = hipMemcpy(m->bias, b.data(), b.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         pip_pair_mlp_destroy(m);
@@ -292,6 +313,7 @@ pip_status pip_pair_mlp_destroy(pip_pair_mlp *m) {
     if (m->w32 && (e2 = hipFree(m->w32)) != hipSuccess) e = e2;
     if (m->w16 && (e2 = hipFree(m->w16)) != hipSuccess) e = e2;
     if (m->wx2 && (e2 = hipFree(m->wx2)) != hipSuccess) e = e2;
+    if (m->wtx2 && (e2 = hipFree(m->wtx2)) != hipSuccess) e = e2;
     if (m->bias && (e2 = hipFree(m->bias)) != hipSuccess) e = e2;
     if (m->wplain && (e2 = hipFree(m->wplain)) != hipSuccess) e = e2;
     if (m->w8 && (e2 = hipFree(m->w8)) != hipSuccess) e = e2;

@@ -151,7 +151,10 @@ template <int kPP>
 __global__ __launch_bounds__(kMbThreads) __attribute__((amdgpu_waves_per_eu(1))) void
 mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
                const float *__restrict__ wplain, const float *__restrict__ bias,
-               const float *__restrict__ dU, float *__restrict__ partial) {
+               const float *__restrict__ dU, float *__restrict__ partial,
+               const int *__restrict__ redo) {
+    // with a redo list, only the slots the fp16 x 2 kernel flagged are computed
+    if (redo && redo[blockIdx.x] == 0) return;
     // W2', W3' row-major and transposed (rows padded to 68 floats: 16-byte
     // aligned, so each lane reads its four k-steps of an operand at once)
     __shared__ float4 Wl4[2][64][17];
@@ -364,6 +367,399 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
     for (int e = tid; e < kGradFloats; e += kMbThreads) out[e] = acc[e];
 }
 
+// ---------------------------------------------------------------- fp16 x 2 kernel
+// The same gradient with every large product on the fp16 matrix cores
+// (v_mfma_f32_16x16x32_f16), each float32 factor carried as hi = fp16(x),
+// lo = fp16(x - hi) and x w = x_hi w_hi + x_hi w_lo + x_lo w_hi (relative
+// error ~2^-22 per product, float32 accumulation), as in the forward chain.
+// One 512-thread workgroup per compute unit walks (jet, row tile) slots; a
+// slot's pair blocks go out in rounds, one block per wave.  Per round:
+//   * every wave runs its block's forward (hidden states feature-major in
+//     registers) and the backward chain dy3 -> dy2 -> dy1 (W'^T operands
+//     packed on the host like the forward ones);
+//   * each activation the weight gradients need (h1, h2, h3, dy1, dy2, dy3,
+//     g, the features) is staged in LDS pair-major as fp16 hi / lo halves,
+//     so a lane reads 8 consecutive pairs of one feature as an MFMA operand
+//     with the round's 128 pairs as the K dimension;
+//   * the gradient tiles are split among the waves (two or three 16x16 tiles
+//     of dW3' and of dW2', one of dW1' or dW4, the bias tiles as products
+//     against a column of ones), so each wave keeps only its own tiles.
+// g is scaled per round by a power of two 2^e so that max |g| lies in [1, 2)
+// (the backward chain is linear in g, so every dy carries the same factor);
+// the accumulators hold their sums in units of 2^e and are rescaled exactly
+// when e changes.  A workgroup whose sums come out non-finite (an activation
+// or a dy beyond the fp16 range) flags its slot, and the float32 kernel above
+// recomputes that slot.  Every sum has a fixed order: the result is the same
+// bit for bit on every run.
+constexpr int kXWaves = 8;
+constexpr int kXThreads = 64 * kXWaves;
+constexpr int kXPairs = 16 * kXWaves;  // pairs per round: one block per wave
+constexpr int kXPitch = kXPairs + 8;   // halves per staged row (272 bytes: rows 4 banks apart)
+constexpr int kXOps = 16;              // fp16 operands of layers 2 and 3 (per half)
+
+// The staged activations come first: every read of them is then one base
+// register plus an immediate offset below 64 KiB.
+template <int kPP>
+struct XLds {
+    _Float16 xa[2][64][kXPitch];  // staged activations: [hi | lo][feature][pair]
+    _Float16 xb[2][64][kXPitch];
+    _Float16 gs[2][8][kXPitch];  // g per head
+    _Float16 fs[2][4][kXPitch];  // the pair features
+    v8h wf[2][kXOps * 64];  // W' of layers 2, 3 as forward operands, hi | lo, [op][lane]
+    v8h wt[2][kXOps * 64];  // W'^T of layers 2, 3 as operands of the backward chain
+    float4 w1[64];          // layer 1 (float32, K = 4)
+    float w4[8][64];        // layer 4 (float32)
+    float bias[200];
+    float emax[kXWaves];
+    int nblk, bad;
+    uint8_t blk[256];
+    PartLds<kPP> part;
+};
+static_assert(sizeof(XLds<256>) <= 160 * 1024, "one workgroup's LDS");
+
+// h = GELU(y) and d = GELU'(y), sharing Phi
+__device__ __forceinline__ void gelu_both(const v4f (&y)[4], v4f (&h)[4], v4f (&d)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = y[t][r], ph = normal_cdf(x);
+            h[t][r] = x * ph;
+            d[t][r] = fmaf(x * 0.39894228040143268f,
+                           __builtin_amdgcn_exp2f(-0.72134752044448170f * x * x), ph);
+        }
+}
+
+// the hi / lo operands of 16 feature-major values (slot j of half s holds
+// feature 16 (2s + j/4) + 4g + j%4, the order of the chain's B operands)
+__device__ __forceinline__ void split16(const v4f (&x)[4], v8h (&hi)[2], v8h (&lo)[2]) {
+    split_f16(x[0], x[1], hi[0], lo[0]);
+    split_f16(x[2], x[3], hi[1], lo[1]);
+}
+
+// X[hi | lo][feature][pair p] = this lane's 16 split values
+__device__ __forceinline__ void stage16(_Float16 (*X)[64][kXPitch], const v8h (&hi)[2],
+                                        const v8h (&lo)[2], int p, int g) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int f = 16 * (2 * s + (j >> 2)) + 4 * g + (j & 3);
+            X[0][f][p] = hi[s][j];
+            X[1][f][p] = lo[s][j];
+        }
+}
+
+// operand of K step q: row `row`, pairs 32q + 8g .. 32q + 8g + 7
+__device__ __forceinline__ v8h xop(const _Float16 (*X)[kXPitch], int row, int q, int g) {
+    return *(const v8h *)&X[row][32 * q + 8 * g];
+}
+
+// acc += A B^T over the round's pairs with the three-term split
+__device__ __forceinline__ v4f mfma_x3(v8h ah, v8h al, v8h bh, v8h bl, v4f acc) {
+    acc = mfma32h(ah, bl, acc);
+    acc = mfma32h(al, bh, acc);
+    return mfma32h(ah, bh, acc);
+}
+
+__device__ __forceinline__ void scale_tile(v4f &a, int e) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = __builtin_amdgcn_ldexpf(a[r], e);
+}
+
+__device__ __forceinline__ bool tile_finite(const v4f &a) {
+    bool ok = true;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ok = ok && __builtin_isfinite(a[r]);
+    return ok;
+}
+
+template <int kPP>
+__global__ __launch_bounds__(kXThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B, int P,
+                  const v8h *__restrict__ wx2, const v8h *__restrict__ wtx2,
+                  const float4 *__restrict__ w32, const float *__restrict__ wplain,
+                  const float *__restrict__ bias, const float *__restrict__ dU,
+                  float *__restrict__ partial, int *__restrict__ redo) {
+    __shared__ XLds<kPP> L;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int T = P / kTile, nslots = B * T;
+    const size_t plane = (size_t)P * P;
+
+    // weights, once per workgroup (wx2: 18 hi operands then 18 lo ones)
+    for (int e = tid; e < 2 * kXOps * 64; e += kXThreads) {
+        const int h = e / (kXOps * 64), k = e % (kXOps * 64);
+        L.wf[h][k] = wx2[h * 18 * 64 + k];
+        L.wt[h][k] = wtx2[e];
+    }
+    if (tid < 64) L.w1[tid] = w32[tid];
+    for (int e = tid; e < 8 * 64; e += kXThreads) L.w4[e >> 6][e & 63] = wplain[8448 + e];
+    if (tid < 200) L.bias[tid] = bias[tid];
+
+    const v8h ones = {1, 1, 1, 1, 1, 1, 1, 1}, zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    // the gradient tiles this wave owns (see the write-out at the end)
+    const int ro = wave >> 1, ci0 = 2 * (wave & 1);
+    const bool odd = (wave & 1) != 0;
+
+    // slots in snake order over passes of gridDim.x, largest row tiles first
+    const int G = (int)gridDim.x;
+    for (int pass = 0; pass * G < nslots; ++pass) {
+        const int slot = pass * G + ((pass & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+        if (slot >= nslots) continue;  // uniform across the workgroup
+        const int jet = slot % B, I = T - 1 - slot / B;
+        const int ncols = (I + 1) * kTile;
+        if (tid < ncols) {
+            const size_t idx = (size_t)jet * P + tid;
+            const float4 pv = p4[idx];
+            const int real = mask[idx] != 0;
+            stage_particle(L.part, tid, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
+        }
+        if (tid == 0) L.bad = 0;
+        __syncthreads();
+        // the blocks with at least one real pair, in order
+        if (wave == 0) {
+            const int nb = 16 * I + 9;
+            int base = 0;
+            for (int ch = 0; ch < 4; ++ch) {
+                const int b = 64 * ch + lane;
+                bool v = false;
+                if (b < 16 * I) {
+                    const int i = I * kTile + (b & 15), J = b >> 4;
+                    bool any = false;
+                    for (int q = 0; q < 16; ++q) any = any || L.part.real[J * kTile + q];
+                    v = L.part.real[i] && any;
+                } else if (b < nb) {
+                    for (int q = 0; q < 16; ++q) {
+                        int ti, tj;
+                        const bool in = tri_pair(b - 16 * I, q, ti, tj);
+                        v = v || (in && L.part.real[I * kTile + ti] && L.part.real[I * kTile + tj]);
+                    }
+                }
+                const uint64_t m = __ballot(v);
+                if (v) L.blk[base + __popcll(m & ((1ull << lane) - 1))] = (uint8_t)b;
+                base += __popcll(m);
+            }
+            if (lane == 0) L.nblk = base;
+        }
+        __syncthreads();
+        const int nr = (L.nblk + kXWaves - 1) / kXWaves;
+        const float *dUj = dU + (size_t)jet * kHeads * plane;
+
+        v4f a3[2], a2[2], b3, b2, ax, b4;
+        a3[0] = a3[1] = a2[0] = a2[1] = b3 = b2 = ax = b4 = (v4f){0.f, 0.f, 0.f, 0.f};
+        int ecur = 0;
+        // the block state carried from one round's preparation to its phases
+        v8h h1h[2], h1l[2], h2h[2], h2l[2], h3h[2], h3l[2];
+        v4f d1[4], d2[4], dy[4];
+        float gv[2], fv;
+
+        for (int r = 0; r <= nr; ++r) {
+            // lane-dependent addresses are recomputed every round rather than
+            // held in registers across the loop
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int gq = ln >> 4, cq = ln & 15, pq = 16 * wave + cq;
+            if (r > 0) {
+                // [A] the round's scale; stage dy3 and h2
+                float M = L.emax[0];
+#pragma unroll
+                for (int k = 1; k < kXWaves; ++k) M = fmaxf(M, L.emax[k]);
+                int e = 0;
+                if (M > 0.f && M <= 3.0e38f) e = 1 - __builtin_amdgcn_frexp_expf(M);
+                if (e != ecur) {
+                    const int de = e - ecur;
+                    scale_tile(a3[0], de), scale_tile(a3[1], de), scale_tile(a2[0], de);
+                    scale_tile(a2[1], de), scale_tile(b3, de), scale_tile(b2, de);
+                    scale_tile(ax, de), scale_tile(b4, de);
+                    ecur = e;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) scale_tile(dy[t], e);
+                gv[0] = __builtin_amdgcn_ldexpf(gv[0], e);
+                gv[1] = __builtin_amdgcn_ldexpf(gv[1], e);
+                v8h dh[2], dl[2];
+                split16(dy, dh, dl);
+                stage16(L.xa, dh, dl, pq, gq);
+                stage16(L.xb, h2h, h2l, pq, gq);
+                __syncthreads();
+                // [D] dW3' (rows ro, column tiles ci0, ci0 + 1), db3' (odd waves); dy2
+#pragma unroll
+                for (int q = 0; q < kXPairs / 32; ++q) {
+                    const v8h ah = xop(L.xa[0], 16 * ro + cq, q, gq), al = xop(L.xa[1], 16 * ro + cq, q, gq);
+#pragma unroll
+                    for (int k = 0; k < 2; ++k)
+                        a3[k] = mfma_x3(ah, al, xop(L.xb[0], 16 * (ci0 + k) + cq, q, gq),
+                                        xop(L.xb[1], 16 * (ci0 + k) + cq, q, gq), a3[k]);
+                    if (odd) b3 = mfma32h(al, ones, mfma32h(ah, ones, b3));
+                }
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const v4f t = mfma_x2(L.wt[0], L.wt[1], 8 + 2 * it, ln, dh, dl,
+                                          (v4f){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) dy[it][k] = t[k] * d2[it][k];
+                }
+                split16(dy, dh, dl);
+                __syncthreads();
+                // [E] stage dy2 and h1
+                stage16(L.xa, dh, dl, pq, gq);
+                stage16(L.xb, h1h, h1l, pq, gq);
+                __syncthreads();
+                // [F] dW2', db2'; dy1
+#pragma unroll
+                for (int q = 0; q < kXPairs / 32; ++q) {
+                    const v8h ah = xop(L.xa[0], 16 * ro + cq, q, gq), al = xop(L.xa[1], 16 * ro + cq, q, gq);
+#pragma unroll
+                    for (int k = 0; k < 2; ++k)
+                        a2[k] = mfma_x3(ah, al, xop(L.xb[0], 16 * (ci0 + k) + cq, q, gq),
+                                        xop(L.xb[1], 16 * (ci0 + k) + cq, q, gq), a2[k]);
+                    if (odd) b2 = mfma32h(al, ones, mfma32h(ah, ones, b2));
+                }
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const v4f t = mfma_x2(L.wt[0], L.wt[1], 2 * it, ln, dh, dl,
+                                          (v4f){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) dy[it][k] = t[k] * d1[it][k];
+                }
+                split16(dy, dh, dl);
+                __syncthreads();
+                // [G] stage dy1, h3, g and the features
+                stage16(L.xa, dh, dl, pq, gq);
+                stage16(L.xb, h3h, h3l, pq, gq);
+                {
+                    v4h qh, ql;
+                    split4_f16(make_float4(gv[0], gv[1], fv, 0.f), qh, ql);
+                    L.gs[0][gq][pq] = qh[0], L.gs[1][gq][pq] = ql[0];
+                    L.gs[0][4 + g][pq] = qh[1], L.gs[1][4 + g][pq] = ql[1];
+                    L.fs[0][gq][pq] = qh[2], L.fs[1][gq][pq] = ql[2];
+                }
+                __syncthreads();
+                // [H] dW1' | db1' (waves 4..7: rows 16 (wave - 4)), dW4 (waves 0..3:
+                // column tile `wave`), db4 (wave 0)
+                if (wave >= 4) {
+                    const int rw = 16 * (wave - 4) + cq, fr = min(cq, 3);
+#pragma unroll
+                    for (int q = 0; q < kXPairs / 32; ++q) {
+                        v8h fh = xop(L.fs[0], fr, q, gq), fl = xop(L.fs[1], fr, q, gq);
+                        if (cq >= 4) fh = (cq == 4) ? ones : zero8, fl = zero8;
+                        ax = mfma_x3(xop(L.xa[0], rw, q, gq), xop(L.xa[1], rw, q, gq), fh, fl, ax);
+                    }
+                } else {
+                    const int gr = min(cq, 7);
+#pragma unroll
+                    for (int q = 0; q < kXPairs / 32; ++q) {
+                        v8h gh = xop(L.gs[0], gr, q, gq), gl = xop(L.gs[1], gr, q, gq);
+                        if (cq >= 8) gh = zero8, gl = zero8;
+                        ax = mfma_x3(gh, gl, xop(L.xb[0], 16 * wave + cq, q, gq),
+                                     xop(L.xb[1], 16 * wave + cq, q, gq), ax);
+                        if (wave == 0) b4 = mfma32h(gl, ones, mfma32h(gh, ones, b4));
+                    }
+                }
+            }
+            if (r < nr) {
+                // prepare round r: the block, g, the features, the forward and dy3
+                const int bi = kXWaves * r + wave < L.nblk ? L.blk[kXWaves * r + wave] : -1;
+                int i = I * kTile, j = I * kTile;
+                bool valid = false;
+                if (bi >= 0 && bi < 16 * I) {
+                    i = I * kTile + (bi & 15);
+                    j = (bi >> 4) * kTile + cq;
+                    valid = true;
+                } else if (bi >= 0) {
+                    int ti, tj;
+                    valid = tri_pair(bi - 16 * I, ln, ti, tj);
+                    i = I * kTile + ti;
+                    j = I * kTile + tj;
+                }
+                valid = valid && L.part.real[i] && L.part.real[j];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int h = 4 * t + gq;
+                    const float x = dUj[h * plane + (size_t)i * P + j];
+                    const float y = dUj[h * plane + (size_t)j * P + i];
+                    gv[t] = valid ? (i != j ? x + y : x) : 0.f;
+                }
+                fv = valid ? pair_feature(L.part, i, j, gq) : 0.f;
+                float m = fmaxf(fabsf(gv[0]), fabsf(gv[1]));
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+                if (lane == 0) L.emax[wave] = m;
+
+                v4f y[4], h[4];
+                {
+                    const float4 w = L.w1[ln];
+                    const float w1[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) y[t] = mfma4(w1[t], fv, bias4(L.bias, 16 * t + 4 * gq));
+                }
+                gelu_both(y, h, d1);
+                split16(h, h1h, h1l);
+#pragma unroll
+                for (int co = 0; co < 4; ++co)
+                    y[co] = mfma_x2(L.wf[0], L.wf[1], 2 * co, ln, h1h, h1l,
+                                    bias4(L.bias, 64 + 16 * co + 4 * gq));
+                gelu_both(y, h, d2);
+                split16(h, h2h, h2l);
+#pragma unroll
+                for (int co = 0; co < 4; ++co)
+                    y[co] = mfma_x2(L.wf[0], L.wf[1], 8 + 2 * co, ln, h2h, h2l,
+                                    bias4(L.bias, 128 + 16 * co + 4 * gq));
+                v4f d3[4];
+                gelu_both(y, h, d3);
+                split16(h, h3h, h3l);
+                // dy3 = (W4^T g) o GELU'(y3), before the round's scale
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) d = mfma4(L.w4[4 * t + gq][16 * it + cq], gv[t], d);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) dy[it][k] = d[k] * d3[it][k];
+                }
+            }
+            __syncthreads();
+        }
+
+        // write this wave's tiles (sums back to unit scale) and flag non-finite ones
+        float *out = partial + (size_t)slot * kGradFloats;
+        const int ue = -ecur;
+        int lo_ = lane;
+        asm volatile("" : "+v"(lo_));
+        const int go = lo_ >> 4, co_ = lo_ & 15;
+        bool ok = tile_finite(a3[0]) && tile_finite(a3[1]) && tile_finite(a2[0]) &&
+                  tile_finite(a2[1]) && tile_finite(ax);
+        if (odd) ok = ok && tile_finite(b3) && tile_finite(b2);
+        if (wave == 0) ok = ok && tile_finite(b4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * ro + 4 * go + r;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                out[kGW3 + row * 64 + 16 * (ci0 + k) + co_] = __builtin_amdgcn_ldexpf(a3[k][r], ue);
+                out[kGW2 + row * 64 + 16 * (ci0 + k) + co_] = __builtin_amdgcn_ldexpf(a2[k][r], ue);
+            }
+            if (odd && co_ == 0) {
+                out[kGB3 + row] = __builtin_amdgcn_ldexpf(b3[r], ue);
+                out[kGB2 + row] = __builtin_amdgcn_ldexpf(b2[r], ue);
+            }
+            if (wave >= 4) {
+                const int o = 16 * (wave - 4) + 4 * go + r;
+                if (co_ < 4) out[kGW1 + o * 4 + co_] = __builtin_amdgcn_ldexpf(ax[r], ue);
+                else if (co_ == 4) out[kGB1 + o] = __builtin_amdgcn_ldexpf(ax[r], ue);
+            } else if (go < 2) {
+                out[kGW4 + (4 * go + r) * 64 + 16 * wave + co_] = __builtin_amdgcn_ldexpf(ax[r], ue);
+                if (wave == 0 && co_ == 0) out[kGB4 + 4 * go + r] = __builtin_amdgcn_ldexpf(b4[r], ue);
+            }
+        }
+        if (!__all(ok) && lane == 0) L.bad = 1;
+        __syncthreads();
+        if (tid == 0) redo[slot] = L.bad;
+    }
+}
+
 // grad[e] = sum over the workgroup slots w = 0 .. nslots-1 of partial[w][e],
 // in a fixed order: chunk k = blockIdx.y of kRedChunk consecutive slots is
 // summed in slot order (its loads issued together) into chunk[k][e], then the
@@ -396,10 +792,12 @@ __global__ __launch_bounds__(256) void mlp_bwd_final_kernel(const float *__restr
     grad[e] = s;
 }
 
-// one slot per (jet, row tile) workgroup, then one chunk sum per kRedChunk slots
+// one slot per (jet, row tile), then one chunk sum per kRedChunk slots, then
+// the fp16 x 2 kernel's redo flag per slot
 size_t mlp_bwd_workspace(int B, int P) {
     const size_t nslots = (size_t)B * (P / kTile);
-    return (nslots + (nslots + kRedChunk - 1) / kRedChunk) * kGradFloats * sizeof(float);
+    return (nslots + (nslots + kRedChunk - 1) / kRedChunk) * kGradFloats * sizeof(float) +
+           nslots * sizeof(int);
 }
 
 hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P,
@@ -412,14 +810,33 @@ hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P
         hipLaunchKernelGGL(mlp_bwd_final_kernel, rg, dim3(256), 0, s, partial, 0, grad);
         return hipGetLastError();
     }
-    if (P <= 128)
-        hipLaunchKernelGGL(mlp_bwd_kernel<128>, dim3((unsigned)(B * T)), dim3(kMbThreads), 0, s,
-                           (const float4 *)p4, mask, P, m->wplain, m->bias, dU, partial);
-    else
-        hipLaunchKernelGGL(mlp_bwd_kernel<256>, dim3((unsigned)(B * T)), dim3(kMbThreads), 0, s,
-                           (const float4 *)p4, mask, P, m->wplain, m->bias, dU, partial);
     const int nslots = B * T, nchunks = (nslots + kRedChunk - 1) / kRedChunk;
     float *chunk = partial + (size_t)nslots * kGradFloats;
+    int *redo = nullptr;
+    if (m->f16ok) {
+        // the fp16 x 2 kernel over every slot, then the float32 kernel for the
+        // slots it flagged
+        redo = (int *)(chunk + (size_t)nchunks * kGradFloats);
+        const dim3 grid((unsigned)min(nslots, cu_count()));
+        if (P <= 128)
+            hipLaunchKernelGGL(mlp_bwd_x2_kernel<128>, grid, dim3(kXThreads), 0, s,
+                               (const float4 *)p4, mask, B, P, (const v8h *)m->wx2,
+                               (const v8h *)m->wtx2, (const float4 *)m->w32, m->wplain, m->bias,
+                               dU, partial, redo);
+        else
+            hipLaunchKernelGGL(mlp_bwd_x2_kernel<256>, grid, dim3(kXThreads), 0, s,
+                               (const float4 *)p4, mask, B, P, (const v8h *)m->wx2,
+                               (const v8h *)m->wtx2, (const float4 *)m->w32, m->wplain, m->bias,
+                               dU, partial, redo);
+    }
+    if (P <= 128)
+        hipLaunchKernelGGL(mlp_bwd_kernel<128>, dim3((unsigned)nslots), dim3(kMbThreads), 0, s,
+                           (const float4 *)p4, mask, P, m->wplain, m->bias, dU, partial,
+                           (const int *)redo);
+    else
+        hipLaunchKernelGGL(mlp_bwd_kernel<256>, dim3((unsigned)nslots), dim3(kMbThreads), 0, s,
+                           (const float4 *)p4, mask, P, m->wplain, m->bias, dU, partial,
+                           (const int *)redo);
     hipLaunchKernelGGL(mlp_bwd_reduce_kernel, dim3(rg.x, (unsigned)nchunks), dim3(256), 0, s,
                        (const float *)partial, nslots, chunk);
     hipLaunchKernelGGL(mlp_bwd_final_kernel, rg, dim3(256), 0, s, (const float *)chunk, nchunks,

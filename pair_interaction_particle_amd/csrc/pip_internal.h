@@ -13,14 +13,18 @@
 // W'[16co + l%16][32s + (j < 4 ? 0 : 16) + 4(l/16) + (j & 3)], stored at
 // ((layer * 8 + co * 2 + s) * 64 + l) * 8 + j; layer 4 uses operands 16 + s.
 // wx2 holds the fp16 hi operands of layers 2..4 followed by the fp16 lo
-// operands (same layout as w16); f16ok is set when every folded weight of
-// layers 2..4 lies inside the fp16 range, which the fp16 x 2 chain needs.
+// operands (same layout as w16); wtx2 the same for W'^T of layers 2 and 3
+// (operand (layer, it, s) of lane l holds in slot j W'[32s + (j < 4 ? 0 :
+// 16) + 4(l/16) + (j & 3)][16it + l%16], 16 hi operands then 16 lo ones),
+// the operands of the backward chain; f16ok is set when every folded weight
+// of layers 2..4 lies inside the fp16 range, which the fp16 x 2 chain needs.
 struct pip_pair_mlp {
     int device;
     int f16ok;
     float *w32;
     uint16_t *w16;
     uint16_t *wx2;
+    uint16_t *wtx2;
     float *bias;
     float *wplain;  // the folded weights in pip_pair_mlp_fold's plain layout (backward)
     int8_t *w8;     // int8 operands of layers 2..4 (int8 mode, layout in abi.hip)

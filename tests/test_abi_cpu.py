@@ -189,9 +189,10 @@ def test_packed_validation(L):
 
 
 def test_pair_mlp_backward_workspace_bytes(L):
-    # one slot of PIP_PAIR_MLP_FOLDED_GRADS floats per (jet, row tile)
-    # workgroup, then one per 32 slots for the fixed-order reduction
+    # one slot of PIP_PAIR_MLP_FOLDED_GRADS floats per (jet, row tile),
+    # then one per 32 slots for the fixed-order reduction, then one int per
+    # slot (the slots to recompute in float32)
     f = L.pip_pair_mlp_backward_workspace_bytes
     for B, P in ((1, 16), (128, 128), (3, 256), (33, 48)):
         slots = B * (P // 16)
-        assert f(B, P) == (slots + (slots + 31) // 32) * 9160 * 4
+        assert f(B, P) == (slots + (slots + 31) // 32) * 9160 * 4 + 4 * slots

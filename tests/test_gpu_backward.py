@@ -132,3 +132,80 @@ def test_pair_mlp_backward_kernel_workload():
     check_grads(got, ref, "MLP grads (B=128, P=128)")
     gf2 = host(pip.pair_mlp_backward(g(d["p4"]), g(mask), mlp, g(dU)))
     assert np.array_equal(gf2.view(np.uint32), gf.view(np.uint32))
+
+
+def _redo_flags(ws, B, P):
+    # the workspace ends with one int per (jet, row tile) slot: 1 where the
+    # fp16 x 2 kernel's sums left the fp16 range and float32 recomputed it
+    slots = B * (P // 16)
+    chunks = (slots + 31) // 32
+    flat = host(ws).view(np.int32)
+    off = (slots + chunks) * 9160
+    return flat[off:off + slots]
+
+
+def _ws(B, P):
+    n = int(pip.lib().pip_pair_mlp_backward_workspace_bytes(B, P))
+    return torch.empty(n // 4, device="cuda", dtype=torch.float32)
+
+
+def test_pair_mlp_backward_fp16_path_is_taken_and_scale_equivariant():
+    # Well-scaled weights take the fp16 x 2 kernel, and no slot of this input
+    # needs the float32 redo.  g is scaled per round by a power of two, so
+    # scaling dU by 2^40 or 2^-40 scales the gradient by exactly that factor,
+    # bit for bit.
+    B, P = 3, 48
+    p4, mask = ragged_jets(B, P, (48, 37, 9), seed=240)
+    params = mlp_for(240, biases=True)
+    mlp = pip.PairMLP(params)
+    rng = np.random.default_rng(241)
+    dU = rng.normal(0, 1, size=(B, 8, P, P)).astype(np.float32)
+    ws = _ws(B, P)
+    gf = host(pip.pair_mlp_backward(g(p4), g(mask), mlp, g(dU), workspace=ws))
+    assert not _redo_flags(ws, B, P).any()
+    got = {k: v for k, v in pip.unfold_grads(params, gf).items() if not k.startswith("in_")}
+    check_grads(got, oracle.pair_embed_backward(p4, mask, params, dU), "MLP grads fp16 x 2")
+    for k in (40, -40):
+        s = np.float32(2.0 ** k)
+        gk = host(pip.pair_mlp_backward(g(p4), g(mask), mlp, g(dU * s), workspace=ws))
+        assert not _redo_flags(ws, B, P).any()
+        np.testing.assert_array_equal((gf * s).view(np.uint32), gk.view(np.uint32))
+
+
+def test_pair_mlp_backward_fp16_overflow_redoes_exactly():
+    # One hidden channel of layer 1 at ~8e4 (beyond fp16), read out through
+    # tiny layer-2 weights: the folded weights are well scaled, so the fp16 x 2
+    # kernel runs, its sums for the real slots come out non-finite, and those
+    # slots are recomputed with float32 products.
+    B, P = 3, 48
+    p4, mask = ragged_jets(B, P, (48, 30, 17), seed=242)
+    params = mlp_for(242, biases=True)
+    params["b1"] = params["b1"].copy()
+    params["b1"][5] = 8.0e4
+    params["w2"] = params["w2"].copy()
+    params["w2"][:, 5] = 1.0e-5
+    ws_f = pip.fold(params)[0]
+    assert all(2 ** -8 <= np.abs(w).max() <= 2 ** 14 for w in ws_f[1:])
+    mlp = pip.PairMLP(params)
+    rng = np.random.default_rng(243)
+    dU = rng.normal(0, 1, size=(B, 8, P, P)).astype(np.float32)
+    ws = _ws(B, P)
+    gf = host(pip.pair_mlp_backward(g(p4), g(mask), mlp, g(dU), workspace=ws))
+    assert _redo_flags(ws, B, P).any()
+    got = {k: v for k, v in pip.unfold_grads(params, gf).items() if not k.startswith("in_")}
+    check_grads(got, oracle.pair_embed_backward(p4, mask, params, dU), "MLP grads, redo")
+
+
+def test_pair_mlp_backward_badly_scaled_weights():
+    # weights outside the fp16 range: every slot takes float32 products
+    B, P = 2, 32
+    p4, mask = ragged_jets(B, P, (32, 19), seed=244)
+    params = mlp_for(244)
+    params["w3"] = (params["w3"] * 1e5).astype(np.float32)
+    params["w4"] = (params["w4"] * 1e-5).astype(np.float32)
+    mlp = pip.PairMLP(params)
+    rng = np.random.default_rng(245)
+    dU = rng.normal(0, 1, size=(B, 8, P, P)).astype(np.float32)
+    gf = host(pip.pair_mlp_backward(g(p4), g(mask), mlp, g(dU)))
+    got = {k: v for k, v in pip.unfold_grads(params, gf).items() if not k.startswith("in_")}
+    check_grads(got, oracle.pair_embed_backward(p4, mask, params, dU), "MLP grads, f32 weights")
