@@ -222,10 +222,11 @@ pip_status pip_pair_bias_attention_backward(const void *Q, const void *K, const 
                                             int64_t D, float scale, void *dQ, void *dK,
                                             void *dV, void *dU, int dtype, void *stream);
 
-/* Bytes of workspace pip_pair_mlp_backward needs: one slot of
- * PIP_PAIR_MLP_FOLDED_GRADS floats per (jet, row tile of 16) (B * P/16
- * slots), then one per 32 slots for the partial sums of the fixed-order
- * reduction, then one int per slot (the slots to recompute in float32). */
+/* Bytes of workspace pip_pair_mlp_backward needs: PIP_PAIR_MLP_FOLDED_GRADS
+ * floats per (jet, row tile of 16) slot (S = B * P/16 slots) and per
+ * workgroup of the fp16 x 2 kernel (Gx = 16 S for S < 16, else 256), one per
+ * 32 of max(S, Gx) for the fixed-order reduction; then 2 Gx + S + 1 ints
+ * (the workgroups' overflow flags and the plan of their shares). */
 size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
 
 /* Gradient of L with respect to the folded pair-MLP parameters, for dL/dU =
@@ -239,8 +240,8 @@ size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
  * fit fp16 (as for the fp16 x 2 forward), the products run on the fp16
  * matrix cores with every float32 factor split into two fp16 halves
  * (relative error ~2^-22 per product) and g scaled by a power of two per
- * round of 128 pairs; a slot whose sums leave the fp16 range is recomputed
- * with float32 products, as are all slots otherwise.
+ * round of 128 pairs; if a sum leaves the fp16 range, the whole gradient is
+ * recomputed with float32 products, as it is for other weights.
  * workspace: pip_pair_mlp_backward_workspace_bytes(B, P) bytes, scratch
  * (overwritten; calls sharing one on different streams race).  Every sum
  * is taken in a fixed order: the result is the same bit for bit on every

@@ -27,6 +27,8 @@
 // end the 4 waves merge their sums into LDS in a fixed order (no atomics),
 // each workgroup writes one slot of the workspace, and two more kernels add
 // the slots in a fixed order: the result is the same bit for bit on every run.
+#include <algorithm>
+
 #include "pip_internal.h"
 #include "pip_mlp.h"
 
@@ -149,12 +151,17 @@ __device__ __forceinline__ void flush_rows(float *acc, const v4f (&R)[kN], int r
 
 template <int kPP>
 __global__ __launch_bounds__(kMbThreads) __attribute__((amdgpu_waves_per_eu(1))) void
-mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
+mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B, int P,
                const float *__restrict__ wplain, const float *__restrict__ bias,
                const float *__restrict__ dU, float *__restrict__ partial,
-               const int *__restrict__ redo) {
-    // with a redo list, only the slots the fp16 x 2 kernel flagged are computed
-    if (redo && redo[blockIdx.x] == 0) return;
+               const int *__restrict__ flags, int nflags) {
+    // after the fp16 x 2 kernel: runs only if one of its workgroups flagged
+    // a non-finite sum
+    if (flags) {
+        bool any = false;
+        for (int k = (int)(threadIdx.x & 63); k < nflags; k += 64) any = any || flags[k] != 0;
+        if (!__any(any)) return;
+    }
     // W2', W3' row-major and transposed (rows padded to 68 floats: 16-byte
     // aligned, so each lane reads its four k-steps of an operand at once)
     __shared__ float4 Wl4[2][64][17];
@@ -167,9 +174,8 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
     __shared__ float tr[kMbWaves][2][64][17];
 
     const int T = P / kTile;
-    // the largest row tiles of every jet first (longest workgroups start early)
-    const int nj = (int)(gridDim.x / T);
-    const int jet = (int)(blockIdx.x % nj), I = T - 1 - (int)(blockIdx.x / nj);
+    // slot = jet + B (T - 1 - I): the largest row tiles of every jet first
+    const int slot = blockIdx.x, jet = slot % B, I = T - 1 - slot / B;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
@@ -363,8 +369,126 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
         }
         __syncthreads();
     }
-    float *out = partial + (size_t)blockIdx.x * kGradFloats;
+    float *out = partial + (size_t)slot * kGradFloats;
     for (int e = tid; e < kGradFloats; e += kMbThreads) out[e] = acc[e];
+}
+
+// ---------------------------------------------------------------- block plan
+// The blocks of slot (jet, I) holding a real pair are the off-diagonal blocks
+// (row i of tile I, column tile J < I) whose row is real and whose column tile
+// holds a real particle, and those of the diagonal tile's 9 blocks (its 136
+// pairs (a, c), a >= c, in order) with a pair of two real particles.
+// diag_row_blocks: the diagonal blocks that row a of a tile with real bits R
+// puts a real pair into.  Row a's pairs are p = a(a+1)/2 + c, c <= a, at most
+// 16 of them, so they fall into one block or two neighbouring ones.
+__device__ __forceinline__ uint32_t diag_row_blocks(uint32_t R, int a) {
+    if (!((R >> a) & 1u)) return 0u;
+    const int p0 = a * (a + 1) / 2, k0 = p0 >> 4, k1 = (p0 + a) >> 4;
+    const uint32_t cols = R & ((2u << a) - 1u);               // real c <= a
+    const uint32_t low = (1u << (16 * (k0 + 1) - p0)) - 1u;   // the columns of block k0
+    return ((cols & low) ? 1u << k0 : 0u) | ((k1 != k0 && (cols & ~low)) ? 1u << k1 : 0u);
+}
+
+// start[s] = blocks of the slots before s (s = jet * T + I), start[nslots] =
+// all blocks N; first[k] = the slot holding block floor(k N / G), where share
+// k of G begins.  One workgroup.  Counts: one wave per jet (its real bits by
+// ballot, lane 16 I + a handles row a of tile I), kept in LDS (in start[]
+// beyond kPlanLds slots); then each thread sums a run of slots, the run
+// totals are scanned, and the runs are written out as prefix sums.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanLds = 8192;  // slot counts kept in LDS up to this many slots
+__global__ __launch_bounds__(kPlanThreads) void mlp_bwd_plan_kernel(
+    const uint8_t *__restrict__ mask, int B, int P, int G, int *__restrict__ start,
+    int *__restrict__ first) {
+    __shared__ int wsum[kPlanThreads / 64];
+    __shared__ int total;
+    __shared__ int lcnt[kPlanLds];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = P / kTile, nslots = B * T;
+    int *cnt = nslots <= kPlanLds ? lcnt : start;
+    // eight jets per wave at a time, all their mask loads issued first
+    for (int j0 = 8 * wave; j0 < B; j0 += 8 * (kPlanThreads / 64)) {
+        uint8_t mb[8][4];  // unconditional loads of clamped addresses, masked after
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch)
+                mb[q][ch] = mask[(size_t)min(j0 + q, B - 1) * P + min(64 * ch + lane, P - 1)];
+        bool mv[8][4];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch)
+                mv[q][ch] = mb[q][ch] != 0 && 64 * ch + lane < P;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int jet = j0 + q;
+            if (jet >= B) break;
+            uint32_t rb[8];  // real bits of the jet, 32 particles per word
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const uint64_t m = __ballot(mv[q][ch]);
+                rb[2 * ch] = (uint32_t)m;
+                rb[2 * ch + 1] = (uint32_t)(m >> 32);
+            }
+            uint32_t tany = 0;  // bit J: tile J holds a real particle
+#pragma unroll
+            for (int J = 0; J < 16; ++J)
+                if ((rb[J >> 1] >> (16 * (J & 1))) & 0xffffu) tany |= 1u << J;
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                const int idx = 64 * ch + lane, I = idx >> 4, a = idx & 15;
+                uint32_t R = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if ((I >> 1) == k) R = (rb[k] >> (16 * (I & 1))) & 0xffffu;
+                uint32_t dv = diag_row_blocks(R, a);
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) dv |= __shfl_xor(dv, o);
+                if (a == 0 && I < T)
+                    cnt[jet * T + I] = __popc(R) * __popc(tany & ((1u << I) - 1u)) + __popc(dv);
+            }
+        }
+    }
+    __syncthreads();
+    const int per = (nslots + kPlanThreads - 1) / kPlanThreads;
+    const int s0 = min(tid * per, nslots), s1 = min(s0 + per, nslots);
+    int mine = 0;
+    for (int s = s0; s < s1; ++s) mine += cnt[s];
+    // exclusive prefix of the run totals: within the wave, then across waves
+    int inc = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < kPlanThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int v = __shfl_up(w, o);
+            if (lane >= o) w += v;
+        }
+        if (lane < kPlanThreads / 64) wsum[lane] = w;  // inclusive wave totals
+        if (lane == kPlanThreads / 64 - 1) total = w;
+    }
+    __syncthreads();
+    const int N = total;
+    int acc = inc - mine + (wave > 0 ? wsum[wave - 1] : 0);
+    for (int s = s0; s < s1; ++s) {
+        const int c = cnt[s];
+        start[s] = acc;
+        if (c > 0) {
+            // the shares that begin inside [acc, acc + c)
+            int k = (int)(((unsigned long long)acc * G + N - 1) / (unsigned)N);
+            for (; k < G && (int)((unsigned long long)k * N / (unsigned)G) < acc + c; ++k)
+                first[k] = s;
+        }
+        acc += c;
+    }
+    if (tid == 0) start[nslots] = N;
 }
 
 // ---------------------------------------------------------------- fp16 x 2 kernel
@@ -372,8 +496,10 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
 // (v_mfma_f32_16x16x32_f16), each float32 factor carried as hi = fp16(x),
 // lo = fp16(x - hi) and x w = x_hi w_hi + x_hi w_lo + x_lo w_hi (relative
 // error ~2^-22 per product, float32 accumulation), as in the forward chain.
-// One 512-thread workgroup per compute unit walks (jet, row tile) slots; a
-// slot's pair blocks go out in rounds, one block per wave.  Per round:
+// One 512-thread workgroup per compute unit takes an equal share of the
+// flattened list of all slots' blocks with a real pair (mlp_bwd_plan_kernel
+// lays it out), slot by slot; the blocks go out in rounds, one per wave.
+// Per round:
 //   * every wave runs its block's forward (hidden states feature-major in
 //     registers) and the backward chain dy3 -> dy2 -> dy1 (W'^T operands
 //     packed on the host like the forward ones);
@@ -387,10 +513,11 @@ mlp_bwd_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, 
 // g is scaled per round by a power of two 2^e so that max |g| lies in [1, 2)
 // (the backward chain is linear in g, so every dy carries the same factor);
 // the accumulators hold their sums in units of 2^e and are rescaled exactly
-// when e changes.  A workgroup whose sums come out non-finite (an activation
-// or a dy beyond the fp16 range) flags its slot, and the float32 kernel above
-// recomputes that slot.  Every sum has a fixed order: the result is the same
-// bit for bit on every run.
+// when e changes.  Each workgroup writes one partial sum.  If any of them
+// comes out non-finite (an activation or a dy beyond the fp16 range), the
+// workgroup raises its flag and the float32 kernel above recomputes every
+// slot.  Every sum has a fixed order: the result is the same bit for bit on
+// every run.
 constexpr int kXWaves = 8;
 constexpr int kXThreads = 64 * kXWaves;
 constexpr int kXPairs = 16 * kXWaves;  // pairs per round: one block per wave
@@ -411,7 +538,7 @@ struct XLds {
     float w4[8][64];        // layer 4 (float32)
     float bias[200];
     float emax[kXWaves];
-    int nblk, bad;
+    int bad;
     uint8_t blk[256];
     PartLds<kPP> part;
 };
@@ -480,11 +607,11 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
                   const v8h *__restrict__ wx2, const v8h *__restrict__ wtx2,
                   const float4 *__restrict__ w32, const float *__restrict__ wplain,
                   const float *__restrict__ bias, const float *__restrict__ dU,
-                  float *__restrict__ partial, int *__restrict__ redo) {
+                  const int *__restrict__ start, const int *__restrict__ first,
+                  float *__restrict__ partial, int *__restrict__ flags) {
     __shared__ XLds<kPP> L;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, c = lane & 15;
     const int T = P / kTile, nslots = B * T;
     const size_t plane = (size_t)P * P;
 
@@ -503,12 +630,33 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
     const int ro = wave >> 1, ci0 = 2 * (wave & 1);
     const bool odd = (wave & 1) != 0;
 
-    // slots in snake order over passes of gridDim.x, largest row tiles first
-    const int G = (int)gridDim.x;
-    for (int pass = 0; pass * G < nslots; ++pass) {
-        const int slot = pass * G + ((pass & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
-        if (slot >= nslots) continue;  // uniform across the workgroup
-        const int jet = slot % B, I = T - 1 - slot / B;
+    // this workgroup's share [lo, hi) of the flattened list of every slot's
+    // blocks with a real pair (slots s = jet * T + I in order; start[s] is
+    // the first block of slot s, first[k] the slot where share k begins)
+    const long long N = start[nslots];
+    const long long lo = (long long)blockIdx.x * N / gridDim.x;
+    const long long hi = ((long long)blockIdx.x + 1) * N / gridDim.x;
+
+    v4f a3[2], a2[2], b3, b2, ax, b4;
+    a3[0] = a3[1] = a2[0] = a2[1] = b3 = b2 = ax = b4 = (v4f){0.f, 0.f, 0.f, 0.f};
+    int ecur = 0;
+    // the block state carried from one round's preparation to its phases
+    v8h h1h[2], h1l[2], h2h[2], h2l[2], h3h[2], h3l[2];
+    v4f d1[4], d2[4], dy[4];
+    float gv[2], fv;
+    if (tid == 0) L.bad = 0;
+
+    long long pos = lo;
+    int s = lo < hi ? __builtin_amdgcn_readfirstlane(first[blockIdx.x]) : nslots;
+    while (pos < hi) {
+        const int sb = __builtin_amdgcn_readfirstlane(start[s]);
+        const int se = __builtin_amdgcn_readfirstlane(start[s + 1]);
+        if (se == sb) {  // a slot without a real pair
+            ++s;
+            continue;
+        }
+        const int jet = s / T, I = s - jet * T;
+        const int from = (int)(pos - sb), to = (int)(min(hi, (long long)se) - sb);
         const int ncols = (I + 1) * kTile;
         if (tid < ncols) {
             const size_t idx = (size_t)jet * P + tid;
@@ -516,44 +664,38 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
             const int real = mask[idx] != 0;
             stage_particle(L.part, tid, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
         }
-        if (tid == 0) L.bad = 0;
         __syncthreads();
-        // the blocks with at least one real pair, in order
+        // the slot's blocks with a real pair, in order (the plan's test)
         if (wave == 0) {
+            const uint32_t rows = (uint32_t)__ballot(lane < 16 && L.part.real[I * kTile + lane]);
+            uint32_t tany = 0;
+            for (int ch = 0; ch < 4; ++ch) {
+                const int t = 64 * ch + lane;
+                const uint64_t m = __ballot(t < I * kTile && L.part.real[t]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if ((m >> (16 * q)) & 0xffffull) tany |= 1u << (4 * ch + q);
+            }
+            // diagonal tile: lane a < 16 marks the blocks of its real pairs (a, c)
+            uint32_t dv = lane < 16 ? diag_row_blocks(rows, lane) : 0u;
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) dv |= __shfl_xor(dv, o);
+            dv = __builtin_amdgcn_readfirstlane(dv);
             const int nb = 16 * I + 9;
             int base = 0;
             for (int ch = 0; ch < 4; ++ch) {
                 const int b = 64 * ch + lane;
-                bool v = false;
-                if (b < 16 * I) {
-                    const int i = I * kTile + (b & 15), J = b >> 4;
-                    bool any = false;
-                    for (int q = 0; q < 16; ++q) any = any || L.part.real[J * kTile + q];
-                    v = L.part.real[i] && any;
-                } else if (b < nb) {
-                    for (int q = 0; q < 16; ++q) {
-                        int ti, tj;
-                        const bool in = tri_pair(b - 16 * I, q, ti, tj);
-                        v = v || (in && L.part.real[I * kTile + ti] && L.part.real[I * kTile + tj]);
-                    }
-                }
+                const bool v = b < 16 * I ? ((rows >> (b & 15)) & (tany >> (b >> 4)) & 1u) != 0
+                                          : (b < nb && ((dv >> (b - 16 * I)) & 1u) != 0);
                 const uint64_t m = __ballot(v);
                 if (v) L.blk[base + __popcll(m & ((1ull << lane) - 1))] = (uint8_t)b;
                 base += __popcll(m);
             }
-            if (lane == 0) L.nblk = base;
         }
         __syncthreads();
-        const int nr = (L.nblk + kXWaves - 1) / kXWaves;
+        const int nr = (to - from + kXWaves - 1) / kXWaves;
         const float *dUj = dU + (size_t)jet * kHeads * plane;
 
-        v4f a3[2], a2[2], b3, b2, ax, b4;
-        a3[0] = a3[1] = a2[0] = a2[1] = b3 = b2 = ax = b4 = (v4f){0.f, 0.f, 0.f, 0.f};
-        int ecur = 0;
-        // the block state carried from one round's preparation to its phases
-        v8h h1h[2], h1l[2], h2h[2], h2l[2], h3h[2], h3l[2];
-        v4f d1[4], d2[4], dy[4];
-        float gv[2], fv;
 
         for (int r = 0; r <= nr; ++r) {
             // lane-dependent addresses are recomputed every round rather than
@@ -561,6 +703,31 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const int gq = ln >> 4, cq = ln & 15, pq = 16 * wave + cq;
+            // round r's block and its dU values, loaded a round ahead of use
+            int ni = I * kTile, nj = I * kTile;
+            bool nvalid = false;
+            float nx[2], ny[2];
+            if (r < nr) {
+                const int kb = from + kXWaves * r + wave;
+                const int bi = kb < to ? L.blk[kb] : -1;
+                if (bi >= 0 && bi < 16 * I) {
+                    ni = I * kTile + (bi & 15);
+                    nj = (bi >> 4) * kTile + cq;
+                    nvalid = true;
+                } else if (bi >= 0) {
+                    int ti, tj;
+                    nvalid = tri_pair(bi - 16 * I, ln, ti, tj);
+                    ni = I * kTile + ti;
+                    nj = I * kTile + tj;
+                }
+                nvalid = nvalid && L.part.real[ni] && L.part.real[nj];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int h = 4 * t + gq;
+                    nx[t] = dUj[h * plane + (size_t)ni * P + nj];
+                    ny[t] = dUj[h * plane + (size_t)nj * P + ni];
+                }
+            }
             if (r > 0) {
                 // [A] the round's scale; stage dy3 and h2
                 float M = L.emax[0];
@@ -633,7 +800,7 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
                     v4h qh, ql;
                     split4_f16(make_float4(gv[0], gv[1], fv, 0.f), qh, ql);
                     L.gs[0][gq][pq] = qh[0], L.gs[1][gq][pq] = ql[0];
-                    L.gs[0][4 + g][pq] = qh[1], L.gs[1][4 + g][pq] = ql[1];
+                    L.gs[0][4 + gq][pq] = qh[1], L.gs[1][4 + gq][pq] = ql[1];
                     L.fs[0][gq][pq] = qh[2], L.fs[1][gq][pq] = ql[2];
                 }
                 __syncthreads();
@@ -660,29 +827,11 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
                 }
             }
             if (r < nr) {
-                // prepare round r: the block, g, the features, the forward and dy3
-                const int bi = kXWaves * r + wave < L.nblk ? L.blk[kXWaves * r + wave] : -1;
-                int i = I * kTile, j = I * kTile;
-                bool valid = false;
-                if (bi >= 0 && bi < 16 * I) {
-                    i = I * kTile + (bi & 15);
-                    j = (bi >> 4) * kTile + cq;
-                    valid = true;
-                } else if (bi >= 0) {
-                    int ti, tj;
-                    valid = tri_pair(bi - 16 * I, ln, ti, tj);
-                    i = I * kTile + ti;
-                    j = I * kTile + tj;
-                }
-                valid = valid && L.part.real[i] && L.part.real[j];
+                // prepare round r: g, the features, the forward and dy3
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int h = 4 * t + gq;
-                    const float x = dUj[h * plane + (size_t)i * P + j];
-                    const float y = dUj[h * plane + (size_t)j * P + i];
-                    gv[t] = valid ? (i != j ? x + y : x) : 0.f;
-                }
-                fv = valid ? pair_feature(L.part, i, j, gq) : 0.f;
+                for (int t = 0; t < 2; ++t)
+                    gv[t] = nvalid ? (ni != nj ? nx[t] + ny[t] : nx[t]) : 0.f;
+                fv = nvalid ? pair_feature(L.part, ni, nj, gq) : 0.f;
                 float m = fmaxf(fabsf(gv[0]), fabsf(gv[1]));
 #pragma unroll
                 for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -723,124 +872,162 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
             __syncthreads();
         }
 
-        // write this wave's tiles (sums back to unit scale) and flag non-finite ones
-        float *out = partial + (size_t)slot * kGradFloats;
-        const int ue = -ecur;
-        int lo_ = lane;
-        asm volatile("" : "+v"(lo_));
-        const int go = lo_ >> 4, co_ = lo_ & 15;
-        bool ok = tile_finite(a3[0]) && tile_finite(a3[1]) && tile_finite(a2[0]) &&
-                  tile_finite(a2[1]) && tile_finite(ax);
-        if (odd) ok = ok && tile_finite(b3) && tile_finite(b2);
-        if (wave == 0) ok = ok && tile_finite(b4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * ro + 4 * go + r;
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                out[kGW3 + row * 64 + 16 * (ci0 + k) + co_] = __builtin_amdgcn_ldexpf(a3[k][r], ue);
-                out[kGW2 + row * 64 + 16 * (ci0 + k) + co_] = __builtin_amdgcn_ldexpf(a2[k][r], ue);
-            }
-            if (odd && co_ == 0) {
-                out[kGB3 + row] = __builtin_amdgcn_ldexpf(b3[r], ue);
-                out[kGB2 + row] = __builtin_amdgcn_ldexpf(b2[r], ue);
-            }
-            if (wave >= 4) {
-                const int o = 16 * (wave - 4) + 4 * go + r;
-                if (co_ < 4) out[kGW1 + o * 4 + co_] = __builtin_amdgcn_ldexpf(ax[r], ue);
-                else if (co_ == 4) out[kGB1 + o] = __builtin_amdgcn_ldexpf(ax[r], ue);
-            } else if (go < 2) {
-                out[kGW4 + (4 * go + r) * 64 + 16 * wave + co_] = __builtin_amdgcn_ldexpf(ax[r], ue);
-                if (wave == 0 && co_ == 0) out[kGB4 + 4 * go + r] = __builtin_amdgcn_ldexpf(b4[r], ue);
-            }
-        }
-        if (!__all(ok) && lane == 0) L.bad = 1;
-        __syncthreads();
-        if (tid == 0) redo[slot] = L.bad;
+        pos = sb + to;
+        ++s;
     }
+
+    // write this wave's tiles (sums back to unit scale) and flag non-finite ones
+    float *out = partial + (size_t)blockIdx.x * kGradFloats;
+    const int ue = -ecur;
+    int lo_ = lane;
+    asm volatile("" : "+v"(lo_));
+    const int go = lo_ >> 4, co_ = lo_ & 15;
+    bool ok = tile_finite(a3[0]) && tile_finite(a3[1]) && tile_finite(a2[0]) &&
+              tile_finite(a2[1]) && tile_finite(ax);
+    if (odd) ok = ok && tile_finite(b3) && tile_finite(b2);
+    if (wave == 0) ok = ok && tile_finite(b4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 16 * ro + 4 * go + r;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            out[kGW3 + row * 64 + 16 * (ci0 + k) + co_] = __builtin_amdgcn_ldexpf(a3[k][r], ue);
+            out[kGW2 + row * 64 + 16 * (ci0 + k) + co_] = __builtin_amdgcn_ldexpf(a2[k][r], ue);
+        }
+        if (odd && co_ == 0) {
+            out[kGB3 + row] = __builtin_amdgcn_ldexpf(b3[r], ue);
+            out[kGB2 + row] = __builtin_amdgcn_ldexpf(b2[r], ue);
+        }
+        if (wave >= 4) {
+            const int o = 16 * (wave - 4) + 4 * go + r;
+            if (co_ < 4) out[kGW1 + o * 4 + co_] = __builtin_amdgcn_ldexpf(ax[r], ue);
+            else if (co_ == 4) out[kGB1 + o] = __builtin_amdgcn_ldexpf(ax[r], ue);
+        } else if (go < 2) {
+            out[kGW4 + (4 * go + r) * 64 + 16 * wave + co_] = __builtin_amdgcn_ldexpf(ax[r], ue);
+            if (wave == 0 && co_ == 0) out[kGB4 + 4 * go + r] = __builtin_amdgcn_ldexpf(b4[r], ue);
+        }
+    }
+    if (!__all(ok) && lane == 0) L.bad = 1;
+    __syncthreads();
+    if (tid == 0) flags[blockIdx.x] = L.bad;
 }
 
-// grad[e] = sum over the workgroup slots w = 0 .. nslots-1 of partial[w][e],
-// in a fixed order: chunk k = blockIdx.y of kRedChunk consecutive slots is
-// summed in slot order (its loads issued together) into chunk[k][e], then the
-// chunk sums are added in chunk order.  The chunk sums have their own region
-// after the slots.
+// grad[e] = the sum over n partial sums w of partial[w][e] in a fixed order:
+// chunk k = blockIdx.y of kRedChunk consecutive partials is summed in order
+// (its loads issued together) into chunk[k][e], then the chunk sums are added
+// in chunk order.  The partials are the fp16 x 2 kernel's (nx2 of them) unless
+// that kernel did not run (flags null) or one of its workgroups raised its
+// flag; then they are the float32 kernel's (n32, one per slot).  Both kernels
+// take the same decision from the flags.
 constexpr int kRedChunk = 32;
-__global__ __launch_bounds__(256) void mlp_bwd_reduce_kernel(const float *__restrict__ partial,
-                                                             int nslots,
-                                                             float *__restrict__ chunk) {
+__global__ __launch_bounds__(256) void mlp_bwd_reduce_kernel(
+    const float *__restrict__ p32, int n32, const float *__restrict__ px2, int nx2,
+    const int *__restrict__ flags, float *__restrict__ chunk) {
+    bool use32 = flags == nullptr;
+    if (!use32) {
+        bool any = false;
+        for (int k = (int)(threadIdx.x & 63); k < nx2; k += 64) any = any || flags[k] != 0;
+        use32 = __any(any);
+    }
+    const float *partial = use32 ? p32 : px2;
+    const int n = use32 ? n32 : nx2;
     const int e = blockIdx.x * 256 + threadIdx.x;
     const int w0 = blockIdx.y * kRedChunk;
-    if (e >= kGradFloats) return;
+    if (e >= kGradFloats || w0 >= n) return;  // the final sum stops before this chunk
     float v[kRedChunk];
 #pragma unroll
     for (int w = 0; w < kRedChunk; ++w)
-        v[w] = w0 + w < nslots ? partial[(size_t)(w0 + w) * kGradFloats + e] : 0.f;
-    float s = 0.f;
+        v[w] = w0 + w < n ? partial[(size_t)(w0 + w) * kGradFloats + e] : 0.f;
+    float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kRedChunk; ++w) s += v[w];
-    chunk[(size_t)blockIdx.y * kGradFloats + e] = s;
+    for (int w = 0; w < kRedChunk; ++w) sum += v[w];
+    chunk[(size_t)blockIdx.y * kGradFloats + e] = sum;
 }
 
-__global__ __launch_bounds__(256) void mlp_bwd_final_kernel(const float *__restrict__ partial,
-                                                            int nchunks,
-                                                            float *__restrict__ grad) {
+__global__ __launch_bounds__(256) void mlp_bwd_final_kernel(
+    const float *__restrict__ partial, int n32, int nx2, const int *__restrict__ flags,
+    float *__restrict__ grad) {
+    bool use32 = flags == nullptr;
+    if (!use32) {
+        bool any = false;
+        for (int k = (int)(threadIdx.x & 63); k < nx2; k += 64) any = any || flags[k] != 0;
+        use32 = __any(any);
+    }
+    const int nchunks = ((use32 ? n32 : nx2) + kRedChunk - 1) / kRedChunk;
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= kGradFloats) return;
-    float s = 0.f;
-    for (int k = 0; k < nchunks; ++k) s += partial[(size_t)k * kGradFloats + e];
-    grad[e] = s;
+    float sum = 0.f;
+    for (int k0 = 0; k0 < nchunks; k0 += 8) {  // eight loads in flight, added in order
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[k] = k0 + k < nchunks ? partial[(size_t)(k0 + k) * kGradFloats + e] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum += v[k];
+    }
+    grad[e] = sum;
 }
 
-// one slot per (jet, row tile), then one chunk sum per kRedChunk slots, then
-// the fp16 x 2 kernel's redo flag per slot
+// workgroups of the fp16 x 2 kernel (at most; fewer on a smaller device)
+static int x2_groups(int nslots) { return nslots < 16 ? 16 * nslots : 256; }
+
+// Workspace, in order: one float32 partial per (jet, row tile) slot; one per
+// fp16 x 2 workgroup; the reduction's chunk sums; then ints: the fp16 x 2
+// workgroups' flags, the block plan's start (nslots + 1) and first (one per
+// workgroup).
 size_t mlp_bwd_workspace(int B, int P) {
-    const size_t nslots = (size_t)B * (P / kTile);
-    return (nslots + (nslots + kRedChunk - 1) / kRedChunk) * kGradFloats * sizeof(float) +
-           nslots * sizeof(int);
+    const size_t nslots = (size_t)B * (P / kTile), gx = (size_t)x2_groups((int)nslots);
+    const size_t nchunks = (std::max(nslots, gx) + kRedChunk - 1) / kRedChunk;
+    return (nslots + gx + nchunks) * kGradFloats * sizeof(float) +
+           (gx + nslots + 1 + gx) * sizeof(int);
 }
 
 hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P,
                               const pip_pair_mlp *m, const float *dU, float *grad, void *ws,
                               hipStream_t s) {
     const int T = P / kTile;
-    float *partial = (float *)ws;
+    float *p32 = (float *)ws;
     const dim3 rg((kGradFloats + 255) / 256);
     if (B == 0) {  // no pair: the sum over no chunk writes zeros
-        hipLaunchKernelGGL(mlp_bwd_final_kernel, rg, dim3(256), 0, s, partial, 0, grad);
+        hipLaunchKernelGGL(mlp_bwd_final_kernel, rg, dim3(256), 0, s, p32, 0, 0,
+                           (const int *)nullptr, grad);
         return hipGetLastError();
     }
-    const int nslots = B * T, nchunks = (nslots + kRedChunk - 1) / kRedChunk;
-    float *chunk = partial + (size_t)nslots * kGradFloats;
-    int *redo = nullptr;
-    if (m->f16ok) {
-        // the fp16 x 2 kernel over every slot, then the float32 kernel for the
-        // slots it flagged
-        redo = (int *)(chunk + (size_t)nchunks * kGradFloats);
-        const dim3 grid((unsigned)min(nslots, cu_count()));
+    const int nslots = B * T, gx = x2_groups(nslots);
+    const int nchunks = (std::max(nslots, gx) + kRedChunk - 1) / kRedChunk;
+    float *px2 = p32 + (size_t)nslots * kGradFloats;
+    float *chunk = px2 + (size_t)gx * kGradFloats;
+    int *flags = (int *)(chunk + (size_t)nchunks * kGradFloats);
+    int *start = flags + gx, *first = start + nslots + 1;
+    // the fp16 x 2 path needs well-scaled weights and a block count within int
+    const bool x2 = m->f16ok && (long long)nslots * (16 * kTile + 9) < (1ll << 31);
+    const int G = std::min(gx, cu_count());
+    if (x2) {
+        hipLaunchKernelGGL(mlp_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, mask, B, P, G,
+                           start, first);
         if (P <= 128)
-            hipLaunchKernelGGL(mlp_bwd_x2_kernel<128>, grid, dim3(kXThreads), 0, s,
+            hipLaunchKernelGGL(mlp_bwd_x2_kernel<128>, dim3((unsigned)G), dim3(kXThreads), 0, s,
                                (const float4 *)p4, mask, B, P, (const v8h *)m->wx2,
                                (const v8h *)m->wtx2, (const float4 *)m->w32, m->wplain, m->bias,
-                               dU, partial, redo);
+                               dU, (const int *)start, (const int *)first, px2, flags);
         else
-            hipLaunchKernelGGL(mlp_bwd_x2_kernel<256>, grid, dim3(kXThreads), 0, s,
+            hipLaunchKernelGGL(mlp_bwd_x2_kernel<256>, dim3((unsigned)G), dim3(kXThreads), 0, s,
                                (const float4 *)p4, mask, B, P, (const v8h *)m->wx2,
                                (const v8h *)m->wtx2, (const float4 *)m->w32, m->wplain, m->bias,
-                               dU, partial, redo);
+                               dU, (const int *)start, (const int *)first, px2, flags);
     }
+    const int *fl = x2 ? flags : nullptr;
+    const dim3 g32((unsigned)nslots);
     if (P <= 128)
-        hipLaunchKernelGGL(mlp_bwd_kernel<128>, dim3((unsigned)nslots), dim3(kMbThreads), 0, s,
-                           (const float4 *)p4, mask, P, m->wplain, m->bias, dU, partial,
-                           (const int *)redo);
+        hipLaunchKernelGGL(mlp_bwd_kernel<128>, g32, dim3(kMbThreads), 0, s, (const float4 *)p4,
+                           mask, B, P, m->wplain, m->bias, dU, p32, fl, G);
     else
-        hipLaunchKernelGGL(mlp_bwd_kernel<256>, dim3((unsigned)nslots), dim3(kMbThreads), 0, s,
-                           (const float4 *)p4, mask, P, m->wplain, m->bias, dU, partial,
-                           (const int *)redo);
+        hipLaunchKernelGGL(mlp_bwd_kernel<256>, g32, dim3(kMbThreads), 0, s, (const float4 *)p4,
+                           mask, B, P, m->wplain, m->bias, dU, p32, fl, G);
     hipLaunchKernelGGL(mlp_bwd_reduce_kernel, dim3(rg.x, (unsigned)nchunks), dim3(256), 0, s,
-                       (const float *)partial, nslots, chunk);
-    hipLaunchKernelGGL(mlp_bwd_final_kernel, rg, dim3(256), 0, s, (const float *)chunk, nchunks,
-                       grad);
+                       (const float *)p32, nslots, (const float *)px2, G, fl, chunk);
+    hipLaunchKernelGGL(mlp_bwd_final_kernel, rg, dim3(256), 0, s, (const float *)chunk, nslots,
+                       G, fl, grad);
     return hipGetLastError();
 }
 

@@ -189,10 +189,13 @@ def test_packed_validation(L):
 
 
 def test_pair_mlp_backward_workspace_bytes(L):
-    # one slot of PIP_PAIR_MLP_FOLDED_GRADS floats per (jet, row tile),
-    # then one per 32 slots for the fixed-order reduction, then one int per
-    # slot (the slots to recompute in float32)
+    # PIP_PAIR_MLP_FOLDED_GRADS floats per (jet, row tile) slot and per
+    # fp16 x 2 workgroup (16 per slot up to 256), one per 32 of the larger
+    # count for the fixed-order reduction; then ints: the workgroups' flags,
+    # the block plan (slots + 1 starts, one first slot per workgroup)
     f = L.pip_pair_mlp_backward_workspace_bytes
     for B, P in ((1, 16), (128, 128), (3, 256), (33, 48)):
         slots = B * (P // 16)
-        assert f(B, P) == (slots + (slots + 31) // 32) * 9160 * 4 + 4 * slots
+        gx = 16 * slots if slots < 16 else 256
+        chunks = (max(slots, gx) + 31) // 32
+        assert f(B, P) == (slots + gx + chunks) * 9160 * 4 + (2 * gx + slots + 1) * 4

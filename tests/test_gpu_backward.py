@@ -135,13 +135,16 @@ def test_pair_mlp_backward_kernel_workload():
 
 
 def _redo_flags(ws, B, P):
-    # the workspace ends with one int per (jet, row tile) slot: 1 where the
-    # fp16 x 2 kernel's sums left the fp16 range and float32 recomputed it
+    # after the partial sums (one per slot, one per fp16 x 2 workgroup, the
+    # chunk sums) the workspace holds one int per fp16 x 2 workgroup: 1 where
+    # its sums left the fp16 range (then float32 recomputes the gradient)
     slots = B * (P // 16)
-    chunks = (slots + 31) // 32
+    gx = 16 * slots if slots < 16 else 256
+    G = min(gx, torch.cuda.get_device_properties(0).multi_processor_count)
+    chunks = (max(slots, gx) + 31) // 32
     flat = host(ws).view(np.int32)
-    off = (slots + chunks) * 9160
-    return flat[off:off + slots]
+    off = (slots + gx + chunks) * 9160
+    return flat[off:off + G]
 
 
 def _ws(B, P):
