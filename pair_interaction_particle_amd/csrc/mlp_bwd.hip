@@ -391,66 +391,59 @@ __device__ __forceinline__ uint32_t diag_row_blocks(uint32_t R, int a) {
 
 // start[s] = blocks of the slots before s (s = jet * T + I), start[nslots] =
 // all blocks N; first[k] = the slot holding block floor(k N / G), where share
-// k of G begins.  One workgroup.  Counts: one wave per jet (its real bits by
-// ballot, lane 16 I + a handles row a of tile I), kept in LDS (in start[]
-// beyond kPlanLds slots); then each thread sums a run of slots, the run
-// totals are scanned, and the runs are written out as prefix sums.
+// k of G begins.  One workgroup, jets in chunks of kPlanJets: each wave takes
+// the real bits of eight jets at a time (all loads issued first, then one
+// ballot per 64 particles) into LDS; then one thread per slot counts its
+// blocks.  The counts stay in LDS (in start[] beyond kPlanLds slots); each
+// thread then sums a run of slots, the run totals are scanned, and the runs
+// are written out as prefix sums.
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanLds = 8192;  // slot counts kept in LDS up to this many slots
+constexpr int kPlanLds = 8192;   // slot counts kept in LDS up to this many slots
+constexpr int kPlanJets = 1024;  // jets whose real bits are in LDS at once
 __global__ __launch_bounds__(kPlanThreads) void mlp_bwd_plan_kernel(
     const uint8_t *__restrict__ mask, int B, int P, int G, int *__restrict__ start,
     int *__restrict__ first) {
     __shared__ int wsum[kPlanThreads / 64];
     __shared__ int total;
     __shared__ int lcnt[kPlanLds];
+    __shared__ uint32_t bits[kPlanJets][8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = P / kTile, nslots = B * T;
     int *cnt = nslots <= kPlanLds ? lcnt : start;
-    // eight jets per wave at a time, all their mask loads issued first
-    for (int j0 = 8 * wave; j0 < B; j0 += 8 * (kPlanThreads / 64)) {
-        uint8_t mb[8][4];  // unconditional loads of clamped addresses, masked after
+    for (int c0 = 0; c0 < B; c0 += kPlanJets) {
+        const int nj = min(kPlanJets, B - c0);
+        for (int j0 = 8 * wave; j0 < nj; j0 += 8 * (kPlanThreads / 64)) {
+            uint8_t mb[8][4];  // unconditional loads of clamped addresses
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch)
-                mb[q][ch] = mask[(size_t)min(j0 + q, B - 1) * P + min(64 * ch + lane, P - 1)];
-        bool mv[8][4];
+                for (int ch = 0; ch < 4; ++ch)
+                    mb[q][ch] = mask[(size_t)(c0 + min(j0 + q, nj - 1)) * P +
+                                     min(64 * ch + lane, P - 1)];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch)
-                mv[q][ch] = mb[q][ch] != 0 && 64 * ch + lane < P;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int jet = j0 + q;
-            if (jet >= B) break;
-            uint32_t rb[8];  // real bits of the jet, 32 particles per word
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const uint64_t m = __ballot(mv[q][ch]);
-                rb[2 * ch] = (uint32_t)m;
-                rb[2 * ch + 1] = (uint32_t)(m >> 32);
-            }
-            uint32_t tany = 0;  // bit J: tile J holds a real particle
-#pragma unroll
-            for (int J = 0; J < 16; ++J)
-                if ((rb[J >> 1] >> (16 * (J & 1))) & 0xffffu) tany |= 1u << J;
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const int idx = 64 * ch + lane, I = idx >> 4, a = idx & 15;
-                uint32_t R = 0;
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if ((I >> 1) == k) R = (rb[k] >> (16 * (I & 1))) & 0xffffu;
-                uint32_t dv = diag_row_blocks(R, a);
-#pragma unroll
-                for (int o = 8; o > 0; o >>= 1) dv |= __shfl_xor(dv, o);
-                if (a == 0 && I < T)
-                    cnt[jet * T + I] = __popc(R) * __popc(tany & ((1u << I) - 1u)) + __popc(dv);
-            }
+                for (int ch = 0; ch < 4; ++ch) {
+                    const uint64_t m = __ballot(mb[q][ch] != 0 && 64 * ch + lane < P);
+                    if (lane == 0 && j0 + q < nj) {
+                        bits[j0 + q][2 * ch] = (uint32_t)m;
+                        bits[j0 + q][2 * ch + 1] = (uint32_t)(m >> 32);
+                    }
+                }
         }
+        __syncthreads();
+        for (int s = c0 * T + tid; s < (c0 + nj) * T; s += kPlanThreads) {
+            const int jl = s / T - c0, I = s % T;
+            const uint32_t R = (bits[jl][I >> 1] >> (16 * (I & 1))) & 0xffffu;
+            int tiles = 0;
+            for (int J = 0; J < I; ++J) tiles += ((bits[jl][J >> 1] >> (16 * (J & 1))) & 0xffffu) != 0;
+            uint32_t dv = 0;
+#pragma unroll
+            for (int a = 0; a < kTile; ++a) dv |= diag_row_blocks(R, a);
+            cnt[s] = __popc(R) * tiles + __popc(dv);
+        }
+        __syncthreads();
     }
-    __syncthreads();
     const int per = (nslots + kPlanThreads - 1) / kPlanThreads;
     const int s0 = min(tid * per, nslots), s1 = min(s0 + per, nslots);
     int mine = 0;
