@@ -126,6 +126,73 @@ def test_block_stack_ragged_padded_rows_untouched(B, P, C, L, ns):
     np.testing.assert_array_equal(got[~real].view(np.uint32), x0[~real].view(np.uint32))
 
 
+@pytest.mark.parametrize("B,P,C,L,ns", [
+    (5, 128, 80, 2, (128, 100, 33, 1, 0)),  # H = 5: the last head pair has one head
+    (2, 16, 16, 3, (16, 5)),                # H = 1, one row block
+    (3, 112, 128, 1, (112, 97, 64)),        # P = 112: seven row blocks (odd)
+])
+def test_block_stack_shapes(B, P, C, L, ns):
+    # odd head counts, a single head, odd block counts, empty and
+    # one-particle jets, a non-prefix hole, junk padding
+    rng = np.random.default_rng(B * 1000 + C)
+    _, mask = ragged_jets(B, P, ns, seed=C + 1)
+    x0, wq, wk, wv, wo = synth.make_block_stack(B, P, C, L, mask, rng=rng)
+    x0 = x0.copy()
+    x0[mask == 0] = rng.normal(0, 5, size=(int((mask == 0).sum()), C))
+    H = C // 16
+    U = rng.normal(0, 1, size=(B, H, P, P)).astype(np.float32)
+    X = g(x0)
+    pip.block_stack(X, g(wq), g(wk), g(wv), g(wo), g(U), g(mask))
+    got = host(X)
+    ref = oracle.block_stack(x0, wq, wk, wv, wo, U, mask)
+    real = mask != 0
+    assert_close(got[real], ref[real], TOL32, "block stack X B=%d P=%d C=%d" % (B, P, C))
+    np.testing.assert_array_equal(got[~real].view(np.uint32), x0[~real].view(np.uint32))
+
+
+def test_block_stack_more_jets_than_compute_units_scattered_masks():
+    # 300 jets (more workgroups than CUs), masks with holes anywhere
+    B, P, C, L = 300, 64, 128, 1
+    rng = np.random.default_rng(300)
+    mask = (rng.random((B, P)) < rng.uniform(0.1, 1.0, size=(B, 1))).astype(np.uint8)
+    x0, wq, wk, wv, wo = synth.make_block_stack(B, P, C, L, mask, rng=rng)
+    U = rng.normal(0, 1, size=(B, 8, P, P)).astype(np.float32)
+    X = g(x0)
+    pip.block_stack(X, g(wq), g(wk), g(wv), g(wo), g(U), g(mask))
+    got = host(X)
+    ref = oracle.block_stack(x0, wq, wk, wv, wo, U, mask)
+    real = mask != 0
+    assert_close(got[real], ref[real], TOL32, "block stack X B=300 scattered masks")
+    np.testing.assert_array_equal(got[~real].view(np.uint32), x0[~real].view(np.uint32))
+
+
+def test_block_stack_badly_scaled_rows_and_weights():
+    # X rows over nine decades (up to ~3e5, beyond the fp16 range) and
+    # weights scaled per matrix: every product runs on split fp16 operands
+    # after exact powers of two, so large rows must not overflow and tiny
+    # ones keep their relative accuracy.  Q and K are scaled down so that the
+    # scores stay O(10) (a softmax over scores of size S amplifies float32
+    # rounding by S, in any implementation).
+    B, P, C, L = 3, 64, 64, 2
+    rng = np.random.default_rng(77)
+    _, mask = ragged_jets(B, P, (64, 40, 9), seed=77)
+    x0, wq, wk, wv, wo = synth.make_block_stack(B, P, C, L, mask, rng=rng)
+    x0 = (x0 * 10.0 ** rng.uniform(-4, 5.5, size=(B, P, 1))).astype(np.float32)
+    wq = (wq * 1e-5).astype(np.float32)
+    wk = (wk * 1e-5).astype(np.float32)
+    wo = (wo * 1e-2).astype(np.float32)
+    U = rng.normal(0, 1, size=(B, 4, P, P)).astype(np.float32)
+    X = g(x0)
+    pip.block_stack(X, g(wq), g(wk), g(wv), g(wo), g(U), g(mask))
+    got = host(X)
+    ref = oracle.block_stack(x0, wq, wk, wv, wo, U, mask)
+    real = mask != 0
+    # the bar relative to each row's own largest entry (attention mixes rows
+    # of very different magnitude into each row)
+    scale = np.abs(ref).max(axis=-1, keepdims=True) + 1e-30
+    assert_close((got / scale)[real], (ref / scale)[real], TOL32, "block stack, scaled rows")
+
+
 def test_fused_many_jets_unsorted_path():
     # more jets than the in-kernel ranking takes: workgroups take jets in index order
     B, P = 2100, 16
