@@ -377,7 +377,7 @@ pip_status pip_pair_bias_attention(const void *Q, const void *K, const void *V, 
     if (B == 0 || P == 0 || H == 0) return PIP_OK;
     if (!Q || !K || !V || !U || !mask || !O) return PIP_ERR_NULL;
     if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
-    if (B * H * pip::attention_chunks((int)P) > ((int64_t)1 << 31) - 1)
+    if (pip::attention_jet_slots(B) * H * pip::attention_chunks((int)P) > ((int64_t)1 << 31) - 1)
         return PIP_ERR_UNSUPPORTED;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(O))
         return PIP_ERR_ALIGN;
@@ -474,7 +474,8 @@ pip_status pip_pair_bias_attention_packed(const void *Q, const void *K, const vo
     if (B == 0 || H == 0 || max_n == 0) return PIP_OK;
     if (!Q || !K || !V || !U || !cu_seqlens || !u_offsets || !O) return PIP_ERR_NULL;
     if (D != PIP_HEAD_DIM) return PIP_ERR_UNSUPPORTED;
-    if (B * H * pip::attention_chunks((int)((max_n + 15) & ~15)) > ((int64_t)1 << 31) - 1 ||
+    if (pip::attention_jet_slots(B) * H * pip::attention_chunks((int)((max_n + 15) & ~15)) >
+            ((int64_t)1 << 31) - 1 ||
         H * N > ((int64_t)1 << 31))
         return PIP_ERR_UNSUPPORTED;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(O) ||

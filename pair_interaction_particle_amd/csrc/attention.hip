@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64 * kAttnQBlocks / kQ)
 __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_kernel(
     const AttnElt<kBf16> *__restrict__ Q, const AttnElt<kBf16> *__restrict__ K,
     const AttnElt<kBf16> *__restrict__ V, const AttnElt<kBf16> *__restrict__ U,
-    const uint8_t *__restrict__ mask, int H, int P, int chunks, float scale,
+    const uint8_t *__restrict__ mask, int B, int H, int P, int chunks, float scale,
     AttnElt<kBf16> *__restrict__ O, const int *__restrict__ cu,
     const int64_t *__restrict__ uoff, int N, int64_t u_elems) {
     using E = AttnElt<kBf16>;
@@ -178,7 +178,15 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int chunk = blockIdx.x % chunks, bh = blockIdx.x / chunks, jet = bh / H;
+    // Workgroup i runs on XCD i % 8; XCD x takes the H * chunks workgroups of
+    // jets x, x + 8, ..., so a jet's mask row (or cu / u_off entries), the
+    // first load of every chain, is fetched from HBM once and then hit in
+    // that XCD's L2.  The grid is rounded up to 8 jets.
+    const int per_jet = H * chunks;
+    const int xcd = blockIdx.x & 7, t8 = blockIdx.x >> 3;
+    const int jet = xcd + 8 * (t8 / per_jet), sub = t8 - (t8 / per_jet) * per_jet;
+    if (jet >= B) return;  // uniform: a slot of the rounding
+    const int chunk = sub % chunks, bh = jet * H + sub / chunks;
     // rows: rows of this (jet, head) that exist (P, or n in the packed
     // layout); ld: U row stride; T: blocks of 16 rows
     int rows, ld, T;
@@ -368,21 +376,24 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
 
 int attention_chunks(int P) { return (P / kTile + kAttnQBlocks - 1) / kAttnQBlocks; }
 
+// jets the grid covers: B rounded up to the 8 XCDs
+int64_t attention_jet_slots(int64_t B) { return (B + 7) / 8 * 8; }
+
 template <bool kBf16>
 static hipError_t launch_attention(const AttnElt<kBf16> *Q, const AttnElt<kBf16> *K,
                                    const AttnElt<kBf16> *V, const AttnElt<kBf16> *U,
                                    const uint8_t *mask, int B, int H, int P, float scale,
                                    AttnElt<kBf16> *O, hipStream_t s) {
     const int chunks = attention_chunks(P);
-    const dim3 grid((unsigned)((size_t)B * H * chunks));
+    const dim3 grid((unsigned)(attention_jet_slots(B) * H * chunks));
     if (P <= 128)
         hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1, false>), grid, dim3(64 * kAttnQBlocks),
-                           0, s, Q, K, V, U, mask, H, P, chunks, scale, O, nullptr, nullptr, 0,
-                           (int64_t)0);
+                           0, s, Q, K, V, U, mask, B, H, P, chunks, scale, O, nullptr, nullptr,
+                           0, (int64_t)0);
     else
         hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1, false>), grid,
-                           dim3(64 * kAttnQBlocks), 0, s, Q, K, V, U, mask, H, P, chunks, scale,
-                           O, nullptr, nullptr, 0, (int64_t)0);
+                           dim3(64 * kAttnQBlocks), 0, s, Q, K, V, U, mask, B, H, P, chunks,
+                           scale, O, nullptr, nullptr, 0, (int64_t)0);
     return hipGetLastError();
 }
 
@@ -408,15 +419,15 @@ static hipError_t launch_attention_packed(const AttnElt<kBf16> *Q, const AttnElt
                                           AttnElt<kBf16> *O, hipStream_t s) {
     const int chunks = attention_chunks((max_n + 15) & ~15);
     if (chunks == 0) return hipSuccess;
-    const dim3 grid((unsigned)((size_t)B * H * chunks));
+    const dim3 grid((unsigned)(attention_jet_slots(B) * H * chunks));
     if (max_n <= 128)
         hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1, true>), grid, dim3(64 * kAttnQBlocks),
-                           0, s, Q, K, V, U, nullptr, H, max_n, chunks, scale, O, cu, uoff, N,
-                           u_elems);
+                           0, s, Q, K, V, U, nullptr, B, H, max_n, chunks, scale, O, cu, uoff,
+                           N, u_elems);
     else
         hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1, true>), grid,
-                           dim3(64 * kAttnQBlocks), 0, s, Q, K, V, U, nullptr, H, max_n, chunks,
-                           scale, O, cu, uoff, N, u_elems);
+                           dim3(64 * kAttnQBlocks), 0, s, Q, K, V, U, nullptr, B, H, max_n,
+                           chunks, scale, O, cu, uoff, N, u_elems);
     return hipGetLastError();
 }
 

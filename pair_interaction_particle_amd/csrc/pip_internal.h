@@ -46,8 +46,10 @@ hipError_t launch_pair_embed_bf16(const float *p4, const uint8_t *mask, int B, i
 hipError_t launch_pair_embed_int8(const float *p4, const uint8_t *mask, int B, int P,
                                   const pip_pair_mlp *m, const float *act_scale,
                                   const int *act_zero, uint16_t *U, hipStream_t s);
-// workgroups per (jet, head) of the attention kernel
+// workgroups per (jet, head) of the attention kernel, and the jets its grid
+// covers (B rounded up to a multiple of 8)
 int attention_chunks(int P);
+int64_t attention_jet_slots(int64_t B);
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V,
                                 const float *U, const uint8_t *mask, int B, int H, int P,
                                 float scale, float *O, hipStream_t s);
