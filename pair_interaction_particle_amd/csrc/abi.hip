@@ -505,7 +505,7 @@ pip_status pip_pair_bias_attention_backward(const void *Q, const void *K, const 
     if (B == 0 || P == 0 || H == 0) return PIP_OK;
     if (!Q || !K || !V || !U || !mask || !dO || !dQ || !dK || !dV || !dU) return PIP_ERR_NULL;
     if (D != PIP_HEAD_DIM || dtype != PIP_F32) return PIP_ERR_UNSUPPORTED;
-    if (B * H > ((int64_t)1 << 31) - 1) return PIP_ERR_UNSUPPORTED;
+    if (pip::attention_jet_slots(B) * H > ((int64_t)1 << 31) - 1) return PIP_ERR_UNSUPPORTED;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(U) || !aligned16(dO) ||
         !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(dU))
         return PIP_ERR_ALIGN;

@@ -50,7 +50,7 @@ template <int kT>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kT <= 8 ? 4 : 2))) void attention_bwd_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     const float *__restrict__ U, const uint8_t *__restrict__ mask,
-    const float *__restrict__ dO, int H, int P, float scale, float *__restrict__ dQ,
+    const float *__restrict__ dO, int B, int H, int P, float scale, float *__restrict__ dQ,
     float *__restrict__ dK, float *__restrict__ dV, float *__restrict__ dU) {
     constexpr int kP = kT * 16;
     __shared__ float Ks[kP][16];
@@ -64,7 +64,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kT 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int bh = blockIdx.x, jet = bh / H;
+    // workgroup i runs on XCD i % 8; XCD x takes the H workgroups of jets x,
+    // x + 8, ... (the grid is rounded up to 8 jets), so a jet's mask row is
+    // fetched from HBM once and hit in that XCD's L2 by its other heads
+    const int xcd = blockIdx.x & 7, t8 = blockIdx.x >> 3;
+    const int jet = xcd + 8 * (t8 / H), bh = jet * H + t8 % H;
+    if (jet >= B) return;  // uniform: a slot of the rounding
     const int T = P / kTile;
     const size_t base = (size_t)bh * P;
     const float *Qh = Q + base * 16, *Kh = K + base * 16, *Vh = V + base * 16;
@@ -260,13 +265,13 @@ hipError_t launch_attention_bwd_f32(const float *Q, const float *K, const float 
                                     const float *U, const uint8_t *mask, const float *dO, int B,
                                     int H, int P, float scale, float *dQ, float *dK, float *dV,
                                     float *dU, hipStream_t s) {
-    const dim3 grid((unsigned)((size_t)B * H));
+    const dim3 grid((unsigned)(attention_jet_slots(B) * H));
     if (P <= 128)
         hipLaunchKernelGGL(attention_bwd_kernel<8>, grid, dim3(kBwdThreads), 0, s, Q, K, V, U,
-                           mask, dO, H, P, scale, dQ, dK, dV, dU);
+                           mask, dO, B, H, P, scale, dQ, dK, dV, dU);
     else
         hipLaunchKernelGGL(attention_bwd_kernel<16>, grid, dim3(kBwdThreads), 0, s, Q, K, V, U,
-                           mask, dO, H, P, scale, dQ, dK, dV, dU);
+                           mask, dO, B, H, P, scale, dQ, dK, dV, dU);
     return hipGetLastError();
 }
 
