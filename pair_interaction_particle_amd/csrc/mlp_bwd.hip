@@ -14,7 +14,13 @@
 // GELU is the erf form x Phi(x), GELU'(x) = Phi(x) + x phi(x), with Phi from a
 // fitted exponent (absolute error <= 7.5e-8).
 //
-// One 256-thread workgroup per (jet, row tile I) of 16 particles; its pair
+// Two kernels compute it.  The fp16 x 2 kernel further down (every large
+// product on the fp16 matrix cores with split operands, a balanced share of
+// all blocks per compute unit) is the one that runs; the float32 kernel
+// described next takes over when the folded weights leave the fp16 range or
+// the fp16 x 2 sums come out non-finite.
+//
+// Float32 kernel: one 256-thread workgroup per (jet, row tile I) of 16 particles; its pair
 // blocks (row i of tile (I, J < I): 16 pairs; the diagonal tile: 136 pairs
 // in 9 blocks) go round-robin to the 4 waves.  Per block a wave recomputes
 // the forward on the float32 matrix cores (v_mfma_f32_16x16x4_f32, hidden
