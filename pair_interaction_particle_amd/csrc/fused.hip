@@ -2,16 +2,19 @@
 // lives on chip ("Fusion 2" and "Fusion 3" of the ml4sci_cms_e2e26 README,
 // "How the Kernel Fusion Works", composed).
 //
-// Jet kernel (P <= 128).  One 512-thread workgroup per jet walks the lower
-// triangle of 16x16 tiles in rounds.  In each round the 8 waves push the
-// tile's pair blocks through the MFMA MLP chain into an LDS tile of U (8
-// heads), then wave h applies head h of that tile twice: to query block I
-// against key block J, and (transposed) to query block J against key block I.
-// So every unique pair goes through the MLP once, as in pair_embed.  Each
-// wave owns the online-softmax state (O, running max, running sum) of its
-// head for every query block, kept in LDS, so no two waves ever update the
-// same state and one barrier per round suffices (the U tile is double
-// buffered).  Jets are taken largest first: every workgroup ranks the jets
+// Jet kernel (P <= 128).  One 1024-thread workgroup per jet walks the lower
+// triangle of 16x16 tiles in rounds.  In each round the 16 waves push the
+// tile's pair blocks (one each) through the MFMA MLP chain into an LDS tile
+// of U (8 heads); then the two waves of head h apply head h of that tile:
+// wave h to query block I against key block J, wave h + 8 (transposed) to
+// query block J against key block I.  So every unique pair goes through the
+// MLP once, as in pair_embed.  The online-softmax state (O, running max,
+// running sum) of every (head, query block) is kept in LDS; within a round
+// no two waves update the same state, and the round's barrier orders the
+// updates of consecutive rounds (the U tile is double buffered).  One pair
+// block per wave keeps the kernel within 128 registers, so 16 waves (4 per
+// SIMD) share a CU; with two blocks per wave (8 waves, 238 registers) the
+// same kernel ran at 2 waves per SIMD.  Jets are taken largest first: every workgroup ranks the jets
 // by real multiplicity (from the mask) and takes the one whose rank is its
 // block index, so the hardware dispatcher schedules longest-job-first.
 //
@@ -136,13 +139,13 @@ __device__ __forceinline__ void mlp_pair_blocks(const MlpLds<kMode> &M,
 }
 
 // ------------------------------------------------------------ jet kernel
-constexpr int kJetThreads = 512;
+constexpr int kJetThreads = 1024;
 constexpr int kJetMaxP = 128;
 constexpr int kJetMaxT = kJetMaxP / kTile;
 constexpr int kSortMaxB = 2048;
 
-template <int kMode, bool kBf16 = (kMode == kMlpBf16)>
-__global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
+template <int kMode, int kThreads, bool kBf16 = (kMode == kMlpBf16)>
+__global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
     const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B, int P, int sort,
     const float4 *__restrict__ w32, const v8bf *__restrict__ w16, const v8h *__restrict__ wx2,
     const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
     __shared__ int blkAny[kJetMaxT];
     __shared__ uint16_t nj[kSortMaxB];
     __shared__ int hist[kJetMaxP + 2];
-    __shared__ int scanbuf[kJetThreads];
+    __shared__ int scanbuf[kThreads];
     __shared__ int jetSel;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -165,9 +168,9 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
 
     // ---- which jet: rank blockIdx.x in the order (n descending, index ascending)
     if (sort) {
-        for (int i = tid; i <= P + 1; i += kJetThreads) hist[i] = 0;
+        for (int i = tid; i <= P + 1; i += kThreads) hist[i] = 0;
         __syncthreads();
-        for (int b = tid; b < B; b += kJetThreads) {
+        for (int b = tid; b < B; b += kThreads) {
             // every load of the row issued before the first is used
             // (addresses clamped into the row; blocks past P / 16 not counted)
             const uint4 *row = (const uint4 *)(mask + (size_t)b * P);
@@ -197,14 +200,14 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
         __syncthreads();
         const int nstar = hist[P + 1], k = scanbuf[0];
         // k-th jet (index order) with n == nstar: contiguous ranges per thread
-        const int per = (B + kJetThreads - 1) / kJetThreads;
+        const int per = (B + kThreads - 1) / kThreads;
         const int b0 = tid * per, b1 = min(b0 + per, B);
         int cnt = 0;
         for (int b = b0; b < b1; ++b) cnt += nj[b] == nstar;
         __syncthreads();
         scanbuf[tid] = cnt;
         __syncthreads();
-        for (int off = 1; off < kJetThreads; off <<= 1) {  // inclusive scan
+        for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
             const int v = (tid >= off) ? scanbuf[tid - off] : 0;
             __syncthreads();
             scanbuf[tid] += v;
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
     const int jet = jetSel;
 
     // ---- stage particles, weights, state
-    for (int s = tid; s < P; s += kJetThreads) {
+    for (int s = tid; s < P; s += kThreads) {
         const size_t idx = (size_t)jet * P + s;
         const float4 pv = p4[idx];  // both loads issued before either is used
         const uint8_t mb = mask[idx];
@@ -235,11 +238,11 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
         const int real = mb != 0;
         stage_particle(L, s, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
     }
-    M.template stage<kJetThreads>(w32, w16, wx2, bias);
-    for (int i = tid; i < kHeads * T * 64; i += kJetThreads)
+    M.template stage<kThreads>(w32, w16, wx2, bias);
+    for (int i = tid; i < kHeads * T * 64; i += kThreads)
         (&Ost[0][0][0])[(i / (T * 64)) * kJetMaxT * 64 + i % (T * 64)] =
             make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = tid; i < kHeads * kJetMaxT * 16; i += kJetThreads) {
+    for (int i = tid; i < kHeads * kJetMaxT * 16; i += kThreads) {
         (&mst[0][0][0])[i] = -INFINITY;
         (&lst[0][0][0])[i] = 0.0f;
     }
@@ -251,7 +254,11 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
     }
     __syncthreads();
 
-    const int h = wave;  // this wave's head
+    // this wave's head; with 16 waves, the two waves of a head take the two
+    // attention units of a round (half 0: query block I, half 1: block J)
+    constexpr int kWaves = kThreads / 64;
+    static_assert(kWaves == 8 || kWaves == 16, "one or two waves per head");
+    const int h = wave & 7, half = wave >> 3;
     const size_t hb = ((size_t)jet * kHeads + h) * P;
     const QkvT<kBf16> *Qh = Q + hb * 16, *Kh = K + hb * 16, *Vh = V + hb * 16;
 
@@ -290,43 +297,65 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
         const bool diag = (I == J);
         const int nblk = diag ? 9 : 16;
         const int r0 = I * kTile, c0 = J * kTile;
-        // this round's Q, K, V (both units), in flight during the MLP
+        // this round's Q, K, V (the wave's units), in flight during the MLP
         UnitIn<kBf16> inIJ, inJI;
-        inIJ.load(Qh, Kh, Vh, r0, c0);
-        inJI.load(Qh, Kh, Vh, c0, r0);
-        int iA, jA, iB, jB;
-        const bool vA = block_pair_f(diag, 2 * wave, nblk, lane, iA, jA);
-        const bool vB = block_pair_f(diag, 2 * wave + 1, nblk, lane, iB, jB);
-        const bool realA = vA && L.real[r0 + iA] && L.real[c0 + jA];
-        const bool realB = vB && L.real[r0 + iB] && L.real[c0 + jB];
-        if (__ballot(realA || realB) != 0) {
-            const int k = lane >> 4;
-            const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, k) : 0.0f;
-            const float fB = realB ? pair_feature(L, r0 + iB, c0 + jB, k) : 0.0f;
-            v4f uA, uB;
-            mlp_pair_blocks<kMode>(M, w32, fA, fB, uA, uB);
-            if (lane < 32) {
-                const int h0 = (lane >> 4) * 4;
+        if (kWaves == 8 || half == 0) inIJ.load(Qh, Kh, Vh, r0, c0);
+        if (kWaves == 8 || half == 1) inJI.load(Qh, Kh, Vh, c0, r0);
+        if constexpr (kWaves == 8) {  // two pair blocks per wave
+            int iA, jA, iB, jB;
+            const bool vA = block_pair_f(diag, 2 * wave, nblk, lane, iA, jA);
+            const bool vB = block_pair_f(diag, 2 * wave + 1, nblk, lane, iB, jB);
+            const bool realA = vA && L.real[r0 + iA] && L.real[c0 + jA];
+            const bool realB = vB && L.real[r0 + iB] && L.real[c0 + jB];
+            if (__ballot(realA || realB) != 0) {
+                const int k = lane >> 4;
+                const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, k) : 0.0f;
+                const float fB = realB ? pair_feature(L, r0 + iB, c0 + jB, k) : 0.0f;
+                v4f uA, uB;
+                mlp_pair_blocks<kMode>(M, w32, fA, fB, uA, uB);
+                if (lane < 32) {
+                    const int h0 = (lane >> 4) * 4;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (vA) {
+                    for (int r = 0; r < 4; ++r) {
+                        if (vA) {
+                            us[buf][h0 + r][iA][jA] = uA[r];
+                            if (diag) us[buf][h0 + r][jA][iA] = uA[r];
+                        }
+                        if (vB) {
+                            us[buf][h0 + r][iB][jB] = uB[r];
+                            if (diag) us[buf][h0 + r][jB][iB] = uB[r];
+                        }
+                    }
+                }
+            }
+        } else {  // one pair block per wave
+            int iA, jA;
+            const bool vA = block_pair_f(diag, wave, nblk, lane, iA, jA);
+            const bool realA = vA && L.real[r0 + iA] && L.real[c0 + jA];
+            if (__ballot(realA) != 0) {
+                const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, lane >> 4) : 0.0f;
+                v4f uA;
+                if (!M.run1(fA, uA)) uA = mlp1_f32(w32, M.bl, fA);
+                if (lane < 32 && vA) {
+                    const int h0 = (lane >> 4) * 4;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
                         us[buf][h0 + r][iA][jA] = uA[r];
                         if (diag) us[buf][h0 + r][jA][iA] = uA[r];
-                    }
-                    if (vB) {
-                        us[buf][h0 + r][iB][jB] = uB[r];
-                        if (diag) us[buf][h0 + r][jB][iB] = uB[r];
                     }
                 }
             }
         }
         __syncthreads();
-        unit(us[buf][h], false, I, J, inIJ);
-        if (!diag) unit(us[buf][h], true, J, I, inJI);
+        if (kWaves == 8 || half == 0) unit(us[buf][h], false, I, J, inIJ);
+        if (!diag && (kWaves == 8 || half == 1)) unit(us[buf][h], true, J, I, inJI);
     }
 
     // ---- finalise this head: O = acc / l on real queries, exact 0 elsewhere
-    for (int qb = 0; qb < T; ++qb) {
+    // (with 16 waves the other wave of the head may have updated a query
+    // block in the last round: wait for it)
+    if constexpr (kWaves == 16) __syncthreads();
+    for (int qb = (kWaves == 8 ? 0 : half); qb < T; qb += kWaves / 8) {
         const int q = qb * kTile + c;
         const bool rq = blkAny[qb] && L.real[q];
         v4f o = {0.f, 0.f, 0.f, 0.f};
@@ -455,7 +484,8 @@ static hipError_t launch_fused(const float *p4, const uint8_t *mask, int B, int 
     const float qk2 = scale * kLog2e;  // scores in base-2 units
     if (P <= kJetMaxP) {
         const int sort = B <= kSortMaxB ? 1 : 0;
-        hipLaunchKernelGGL(embed_attention_jet_kernel<kMode>, dim3(B), dim3(kJetThreads), 0, s,
+        hipLaunchKernelGGL((embed_attention_jet_kernel<kMode, kJetThreads>), dim3(B),
+                           dim3(kJetThreads), 0, s,
                            (const float4 *)p4, mask, B, P, sort, (const float4 *)m->w32,
                            (const v8bf *)m->w16, (const v8h *)m->wx2, m->bias, Q, K, V, qk2, O);
     } else {

@@ -323,6 +323,84 @@ __device__ __forceinline__ void mlp2_f16x2(const float4 *__restrict__ wl,
     }
 }
 
+// One pair block through the fp16 x 2 chain (as mlp2_f16x2, for kernels that
+// give each wave a single block).
+__device__ __forceinline__ v4f mlp1_f16x2(const float4 *__restrict__ wl,
+                                          const v8h *__restrict__ wh,
+                                          const v8h *__restrict__ wlo,
+                                          const float *__restrict__ bl, float v) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    v4f h[4], u;
+    {
+        const float4 w = wl[lane];
+        const float w1[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) h[c] = mfma4(w1[c], v, bias4(bl, 16 * c + 4 * g));
+    }
+#pragma unroll
+    for (int layer = 0; layer < 3; ++layer) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[c][r] = gelu_f32(h[c][r]);
+        v8h xh[2], xl[2];
+        split_f16(h[0], h[1], xh[0], xl[0]);
+        split_f16(h[2], h[3], xh[1], xl[1]);
+        if (layer < 2) {
+#pragma unroll
+            for (int co = 0; co < 4; ++co)
+                h[co] = mfma_x2(wh, wlo, layer * 8 + co * 2, lane, xh, xl,
+                                bias4(bl, 64 * (layer + 1) + 16 * co + 4 * g));
+        } else {
+            v4f b4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b4[r] = (4 * g + r < kHeads) ? bl[192 + 4 * g + r] : 0.0f;
+            u = mfma_x2(wh, wlo, 16, lane, xh, xl, b4);
+        }
+    }
+    return u;
+}
+
+// One pair block through the bf16 chain (as mlp2_bf16).
+__device__ __forceinline__ v4f mlp1_bf16(const float4 *__restrict__ wl,
+                                         const v8bf *__restrict__ w16,
+                                         const float *__restrict__ bl, float v) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    v4f h[4], t[4];
+    {
+        const float4 w = wl[lane];
+        const float w1[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) h[c] = mfma4(w1[c], v, bias4(bl, 16 * c + 4 * g));
+    }
+#pragma unroll
+    for (int layer = 0; layer < 2; ++layer) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[c][r] = gelu_lo(h[c][r]);
+        const v8bf x0 = pack_bf16(h[0], h[1]), x1 = pack_bf16(h[2], h[3]);
+#pragma unroll
+        for (int co = 0; co < 4; ++co) {
+            const v4f b = bias4(bl, 64 * (layer + 1) + 16 * co + 4 * g);
+            const v8bf w0 = w16[(layer * 8 + co * 2 + 0) * 64 + lane];
+            const v8bf w1 = w16[(layer * 8 + co * 2 + 1) * 64 + lane];
+            t[co] = mfma32bf(w1, x1, mfma32bf(w0, x0, b));
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) h[c] = t[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[c][r] = gelu_lo(h[c][r]);
+    v4f b4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b4[r] = (4 * g + r < kHeads) ? bl[192 + 4 * g + r] : 0.0f;
+    const v8bf w0 = w16[16 * 64 + lane], w1 = w16[17 * 64 + lane];
+    return mfma32bf(w1, pack_bf16(h[2], h[3]), mfma32bf(w0, pack_bf16(h[0], h[1]), b4));
+}
+
 // One pair block through the float32 chain (weights through any pointer):
 // the exact fall back of the fp16 x 2 chain, which runs only for the rare
 // block whose fp16 x 2 result was not finite.  One block at a time keeps its
@@ -654,6 +732,25 @@ struct MlpLds {
                                               v4f &uA, v4f &uB) const {
         uA = mlp1_f32(w32, bl, fA);
         uB = mlp1_f32(w32, bl, fB);
+    }
+
+    // One pair block through this mode's chain (float32, fp16 x 2 or bf16),
+    // with run()'s meaning of the return value.
+    __device__ __forceinline__ bool run1(float f, v4f &u) const {
+        static_assert(kMode != kMlpInt8, "the int8 chain runs two blocks");
+        if constexpr (kMode == kMlpF32) {
+            u = mlp1_f32(wl, bl, f);
+            return true;
+        } else if constexpr (kMode == kMlpF16x2) {
+            u = mlp1_f16x2(wl, wh, wlo, bl, f);
+            bool ok = true;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ok = ok && __builtin_isfinite(u[r]);
+            return __ballot(!ok) == 0;
+        } else {
+            u = mlp1_bf16(wl, wb, bl, f);
+            return true;
+        }
     }
 };
 
