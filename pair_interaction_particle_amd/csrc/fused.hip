@@ -144,8 +144,8 @@ constexpr int kJetMaxP = 128;
 constexpr int kJetMaxT = kJetMaxP / kTile;
 constexpr int kSortMaxB = 2048;
 
-template <int kMode, int kThreads, bool kBf16 = (kMode == kMlpBf16)>
-__global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
+template <int kMode, bool kBf16 = (kMode == kMlpBf16)>
+__global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
     const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B, int P, int sort,
     const float4 *__restrict__ w32, const v8bf *__restrict__ w16, const v8h *__restrict__ wx2,
     const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
     __shared__ int blkAny[kJetMaxT];
     __shared__ uint16_t nj[kSortMaxB];
     __shared__ int hist[kJetMaxP + 2];
-    __shared__ int scanbuf[kThreads];
+    __shared__ int scanbuf[kJetThreads];
     __shared__ int jetSel;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -168,9 +168,9 @@ __global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
 
     // ---- which jet: rank blockIdx.x in the order (n descending, index ascending)
     if (sort) {
-        for (int i = tid; i <= P + 1; i += kThreads) hist[i] = 0;
+        for (int i = tid; i <= P + 1; i += kJetThreads) hist[i] = 0;
         __syncthreads();
-        for (int b = tid; b < B; b += kThreads) {
+        for (int b = tid; b < B; b += kJetThreads) {
             // every load of the row issued before the first is used
             // (addresses clamped into the row; blocks past P / 16 not counted)
             const uint4 *row = (const uint4 *)(mask + (size_t)b * P);
@@ -200,14 +200,14 @@ __global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
         __syncthreads();
         const int nstar = hist[P + 1], k = scanbuf[0];
         // k-th jet (index order) with n == nstar: contiguous ranges per thread
-        const int per = (B + kThreads - 1) / kThreads;
+        const int per = (B + kJetThreads - 1) / kJetThreads;
         const int b0 = tid * per, b1 = min(b0 + per, B);
         int cnt = 0;
         for (int b = b0; b < b1; ++b) cnt += nj[b] == nstar;
         __syncthreads();
         scanbuf[tid] = cnt;
         __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
+        for (int off = 1; off < kJetThreads; off <<= 1) {  // inclusive scan
             const int v = (tid >= off) ? scanbuf[tid - off] : 0;
             __syncthreads();
             scanbuf[tid] += v;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
     const int jet = jetSel;
 
     // ---- stage particles, weights, state
-    for (int s = tid; s < P; s += kThreads) {
+    for (int s = tid; s < P; s += kJetThreads) {
         const size_t idx = (size_t)jet * P + s;
         const float4 pv = p4[idx];  // both loads issued before either is used
         const uint8_t mb = mask[idx];
@@ -238,11 +238,11 @@ __global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
         const int real = mb != 0;
         stage_particle(L, s, real ? pv : make_float4(0.f, 0.f, 0.f, 0.f), real);
     }
-    M.template stage<kThreads>(w32, w16, wx2, bias);
-    for (int i = tid; i < kHeads * T * 64; i += kThreads)
+    M.template stage<kJetThreads>(w32, w16, wx2, bias);
+    for (int i = tid; i < kHeads * T * 64; i += kJetThreads)
         (&Ost[0][0][0])[(i / (T * 64)) * kJetMaxT * 64 + i % (T * 64)] =
             make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = tid; i < kHeads * kJetMaxT * 16; i += kThreads) {
+    for (int i = tid; i < kHeads * kJetMaxT * 16; i += kJetThreads) {
         (&mst[0][0][0])[i] = -INFINITY;
         (&lst[0][0][0])[i] = 0.0f;
     }
@@ -254,10 +254,9 @@ __global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
     }
     __syncthreads();
 
-    // this wave's head; with 16 waves, the two waves of a head take the two
-    // attention units of a round (half 0: query block I, half 1: block J)
-    constexpr int kWaves = kThreads / 64;
-    static_assert(kWaves == 8 || kWaves == 16, "one or two waves per head");
+    // this wave's head; the two waves of a head take the two attention units
+    // of a round (half 0: query block I, half 1: query block J)
+    static_assert(kJetThreads == 64 * 2 * kHeads, "two waves per head");
     const int h = wave & 7, half = wave >> 3;
     const size_t hb = ((size_t)jet * kHeads + h) * P;
     const QkvT<kBf16> *Qh = Q + hb * 16, *Kh = K + hb * 16, *Vh = V + hb * 16;
@@ -297,65 +296,37 @@ __global__ __launch_bounds__(kThreads) void embed_attention_jet_kernel(
         const bool diag = (I == J);
         const int nblk = diag ? 9 : 16;
         const int r0 = I * kTile, c0 = J * kTile;
-        // this round's Q, K, V (the wave's units), in flight during the MLP
-        UnitIn<kBf16> inIJ, inJI;
-        if (kWaves == 8 || half == 0) inIJ.load(Qh, Kh, Vh, r0, c0);
-        if (kWaves == 8 || half == 1) inJI.load(Qh, Kh, Vh, c0, r0);
-        if constexpr (kWaves == 8) {  // two pair blocks per wave
-            int iA, jA, iB, jB;
-            const bool vA = block_pair_f(diag, 2 * wave, nblk, lane, iA, jA);
-            const bool vB = block_pair_f(diag, 2 * wave + 1, nblk, lane, iB, jB);
-            const bool realA = vA && L.real[r0 + iA] && L.real[c0 + jA];
-            const bool realB = vB && L.real[r0 + iB] && L.real[c0 + jB];
-            if (__ballot(realA || realB) != 0) {
-                const int k = lane >> 4;
-                const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, k) : 0.0f;
-                const float fB = realB ? pair_feature(L, r0 + iB, c0 + jB, k) : 0.0f;
-                v4f uA, uB;
-                mlp_pair_blocks<kMode>(M, w32, fA, fB, uA, uB);
-                if (lane < 32) {
-                    const int h0 = (lane >> 4) * 4;
+        // this round's Q, K, V (the wave's unit), in flight during the MLP
+        UnitIn<kBf16> in;
+        if (half == 0) in.load(Qh, Kh, Vh, r0, c0);
+        else in.load(Qh, Kh, Vh, c0, r0);
+        // one pair block per wave
+        int iA, jA;
+        const bool vA = block_pair_f(diag, wave, nblk, lane, iA, jA);
+        const bool realA = vA && L.real[r0 + iA] && L.real[c0 + jA];
+        if (__ballot(realA) != 0) {
+            const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, lane >> 4) : 0.0f;
+            v4f uA;
+            if (!M.run1(fA, uA)) uA = mlp1_f32(w32, M.bl, fA);  // fp16 x 2 left its range
+            if (lane < 32 && vA) {
+                const int h0 = (lane >> 4) * 4;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (vA) {
-                            us[buf][h0 + r][iA][jA] = uA[r];
-                            if (diag) us[buf][h0 + r][jA][iA] = uA[r];
-                        }
-                        if (vB) {
-                            us[buf][h0 + r][iB][jB] = uB[r];
-                            if (diag) us[buf][h0 + r][jB][iB] = uB[r];
-                        }
-                    }
-                }
-            }
-        } else {  // one pair block per wave
-            int iA, jA;
-            const bool vA = block_pair_f(diag, wave, nblk, lane, iA, jA);
-            const bool realA = vA && L.real[r0 + iA] && L.real[c0 + jA];
-            if (__ballot(realA) != 0) {
-                const float fA = realA ? pair_feature(L, r0 + iA, c0 + jA, lane >> 4) : 0.0f;
-                v4f uA;
-                if (!M.run1(fA, uA)) uA = mlp1_f32(w32, M.bl, fA);
-                if (lane < 32 && vA) {
-                    const int h0 = (lane >> 4) * 4;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        us[buf][h0 + r][iA][jA] = uA[r];
-                        if (diag) us[buf][h0 + r][jA][iA] = uA[r];
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    us[buf][h0 + r][iA][jA] = uA[r];
+                    if (diag) us[buf][h0 + r][jA][iA] = uA[r];
                 }
             }
         }
         __syncthreads();
-        if (kWaves == 8 || half == 0) unit(us[buf][h], false, I, J, inIJ);
-        if (!diag && (kWaves == 8 || half == 1)) unit(us[buf][h], true, J, I, inJI);
+        if (half == 0) unit(us[buf][h], false, I, J, in);
+        else if (!diag) unit(us[buf][h], true, J, I, in);
     }
 
-    // ---- finalise this head: O = acc / l on real queries, exact 0 elsewhere
-    // (with 16 waves the other wave of the head may have updated a query
-    // block in the last round: wait for it)
-    if constexpr (kWaves == 16) __syncthreads();
-    for (int qb = (kWaves == 8 ? 0 : half); qb < T; qb += kWaves / 8) {
+    // ---- finalise this head's query blocks of this half: O = acc / l on
+    // real queries, exact 0 elsewhere (the other wave of the head may have
+    // updated one of them in the last round: wait for it)
+    __syncthreads();
+    for (int qb = half; qb < T; qb += 2) {
         const int q = qb * kTile + c;
         const bool rq = blkAny[qb] && L.real[q];
         v4f o = {0.f, 0.f, 0.f, 0.f};
@@ -484,8 +455,7 @@ static hipError_t launch_fused(const float *p4, const uint8_t *mask, int B, int 
     const float qk2 = scale * kLog2e;  // scores in base-2 units
     if (P <= kJetMaxP) {
         const int sort = B <= kSortMaxB ? 1 : 0;
-        hipLaunchKernelGGL((embed_attention_jet_kernel<kMode, kJetThreads>), dim3(B),
-                           dim3(kJetThreads), 0, s,
+        hipLaunchKernelGGL(embed_attention_jet_kernel<kMode>, dim3(B), dim3(kJetThreads), 0, s,
                            (const float4 *)p4, mask, B, P, sort, (const float4 *)m->w32,
                            (const v8bf *)m->w16, (const v8h *)m->wx2, m->bias, Q, K, V, qk2, O);
     } else {
