@@ -55,11 +55,11 @@ PROFILES = os.path.join(ROOT, "profiles")
 # kernel -> (profile summary file, sources whose sha256 it was taken on)
 KERNELS = {
     "pair_embed_f32": ("pair_embed_f32_kernel_B128_P128.md",
-                       ["pair_embed.hip", "pip_device.h", "pip_mlp.h"]),
+                       ["pair_embed.hip", "pip_packed.h", "pip_device.h", "pip_mlp.h"]),
     "attention_f32": ("attention_f32_kernel_B128_P128.md",
                       ["attention.hip", "pip_attn_core.h", "pip_attn.h", "pip_device.h"]),
     "pair_embed_bf16": ("pair_embed_bf16_large_B64_P256.md",
-                        ["pair_embed.hip", "pip_device.h", "pip_mlp.h"]),
+                        ["pair_embed.hip", "pip_packed.h", "pip_device.h", "pip_mlp.h"]),
     "attention_bf16": ("attention_bf16_large_B64_P256.md",
                        ["attention.hip", "pip_attn_core.h", "pip_attn.h", "pip_device.h"]),
     "fused_f32": ("pair_embed_attention_f32_fused512_B512_P128.md",
@@ -71,12 +71,12 @@ KERNELS = {
     "pair_mlp_bwd_f32": ("pair_mlp_backward_f32_kernel_B128_P128.md",
                          ["mlp_bwd.hip", "pip_device.h", "pip_mlp.h"]),
     "pair_embed_int8": ("pair_embed_int8_kernel_B128_P128.md",
-                        ["pair_embed.hip", "pip_device.h", "pip_mlp.h"]),
+                        ["pair_embed.hip", "pip_packed.h", "pip_device.h", "pip_mlp.h"]),
     "attention_bf16_kernel": ("attention_bf16_kernel_B128_P128.md",
                               ["attention.hip", "pip_attn_core.h", "pip_attn.h",
                                "pip_device.h"]),
     "pair_embed_packed_f32": ("pair_embed_packed_f32_kernel_B128_n20-128.md",
-                              ["packed_embed.hip", "pip_device.h", "pip_mlp.h"]),
+                              ["pair_embed.hip", "pip_packed.h", "pip_device.h", "pip_mlp.h"]),
     "attention_packed_f32": ("attention_packed_f32_kernel_B128_n20-128.md",
                              ["attention.hip", "pip_attn_core.h", "pip_attn.h",
                               "pip_device.h"]),

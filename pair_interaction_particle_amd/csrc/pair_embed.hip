@@ -19,11 +19,20 @@
 // diagonal tiles pack their 136 unique pairs into 9 (plus an empty 10th).
 // Each of the 8 waves pushes two pair blocks at a time through the MFMA layer
 // chain; hidden activations never leave registers.
+//
+// The same kernel takes a packed batch (jets back to back, no padding: the
+// layout of packed_embed.hip).  A packed jet of n particles has exactly
+// ceil(n/16) active blocks with its real slots first, so the work estimate
+// is exact; U is written into the jet's (8, n, ld) block, guarded to its n
+// rows and ld columns, and there are no zero tiles.  (The earlier packed
+// kernel dealt single tiles with one barrier per tile: 70.6 us against
+// 57.6 us here on the kernel workload's jets, bit-identical U.)
 #include <algorithm>
 #include <type_traits>
 
 #include "pip_internal.h"
 #include "pip_mlp.h"
+#include "pip_packed.h"
 
 namespace pip {
 
@@ -245,6 +254,70 @@ __device__ __forceinline__ void write_row_pair(const PL &L, OutT *U, int P, int 
     }
 }
 
+// ---- packed batches (jets back to back, no padding)
+// The padded kernel below also takes a packed batch (PackedArgs.cu set): jet
+// b's particles are rows cu[b] .. cu[b+1]-1 of p4, all real, and its bias is
+// the (8, n, ld) block at element 8 u_off[b], ld = n rounded up to 8.  A jet
+// whose entries are inconsistent (packed_jet_ok) counts as empty: it gets no
+// pair blocks and nothing of it is written.
+struct PackedArgs {
+    const int *cu;
+    const int64_t *uoff;
+    int N, max_n;
+    int64_t u_elems;
+};
+// real count n of packed jet b (0 when inconsistent), first row, U offset
+__device__ __forceinline__ int packed_jet(const PackedArgs &pk, int b, int &start, int64_t &u0) {
+    int n;
+    const bool ok = packed_jet_ok(pk.cu, pk.uoff, b, pk.N, pk.max_n, pk.u_elems, kHeads, n);
+    start = pk.cu[b];
+    u0 = pk.uoff[b];
+    return ok ? n : 0;
+}
+
+// The packed forms of write_row_pair / write_block: rows are n long with
+// stride ld and planes of n ld elements; nothing is written in row a >= n
+// (the next jet's) or column >= ld, and the columns n .. ld-1 of a row get
+// zeros (their pairs are not real).  ld is a multiple of 8 and a0 even, so
+// a mirrored pair (a0, a0 + 1) lies inside a row whenever a0 < ld.
+template <typename OutT, class PL>
+__device__ __forceinline__ void write_row_pair_packed(const PL &L, OutT *U, int n, int ld,
+                                                     uint32_t plane, int a0, int b,
+                                                     const v4f &uA, const v4f &uB, bool zero) {
+    const int lane = threadIdx.x & 63;
+    if (lane >= 32) return;
+    const bool rb = !zero && L.real[b];
+    const bool rA = rb && L.real[a0], rB = rb && L.real[a0 + 1];
+    const bool dA = a0 < n && b < ld, dB = a0 + 1 < n && b < ld, mir = b < n && a0 < ld;
+    const uint32_t h0 = (lane >> 4) * 4 * plane;
+    const uint32_t oab = h0 + (uint32_t)a0 * ld + b, oba = h0 + (uint32_t)b * ld + a0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float vA = rA ? uA[q] : 0.0f, vB = rB ? uB[q] : 0.0f;
+        if (dA) store_u(U, oab + q * plane, vA);
+        if (dB) store_u(U, oab + q * plane + ld, vB);
+        if (mir) store_u2(U, oba + q * plane, vA, vB);
+    }
+}
+template <typename OutT, class PL>
+__device__ __forceinline__ void write_block_packed(const PL &L, OutT *U, int n, int ld,
+                                                  uint32_t plane, int I, int J, bool valid,
+                                                  int i, int j, const v4f &u, bool zero) {
+    const int lane = threadIdx.x & 63;
+    if (lane >= 32 || !valid) return;
+    const int a = I * kTile + i, b = J * kTile + j;
+    const bool real = !zero && L.real[a] && L.real[b];
+    const bool d = a < n && b < ld, mir = a != b && b < n && a < ld;
+    const uint32_t h0 = (lane >> 4) * 4 * plane;
+    const uint32_t oab = h0 + (uint32_t)a * ld + b, oba = h0 + (uint32_t)b * ld + a;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float v = real ? u[q] : 0.0f;
+        if (d) store_u(U, oab + q * plane, v);
+        if (mir) store_u(U, oba + q * plane, v);
+    }
+}
+
 // ---- work estimate for the balanced split
 // A CU's time follows the wave iterations (pairs of blocks) it runs and the
 // jets it starts: an iteration that holds a real pair runs the MLP, an
@@ -268,6 +341,11 @@ struct JetInfo {
     uint32_t act;  // bit t: block t holds a real slot
     int n;         // real slots
 };
+// a packed jet of n real slots (all first): blocks 0 .. ceil(n/16)-1 active
+__device__ __forceinline__ JetInfo packed_info(int n) {
+    const int T = (n + kTile - 1) / kTile;  // <= 16
+    return JetInfo{(1u << T) - 1u, n};
+}
 // bit k set when byte k of x is nonzero (k < 4)
 __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
     x |= x >> 4;
@@ -394,12 +472,15 @@ __device__ __forceinline__ int jet_blocks(uint32_t act) { return blocks_before_r
 // jets), writing U straight from registers.  Workgroup w is remapped so
 // that the workgroups of one XCD (dispatch is round-robin over 8 XCDs) hold
 // adjacent ranges and thus write neighbouring parts of U.
-template <int kMode>
+// kPacked: a packed batch (PackedArgs above; mask unused, P = 16 times the
+// largest jet's block count); its jets have no padded tiles, so there are no
+// zero tiles.
+template <int kMode, bool kPacked>
 __global__ __launch_bounds__(kEmbedThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int B,
                        int P, const float4 *__restrict__ w32, const v8bf *__restrict__ w16,
                        const v8h *__restrict__ wx2, const float *__restrict__ bias,
-                       void *__restrict__ Uout, int wz, Int8Args ia) {
+                       void *__restrict__ Uout, int wz, Int8Args ia, PackedArgs pk) {
     MlpLds<kMode> M;
     if constexpr (kMode == kMlpInt8) M.set_act(ia);
     __shared__ PartLds<kMaxP> Ls[2];  // the particles of two jets
@@ -441,7 +522,16 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     jinfo[tid] = JetInfo{0u, 0};
     scan[tid] = 0;
     __syncthreads();
-    {
+    if constexpr (kPacked) {
+        wst.load(w32, w16, wx2, bias, &ia);
+        for (int b = tid; b < B; b += kEmbedThreads) {
+            int st;
+            int64_t u0;
+            const JetInfo ji = packed_info(packed_jet(pk, b, st, u0));
+            if (per == 1) jinfo[b] = ji;
+            else atomicAdd(&scan[b / per], jet_cost<WorkCost<kMode>>(ji));
+        }
+    } else {
         constexpr int kJ = 4;
         constexpr int kGroups = kEmbedThreads / 16;
         const int grp = tid >> 4;  // 0 .. kGroups - 1
@@ -485,6 +575,16 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // floor(rt (w + i) / W), exact in 32 bits (a 64-bit division costs a long
     // scalar sequence and a register spill whose reload waits for every load
     // in flight).
+    // the info of jet b (b < B), read again from the mask or the packed entries
+    auto info_of = [&](int b) -> JetInfo {
+        if constexpr (kPacked) {
+            int st;
+            int64_t u0;
+            return packed_info(packed_jet(pk, b, st, u0));
+        } else {
+            return jet_info(mask + (size_t)b * P, T);
+        }
+    };
     if (wv == 0) {
         constexpr int kPerLane = kEmbedThreads / 64;
         int cst[kPerLane], sum = 0;
@@ -533,19 +633,19 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
             if (sb[0] < B) js = jinfo[sb[0]];
             if (sb[1] < B) je = jinfo[sb[1]];
         } else {
-            js = sb[0] < B ? jet_info(mask + (size_t)sb[0] * P, T) : JetInfo{0u, 0};
-            je = sb[1] < B ? jet_info(mask + (size_t)sb[1] * P, T) : JetInfo{0u, 0};
+            js = sb[0] < B ? info_of(sb[0]) : JetInfo{0u, 0};
+            je = sb[1] < B ? info_of(sb[1]) : JetInfo{0u, 0};
             for (int jc = jet_cost<WorkCost<kMode>>(js); sb[0] < B && st[0] >= jc;
                  jc = jet_cost<WorkCost<kMode>>(js)) {
                 st[0] -= jc;
                 ++sb[0];
-                js = jet_info(mask + (size_t)min(sb[0], B - 1) * P, T);
+                js = info_of(min(sb[0], B - 1));
             }
             for (int jc = jet_cost<WorkCost<kMode>>(je); sb[1] < B && st[1] >= jc;
                  jc = jet_cost<WorkCost<kMode>>(je)) {
                 st[1] -= jc;
                 ++sb[1];
-                je = jet_info(mask + (size_t)min(sb[1], B - 1) * P, T);
+                je = info_of(min(sb[1], B - 1));
             }
         }
         if (lane == 0) {
@@ -567,6 +667,17 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     auto stage_jet = [&](int j) {
         const int b = bS + j;
         PartLds<kMaxP> &Lj = Ls[j & 1];
+        if constexpr (kPacked) {  // rows 0 .. n-1 real, the rest of the last block padding
+            int st;
+            int64_t u0;
+            const int n = packed_jet(pk, b, st, u0), ns = (n + kTile - 1) / kTile * kTile;
+            for (int s = tid; s < ns; s += kEmbedThreads) {
+                const bool real = s < n;
+                stage_particle(Lj, s, real ? p4[(size_t)st + s] : make_float4(0.f, 0.f, 0.f, 0.f),
+                               real);
+            }
+            return;
+        }
         for (int s = tid; s < P; s += kEmbedThreads) {
             const size_t idx = (size_t)b * P + s;
             // both loads issued before either is used (a load under the mask
@@ -585,7 +696,19 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // the first two jets at once, so that no barrier separates them: thread t
     // takes particle t % kMaxP of jet t / kMaxP
     static_assert(kEmbedThreads >= 2 * kMaxP, "one particle per thread for two jets");
-    {
+    if constexpr (kPacked) {
+        const int j = tid / kMaxP, sl = tid % kMaxP;
+        if (j < min(nj, 2)) {
+            int st;
+            int64_t u0;
+            const int n = packed_jet(pk, bS + j, st, u0);
+            if (sl < (n + kTile - 1) / kTile * kTile) {
+                const bool real = sl < n;
+                stage_particle(Ls[j], sl,
+                               real ? p4[(size_t)st + sl] : make_float4(0.f, 0.f, 0.f, 0.f), real);
+            }
+        }
+    } else {
         const int j = tid / kMaxP, sl = tid % kMaxP;
         if (j < min(nj, 2) && sl < P) {
             const size_t idx = (size_t)(bS + j) * P + sl;
@@ -608,13 +731,25 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
         constexpr bool kExact = decltype(exact_t)::value;
         const int b = bS + j;
         const PartLds<kMaxP> &L = Ls[j & 1];
-        const uint32_t act = b == bS   ? js.act
-                             : b == bE ? je.act
-                             : per == 1 ? jinfo[b].act
-                                        : jet_activity(mask + (size_t)b * P, T);
+        uint32_t act;
+        if (b == bS) act = js.act;
+        else if (b == bE) act = je.act;
+        else if (per == 1) act = jinfo[b].act;
+        else if constexpr (kPacked) act = info_of(b).act;
+        else act = jet_activity(mask + (size_t)b * P, T);
         const int q0 = b == bS ? qS : 0, q1 = b == bE ? qE : jet_blocks(act);
         const int nit = max(0, (q1 - q0) >> 1);
         OutT *U = (OutT *)Uout + (size_t)b * kHeads * P * P;
+        int pn = 0, pld = 0;  // packed: the jet's rows and row stride
+        uint32_t pplane = 0;
+        if constexpr (kPacked) {
+            int st;
+            int64_t u0;
+            pn = packed_jet(pk, b, st, u0);
+            pld = packed_ld(pn);
+            pplane = (uint32_t)(pn * pld);
+            U = (OutT *)Uout + (size_t)kHeads * u0;
+        }
         const uint64_t aidx = active_index(act);
         bool ok = true;
         int ia = block_row(max(q0, 0));
@@ -667,7 +802,14 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
                 if constexpr (kExact) M.run_exact(w32, fA, fB, uA, uB);
                 else ok = M.run(fA, fB, uA, uB) && ok;
             }
-            if (!diag) {  // rows kb, kb + 1 of one off-diagonal tile
+            if constexpr (kPacked) {
+                if (!diag) {
+                    write_row_pair_packed<OutT>(L, U, pn, pld, pplane, aA, bA, uA, uB, !any);
+                } else {
+                    write_block_packed<OutT>(L, U, pn, pld, pplane, I, J, vA, iA, jA, uA, !any);
+                    write_block_packed<OutT>(L, U, pn, pld, pplane, I, J, vB, iB, jB, uB, !any);
+                }
+            } else if (!diag) {  // rows kb, kb + 1 of one off-diagonal tile
                 write_row_pair<OutT>(L, U, P, aA, bA, uA, uB, !any);
             } else {
                 write_block<OutT>(L, U, P, I, J, vA, iA, jA, uA, !any);
@@ -704,7 +846,7 @@ void pair_embed_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict_
     // stores overlap the other workgroups' work; jet activity read once per
     // jet).  Only the first wz workgroups (one per CU: workgroups i and
     // i + wz share a CU, and the older one finishes first) write them.
-    if ((int)blockIdx.x < wz) {
+    if (!kPacked && (int)blockIdx.x < wz) {
         // tiles [tot zw / wz, tot (zw + 1) / wz), floors taken in 32 bits as above
         const int zw = blockIdx.x;
         const int tot = B * ntri, qz = tot / wz, rz = tot - qz * wz;
@@ -764,14 +906,55 @@ static hipError_t launch_embed(const float *p4, const uint8_t *mask, int B, int 
         const int grid = persistent_grid(nb, P);
         // zero tiles: the workgroups that are first on their CU
         const int wz = std::max(1, std::min(grid, cu_count()));
-        hipLaunchKernelGGL(pair_embed_kernel<kMode>, dim3(grid), dim3(kEmbedThreads), 0, s,
-                           (const float4 *)p4 + (size_t)b0 * P, mask + (size_t)b0 * P, nb, P,
+        hipLaunchKernelGGL((pair_embed_kernel<kMode, false>), dim3(grid), dim3(kEmbedThreads), 0,
+                           s, (const float4 *)p4 + (size_t)b0 * P, mask + (size_t)b0 * P, nb, P,
                            (const float4 *)m->w32, (const v8bf *)m->w16, (const v8h *)m->wx2,
-                           m->bias, (void *)((OutT *)U + (size_t)b0 * kHeads * P * P), wz, ia);
+                           m->bias, (void *)((OutT *)U + (size_t)b0 * kHeads * P * P), wz, ia,
+                           PackedArgs{nullptr, nullptr, 0, 0, 0});
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// A packed batch: the same kernel over the jets' real blocks (P = 16 times
+// the largest block count), cut into segments of at most 65,536 jets (cu and
+// u_off of a segment are the batch's, offset; rows and U offsets stay
+// absolute).
+template <int kMode>
+static hipError_t launch_embed_packed(const float *p4, const int *cu, const int64_t *uoff, int B,
+                                      int N, int max_n, const pip_pair_mlp *m, void *U,
+                                      int64_t u_elems, hipStream_t s) {
+    const int P = (max_n + kTile - 1) / kTile * kTile;
+    if (P == 0) return hipSuccess;
+    constexpr int kSeg = 65536;
+    for (int b0 = 0; b0 < B; b0 += kSeg) {
+        const int nb = std::min(kSeg, B - b0);
+        const int grid = persistent_grid(nb, P);
+        const int wz = std::max(1, std::min(grid, cu_count()));
+        hipLaunchKernelGGL((pair_embed_kernel<kMode, true>), dim3(grid), dim3(kEmbedThreads), 0, s,
+                           (const float4 *)p4, (const uint8_t *)nullptr, nb, P,
+                           (const float4 *)m->w32, (const v8bf *)m->w16, (const v8h *)m->wx2,
+                           m->bias, U, wz, Int8Args{},
+                           PackedArgs{cu + b0, uoff + b0, N, max_n, u_elems});
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_pair_embed_packed_f32(const float *p4, const int *cu, const int64_t *uoff,
+                                        int B, int N, int max_n, const pip_pair_mlp *m, float *U,
+                                        int64_t u_elems, hipStream_t s) {
+    return m->f16ok
+               ? launch_embed_packed<kMlpF16x2>(p4, cu, uoff, B, N, max_n, m, U, u_elems, s)
+               : launch_embed_packed<kMlpF32>(p4, cu, uoff, B, N, max_n, m, U, u_elems, s);
+}
+
+hipError_t launch_pair_embed_packed_bf16(const float *p4, const int *cu, const int64_t *uoff,
+                                         int B, int N, int max_n, const pip_pair_mlp *m,
+                                         uint16_t *U, int64_t u_elems, hipStream_t s) {
+    return launch_embed_packed<kMlpBf16>(p4, cu, uoff, B, N, max_n, m, U, u_elems, s);
 }
 
 hipError_t launch_pair_embed_f32(const float *p4, const uint8_t *mask, int B, int P,
