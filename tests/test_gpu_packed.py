@@ -88,6 +88,30 @@ def test_packed_embed_and_attention_ragged(dtype):
     assert_close(O, ref, TOLBF if bf else TOL32, "packed O " + dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_packed_embed_writes_every_element(dtype):
+    # an output buffer full of NaN: every element of every jet's block (rows
+    # < n, the columns up to ld included) must be written, and nothing else
+    ns = NS + (8, 24, 40, 15, 31, 2)
+    P = 256
+    p4, mask = jets(ns, P, seed=141)
+    params = mlp_for(141, biases=True)
+    mlp = pip.PairMLP(params)
+    cu = synth.cu_seqlens(mask)
+    n = np.asarray(ns, dtype=np.int64)
+    total = int(8 * (n * ((n + 7) // 8 * 8)).sum())
+    bf = dtype == "bf16"
+    tdt = torch.bfloat16 if bf else torch.float32
+    out = torch.full((total + 64,), float("nan"), device="cuda", dtype=tdt)
+    U, _ = pip.pair_embed_packed(g(synth.pack_rows(p4, mask)), g(cu), mlp, dtype=dtype,
+                                 out=out[:total])
+    tail = host(out[total:]).astype(np.float64)
+    assert np.isnan(tail).all(), "packed U: written past the last jet's block"
+    Uref = oracle.pair_embed(p4, mask, params)
+    check_u(host(U), Uref, ns, TOLBF if bf else TOL32, TOLBF_U if bf else TOL32,
+            "packed U %s (NaN-filled output)" % dtype)
+
+
 def test_packed_kernel_workload_f32():
     d = synth.make_workload("kernel")
     mask, ns = d["mask"], d["n"]
@@ -156,9 +180,9 @@ def test_inconsistent_jets_are_skipped():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_packed_embed_beyond_the_tile_prefix(dtype):
-    # more jets than the persistent kernel's LDS prefix holds (4096): the
-    # one-workgroup-per-row kernel takes the batch, same results
+def test_packed_embed_more_jets_than_threads(dtype):
+    # far more jets than a workgroup has threads (512): each thread sums the
+    # work of a range of jets, and the split walks the packed entries
     rng = np.random.default_rng(131)
     ns = tuple(int(x) for x in rng.integers(0, 41, size=4100))
     P = 48
