@@ -21,7 +21,8 @@
 // Row kernel (any P <= 256).  One 256-thread workgroup per (jet, query block
 // I) computes the U tiles (I, J) for every key block J and consumes them at
 // once; each wave owns two heads.  It recomputes the MLP for the mirrored
-// pairs and is used only where the jet kernel's LDS state does not fit.
+// pairs and is used where the jet kernel's LDS state does not fit (P > 128)
+// and for batches of at most half as many jets as CUs.
 #include <type_traits>
 
 #include "pip_attn.h"
@@ -453,7 +454,13 @@ static hipError_t launch_fused(const float *p4, const uint8_t *mask, int B, int 
                                const QkvT<kBf16> *K, const QkvT<kBf16> *V, float scale,
                                QkvT<kBf16> *O, hipStream_t s) {
     const float qk2 = scale * kLog2e;  // scores in base-2 units
-    if (P <= kJetMaxP) {
+    // The jet kernel gives each jet one CU for all its rounds: with at most
+    // half as many jets as CUs, half the chip idles and the largest jet sets
+    // the time (about 250 us at P = 128 whatever the batch).  The row kernel
+    // spreads a jet over its query blocks, at twice the MLP work.  Measured
+    // crossover at P = 128: row 212 us against jet 249 at B = 128, 283
+    // against 253 at B = 192 (identical O).
+    if (P <= kJetMaxP && 2 * B > cu_count()) {
         const int sort = B <= kSortMaxB ? 1 : 0;
         hipLaunchKernelGGL(embed_attention_jet_kernel<kMode>, dim3(B), dim3(kJetThreads), 0, s,
                            (const float4 *)p4, mask, B, P, sort, (const float4 *)m->w32,

@@ -15,15 +15,27 @@ from test_gpu_parity import (TOL32, TOLBF, assert_close, assert_zero_bits, g, ho
 pytestmark = pytest.mark.gpu
 
 
+def with_empty_jets(B, ns):
+    """Append empty jets until the batch is more than half the CU count: the
+    fused entry then takes the jet kernel at P <= 128 (smaller batches take
+    the row kernel)."""
+    extra = max(0, torch.cuda.get_device_properties(0).multi_processor_count // 2 + 1 - B)
+    return B + extra, tuple(ns) + (0,) * extra
+
+
+@pytest.mark.parametrize("fill", [False, True])  # True: padded to the jet kernel's batch sizes
 @pytest.mark.parametrize("B,P,ns", [
-    (2, 16, (11, 16)),                 # jet kernel
-    (6, 64, (64, 50, 17, 16, 1, 0)),   # jet kernel, ragged, empty jet, hole
-    (3, 128, (128, 20, 77)),           # jet kernel at its largest P
-    (3, 256, (256, 131, 0)),           # row kernel (P > 128)
-    (2, 144, (144, 40)),               # row kernel, odd block count
+    (2, 16, (11, 16)),
+    (6, 64, (64, 50, 17, 16, 1, 0)),   # ragged, empty jet, hole
+    (3, 128, (128, 20, 77)),           # the jet kernel's largest P
+    (3, 256, (256, 131, 0)),           # row kernel only (P > 128)
+    (2, 144, (144, 40)),               # row kernel only, odd block count
 ])
-def test_fused_f32(B, P, ns):
-    p4, mask = ragged_jets(B, P, ns, seed=P + B)
+def test_fused_f32(B, P, ns, fill):
+    seed = P + B
+    if fill:
+        B, ns = with_empty_jets(B, ns)
+    p4, mask = ragged_jets(B, P, ns, seed=seed)
     params = mlp_for(P, biases=True, input_bn=(P == 64))
     q, k, v = rand_qkv(B, 8, P, mask, seed=P)
     mlp = pip.PairMLP(params)
@@ -33,8 +45,11 @@ def test_fused_f32(B, P, ns):
     assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "fused O padded rows")
 
 
+@pytest.mark.parametrize("fill", [False, True])
 @pytest.mark.parametrize("B,P,ns", [(4, 128, (128, 60, 9, 100)), (2, 256, (256, 90))])
-def test_fused_bf16(B, P, ns):
+def test_fused_bf16(B, P, ns, fill):
+    if fill:
+        B, ns = with_empty_jets(B, ns)
     p4, mask = ragged_jets(B, P, ns, seed=P + 7, sigma=0.8)
     params = mlp_for(P + 1)
     q, k, v = rand_qkv(B, 8, P, mask, seed=P + 1, dtype="bf16")
@@ -46,12 +61,16 @@ def test_fused_bf16(B, P, ns):
     assert_zero_bits(O.transpose(0, 2, 1, 3), mask == 0, "fused bf16 padded rows")
 
 
+@pytest.mark.parametrize("fill", [False, True])
 @pytest.mark.parametrize("P,ns", [(48, (48, 30, 17)), (160, (160, 70, 17))])
-def test_fused_f32_mlp_modes(P, ns):
+def test_fused_f32_mlp_modes(P, ns, fill):
     # The fp16 x 2 chain with a hidden channel beyond fp16 (redone exactly),
     # then the exact chain chosen for badly scaled weights; jet and row kernel.
-    p4, mask = ragged_jets(3, P, ns, seed=P + 21)
-    q, k, v = rand_qkv(3, 8, P, mask, seed=P + 21)
+    B = 3
+    if fill:
+        B, ns = with_empty_jets(B, ns)
+    p4, mask = ragged_jets(B, P, ns, seed=P + 21)
+    q, k, v = rand_qkv(B, 8, P, mask, seed=P + 21)
     over = mlp_for(21, biases=True)
     over["b1"] = over["b1"].copy()
     over["b1"][5] = 8.0e4
