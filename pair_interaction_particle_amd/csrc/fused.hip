@@ -18,9 +18,10 @@
 // by real multiplicity (from the mask) and takes the one whose rank is its
 // block index, so the hardware dispatcher schedules longest-job-first.
 //
-// Row kernel (any P <= 256).  One 256-thread workgroup per (jet, query block
+// Row kernel (any P <= 256).  One 512-thread workgroup per (jet, query block
 // I) computes the U tiles (I, J) for every key block J and consumes them at
-// once; each wave owns two heads.  It recomputes the MLP for the mirrored
+// once; each of its 8 waves computes two rows of every tile and owns one
+// head.  It recomputes the MLP for the mirrored
 // pairs and is used where the jet kernel's LDS state does not fit (P > 128)
 // and for batches of at most half as many jets as CUs.
 #include <type_traits>
@@ -341,10 +342,11 @@ __global__ __launch_bounds__(kJetThreads) void embed_attention_jet_kernel(
 }
 
 // ------------------------------------------------------------ row kernel
-constexpr int kRowThreads = 256;
+constexpr int kRowThreads = 512;  // 8 waves: two rows of the tile and one head each
 
 template <int kMode, bool kBf16 = (kMode == kMlpBf16)>
-__global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+embed_attention_row_kernel(
     const float4 *__restrict__ p4, const uint8_t *__restrict__ mask, int P,
     const float4 *__restrict__ w32, const v8bf *__restrict__ w16, const v8h *__restrict__ wx2,
     const float *__restrict__ bias, const QkvT<kBf16> *__restrict__ Q,
@@ -387,63 +389,73 @@ __global__ __launch_bounds__(kRowThreads) void embed_attention_row_kernel(
     M.template stage<kRowThreads>(w32, w16, wx2, bias);
     __syncthreads();
 
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-    v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    static_assert(kRowThreads == 64 * kHeads, "one head per wave");
+    const int h = wave;
+    const size_t hb = ((size_t)jet * kHeads + h) * P;
+    float m = -INFINITY, l = 0.f;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
     for (int J = 0; J < T; ++J) {
         if (!blkAny[J]) continue;
         const int c0 = J * kTile;
-        // this key block's Q, K, V for the wave's two heads, in flight during the MLP
-        UnitIn<kBf16> in[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const size_t hb = ((size_t)jet * kHeads + 2 * wave + hh) * P;
-            in[hh].load(Q + hb * 16, K + hb * 16, V + hb * 16, r0, c0);
-        }
-        for (int pass = 0; pass < 2; ++pass) {  // rows 8 pass + 2 wave + {0, 1}
-            const int iA = 8 * pass + 2 * wave, iB = iA + 1, j = lane & 15;
+        // this key block's Q, K, V for the wave's head, in flight during the MLP
+        UnitIn<kBf16> in;
+        in.load(Q + hb * 16, K + hb * 16, V + hb * 16, r0, c0);
+        {  // rows 2 wave and 2 wave + 1 of tile (I, J)
+            const int iA = 2 * wave, iB = iA + 1, j = lane & 15;
             const bool realA = L.real[r0 + iA] && L.real[c0 + j];
             const bool realB = L.real[r0 + iB] && L.real[c0 + j];
-            if (__ballot(realA || realB) == 0) continue;
-            const int k = lane >> 4;
-            const float fA = realA ? pair_feature(L, r0 + iA, c0 + j, k) : 0.0f;
-            const float fB = realB ? pair_feature(L, r0 + iB, c0 + j, k) : 0.0f;
-            v4f uA, uB;
-            mlp_pair_blocks<kMode>(M, w32, fA, fB, uA, uB);
-            if (lane < 32) {
-                const int h0 = (lane >> 4) * 4;
+            if (__ballot(realA || realB) != 0) {
+                const int k = lane >> 4;
+                if constexpr (kMode == kMlpBf16) {  // both blocks at once (102 registers)
+                    const float fA = realA ? pair_feature(L, r0 + iA, c0 + j, k) : 0.0f;
+                    const float fB = realB ? pair_feature(L, r0 + iB, c0 + j, k) : 0.0f;
+                    v4f uA, uB;
+                    mlp_pair_blocks<kMode>(M, w32, fA, fB, uA, uB);
+                    if (lane < 32) {
+                        const int h0 = (lane >> 4) * 4;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    us[h0 + r][iA][j] = uA[r];
-                    us[h0 + r][iB][j] = uB[r];
+                        for (int r = 0; r < 4; ++r) {
+                            us[h0 + r][iA][j] = uA[r];
+                            us[h0 + r][iB][j] = uB[r];
+                        }
+                    }
+                } else {  // float32 chains: one block at a time (two do not fit 128 registers)
+#pragma unroll 1
+                    for (int t = 0; t < 2; ++t) {
+                        const int i = iA + t;
+                        const bool rl = t ? realB : realA;
+                        const float f = rl ? pair_feature(L, r0 + i, c0 + j, k) : 0.0f;
+                        v4f u;
+                        if (!M.run1(f, u)) u = mlp1_f32(w32, M.bl, f);  // fp16 x 2 left its range
+                        if (lane < 32) {
+                            const int h0 = (lane >> 4) * 4;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) us[h0 + r][i][j] = u[r];
+                        }
+                    }
                 }
             }
         }
         __syncthreads();
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int h = 2 * wave + hh;
-            v4f s = in[hh].scores();
+        {
+            v4f sc = in.scores();
             int kreal[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 kreal[r] = L.real[c0 + 4 * g + r];
-                s[r] = kreal[r] ? fmaf(s[r], qk2, us[h][c][4 * g + r] * kLog2e)
-                                : -INFINITY;
+                sc[r] = kreal[r] ? fmaf(sc[r], qk2, us[h][c][4 * g + r] * kLog2e) : -INFINITY;
             }
-            const float corr = online_softmax(s, m[hh], l[hh]);
-            acc[hh] *= corr;
-            acc[hh] = in[hh].pv(s, kreal, acc[hh]);
+            const float corr = online_softmax(sc, m, l);
+            acc *= corr;
+            acc = in.pv(sc, kreal, acc);
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int h = 2 * wave + hh;
-        const size_t hb = ((size_t)jet * kHeads + h) * P;
+    {
         const int q = r0 + c;
         const bool rq = L.real[q];
-        const float inv = rq ? 1.0f / l[hh] : 0.0f;
-        v4f o = rq ? acc[hh] * inv : (v4f){0.f, 0.f, 0.f, 0.f};
+        const float inv = rq ? 1.0f / l : 0.0f;
+        const v4f o = rq ? acc * inv : (v4f){0.f, 0.f, 0.f, 0.f};
         store_o<kBf16>(O + (hb + q) * 16 + 4 * g, o);
     }
 }
