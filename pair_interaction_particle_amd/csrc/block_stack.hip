@@ -28,6 +28,7 @@ namespace pip {
 
 constexpr int kStackWaves = 4;
 constexpr int kStackThreads = 64 * kStackWaves;
+constexpr int kMaxC = 256;  // channels (C % 16 == 0, C <= 256)
 
 // ------------------------------------------------------------ prep
 // One workgroup per (layer, matrix, column tile nt).  Packed operand index:
@@ -38,43 +39,61 @@ __global__ __launch_bounds__(kStackThreads) void stack_prep_kernel(
     const float *__restrict__ Wq, const float *__restrict__ Wk, const float *__restrict__ Wv,
     const float *__restrict__ Wo, int C, uint16_t *__restrict__ Ahi, uint16_t *__restrict__ Alo,
     float *__restrict__ colinv) {
+    // Thread t converts operand elements idx = t + 256 i (i < KS * 2): all of
+    // them in column c = (t / 8) % 16, so one round of loads (every load
+    // issued before the first is used) gives both the column maximum and the
+    // values to convert.
+    constexpr int kMaxKS = kMaxC / 32, kPer = kMaxKS * 512 / kStackThreads;
     __shared__ float part[kStackThreads];
     __shared__ int partnan[kStackThreads];
     __shared__ float cs[16];
     const int NT = C / 16, KS = (C + 31) / 32;
     const int nt = blockIdx.x % NT, lm = blockIdx.x / NT, m = lm & 3, layer = lm >> 2;
     const float *W = (m == 0 ? Wq : m == 1 ? Wk : m == 2 ? Wv : Wo) + (size_t)layer * C * C;
-    const int tid = threadIdx.x, col = tid & 15;
+    const int tid = threadIdx.x, col = (tid >> 3) & 15;
+    const int n = KS * 512 / kStackThreads;  // elements of this thread (<= kPer)
+    float w[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int idx = tid + kStackThreads * i;
+        const int s = idx >> 9, lane = (idx >> 3) & 63, j = idx & 7;
+        const int k = 32 * s + 8 * (lane >> 4) + j;
+        w[i] = (i < n && k < C) ? W[(size_t)k * C + 16 * nt + col] : 0.f;
+    }
     float mx = 0.f;
     int nan = 0;  // fmaxf drops NaN: a NaN column keeps scale 1
-    for (int k = tid >> 4; k < C; k += kStackThreads / 16) {
-        const float w = W[(size_t)k * C + 16 * nt + col];
-        mx = fmaxf(mx, fabsf(w));
-        nan |= w != w;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        mx = fmaxf(mx, fabsf(w[i]));
+        nan |= w[i] != w[i];
     }
     part[tid] = mx;
     partnan[tid] = nan;
     __syncthreads();
-    if (tid < 16) {
+    if (tid < 16) {  // column tid: threads t with (t / 8) % 16 == tid
         float a = 0.f;
         int anynan = 0;
-        for (int i = tid; i < kStackThreads; i += 16) {
-            a = fmaxf(a, part[i]);
-            anynan |= partnan[i];
-        }
-        float s, inv;
-        pow2_scale(anynan ? __uint_as_float(0x7fc00000u) : a, s, inv);
-        cs[tid] = s;
+        for (int t = 8 * tid; t < kStackThreads; t += 128)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                a = fmaxf(a, part[t + e]);
+                anynan |= partnan[t + e];
+            }
+        float sc, inv;
+        pow2_scale(anynan ? __uint_as_float(0x7fc00000u) : a, sc, inv);
+        cs[tid] = sc;
         colinv[(size_t)lm * C + 16 * nt + tid] = inv;
     }
     __syncthreads();
     const size_t base = ((size_t)lm * NT + nt) * KS * 512;
-    for (int idx = tid; idx < KS * 512; idx += kStackThreads) {
-        const int s = idx >> 9, lane = (idx >> 3) & 63, j = idx & 7;
-        const int k = 32 * s + 8 * (lane >> 4) + j, c = lane & 15;
-        const float w = k < C ? W[(size_t)k * C + 16 * nt + c] * cs[c] : 0.f;
-        const _Float16 hi = (_Float16)w;
-        const _Float16 lo = (_Float16)(w - (float)hi);
+    const float sc = cs[col];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (i >= n) break;
+        const int idx = tid + kStackThreads * i;
+        const float x = w[i] * sc;
+        const _Float16 hi = (_Float16)x;
+        const _Float16 lo = (_Float16)(x - (float)hi);
         Ahi[base + idx] = __builtin_bit_cast(uint16_t, hi);
         Alo[base + idx] = __builtin_bit_cast(uint16_t, lo);
     }
