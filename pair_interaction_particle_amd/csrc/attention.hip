@@ -8,7 +8,8 @@
 // The kernel reads U once and is bound by HBM, so the design is about bytes in
 // flight: every workgroup of the launch should be resident at once, issue all
 // of its loads early and have little work left once the data is there.  One
-// workgroup per (jet, head, group of up to 8 query blocks of 16 queries); each
+// workgroup per (jet, head, group of up to 4 (P <= 128) or 8 query blocks of 16
+// queries); each
 // wave owns one query block.
 //   1. Each wave takes the jet's real-slot bits with ballots (wave-uniform,
 //      no LDS), then issues the loads of its U strips (16 queries x every key
@@ -44,7 +45,11 @@
 
 namespace pip {
 
-constexpr int kAttnQBlocks = 8;  // query blocks per workgroup
+// Query blocks per workgroup: 4 for P <= 128 (a jet of at most 64 real
+// slots then leaves its second workgroup nothing to do, and it ends at once,
+// instead of holding four idle waves), 8 beyond (the larger register
+// strips would lower the occupancy with 4).
+__host__ __device__ constexpr int attn_qblocks(int kT) { return kT <= 8 ? 4 : 8; }
 // ------------------------------------------------------------ float32
 // One query block (rows q0 .. q0+15) of a float32 head.  u is the U strip
 // (-inf for key blocks without a real key), qa / qc are this lane's Q row
@@ -155,7 +160,7 @@ __device__ __forceinline__ void attend_bf16(uint2 (&u)[kT], v4s qv, bool rq, boo
 // (float32 at P <= 128: held to 6 waves per SIMD, i.e. at most 80 VGPRs, so
 // that three workgroups stay resident per CU)
 template <bool kBf16, int kT, int kQ, bool kPacked>
-__global__ __launch_bounds__(64 * kAttnQBlocks / kQ)
+__global__ __launch_bounds__(64 * attn_qblocks(kT) / kQ)
 __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_kernel(
     const AttnElt<kBf16> *__restrict__ Q, const AttnElt<kBf16> *__restrict__ K,
     const AttnElt<kBf16> *__restrict__ V, const AttnElt<kBf16> *__restrict__ U,
@@ -163,7 +168,8 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     AttnElt<kBf16> *__restrict__ O, const int *__restrict__ cu,
     const int64_t *__restrict__ uoff, int N, int64_t u_elems) {
     using E = AttnElt<kBf16>;
-    constexpr int kWaves = kAttnQBlocks / kQ, kThreads = 64 * kWaves;
+    constexpr int kQB = attn_qblocks(kT);
+    constexpr int kWaves = kQB / kQ, kThreads = 64 * kWaves;
     constexpr int kWords = (kT * 16 + 63) / 64;
     // fp32: K rows as 32 fp16 [hi d0..15 | lo d0..15], V hi and lo;
     // bf16: K rows of 16 bf16 and V.  K rows in key order (fp32) or key_row
@@ -215,7 +221,7 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
         rows = n;
         ld = lp;
         T = (n + kTile - 1) / kTile;
-        if (chunk * kAttnQBlocks >= T) return;  // uniform: nothing of this jet here
+        if (chunk * kQB >= T) return;  // uniform: nothing of this jet here
         const size_t base = (size_t)h * N + start;
         Qh = Q + base * 16;
         Kh = K + base * 16;
@@ -253,7 +259,7 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     const int zero = P >> 16;
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
-        const int qb = chunk * kAttnQBlocks + wave + j * kWaves;
+        const int qb = chunk * kQB + wave + j * kWaves;
         const bool act = qb < T && real.block_rt(qb) != 0;
         const int qr = act && qb * kTile + c < rows ? qb * kTile + c : 0;  // query row read
         const E *urow = Ub + (size_t)qr * ld;
@@ -343,7 +349,7 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     // ---- 3. per query block
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
-        const int qb = chunk * kAttnQBlocks + wave + j * kWaves;
+        const int qb = chunk * kQB + wave + j * kWaves;
         const int q0 = qb * kTile;
         if (qb >= T) continue;
         E *orow = Oh + (size_t)(q0 + c) * 16 + 4 * g;
@@ -374,7 +380,11 @@ __attribute__((amdgpu_waves_per_eu(!kBf16 && kT == 8 ? 6 : 1))) void attention_k
     }
 }
 
-int attention_chunks(int P) { return (P / kTile + kAttnQBlocks - 1) / kAttnQBlocks; }
+// workgroups per (jet, head) (P rounded up to 16)
+int attention_chunks(int P) {
+    const int T = P / kTile, qb = attn_qblocks(T <= 8 ? 8 : 16);
+    return (T + qb - 1) / qb;
+}
 
 // jets the grid covers: B rounded up to the 8 XCDs
 int64_t attention_jet_slots(int64_t B) { return (B + 7) / 8 * 8; }
@@ -387,12 +397,12 @@ static hipError_t launch_attention(const AttnElt<kBf16> *Q, const AttnElt<kBf16>
     const int chunks = attention_chunks(P);
     const dim3 grid((unsigned)(attention_jet_slots(B) * H * chunks));
     if (P <= 128)
-        hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1, false>), grid, dim3(64 * kAttnQBlocks),
+        hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1, false>), grid, dim3(64 * attn_qblocks(8)),
                            0, s, Q, K, V, U, mask, B, H, P, chunks, scale, O, nullptr, nullptr,
                            0, (int64_t)0);
     else
         hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1, false>), grid,
-                           dim3(64 * kAttnQBlocks), 0, s, Q, K, V, U, mask, B, H, P, chunks,
+                           dim3(64 * attn_qblocks(16)), 0, s, Q, K, V, U, mask, B, H, P, chunks,
                            scale, O, nullptr, nullptr, 0, (int64_t)0);
     return hipGetLastError();
 }
@@ -421,12 +431,12 @@ static hipError_t launch_attention_packed(const AttnElt<kBf16> *Q, const AttnElt
     if (chunks == 0) return hipSuccess;
     const dim3 grid((unsigned)(attention_jet_slots(B) * H * chunks));
     if (max_n <= 128)
-        hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1, true>), grid, dim3(64 * kAttnQBlocks),
+        hipLaunchKernelGGL((attention_kernel<kBf16, 8, 1, true>), grid, dim3(64 * attn_qblocks(8)),
                            0, s, Q, K, V, U, nullptr, B, H, max_n, chunks, scale, O, cu, uoff,
                            N, u_elems);
     else
         hipLaunchKernelGGL((attention_kernel<kBf16, 16, 1, true>), grid,
-                           dim3(64 * kAttnQBlocks), 0, s, Q, K, V, U, nullptr, B, H, max_n,
+                           dim3(64 * attn_qblocks(16)), 0, s, Q, K, V, U, nullptr, B, H, max_n,
                            chunks, scale, O, cu, uoff, N, u_elems);
     return hipGetLastError();
 }
