@@ -30,7 +30,7 @@
  *      SO(2) x SO+(1,1) (azimuthal rotation x longitudinal boost).
  *  [L] lloca transformer_v2.Transformer.forward: 4-momenta energy-first.
  *
- * Readings taken where the pages are silent (each also listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - eps is a parameter (1e-8 in every workload); each feature is the log of
  *    its argument clamped below at eps.
  *  - y is the true rapidity 0.5 ln((E+pz)/(E-pz)), both arguments floored at

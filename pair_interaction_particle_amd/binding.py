@@ -60,8 +60,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libpip.so is not built (%s); run __graft_entry__.build()"
-                               % LIB_PATH)
+            raise RuntimeError("libpip.so is not built (%s); build it with "
+                               "python -m pair_interaction_particle_amd.build" % LIB_PATH)
         L = C.CDLL(LIB_PATH)
         vp, i64, i = C.c_void_p, C.c_int64, C.c_int
         L.pip_status_string.argtypes = [i]
