@@ -112,6 +112,30 @@ def test_packed_embed_writes_every_element(dtype):
             "packed U %s (NaN-filled output)" % dtype)
 
 
+def test_packed_embed_across_launch_segments():
+    # more than 65,536 jets: the launcher passes each segment its part of
+    # cu / u_off (rows and U offsets stay absolute); jets on both sides of the
+    # cut and a few early ones are compared with the oracle
+    B, P = 65536 + 40, 16
+    rng = np.random.default_rng(92)
+    ns = tuple(int(x) for x in rng.integers(0, 5, size=B))
+    p4, mask = jets(ns, P, seed=92)
+    params = mlp_for(92, biases=True)
+    mlp = pip.PairMLP(params)
+    cu = synth.cu_seqlens(mask)
+    U, uoff = pip.pair_embed_packed(g(synth.pack_rows(p4, mask)), g(cu), mlp)
+    Ug, uo = host(U), uoff.cpu().numpy()
+    sel = np.r_[0:24, 65536 - 24:B]
+    ref = oracle.pair_embed(p4[sel], mask[sel], params)
+    for i, b in enumerate(sel):
+        n = ns[b]
+        ld = pip.packed_ld(n)
+        blk = Ug[8 * uo[b]:8 * uo[b + 1]].reshape(8, n, ld)
+        assert_close(blk[:, :, :n], ref[i, :, :n, :n], TOL32, "packed U jet %d" % b)
+        pad = np.ascontiguousarray(blk[:, :, n:])
+        assert not pad.view(np.uint32).any(), "packed U jet %d: row padding not +0.0" % b
+
+
 def test_packed_kernel_workload_f32():
     d = synth.make_workload("kernel")
     mask, ns = d["mask"], d["n"]

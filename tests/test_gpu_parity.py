@@ -371,6 +371,24 @@ def test_pair_embed_bf16_ragged(B, P, ns):
     assert_zero_bits(U.transpose(0, 2, 3, 1), ~pair_mask(mask), "U bf16 padding")
 
 
+def test_pair_embed_across_launch_segments():
+    # more than 65,536 jets: the launcher cuts the batch into segments (p4,
+    # mask and U offset per segment); the jets on both sides of the cut and a
+    # few early ones are compared with the oracle (each jet is independent)
+    B, P = 65536 + 40, 16
+    rng = np.random.default_rng(91)
+    ns = tuple(int(x) for x in rng.integers(0, 5, size=B))
+    p4, mask = ragged_jets(B, P, ns, seed=91, hole=False)
+    params = mlp_for(91, biases=True)
+    mlp = pip.PairMLP(params)
+    Ud = pip.pair_embed(g(p4), g(mask), mlp)
+    sel = np.r_[0:24, 65536 - 24:B]
+    U = host(Ud[torch.from_numpy(sel).cuda()])
+    ref = oracle.pair_embed(p4[sel], mask[sel], params)
+    assert_close(U, ref, TOL32, "U across the 65,536-jet segment boundary")
+    assert_zero_bits(U, np.broadcast_to(~pair_mask(mask[sel])[:, None], U.shape), "U padded pairs")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_pair_embed_more_jets_than_threads(dtype):
     # B > 512: each entry of the in-kernel cost scan covers a range of jets, the
