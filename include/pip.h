@@ -225,7 +225,7 @@ pip_status pip_pair_bias_attention_backward(const void *Q, const void *K, const 
 /* Bytes of workspace pip_pair_mlp_backward needs: PIP_PAIR_MLP_FOLDED_GRADS
  * floats per (jet, row tile of 16) slot (S = B * P/16 slots) and per
  * workgroup of the fp16 x 2 kernel (Gx = 16 S for S < 16, else 256), one per
- * 32 of max(S, Gx) for the fixed-order reduction; then 2 Gx + S + 1 ints
+ * 32 of max(S, Gx) for the fixed-order reduction; then 3 Gx + S + 2 ints
  * (the workgroups' overflow flags and the plan of their shares). */
 size_t pip_pair_mlp_backward_workspace_bytes(int64_t B, int64_t P);
 

@@ -396,19 +396,29 @@ __device__ __forceinline__ uint32_t diag_row_blocks(uint32_t R, int a) {
 }
 
 // start[s] = blocks of the slots before s (s = jet * T + I), start[nslots] =
-// all blocks N; first[k] = the slot holding block floor(k N / G), where share
-// k of G begins.  One workgroup, jets in chunks of kPlanJets: each wave takes
+// all blocks N; share k of G is the blocks [bpos[k], bpos[k + 1]) (equal in
+// cost, kSlotCost above), and first[k] the slot holding block bpos[k].  One workgroup, jets in chunks of kPlanJets: each wave takes
 // the real bits of eight jets at a time (all loads issued first, then one
 // ballot per 64 particles) into LDS; then one thread per slot counts its
 // blocks.  The counts stay in LDS (in start[] beyond kPlanLds slots); each
 // thread then sums a run of slots, the run totals are scanned, and the runs
 // are written out as prefix sums.
 constexpr int kPlanThreads = 1024;
+// A workgroup's time follows its rounds: a slot's blocks in rounds of 8 plus
+// one round to drain the pipeline, and the slot's particle staging.  The
+// shares are equal in cost, a slot costing its blocks plus kSlotCost: with
+// equal block counts, a share cut into many slot pieces took up to 27 rounds
+// where the mean was 19 (kernel workload, 256 workgroups); with a slot cost
+// of 8 the largest takes 21.  Measured: 275.7 us with equal block counts,
+// 246.2, 234.4, 233.1, 237.1, 239.3 and 250.5 us for slot costs 4, 6, 8, 10,
+// 12 and 16.
+constexpr int kSlotCost = 8;
+__host__ __device__ constexpr int slot_cost(int blocks) { return blocks > 0 ? blocks + kSlotCost : 0; }
 constexpr int kPlanLds = 8192;   // slot counts kept in LDS up to this many slots
 constexpr int kPlanJets = 1024;  // jets whose real bits are in LDS at once
 __global__ __launch_bounds__(kPlanThreads) void mlp_bwd_plan_kernel(
     const uint8_t *__restrict__ mask, int B, int P, int G, int *__restrict__ start,
-    int *__restrict__ first) {
+    int *__restrict__ first, int *__restrict__ bpos) {
     __shared__ int wsum[kPlanThreads / 64];
     __shared__ int total;
     __shared__ int lcnt[kPlanLds];
@@ -452,42 +462,64 @@ __global__ __launch_bounds__(kPlanThreads) void mlp_bwd_plan_kernel(
     }
     const int per = (nslots + kPlanThreads - 1) / kPlanThreads;
     const int s0 = min(tid * per, nslots), s1 = min(s0 + per, nslots);
-    int mine = 0;
-    for (int s = s0; s < s1; ++s) mine += cnt[s];
-    // exclusive prefix of the run totals: within the wave, then across waves
-    int inc = mine;
+    // exclusive prefix of the run totals and the grand total: within the
+    // wave, then across waves (two passes: blocks, then costs)
+    auto scan = [&](int mine, int &excl) {
+        int inc = mine;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(inc, o);
-        if (lane >= o) inc += v;
-    }
-    if (lane == 63) wsum[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        int w = lane < kPlanThreads / 64 ? wsum[lane] : 0;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int v = __shfl_up(w, o);
-            if (lane >= o) w += v;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(inc, o);
+            if (lane >= o) inc += v;
         }
-        if (lane < kPlanThreads / 64) wsum[lane] = w;  // inclusive wave totals
-        if (lane == kPlanThreads / 64 - 1) total = w;
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
+        if (wave == 0) {
+            int w = lane < kPlanThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const int v = __shfl_up(w, o);
+                if (lane >= o) w += v;
+            }
+            if (lane < kPlanThreads / 64) wsum[lane] = w;  // inclusive wave totals
+            if (lane == kPlanThreads / 64 - 1) total = w;
+        }
+        __syncthreads();
+        excl = inc - mine + (wave > 0 ? wsum[wave - 1] : 0);
+        const int t = total;
+        __syncthreads();  // wsum and total are reused by the next pass
+        return t;
+    };
+    int mine = 0, minec = 0;
+    for (int s = s0; s < s1; ++s) {
+        mine += cnt[s];
+        minec += slot_cost(cnt[s]);
     }
-    __syncthreads();
-    const int N = total;
-    int acc = inc - mine + (wave > 0 ? wsum[wave - 1] : 0);
+    int acc, accc;
+    const int N = scan(mine, acc), Ct = scan(minec, accc);
     for (int s = s0; s < s1; ++s) {
         const int c = cnt[s];
         start[s] = acc;
         if (c > 0) {
-            // the shares that begin inside [acc, acc + c)
-            int k = (int)(((unsigned long long)acc * G + N - 1) / (unsigned)N);
-            for (; k < G && (int)((unsigned long long)k * N / (unsigned)G) < acc + c; ++k)
+            // the shares whose cost position floor(k Ct / G) falls inside this
+            // slot's cost range [accc, accc + kSlotCost + c): they begin at
+            // the slot's first block while inside its overhead, else in it
+            int k = (int)(((unsigned long long)accc * G + Ct - 1) / (unsigned)Ct);
+            for (; k < G; ++k) {
+                const int ck = (int)((unsigned long long)k * Ct / (unsigned)G);
+                if (ck >= accc + slot_cost(c)) break;
                 first[k] = s;
+                bpos[k] = acc + max(0, ck - accc - kSlotCost);
+            }
         }
         acc += c;
+        accc += slot_cost(c);
     }
-    if (tid == 0) start[nslots] = N;
+    if (Ct == 0)  // no block at all: every share is empty
+        for (int k = tid; k < G; k += kPlanThreads) bpos[k] = 0;
+    if (tid == 0) {
+        start[nslots] = N;
+        bpos[G] = N;
+    }
 }
 
 // ---------------------------------------------------------------- fp16 x 2 kernel
@@ -495,7 +527,7 @@ __global__ __launch_bounds__(kPlanThreads) void mlp_bwd_plan_kernel(
 // (v_mfma_f32_16x16x32_f16), each float32 factor carried as hi = fp16(x),
 // lo = fp16(x - hi) and x w = x_hi w_hi + x_hi w_lo + x_lo w_hi (relative
 // error ~2^-22 per product, float32 accumulation), as in the forward chain.
-// One 512-thread workgroup per compute unit takes an equal share of the
+// One 512-thread workgroup per compute unit takes an equal-cost share of the
 // flattened list of all slots' blocks with a real pair (mlp_bwd_plan_kernel
 // lays it out), slot by slot; the blocks go out in rounds, one per wave.
 // Per round:
@@ -607,7 +639,8 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
                   const float4 *__restrict__ w32, const float *__restrict__ wplain,
                   const float *__restrict__ bias, const float *__restrict__ dU,
                   const int *__restrict__ start, const int *__restrict__ first,
-                  float *__restrict__ partial, int *__restrict__ flags) {
+                  const int *__restrict__ bpos, float *__restrict__ partial,
+                  int *__restrict__ flags) {
     __shared__ XLds<kPP> L;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -632,9 +665,7 @@ mlp_bwd_x2_kernel(const float4 *__restrict__ p4, const uint8_t *__restrict__ mas
     // this workgroup's share [lo, hi) of the flattened list of every slot's
     // blocks with a real pair (slots s = jet * T + I in order; start[s] is
     // the first block of slot s, first[k] the slot where share k begins)
-    const long long N = start[nslots];
-    const long long lo = (long long)blockIdx.x * N / gridDim.x;
-    const long long hi = ((long long)blockIdx.x + 1) * N / gridDim.x;
+    const long long lo = bpos[blockIdx.x], hi = bpos[blockIdx.x + 1];
 
     v4f a3[2], a2[2], b3, b2, ax, b4;
     a3[0] = a3[1] = a2[0] = a2[1] = b3 = b2 = ax = b4 = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -978,7 +1009,7 @@ size_t mlp_bwd_workspace(int B, int P) {
     const size_t nslots = (size_t)B * (P / kTile), gx = (size_t)x2_groups((int)nslots);
     const size_t nchunks = (std::max(nslots, gx) + kRedChunk - 1) / kRedChunk;
     return (nslots + gx + nchunks) * kGradFloats * sizeof(float) +
-           (gx + nslots + 1 + gx) * sizeof(int);
+           (gx + nslots + 1 + gx + gx + 1) * sizeof(int);
 }
 
 hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P,
@@ -997,23 +1028,25 @@ hipError_t launch_mlp_bwd_f32(const float *p4, const uint8_t *mask, int B, int P
     float *px2 = p32 + (size_t)nslots * kGradFloats;
     float *chunk = px2 + (size_t)gx * kGradFloats;
     int *flags = (int *)(chunk + (size_t)nchunks * kGradFloats);
-    int *start = flags + gx, *first = start + nslots + 1;
+    int *start = flags + gx, *first = start + nslots + 1, *bpos = first + gx;
     // the fp16 x 2 path needs well-scaled weights and a block count within int
-    const bool x2 = m->f16ok && (long long)nslots * (16 * kTile + 9) < (1ll << 31);
+    const bool x2 = m->f16ok && (long long)nslots * slot_cost(16 * kTile + 9) < (1ll << 31);
     const int G = std::min(gx, cu_count());
     if (x2) {
         hipLaunchKernelGGL(mlp_bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, mask, B, P, G,
-                           start, first);
+                           start, first, bpos);
         if (P <= 128)
             hipLaunchKernelGGL(mlp_bwd_x2_kernel<128>, dim3((unsigned)G), dim3(kXThreads), 0, s,
                                (const float4 *)p4, mask, B, P, (const v8h *)m->wx2,
                                (const v8h *)m->wtx2, (const float4 *)m->w32, m->wplain, m->bias,
-                               dU, (const int *)start, (const int *)first, px2, flags);
+                               dU, (const int *)start, (const int *)first, (const int *)bpos,
+                               px2, flags);
         else
             hipLaunchKernelGGL(mlp_bwd_x2_kernel<256>, dim3((unsigned)G), dim3(kXThreads), 0, s,
                                (const float4 *)p4, mask, B, P, (const v8h *)m->wx2,
                                (const v8h *)m->wtx2, (const float4 *)m->w32, m->wplain, m->bias,
-                               dU, (const int *)start, (const int *)first, px2, flags);
+                               dU, (const int *)start, (const int *)first, (const int *)bpos,
+                               px2, flags);
     }
     const int *fl = x2 ? flags : nullptr;
     const dim3 g32((unsigned)nslots);

@@ -192,10 +192,11 @@ def test_pair_mlp_backward_workspace_bytes(L):
     # PIP_PAIR_MLP_FOLDED_GRADS floats per (jet, row tile) slot and per
     # fp16 x 2 workgroup (16 per slot up to 256), one per 32 of the larger
     # count for the fixed-order reduction; then ints: the workgroups' flags,
-    # the block plan (slots + 1 starts, one first slot per workgroup)
+    # the block plan (slots + 1 starts, one first slot per workgroup, and the
+    # workgroups' first blocks plus the end)
     f = L.pip_pair_mlp_backward_workspace_bytes
     for B, P in ((1, 16), (128, 128), (3, 256), (33, 48)):
         slots = B * (P // 16)
         gx = 16 * slots if slots < 16 else 256
         chunks = (max(slots, gx) + 31) // 32
-        assert f(B, P) == (slots + gx + chunks) * 9160 * 4 + (2 * gx + slots + 1) * 4
+        assert f(B, P) == (slots + gx + chunks) * 9160 * 4 + (3 * gx + slots + 2) * 4
