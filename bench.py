@@ -434,17 +434,16 @@ def measure(k, reps, warmup, cold):
         kind, work, peak = work_of(name, k["d"])
         prof = read_profile(name)
         extra = {"algorithmic_%s_per_launch" % ("flop" if kind == "mfma" else "bytes"): work}
-        if name in ("pair_embed_bf16", "pair_embed_int8") and prof and \
-                "valu_lane_ops_per_launch" in prof:
-            # the bf16 embed is bound by VALU issue (GELU), not by its bf16
-            # matrix cores: report the issued VALU lane-ops against the
-            # non-packed VALU peak beside the bf16 MFMA fraction
-            lane_ops = prof["valu_lane_ops_per_launch"]
-            extra["valu"] = {"bound": "alu", "achieved": lane_ops / (warm["median_us"] * 1e-6)
-                             / 1e12, "peak": PEAK_VALU_TLANEOPS, "unit": "T lane-ops/s (issued)",
-                             "frac": lane_ops / (warm["median_us"] * 1e-6) / 1e12
-                             / PEAK_VALU_TLANEOPS}
         out[name] = roofline(kind, work, warm, cld, prof, peak, extra)
+        if out[name].get("counter_bound") == "valu" and "valu_lane_ops_per_launch" in prof:
+            # the counters say VALU issue is the busiest unit (GELU, softmax,
+            # operand splits), whatever the matrix-core or HBM fraction above:
+            # the issued VALU lane-ops over the warm median against the
+            # non-packed VALU issue peak
+            lane_rate = prof["valu_lane_ops_per_launch"] / (warm["median_us"] * 1e-6) / 1e12
+            out[name]["valu"] = {"bound": "alu", "achieved": lane_rate,
+                                 "peak": PEAK_VALU_TLANEOPS, "unit": "T lane-ops/s (issued)",
+                                 "frac": lane_rate / PEAK_VALU_TLANEOPS}
         if name == "pair_embed_int8":
             out[name]["unit"] = "TOP/s"
     return out
