@@ -259,6 +259,19 @@ def roofline(kind, work, warm, cold, prof, peak, extra=None):
     return out
 
 
+def valu_roofline(block, prof, warm):
+    """When the counters of a roofline block say VALU issue is the busiest
+    unit (GELU, softmax, operand splits), whatever its matrix-core or HBM
+    fraction: the profile's issued VALU lane-ops per launch over the warm
+    median, against the non-packed VALU issue peak.  None otherwise."""
+    if not prof or block.get("counter_bound") != "valu" or \
+            "valu_lane_ops_per_launch" not in prof:
+        return None
+    lane_rate = prof["valu_lane_ops_per_launch"] / (warm["median_us"] * 1e-6) / 1e12
+    return {"bound": "alu", "achieved": lane_rate, "peak": PEAK_VALU_TLANEOPS,
+            "unit": "T lane-ops/s (issued)", "frac": lane_rate / PEAK_VALU_TLANEOPS}
+
+
 def to_dev(x, dtype=None):
     import numpy as np
     import torch
@@ -435,15 +448,9 @@ def measure(k, reps, warmup, cold):
         prof = read_profile(name)
         extra = {"algorithmic_%s_per_launch" % ("flop" if kind == "mfma" else "bytes"): work}
         out[name] = roofline(kind, work, warm, cld, prof, peak, extra)
-        if out[name].get("counter_bound") == "valu" and "valu_lane_ops_per_launch" in prof:
-            # the counters say VALU issue is the busiest unit (GELU, softmax,
-            # operand splits), whatever the matrix-core or HBM fraction above:
-            # the issued VALU lane-ops over the warm median against the
-            # non-packed VALU issue peak
-            lane_rate = prof["valu_lane_ops_per_launch"] / (warm["median_us"] * 1e-6) / 1e12
-            out[name]["valu"] = {"bound": "alu", "achieved": lane_rate,
-                                 "peak": PEAK_VALU_TLANEOPS, "unit": "T lane-ops/s (issued)",
-                                 "frac": lane_rate / PEAK_VALU_TLANEOPS}
+        vb = valu_roofline(out[name], prof, warm)
+        if vb:
+            out[name]["valu"] = vb
         if name == "pair_embed_int8":
             out[name]["unit"] = "TOP/s"
     return out
